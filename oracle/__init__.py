@@ -1,0 +1,149 @@
+"""CPU oracle for paged-attention decode, the paged KV write and the gather.
+
+TEST INFRASTRUCTURE: only the tests, ``__graft_entry__.smoke()`` and the
+bench's CPU-baseline leg may import this package.  The product path never
+calls it.  It wraps ``liboracle.so`` (built from ``paged_attention_oracle.c``
+by ``oracle/build.py``), a plain fp64 implementation that shares no code with
+the HIP library.
+
+Arrays are numpy, element data as stored bits (float32 for f32, uint16 for
+f16/bf16); dtype codes are 0 = f32, 1 = f16, 2 = bf16.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+from .build import LIBRARY, build
+
+_CODES = {"f32": 0, "f16": 1, "bf16": 2}
+
+
+def _code(dtype) -> int:
+    return _CODES[dtype] if isinstance(dtype, str) else int(dtype)
+
+
+def _ptr(a):
+    if a is None:
+        return None
+    assert a.flags["C_CONTIGUOUS"], "oracle arrays must be C-contiguous"
+    return a.ctypes.data_as(ctypes.c_void_p)
+
+
+class Oracle:
+    """ctypes wrapper around one build of the oracle library."""
+
+    def __init__(self, path: str):
+        lib = ctypes.CDLL(path)
+        vp, ci, cf = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
+        sig = {
+            "oracle_paged_attention_decode": [vp, vp, vp, vp, vp, cf] + [ci] * 7 + [vp, vp, ci],
+            "oracle_paged_attention_decode_partitioned": [vp, vp, vp, vp, vp, cf] + [ci] * 8 + [vp],
+            "oracle_kv_cache_write": [vp, vp, vp, vp, vp] + [ci] * 5,
+            "oracle_paged_kv_gather": [vp, vp, vp, vp, vp, vp] + [ci] * 7,
+            "oracle_elements_to_double": [vp, ctypes.c_int64, ci, vp],
+            "oracle_set_threads": [ci],
+            "oracle_max_threads": [],
+        }
+        for name, args in sig.items():
+            fn = getattr(lib, name)
+            fn.argtypes = args
+            fn.restype = ci if name == "oracle_max_threads" else None
+        self.lib = lib
+        self.path = path
+
+    def max_threads(self) -> int:
+        return self.lib.oracle_max_threads()
+
+    def set_threads(self, n: int) -> None:
+        self.lib.oracle_set_threads(int(n))
+
+    def elements_to_double(self, bits: np.ndarray, dtype) -> np.ndarray:
+        bits = np.ascontiguousarray(bits)
+        out = np.empty(bits.size, dtype=np.float64)
+        self.lib.oracle_elements_to_double(_ptr(bits), bits.size, _code(dtype), _ptr(out))
+        return out.reshape(bits.shape)
+
+    def paged_attention_decode(self, query, key_cache, value_cache, block_tables,
+                               context_lens, scale, dtype, *, return_weights=False):
+        """fp64 decode attention -> out [S, Hq, D] (and weights [S, Hq, max L])."""
+        S, Hq, D = query.shape
+        nb, bs, Hkv, D2 = key_cache.shape
+        assert D2 == D and value_cache.shape == key_cache.shape and Hq % Hkv == 0
+        bt = np.ascontiguousarray(block_tables, dtype=np.int32)
+        cl = np.ascontiguousarray(context_lens, dtype=np.int32)
+        out = np.empty((S, Hq, D), dtype=np.float64)
+        wstride = max(1, int(cl.max()) if S else 1)
+        weights = np.zeros((S, Hq, wstride), dtype=np.float64) if return_weights else None
+        self.lib.oracle_paged_attention_decode(
+            _ptr(query), _ptr(key_cache), _ptr(value_cache), _ptr(bt), _ptr(cl),
+            ctypes.c_float(scale), S, Hq, Hkv, D, bs, bt.shape[1], _code(dtype), _ptr(out),
+            _ptr(weights), wstride)
+        return (out, weights) if return_weights else out
+
+    def paged_attention_decode_partitioned(self, query, key_cache, value_cache, block_tables,
+                                           context_lens, scale, dtype, partition_size):
+        S, Hq, D = query.shape
+        nb, bs, Hkv, _ = key_cache.shape
+        bt = np.ascontiguousarray(block_tables, dtype=np.int32)
+        cl = np.ascontiguousarray(context_lens, dtype=np.int32)
+        out = np.empty((S, Hq, D), dtype=np.float64)
+        self.lib.oracle_paged_attention_decode_partitioned(
+            _ptr(query), _ptr(key_cache), _ptr(value_cache), _ptr(bt), _ptr(cl),
+            ctypes.c_float(scale), S, Hq, Hkv, D, bs, bt.shape[1], _code(dtype),
+            int(partition_size), _ptr(out))
+        return out
+
+    def kv_cache_write(self, key, value, slot_mapping, key_cache, value_cache, dtype):
+        """Writes into key_cache / value_cache in place."""
+        T, Hkv, D = key.shape
+        nb, bs, Hkv2, D2 = key_cache.shape
+        assert (Hkv2, D2) == (Hkv, D)
+        sm = np.ascontiguousarray(slot_mapping, dtype=np.int32)
+        self.lib.oracle_kv_cache_write(_ptr(key), _ptr(value), _ptr(sm), _ptr(key_cache),
+                                       _ptr(value_cache), T, Hkv, D, bs, _code(dtype))
+
+    def paged_kv_gather(self, key_cache, value_cache, block_tables, context_lens,
+                        max_context_len, dtype, fill=0):
+        nb, bs, Hkv, D = key_cache.shape
+        bt = np.ascontiguousarray(block_tables, dtype=np.int32)
+        cl = np.ascontiguousarray(context_lens, dtype=np.int32)
+        S = bt.shape[0]
+        out_k = np.full((S, max_context_len, Hkv, D), fill, dtype=key_cache.dtype)
+        out_v = np.full((S, max_context_len, Hkv, D), fill, dtype=key_cache.dtype)
+        self.lib.oracle_paged_kv_gather(_ptr(key_cache), _ptr(value_cache), _ptr(bt), _ptr(cl),
+                                        _ptr(out_k), _ptr(out_v), S, Hkv, D, bs, bt.shape[1],
+                                        int(max_context_len), _code(dtype))
+        return out_k, out_v
+
+    # ---- conveniences on a workloads.DecodeBatch ----
+    def decode_batch(self, batch, *, return_weights=False):
+        return self.paged_attention_decode(batch.query, batch.key_cache, batch.value_cache,
+                                           batch.block_tables, batch.context_lens, batch.scale,
+                                           batch.dtype, return_weights=return_weights)
+
+    def write_batch(self, batch):
+        """Apply the batch's KV write to its own pool (in place)."""
+        self.kv_cache_write(batch.new_key, batch.new_value, batch.slot_mapping,
+                            batch.key_cache, batch.value_cache, batch.dtype)
+
+
+_default = None
+
+
+def default() -> Oracle:
+    global _default
+    if _default is None:
+        if not os.path.exists(LIBRARY):
+            build()
+        _default = Oracle(LIBRARY)
+    return _default
+
+
+def __getattr__(name):
+    # module-level access to the default instance's methods: oracle.decode_batch(...)
+    if name.startswith("_"):
+        raise AttributeError(name)
+    return getattr(default(), name)

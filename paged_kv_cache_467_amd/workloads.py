@@ -1,0 +1,329 @@
+"""Seeded synthetic decode batches for paged attention.
+
+This module only builds inputs: sequence lengths, block tables, the K/V pool,
+the new tokens to be written and their slot_mapping.  It holds none of the
+attention arithmetic, and it is the one module that both the HIP path's tests
+and the CPU oracle are fed from.
+
+The layout follows the pages:
+  * key_cache / value_cache are ``[num_blocks, block_size, num_kv_heads,
+    head_dim]`` ("vLLM 源码解析 一", §三, the paged_attention_v1 description);
+  * ``block_tables[s]`` lists the physical blocks of sequence ``s`` in logical
+    order ("23.1 vLLM：高吞吐推理框架原理与部署", §二.2, steps 1-3);
+  * ``slot_mapping[t]`` names the cell that new token ``t`` is written to
+    ("大模型推理框架VLLM-0.7.3源码", §2.1), encoded as
+    ``physical_block * block_size + offset`` to match the pool's two leading
+    dimensions.
+
+Element data are carried as raw bits: ``float32`` arrays for f32 and
+``uint16`` arrays for f16 / bf16, so that every consumer reads the very same
+bits.  Values are standard normal float32 samples, cast round-to-nearest-even.
+
+Five named workloads stand in for the situations the pages describe (a tiny
+unit case, a Llama-3-8B-shaped GQA batch, a Llama-13B-shaped MHA batch, a
+32K-token long-context batch and a shared-prefix batch); ``make_custom``
+builds arbitrary small shapes for property tests.
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass, field
+
+import numpy as np
+
+# dtype name -> (code used at the C boundary, bytes per element)
+DTYPE_CODES = {"f32": 0, "f16": 1, "bf16": 2}
+DTYPE_BYTES = {"f32": 4, "f16": 2, "bf16": 2}
+NAN_BITS = {"f32": np.float32(np.nan), "f16": np.uint16(0x7E00), "bf16": np.uint16(0x7FC0)}
+
+
+def f32_to_bits(x: np.ndarray, dtype: str) -> np.ndarray:
+    """Cast float32 samples to the storage dtype, round-to-nearest-even."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    if dtype == "f32":
+        return x
+    if dtype == "f16":
+        return x.astype(np.float16).view(np.uint16)
+    if dtype == "bf16":
+        u = x.view(np.uint32).astype(np.uint64)
+        # round half to even on the 16 dropped bits (inputs are finite)
+        u = u + 0x7FFF + ((u >> 16) & 1)
+        return (u >> 16).astype(np.uint16)
+    raise ValueError(dtype)
+
+
+def bits_to_f32(b: np.ndarray, dtype: str) -> np.ndarray:
+    """Widen stored bits to float32 (exact for all three dtypes)."""
+    if dtype == "f32":
+        return np.asarray(b, dtype=np.float32)
+    if dtype == "f16":
+        return np.asarray(b, dtype=np.uint16).view(np.float16).astype(np.float32)
+    if dtype == "bf16":
+        return (np.asarray(b, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32)
+    raise ValueError(dtype)
+
+
+def storage_dtype(dtype: str):
+    return np.float32 if dtype == "f32" else np.uint16
+
+
+@dataclass
+class DecodeBatch:
+    """One decode step's inputs: a paged K/V pool, its block tables and the
+    new tokens (one per sequence) that the step writes before attending."""
+
+    name: str
+    dtype: str
+    num_seqs: int
+    num_q_heads: int
+    num_kv_heads: int
+    head_dim: int
+    block_size: int
+    num_blocks: int
+    max_blocks_per_seq: int
+    scale: float                     # a float32 value
+    query: np.ndarray                # [S, Hq, D] bits
+    key_cache: np.ndarray            # [num_blocks, bs, Hkv, D] bits
+    value_cache: np.ndarray          # [num_blocks, bs, Hkv, D] bits
+    block_tables: np.ndarray         # [S, max_blocks_per_seq] int32
+    context_lens: np.ndarray         # [S] int32
+    new_key: np.ndarray              # [T, Hkv, D] bits
+    new_value: np.ndarray            # [T, Hkv, D] bits
+    slot_mapping: np.ndarray         # [T] int32
+    referenced_blocks: np.ndarray    # sorted unique block ids reachable from block_tables
+    seed: int = 0
+    meta: dict = field(default_factory=dict)
+
+    @property
+    def dtype_code(self) -> int:
+        return DTYPE_CODES[self.dtype]
+
+    @property
+    def elem_bytes(self) -> int:
+        return DTYPE_BYTES[self.dtype]
+
+    @property
+    def max_context_len(self) -> int:
+        return int(self.context_lens.max()) if self.num_seqs else 0
+
+    @property
+    def group(self) -> int:
+        return self.num_q_heads // self.num_kv_heads
+
+    def copy(self) -> "DecodeBatch":
+        out = DecodeBatch(**{k: (v.copy() if isinstance(v, np.ndarray) else v)
+                             for k, v in self.__dict__.items() if k != "meta"})
+        out.meta = dict(self.meta)
+        return out
+
+    # ---- byte accounting used by the bench (algorithmic, not measured) ----
+    def decode_algorithmic_bytes(self) -> int:
+        """K and V rows of positions [0, L_s) for every kv head, the query
+        read and the output written, the block-table entries used and the
+        context lengths."""
+        e = self.elem_bytes
+        L = self.context_lens.astype(np.int64)
+        kv = int(L.sum()) * self.num_kv_heads * self.head_dim * e * 2
+        qo = 2 * self.num_seqs * self.num_q_heads * self.head_dim * e
+        bt = int(np.sum((L + self.block_size - 1) // self.block_size)) * 4
+        return kv + qo + bt + 4 * self.num_seqs
+
+    def write_algorithmic_bytes(self) -> int:
+        t = len(self.slot_mapping)
+        row = self.num_kv_heads * self.head_dim * self.elem_bytes
+        return t * row * 2 * 2 + 4 * t
+
+    def decode_flops(self) -> int:
+        return int(self.context_lens.astype(np.int64).sum()) * self.num_q_heads * 4 * self.head_dim
+
+
+def _normal_bits(rng: np.random.Generator, shape, dtype: str) -> np.ndarray:
+    return f32_to_bits(rng.standard_normal(size=shape, dtype=np.float32), dtype)
+
+
+def _assemble(name, dtype, rng, *, S, Hq, Hkv, D, bs, lens, tables, num_blocks,
+              max_blocks, scale, poison, seed, meta=None, keys_identical=False):
+    """Fill the pool rows that block tables reach, poison or zero the rest,
+    draw queries and the new tokens, and derive slot_mapping for a write of
+    one new token per sequence at position L_s - 1."""
+    sd = storage_dtype(dtype)
+    lens = np.asarray(lens, dtype=np.int32)
+    bt = np.asarray(tables, dtype=np.int32)
+    assert bt.shape == (S, max_blocks)
+    referenced = set()
+    for s in range(S):
+        nb = (int(lens[s]) + bs - 1) // bs
+        referenced.update(int(b) for b in bt[s, :nb])
+    referenced = np.array(sorted(referenced), dtype=np.int64)
+
+    fill = NAN_BITS[dtype] if poison else sd(0)
+    key_cache = np.full((num_blocks, bs, Hkv, D), fill, dtype=sd)
+    value_cache = np.full((num_blocks, bs, Hkv, D), fill, dtype=sd)
+    if len(referenced):
+        key_cache[referenced] = _normal_bits(rng, (len(referenced), bs, Hkv, D), dtype)
+        value_cache[referenced] = _normal_bits(rng, (len(referenced), bs, Hkv, D), dtype)
+    if poison:
+        # Tail slots of each sequence's last block hold stale data: positions
+        # >= L_s must never be read, so make them NaN as well.  Shared blocks
+        # are only ever shared whole (the prefix), so this never hits a slot
+        # that another sequence uses.
+        used = np.zeros((num_blocks, bs), dtype=bool)
+        for s in range(S):
+            L = int(lens[s])
+            nb = (L + bs - 1) // bs
+            for i in range(nb):
+                n = min(bs, L - i * bs)
+                used[bt[s, i], :n] = True
+        key_cache[~used] = NAN_BITS[dtype]
+        value_cache[~used] = NAN_BITS[dtype]
+    query = _normal_bits(rng, (S, Hq, D), dtype)
+    if keys_identical:
+        one = _normal_bits(rng, (Hkv, D), dtype)
+        for b in referenced:
+            key_cache[b] = one[None]
+    new_key = _normal_bits(rng, (S, Hkv, D), dtype)
+    new_value = _normal_bits(rng, (S, Hkv, D), dtype)
+    slots = np.empty(S, dtype=np.int32)
+    for s in range(S):
+        L = int(lens[s])
+        if L <= 0:
+            slots[s] = -1          # nothing to write for an empty sequence
+            continue
+        j = L - 1
+        slots[s] = int(bt[s, j // bs]) * bs + j % bs
+    return DecodeBatch(
+        name=name, dtype=dtype, num_seqs=S, num_q_heads=Hq, num_kv_heads=Hkv,
+        head_dim=D, block_size=bs, num_blocks=num_blocks, max_blocks_per_seq=max_blocks,
+        scale=float(np.float32(scale)), query=query, key_cache=key_cache,
+        value_cache=value_cache, block_tables=bt, context_lens=lens, new_key=new_key,
+        new_value=new_value, slot_mapping=slots, referenced_blocks=referenced,
+        seed=seed, meta=dict(meta or {}))
+
+
+def _deal_tables(rng, lens, bs, max_blocks, pool_factor=1.5, min_pool=None):
+    """Each sequence gets ceil(L/bs) blocks drawn, in order, from one random
+    permutation of the pool; unused table entries point at a block no
+    sequence uses (so that a stray read of padding lands on poisoned data)."""
+    S = len(lens)
+    need = [(int(L) + bs - 1) // bs for L in lens]
+    total = sum(need)
+    pool = int(math.ceil(pool_factor * total))
+    if min_pool is not None:
+        pool = max(pool, min_pool)
+    pool = max(pool, total + 1)
+    perm = rng.permutation(pool)
+    free_block = int(perm[total])
+    tables = np.full((S, max_blocks), free_block, dtype=np.int32)
+    k = 0
+    for s in range(S):
+        assert need[s] <= max_blocks
+        tables[s, :need[s]] = perm[k:k + need[s]]
+        k += need[s]
+    return tables, pool
+
+
+WORKLOADS = ("tiny_f32", "llama3_8b_gqa_bf16", "llama13b_mha_f16",
+             "long_context_bf16", "shared_prefix_bf16")
+
+
+def make_workload(name: str, seed: int | None = None, poison: bool = False) -> DecodeBatch:
+    """Build one of the five named workloads (seed defaults to 46700 + index)."""
+    idx = WORKLOADS.index(name)
+    seed = 46700 + idx + 1 if seed is None else seed
+    rng = np.random.default_rng(seed)
+    if name == "tiny_f32":
+        S, Hq, Hkv, D, bs, pool, mb = 4, 4, 4, 64, 16, 64, 7
+        lens = [1, 17, 33, 100]
+        tables, _ = _deal_tables(rng, lens, bs, mb, min_pool=pool)
+        tables_pool = pool
+        return _assemble(name, "f32", rng, S=S, Hq=Hq, Hkv=Hkv, D=D, bs=bs, lens=lens,
+                         tables=tables, num_blocks=tables_pool, max_blocks=mb,
+                         scale=1.0 / math.sqrt(64), poison=poison, seed=seed)
+    if name == "llama3_8b_gqa_bf16":
+        S, Hq, Hkv, D, bs, mb = 256, 32, 8, 128, 16, 40
+        lens = rng.integers(512, 640, size=S, endpoint=True)
+        tables, pool = _deal_tables(rng, lens, bs, mb)
+        return _assemble(name, "bf16", rng, S=S, Hq=Hq, Hkv=Hkv, D=D, bs=bs, lens=lens,
+                         tables=tables, num_blocks=pool, max_blocks=mb,
+                         scale=1.0 / math.sqrt(D), poison=poison, seed=seed)
+    if name == "llama13b_mha_f16":
+        S, Hq, Hkv, D, bs, mb = 50, 40, 40, 128, 16, 128
+        lens = rng.integers(1, 2048, size=S, endpoint=True)
+        tables, pool = _deal_tables(rng, lens, bs, mb)
+        return _assemble(name, "f16", rng, S=S, Hq=Hq, Hkv=Hkv, D=D, bs=bs, lens=lens,
+                         tables=tables, num_blocks=pool, max_blocks=mb,
+                         scale=1.0 / math.sqrt(D), poison=poison, seed=seed)
+    if name == "long_context_bf16":
+        S, Hq, Hkv, D, bs, mb = 8, 32, 8, 128, 32, 1024
+        lens = rng.integers(24576, 32768, size=S, endpoint=True)
+        tables, pool = _deal_tables(rng, lens, bs, mb)
+        return _assemble(name, "bf16", rng, S=S, Hq=Hq, Hkv=Hkv, D=D, bs=bs, lens=lens,
+                         tables=tables, num_blocks=pool, max_blocks=mb,
+                         scale=1.0 / math.sqrt(D), poison=poison, seed=seed)
+    if name == "shared_prefix_bf16":
+        S, Hq, Hkv, D, bs = 64, 32, 8, 128, 16
+        prefix_blocks = 125                     # 2000 tokens
+        z = rng.standard_normal(S)
+        suffix = np.clip(np.rint(np.exp(math.log(64.0) + 0.5 * z)), 16, 256).astype(np.int64)
+        priv = (suffix + bs - 1) // bs
+        mb = prefix_blocks + 16
+        total = prefix_blocks + int(priv.sum())
+        pool = int(math.ceil(1.5 * total))
+        perm = rng.permutation(pool)
+        prefix = perm[:prefix_blocks]
+        free_block = int(perm[total])
+        tables = np.full((S, mb), free_block, dtype=np.int32)
+        k = prefix_blocks
+        for s in range(S):
+            tables[s, :prefix_blocks] = prefix
+            tables[s, prefix_blocks:prefix_blocks + priv[s]] = perm[k:k + priv[s]]
+            k += int(priv[s])
+        lens = prefix_blocks * bs + suffix
+        return _assemble(name, "bf16", rng, S=S, Hq=Hq, Hkv=Hkv, D=D, bs=bs, lens=lens,
+                         tables=tables, num_blocks=pool, max_blocks=mb,
+                         scale=1.0 / math.sqrt(D), poison=poison, seed=seed,
+                         meta={"prefix_blocks": prefix_blocks})
+    raise ValueError(name)
+
+
+def make_custom(seed: int, *, dtype="f32", num_seqs=2, num_q_heads=2, num_kv_heads=1,
+                head_dim=64, block_size=16, context_lens=(5, 20), extra_blocks=3,
+                max_blocks_per_seq=None, poison=False, scale=None,
+                keys_identical=False) -> DecodeBatch:
+    """A small batch of any shape: blocks dealt from a random permutation of a
+    pool with ``extra_blocks`` spare blocks."""
+    rng = np.random.default_rng(seed)
+    lens = np.asarray(context_lens, dtype=np.int64)
+    assert len(lens) == num_seqs
+    need = [(int(L) + block_size - 1) // block_size for L in lens]
+    mb = max_blocks_per_seq if max_blocks_per_seq is not None else max(1, max(need))
+    tables, pool = _deal_tables(rng, lens, block_size, mb, pool_factor=1.0,
+                                min_pool=sum(need) + max(1, extra_blocks))
+    if scale is None:
+        scale = 1.0 / math.sqrt(head_dim)
+    return _assemble(f"custom{seed}", dtype, rng, S=num_seqs, Hq=num_q_heads,
+                     Hkv=num_kv_heads, D=head_dim, bs=block_size, lens=lens,
+                     tables=tables, num_blocks=pool, max_blocks=mb, scale=scale,
+                     poison=poison, seed=seed, keys_identical=keys_identical)
+
+
+def permute_blocks(batch: DecodeBatch, seed: int) -> DecodeBatch:
+    """Relabel physical blocks by a random permutation pi: pool row b moves
+    to pi[b] and every table entry b becomes pi[b].  The logical contents of
+    every sequence are unchanged."""
+    rng = np.random.default_rng(seed)
+    pi = rng.permutation(batch.num_blocks).astype(np.int64)
+    out = batch.copy()
+    out.key_cache = np.empty_like(batch.key_cache)
+    out.value_cache = np.empty_like(batch.value_cache)
+    out.key_cache[pi] = batch.key_cache
+    out.value_cache[pi] = batch.value_cache
+    out.block_tables = pi[batch.block_tables].astype(np.int32)
+    bs = batch.block_size
+    sl = batch.slot_mapping.astype(np.int64)
+    ok = sl >= 0
+    new_sl = sl.copy()
+    new_sl[ok] = pi[sl[ok] // bs] * bs + sl[ok] % bs
+    out.slot_mapping = new_sl.astype(np.int32)
+    out.referenced_blocks = np.sort(pi[batch.referenced_blocks])
+    return out

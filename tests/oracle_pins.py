@@ -1,0 +1,344 @@
+"""Pins for the CPU oracle: checks against facts other than the oracle itself.
+
+Each ``pin_*`` function takes an ``oracle.Oracle`` instance and raises
+``AssertionError`` when the oracle disagrees with what the pages or the
+mathematics fix: worked expansions of the pages' addressing, closed forms,
+a textbook library routine (PyTorch's scaled_dot_product_attention in fp64 on
+the CPU), exact invariants, and brute force on tiny inputs.  The same
+functions run against deliberately broken copies of the oracle in
+``test_oracle_mutants.py`` to show that a plausible slip fails at least one
+of them.
+"""
+from __future__ import annotations
+
+import json
+import math
+import os
+
+import numpy as np
+
+from paged_kv_cache_467_amd import workloads as W
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def load_facts():
+    with open(os.path.join(GOLDEN, "pages_facts.json")) as f:
+        return json.load(f)
+
+
+def _f64(bits, dtype):
+    with np.errstate(invalid="ignore"):
+        return W.bits_to_f32(bits, dtype).astype(np.float64)
+
+
+# ---------------------------------------------------------------- elements
+def pin_element_decode(orc):
+    """Widening of stored bits to fp64 matches numpy for every f16 and bf16
+    bit pattern, and is exact for f32."""
+    allbits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    for dt in ("f16", "bf16"):
+        got = orc.elements_to_double(allbits, dt)
+        ref = _f64(allbits, dt)
+        nan = np.isnan(ref)
+        assert np.array_equal(np.isnan(got), nan), dt
+        assert np.array_equal(got[~nan], ref[~nan]), dt
+    x = np.random.default_rng(1).standard_normal(4096).astype(np.float32)
+    x[:4] = [0.0, -0.0, 1e-45, 3.4e38]
+    assert np.array_equal(orc.elements_to_double(x, "f32"), x.astype(np.float64))
+
+
+# -------------------------------------------------------------- addressing
+def pin_addressing_worked_example(orc):
+    """The pages' addressing (block_id = blocks[j // block_size], offset =
+    j % block_size) expanded by hand for two small block tables, checked on a
+    pool whose every element carries its own (block, offset, head, dim)."""
+    facts = load_facts()
+    assert facts["pool_axes"]["value"] == ["num_blocks", "block_size", "num_heads", "head_dim"]
+    nb, bs, H, D = 8, 4, 2, 3
+    b, o, h, d = np.meshgrid(np.arange(nb), np.arange(bs), np.arange(H), np.arange(D),
+                             indexing="ij")
+    tag = (b * 1000 + o * 100 + h * 10 + d).astype(np.float32)
+    kc = np.ascontiguousarray(tag)
+    vc = np.ascontiguousarray(-tag)
+    tables = np.array([[7, 2, 5], [3, 0, 1]], dtype=np.int32)
+    lens = np.array([10, 5], dtype=np.int32)
+    # hand expansion of block_tables[s][j // 4], j % 4
+    expect = [
+        [(7, 0), (7, 1), (7, 2), (7, 3), (2, 0), (2, 1), (2, 2), (2, 3), (5, 0), (5, 1)],
+        [(3, 0), (3, 1), (3, 2), (3, 3), (0, 0)],
+    ]
+    gk, gv = orc.paged_kv_gather(kc, vc, tables, lens, 10, "f32", fill=np.float32(-1))
+    for s in range(2):
+        for j in range(10):
+            if j < lens[s]:
+                blk, off = expect[s][j]
+                want = blk * 1000 + off * 100 + np.arange(H)[:, None] * 10 + np.arange(D)[None, :]
+                assert np.array_equal(gk[s, j], want.astype(np.float32)), (s, j)
+                assert np.array_equal(gv[s, j], -want.astype(np.float32)), (s, j)
+            else:
+                assert np.all(gk[s, j] == -1) and np.all(gv[s, j] == -1), (s, j)
+    # slot encoding: cell (block 7, offset 1) is slot 29, (3, 2) is slot 14
+    kc2, vc2 = kc.copy(), vc.copy()
+    new_k = np.full((2, H, D), 0.5, dtype=np.float32)
+    new_k[1] = 0.25
+    orc.kv_cache_write(new_k, -new_k, np.array([29, 14], np.int32), kc2, vc2, "f32")
+    assert np.all(kc2[7, 1] == 0.5) and np.all(vc2[7, 1] == -0.5)
+    assert np.all(kc2[3, 2] == 0.25) and np.all(vc2[3, 2] == -0.25)
+    changed = np.any(kc2 != kc, axis=(2, 3))
+    assert set(zip(*np.nonzero(changed))) == {(7, 1), (3, 2)}
+
+
+def pin_shared_prefix_blocks(orc):
+    """A 2000-token prompt in 16-token blocks spans 125 blocks, shared whole
+    by every sequence; each sequence's gather returns the prefix unchanged."""
+    facts = load_facts()
+    bs = facts["default_block_size"]["value"]
+    prompt = facts["shared_prompt_tokens"]["value"]
+    assert prompt % bs == 0 and prompt // bs == 125
+    rng = np.random.default_rng(3)
+    nb = 140
+    prefix = rng.permutation(nb)[:125]
+    kc = rng.standard_normal((nb, bs, 1, 2)).astype(np.float32)
+    vc = rng.standard_normal((nb, bs, 1, 2)).astype(np.float32)
+    tables = np.stack([prefix, prefix]).astype(np.int32)
+    lens = np.array([prompt, prompt - 7], dtype=np.int32)
+    gk, gv = orc.paged_kv_gather(kc, vc, tables, lens, prompt, "f32")
+    assert np.array_equal(gk[0].reshape(125, bs, 1, 2), kc[prefix])
+    assert np.array_equal(gk[1, :prompt - 7], gk[0, :prompt - 7])
+    assert np.array_equal(gv[0].reshape(125, bs, 1, 2), vc[prefix])
+
+
+def pin_write_gather_roundtrip(orc):
+    """Writing each sequence's new token through slot_mapping, then gathering
+    through the block table, returns the new bits at position L-1 and leaves
+    every other gathered position and every other pool cell unchanged."""
+    for seed, dt, bs in ((11, "f32", 4), (12, "bf16", 16), (13, "f16", 1)):
+        bt = W.make_custom(seed, dtype=dt, num_seqs=3, num_q_heads=4, num_kv_heads=2,
+                           head_dim=8, block_size=bs, context_lens=(1, 9, 23))
+        maxL = bt.max_context_len
+        k0, v0 = orc.paged_kv_gather(bt.key_cache, bt.value_cache, bt.block_tables,
+                                     bt.context_lens, maxL, dt)
+        kc, vc = bt.key_cache.copy(), bt.value_cache.copy()
+        orc.kv_cache_write(bt.new_key, bt.new_value, bt.slot_mapping, kc, vc, dt)
+        k1, v1 = orc.paged_kv_gather(kc, vc, bt.block_tables, bt.context_lens, maxL, dt)
+        for s in range(3):
+            L = int(bt.context_lens[s])
+            assert np.array_equal(k1[s, L - 1], bt.new_key[s]), (dt, s)
+            assert np.array_equal(v1[s, L - 1], bt.new_value[s]), (dt, s)
+            assert np.array_equal(k1[s, :L - 1], k0[s, :L - 1]), (dt, s)
+            assert np.array_equal(v1[s, :L - 1], v0[s, :L - 1]), (dt, s)
+        # every other cell of the pool is untouched
+        flat = np.ones(bt.num_blocks * bs, dtype=bool)
+        flat[bt.slot_mapping[bt.slot_mapping >= 0]] = False
+        m = flat.reshape(bt.num_blocks, bs)
+        assert np.array_equal(kc[m].view(np.uint8), bt.key_cache[m].view(np.uint8))
+        assert np.array_equal(vc[m].view(np.uint8), bt.value_cache[m].view(np.uint8))
+        # a negative slot writes nothing
+        kc2 = bt.key_cache.copy()
+        orc.kv_cache_write(bt.new_key[:1], bt.new_value[:1], np.array([-1], np.int32), kc2,
+                           bt.value_cache.copy(), dt)
+        assert np.array_equal(kc2.view(np.uint8), bt.key_cache.view(np.uint8))
+
+
+# ------------------------------------------------------------- attention
+def _sdpa_reference(orc, batch):
+    """softmax(scale * q K^T) V per sequence, by torch's CPU fp64 routine on
+    the contiguous K/V gathered through the block table."""
+    import torch
+    import torch.nn.functional as F
+
+    L = batch.context_lens
+    gk, gv = orc.paged_kv_gather(batch.key_cache, batch.value_cache, batch.block_tables, L,
+                                 max(1, batch.max_context_len), batch.dtype)
+    out = np.zeros((batch.num_seqs, batch.num_q_heads, batch.head_dim))
+    q = _f64(batch.query, batch.dtype)
+    for s in range(batch.num_seqs):
+        n = int(L[s])
+        if n <= 0:
+            continue
+        k = torch.from_numpy(_f64(gk[s, :n], batch.dtype)).permute(1, 0, 2)[None]
+        v = torch.from_numpy(_f64(gv[s, :n], batch.dtype)).permute(1, 0, 2)[None]
+        qs = torch.from_numpy(q[s])[None, :, None, :]
+        o = F.scaled_dot_product_attention(qs, k.contiguous(), v.contiguous(),
+                                           scale=float(batch.scale), enable_gqa=True)
+        out[s] = o[0, :, 0, :].numpy()
+    return out
+
+
+SHAPES = [
+    # seed, dtype, S, Hq, Hkv, D, bs, lens
+    (21, "f32", 3, 4, 4, 8, 4, (1, 5, 13)),
+    (22, "bf16", 2, 8, 2, 64, 16, (17, 80)),
+    (23, "f16", 4, 4, 1, 8, 1, (3, 1, 9, 30)),
+    (24, "f32", 2, 6, 3, 16, 16, (16, 33)),
+    (25, "bf16", 3, 4, 2, 64, 32, (64, 31, 65)),
+]
+
+
+def pin_decode_vs_sdpa(orc):
+    for seed, dt, S, Hq, Hkv, D, bs, lens in SHAPES:
+        b = W.make_custom(seed, dtype=dt, num_seqs=S, num_q_heads=Hq, num_kv_heads=Hkv,
+                          head_dim=D, block_size=bs, context_lens=lens)
+        got = orc.decode_batch(b)
+        ref = _sdpa_reference(orc, b)
+        err = np.abs(got - ref).max()
+        assert err <= 1e-12 * max(1.0, np.abs(ref).max()), (seed, err)
+
+
+def pin_tiny_workload_vs_sdpa(orc):
+    b = W.make_workload("tiny_f32")
+    got = orc.decode_batch(b)
+    ref = _sdpa_reference(orc, b)
+    assert np.abs(got - ref).max() <= 1e-12
+
+
+def pin_context_len_one(orc):
+    """One cached token: its weight is exactly 1, so the output is its V row."""
+    for dt in ("f32", "f16", "bf16"):
+        b = W.make_custom(31, dtype=dt, num_seqs=3, num_q_heads=4, num_kv_heads=2, head_dim=16,
+                          block_size=4, context_lens=(1, 1, 1))
+        out = orc.decode_batch(b)
+        for s in range(3):
+            blk = b.block_tables[s, 0]
+            v = _f64(b.value_cache[blk, 0], dt)            # [Hkv, D]
+            for h in range(4):
+                assert np.array_equal(out[s, h], v[h // 2]), (dt, s, h)
+
+
+def pin_identical_keys(orc):
+    """All keys equal -> all scores equal -> the output is the mean of V."""
+    b = W.make_custom(32, dtype="bf16", num_seqs=2, num_q_heads=4, num_kv_heads=1, head_dim=32,
+                      block_size=4, context_lens=(7, 29), keys_identical=True)
+    out = orc.decode_batch(b)
+    _, gv = orc.paged_kv_gather(b.key_cache, b.value_cache, b.block_tables, b.context_lens,
+                                b.max_context_len, "bf16")
+    for s in range(2):
+        L = int(b.context_lens[s])
+        mean = _f64(gv[s, :L], "bf16").mean(axis=0)   # [Hkv, D]
+        for h in range(4):
+            assert np.abs(out[s, h] - mean[0]).max() <= 1e-12
+
+
+def pin_two_token_logistic(orc):
+    """Two tokens with scores 0 and 1: weights 1/(1+e) and e/(1+e)."""
+    q = np.array([[[1.0, 0.0, 0.0, 0.0]]], dtype=np.float32)
+    kc = np.zeros((3, 2, 1, 4), dtype=np.float32)
+    vc = np.zeros((3, 2, 1, 4), dtype=np.float32)
+    # logical token 0 -> block 2 offset 0; token 1 -> block 2 offset 1
+    kc[2, 0, 0] = [0.0, 1.0, 2.0, 3.0]
+    kc[2, 1, 0] = [1.0, -1.0, 0.5, 2.0]
+    vc[2, 0, 0] = [1.0, 0.0, 2.0, -4.0]
+    vc[2, 1, 0] = [0.0, 1.0, 2.0, 4.0]
+    kc[0] = np.nan   # blocks the table does not reach
+    vc[0] = np.nan
+    out = orc.paged_attention_decode(q, kc, vc, np.array([[2]], np.int32),
+                                     np.array([2], np.int32), 1.0, "f32")
+    w0 = 1.0 / (1.0 + math.e)
+    w1 = math.e / (1.0 + math.e)
+    want = [w0, w1, 2.0, 4.0 * math.tanh(0.5)]
+    assert np.abs(out[0, 0] - want).max() <= 1e-15, out
+
+
+def pin_weights_sum_to_one(orc):
+    b = W.make_custom(33, dtype="f16", num_seqs=3, num_q_heads=4, num_kv_heads=2, head_dim=64,
+                      block_size=16, context_lens=(1, 40, 77))
+    _, w = orc.decode_batch(b, return_weights=True)
+    for s in range(3):
+        L = int(b.context_lens[s])
+        ws = w[s, :, :L]
+        assert np.all(ws >= 0)
+        assert np.abs(ws.sum(axis=1) - 1.0).max() <= 1e-12
+
+
+def pin_block_permutation(orc):
+    """Relabelling physical blocks leaves every output bit unchanged."""
+    for seed, dt in ((41, "f32"), (42, "bf16")):
+        b = W.make_custom(seed, dtype=dt, num_seqs=3, num_q_heads=4, num_kv_heads=2,
+                          head_dim=16, block_size=4, context_lens=(6, 21, 2), extra_blocks=6)
+        p = W.permute_blocks(b, seed + 100)
+        assert not np.array_equal(p.block_tables, b.block_tables)
+        assert np.array_equal(orc.decode_batch(b), orc.decode_batch(p))
+
+
+def pin_gqa_equals_mha(orc):
+    """Grouped queries equal multi-head attention on K/V heads repeated G
+    times (repeat_interleave: query head h reads kv head h // G)."""
+    b = W.make_custom(43, dtype="f32", num_seqs=2, num_q_heads=6, num_kv_heads=2, head_dim=8,
+                      block_size=4, context_lens=(5, 11))
+    G = 3
+    kc = np.ascontiguousarray(np.repeat(b.key_cache, G, axis=2))
+    vc = np.ascontiguousarray(np.repeat(b.value_cache, G, axis=2))
+    mha = orc.paged_attention_decode(b.query, kc, vc, b.block_tables, b.context_lens, b.scale,
+                                     "f32")
+    assert np.array_equal(orc.decode_batch(b), mha)
+
+
+def pin_split_merge(orc):
+    """Partitioned attention merged by log-sum-exp equals the unsplit result."""
+    b = W.make_custom(44, dtype="bf16", num_seqs=3, num_q_heads=8, num_kv_heads=2, head_dim=32,
+                      block_size=16, context_lens=(1, 70, 300))
+    ref = orc.decode_batch(b)
+    for P in (1, 7, 16, 64, 300):
+        got = orc.paged_attention_decode_partitioned(b.query, b.key_cache, b.value_cache,
+                                                     b.block_tables, b.context_lens, b.scale,
+                                                     b.dtype, P)
+        assert np.abs(got - ref).max() <= 1e-13 * max(1.0, np.abs(ref).max()), P
+
+
+def pin_poison_unreferenced(orc):
+    """NaN in every cell no sequence may read (free blocks, tail slots,
+    blocks named by table padding) changes nothing."""
+    kw = dict(dtype="f16", num_seqs=3, num_q_heads=4, num_kv_heads=4, head_dim=16,
+              block_size=8, context_lens=(3, 8, 19), extra_blocks=4, max_blocks_per_seq=5)
+    clean = W.make_custom(45, poison=False, **kw)
+    dirty = W.make_custom(45, poison=True, **kw)
+    assert np.isnan(W.bits_to_f32(dirty.key_cache, "f16")).any()
+    out = orc.decode_batch(dirty)
+    assert np.all(np.isfinite(out))
+    assert np.array_equal(out, orc.decode_batch(clean))
+
+
+def pin_large_scores(orc):
+    """One score above all others by 900 or more: the other weights underflow
+    to exactly 0 in fp64 (exp(-900) is below the smallest subnormal), so the
+    output is that token's V row.  Scores span 3000, so a softmax that does
+    not subtract the running maximum overflows."""
+    q = np.zeros((1, 1, 4), dtype=np.float32)
+    q[0, 0, 0] = 100.0
+    kc = np.zeros((2, 4, 1, 4), dtype=np.float32)
+    vc = np.random.default_rng(5).standard_normal((2, 4, 1, 4)).astype(np.float32)
+    kc[1, :, 0, 0] = [-20.0, 10.0, 1.0, -5.0]     # scores -2000, 1000, 100, -500
+    out = orc.paged_attention_decode(q, kc, vc, np.array([[1]], np.int32),
+                                     np.array([4], np.int32), 1.0, "f32")
+    assert np.array_equal(out[0, 0], vc[1, 1, 0].astype(np.float64))
+
+
+def pin_empty_context(orc):
+    b = W.make_custom(46, dtype="f32", num_seqs=2, num_q_heads=2, num_kv_heads=1, head_dim=8,
+                      block_size=4, context_lens=(0, 6))
+    out = orc.decode_batch(b)
+    assert np.all(out[0] == 0.0)
+    assert np.all(np.isfinite(out[1]))
+
+
+def pin_linear_in_values(orc):
+    """With the scores fixed, the output is linear in V (values chosen as
+    small integers so that V1 + V2 is exact in f32)."""
+    b = W.make_custom(47, dtype="f32", num_seqs=2, num_q_heads=2, num_kv_heads=2, head_dim=8,
+                      block_size=4, context_lens=(9, 14))
+    rng = np.random.default_rng(9)
+    v1 = rng.integers(-8, 8, size=b.value_cache.shape).astype(np.float32)
+    v2 = rng.integers(-8, 8, size=b.value_cache.shape).astype(np.float32)
+    run = lambda v: orc.paged_attention_decode(b.query, b.key_cache, v, b.block_tables,
+                                               b.context_lens, b.scale, "f32")
+    assert np.abs(run(v1 + v2) - (run(v1) + run(v2))).max() <= 1e-12
+
+
+ALL_PINS = [
+    pin_element_decode, pin_addressing_worked_example, pin_shared_prefix_blocks,
+    pin_write_gather_roundtrip, pin_decode_vs_sdpa, pin_tiny_workload_vs_sdpa,
+    pin_context_len_one, pin_identical_keys, pin_two_token_logistic, pin_weights_sum_to_one,
+    pin_block_permutation, pin_gqa_equals_mha, pin_split_merge, pin_poison_unreferenced,
+    pin_large_scores, pin_empty_context, pin_linear_in_values,
+]
