@@ -1,0 +1,242 @@
+#!/usr/bin/env python3
+"""Paged decode-attention bench on one MI355X.
+
+A step is one decode step of the whole path over one batch: kv_cache_write of
+each sequence's new token (slot_mapping scatter), then paged_attn_decode over
+every sequence's full context (block-table addressing, K/V tiles, online
+softmax, split-context partitions and their reduce when the context is
+split).  Inputs are resident in HBM before timing starts; the K/V pool is
+held in several copies that the steps rotate through, so that a step never
+finds its pool in the 256 MB Infinity Cache from the previous step.
+
+Prints one JSON line.  `value` is algorithmic bytes per step (K/V rows of
+every context token, query, output, block-table entries and lengths, plus
+the write's bytes) divided by the step time.  `roofline` covers the decode
+kernel alone, timed with HIP events on the stream it runs on.
+`cpu_baseline` times the fp64 CPU oracle on this host.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "paged decode attention: achieved HBM GB/s (% of peak) + sequences/sec per layer"
+HBM_PEAK_GBPS = 8000.0
+PROFILES = os.path.join(ROOT, "profiles")
+DECODE_SOURCES = ["paged_kv_cache_467_amd/csrc/paged_attention_decode.hip",
+                  "paged_kv_cache_467_amd/csrc/device_utils.h",
+                  "paged_kv_cache_467_amd/csrc/decode.h",
+                  "paged_kv_cache_467_amd/csrc/capi.cpp"]
+
+
+def decode_source_hash() -> str:
+    h = hashlib.sha256()
+    for rel in DECODE_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per decode launch from the committed rocprofv3 counter
+    summary, or None when there is none or the decode kernel source has
+    changed since it was taken."""
+    path = os.path.join(PROFILES, f"decode_{workload}_traffic.md")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    src = re.search(r"decode_source_sha256:\s*(\w+)", text)
+    tot = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    if not src or not tot or src.group(1) != decode_source_hash():
+        return None
+    return float(tot.group(1))
+
+
+def cpu_baseline(workload: str, batch_values):
+    """The fp64 CPU oracle on this host's cores, on the whole batch (median
+    of three runs)."""
+    import oracle
+
+    b = batch_values
+    orc = oracle.default()
+    threads = len(os.sched_getaffinity(0))
+    orc.set_threads(threads)
+    times = []
+    for _ in range(3):
+        t0 = time.perf_counter()
+        orc.decode_batch(b)
+        times.append(time.perf_counter() - t0)
+    t = statistics.median(times)
+    return {
+        "value": round(b.decode_algorithmic_bytes() / t / 1e9, 3),
+        "unit": "GB/s",
+        "cores": orc.max_threads(),
+        "kind": "oracle",
+        "sample": f"whole {workload} batch ({b.num_seqs} seqs), fp64 decode attention, "
+                  f"median of 3 runs of {t:.3f} s",
+        "seq_per_s": round(b.num_seqs / t, 1),
+        "cpu_model": _cpu_model(),
+    }
+
+
+def _cpu_model() -> str:
+    try:
+        for ln in open("/proc/cpuinfo"):
+            if ln.startswith("model name"):
+                return ln.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="llama3_8b_gqa_bf16")
+    ap.add_argument("--copies", type=int, default=4, help="pool copies rotated across steps")
+    ap.add_argument("--partition-size", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy-mib", type=int, default=0,
+                    help="also run one plain device copy of this many MiB (counter calibration)")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py runs on exactly one GPU: this build has no multi-GPU path "
+              "(--gpus must be 1)", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    from paged_kv_cache_467_amd import binding, tensors, workloads as W
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 1
+    dev = torch.device("cuda:0")
+    torch.manual_seed(0)
+    b = W.make_workload(args.workload, values=False)
+    dt = tensors.TORCH_DTYPE[b.dtype]
+    S, Hq, Hkv, D, bs = b.num_seqs, b.num_q_heads, b.num_kv_heads, b.head_dim, b.block_size
+    pool_shape = (b.num_blocks, bs, Hkv, D)
+    copies = []
+    for _ in range(max(1, args.copies)):
+        copies.append((torch.randn(pool_shape, device=dev).to(dt),
+                       torch.randn(pool_shape, device=dev).to(dt)))
+    query = torch.randn((S, Hq, D), device=dev).to(dt)
+    out = torch.empty_like(query)
+    new_key = torch.randn((S, Hkv, D), device=dev).to(dt)
+    new_value = torch.randn((S, Hkv, D), device=dev).to(dt)
+    bt = tensors.int32(b.block_tables, dev)
+    cl = tensors.int32(b.context_lens, dev)
+    sm = tensors.int32(b.slot_mapping, dev)
+    max_ctx = b.max_context_len
+    P = binding.paged_attn_decode_partition_size(S, Hq, Hkv, D, bs, b.max_blocks_per_seq,
+                                                 max_ctx, args.partition_size, b.dtype_code)
+    ws_bytes = binding.paged_attn_decode_workspace_bytes(S, Hq, Hkv, D, bs, b.max_blocks_per_seq,
+                                                         max_ctx, args.partition_size,
+                                                         b.dtype_code)
+    workspace = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
+
+    def step(i, ev=None):
+        kc, vc = copies[i % len(copies)]
+        binding.kv_cache_write(new_key, new_value, sm, kc, vc)
+        if ev is not None:
+            ev[0].record()
+        binding.paged_attn_decode(query, kc, vc, bt, cl, b.scale, out, max_context_len=max_ctx,
+                                  partition_size=args.partition_size, workspace=workspace)
+        if ev is not None:
+            ev[1].record()
+
+    if args.calibrate_copy_mib:
+        n = args.calibrate_copy_mib * (1 << 20)
+        src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    events = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(args.warmup + i, events[i])
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+
+    ms_per_step = elapsed * 1e3 / args.steps
+    decode_ms = [a.elapsed_time(z) for a, z in events]
+    decode_avg_ms = sum(decode_ms) / len(decode_ms)
+    b_dec = b.decode_algorithmic_bytes()
+    b_step = b_dec + b.write_algorithmic_bytes()
+    achieved = b_dec / (decode_avg_ms * 1e-3) / 1e9
+    traffic = measured_traffic(args.workload)
+
+    result = {
+        "metric": METRIC,
+        "value": round(b_step / (ms_per_step * 1e-3) / 1e9, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": b.dtype,
+        "data": "synthetic",
+        "config": {
+            "workload": args.workload,
+            "num_seqs": S, "num_q_heads": Hq, "num_kv_heads": Hkv, "head_dim": D,
+            "block_size": bs, "num_blocks": b.num_blocks,
+            "context_tokens": int(b.context_lens.sum()),
+            "context_len_range": [int(b.context_lens.min()), int(b.context_lens.max())],
+            "partition_size": P, "pool_copies": len(copies),
+            "step": "kv_cache_write of one token per sequence + paged_attn_decode",
+        },
+        "seq_per_s_per_layer": round(S / (decode_avg_ms * 1e-3), 1),
+        "decode_ms": round(decode_avg_ms, 5),
+        "decode_ms_p10_p90": [round(float(np.percentile(decode_ms, 10)), 5),
+                              round(float(np.percentile(decode_ms, 90)), 5)],
+        "algorithmic_bytes_per_step": b_step,
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(achieved, 2),
+            "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBPS, 4),
+            "traffic": traffic,
+            "kernel": "paged_attn_decode",
+            "algorithmic_bytes_per_launch": b_dec,
+        },
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        del copies
+        torch.cuda.empty_cache()
+        host = W.make_workload(args.workload)
+        result["cpu_baseline"] = cpu_baseline(args.workload, host)
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,164 @@
+/*
+ * paged_kv.h -- C ABI of the MI355X (gfx950) paged-attention decode library.
+ *
+ * The library implements the decode step of PagedAttention: for every
+ * sequence of a batch, the one new query token attends over the sequence's
+ * whole cached history, whose keys and values live in fixed-size physical
+ * blocks of a shared pool and are reached through a per-sequence block table
+ * ("大模型推理框架 vllm 源码解析 一", §三, the paged_attention_v1 description;
+ * "23.1 vLLM：高吞吐推理框架原理与部署", §二.2).  It also implements the
+ * companion write that stores each new token's K/V in the cell named by
+ * slot_mapping ("大模型推理框架VLLM-0.7.3源码", §2.1 and §3.3).
+ *
+ * Conventions shared by every entry point:
+ *  - All array arguments are DEVICE pointers, owned by the caller, dense and
+ *    row-major, 16-byte aligned.  The library never allocates memory and
+ *    keeps no state between calls; entry points are re-entrant.
+ *  - Element data are one dtype per call (paged_kv_dtype); index arrays are
+ *    int32.
+ *  - Every call is asynchronous on `stream` (a hipStream_t; NULL means the
+ *    null stream).  A return of PAGED_KV_OK means the work was enqueued.
+ *    Argument checks run on the host before anything is enqueued and never
+ *    read device memory; an invalid argument returns an error code and
+ *    enqueues nothing.  A failed kernel launch returns PAGED_KV_ERR_HIP.
+ *  - Values that live in device memory (block ids, context lengths, slots)
+ *    are checked by the kernels themselves, so a bad value never makes a
+ *    kernel read or write outside the arrays described here; what the
+ *    kernels do instead is stated per entry point.
+ */
+#ifndef PAGED_KV_H
+#define PAGED_KV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    PAGED_KV_F32 = 0,  /* IEEE binary32 */
+    PAGED_KV_F16 = 1,  /* IEEE binary16 */
+    PAGED_KV_BF16 = 2  /* bfloat16 (upper half of a binary32) */
+} paged_kv_dtype;
+
+typedef enum {
+    PAGED_KV_OK = 0,
+    PAGED_KV_ERR_NULL_POINTER = 1, /* a required pointer is NULL */
+    PAGED_KV_ERR_BAD_SHAPE = 2,    /* sizes inconsistent, out of range or misaligned */
+    PAGED_KV_ERR_UNSUPPORTED = 3,  /* valid but not implemented (dtype, head_dim, ...) */
+    PAGED_KV_ERR_WORKSPACE = 4,    /* workspace missing or smaller than required */
+    PAGED_KV_ERR_HIP = 5           /* the HIP runtime reported an error */
+} paged_kv_status;
+
+/* Human-readable name of a status code (static storage, never NULL). */
+const char *paged_kv_status_string(int status);
+
+/*
+ * Decode attention over a paged KV cache.
+ *
+ * For each sequence s < num_seqs and query head h < num_q_heads, with
+ * L = context_lens[s], G = num_q_heads / num_kv_heads and kv head h / G:
+ *   logical token j < L is read from physical block
+ *   block_tables[s * max_blocks_per_seq + j / block_size] at offset
+ *   j % block_size ("大模型推理框架 vllm 源码解析 一", §三 pseudo-code);
+ *   x_j = scale * dot(query[s, h, :], key_cache[block, offset, h / G, :]);
+ *   out[s, h, :] = sum_j softmax(x)_j * value_cache[block, offset, h / G, :].
+ * Accumulation is in fp32; out is rounded to the element dtype (RNE).
+ *
+ * Arguments:
+ *   query        [num_seqs, num_q_heads, head_dim]
+ *   key_cache    [num_blocks, block_size, num_kv_heads, head_dim]
+ *   value_cache  [num_blocks, block_size, num_kv_heads, head_dim]
+ *   block_tables [num_seqs, max_blocks_per_seq] int32; entries at index
+ *                >= ceil(L / block_size) are never read
+ *   context_lens [num_seqs] int32
+ *   scale        softmax scale (typically 1/sqrt(head_dim)); must be finite
+ *   out          [num_seqs, num_q_heads, head_dim], written
+ *   max_context_len  upper bound on every context_lens[s]; 0 means
+ *                max_blocks_per_seq * block_size.  It sizes the split into
+ *                context partitions and the workspace.
+ *   partition_size   tokens per context partition; 0 picks one.  An
+ *                explicit value must be a positive multiple of 16 and of
+ *                block_size with partition_size / block_size <= 1024.
+ *   workspace, workspace_bytes  device scratch of at least
+ *                paged_attn_decode_workspace_bytes(...) bytes for the same
+ *                arguments; may be NULL when that size is 0.  Its contents
+ *                need no initialisation and are garbage afterwards.
+ * Supported: dtype f32/f16/bf16; head_dim 64, 128, 256; block_size a power
+ * of two in [1, 256]; num_q_heads / num_kv_heads in {1, 2, 4, 8}.
+ * Device-side values: a sequence with context_len == 0 gets a zero output.
+ * A sequence whose context_len is negative or above max_context_len, or one
+ * of whose first ceil(L / block_size) table entries is outside
+ * [0, num_blocks), gets NaN in every output element; nothing out of range
+ * is read.
+ * Pool size: num_blocks * block_size * num_kv_heads * head_dim may exceed
+ * 2^31 elements (64-bit addressing).
+ */
+int paged_attn_decode(const void *query, const void *key_cache, const void *value_cache,
+                      const int32_t *block_tables, const int32_t *context_lens, float scale,
+                      void *out, int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
+                      int block_size, int num_blocks, int max_blocks_per_seq,
+                      int max_context_len, int partition_size, int dtype, void *workspace,
+                      size_t workspace_bytes, void *stream);
+
+/*
+ * The context partition size paged_attn_decode uses for these arguments
+ * (partition_size 0 = its automatic choice), or a negative paged_kv_status
+ * code when the arguments are invalid.  A partition size >= max_context_len
+ * means no split: one pass writes out directly.
+ */
+int paged_attn_decode_partition_size(int num_seqs, int num_q_heads, int num_kv_heads,
+                                     int head_dim, int block_size, int max_blocks_per_seq,
+                                     int max_context_len, int partition_size, int dtype);
+
+/*
+ * Bytes of workspace paged_attn_decode needs for these arguments (0 when the
+ * context is not split); (size_t)-1 for invalid arguments.  The split-context
+ * partials are fp32: per (sequence, query head, partition) a running max, a
+ * running sum and head_dim unnormalised output values.
+ */
+size_t paged_attn_decode_workspace_bytes(int num_seqs, int num_q_heads, int num_kv_heads,
+                                         int head_dim, int block_size, int max_blocks_per_seq,
+                                         int max_context_len, int partition_size, int dtype);
+
+/*
+ * Store new tokens' keys and values in the paged pool.
+ *
+ * For each t < num_tokens with slot = slot_mapping[t]:
+ *   key_cache[slot / block_size, slot % block_size, :, :]   = key[t, :, :]
+ *   value_cache[slot / block_size, slot % block_size, :, :] = value[t, :, :]
+ * as a bit copy ("大模型推理框架VLLM-0.7.3源码", §2.1: slot_mapping tells the
+ * operator which cell each token's KV goes to).
+ *   key, value   [num_tokens, num_kv_heads, head_dim]
+ *   slot_mapping [num_tokens] int32
+ *   key_cache, value_cache  [num_blocks, block_size, num_kv_heads, head_dim]
+ * Device-side values: a slot < 0 or >= num_blocks * block_size writes
+ * nothing.  Two tokens with the same slot in one call leave either token's
+ * row (unspecified which).  Writing into a block that several sequences
+ * share is the caller's responsibility (copy it first).
+ */
+int kv_cache_write(const void *key, const void *value, const int32_t *slot_mapping,
+                   void *key_cache, void *value_cache, int num_tokens, int num_kv_heads,
+                   int head_dim, int block_size, int num_blocks, int dtype, void *stream);
+
+/*
+ * Materialise each sequence's logical K/V through its block table (the
+ * addressing of paged_attn_decode, as a bit copy); used to check the
+ * addressing on its own.
+ *   out_key, out_value [num_seqs, max_context_len, num_kv_heads, head_dim]
+ * Position j < min(context_lens[s], max_context_len) receives logical token
+ * j; later positions are left untouched.  A table entry outside
+ * [0, num_blocks) fills the rows it would supply with NaN.
+ */
+int paged_kv_gather(const void *key_cache, const void *value_cache,
+                    const int32_t *block_tables, const int32_t *context_lens, void *out_key,
+                    void *out_value, int num_seqs, int num_kv_heads, int head_dim,
+                    int block_size, int num_blocks, int max_blocks_per_seq,
+                    int max_context_len, int dtype, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PAGED_KV_H */

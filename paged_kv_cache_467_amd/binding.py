@@ -1,0 +1,190 @@
+"""Thin Python binding of ``libpaged_kv.so`` (the C ABI in include/paged_kv.h).
+
+Argument marshalling only: tensors are checked for device, dtype, shape and
+contiguity, then their device pointers, sizes and the current HIP stream are
+passed to the C entry point of the same name.  Every step of the computation
+runs in the HIP kernels; there is no fallback.  If the library is missing or
+was built for another target the import fails loudly.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIBRARY = os.path.join(HERE, "libpaged_kv.so")
+
+PAGED_KV_F32, PAGED_KV_F16, PAGED_KV_BF16 = 0, 1, 2
+_TORCH_DTYPES = {torch.float32: PAGED_KV_F32, torch.float16: PAGED_KV_F16,
+                 torch.bfloat16: PAGED_KV_BF16}
+
+EXPORTED = (
+    "paged_kv_status_string",
+    "paged_attn_decode",
+    "paged_attn_decode_partition_size",
+    "paged_attn_decode_workspace_bytes",
+    "kv_cache_write",
+    "paged_kv_gather",
+)
+
+
+def _load_library(path: str = LIBRARY) -> ctypes.CDLL:
+    if not os.path.exists(path):
+        raise ImportError(
+            f"{path} is missing: build it first (python -c 'import __graft_entry__ as g; g.build()' "
+            "or python paged_kv_cache_467_amd/build.py)")
+    lib = ctypes.CDLL(path)
+    vp, ci, cf, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+    lib.paged_kv_status_string.argtypes = [ci]
+    lib.paged_kv_status_string.restype = ctypes.c_char_p
+    lib.paged_attn_decode.argtypes = [vp, vp, vp, vp, vp, cf, vp] + [ci] * 10 + [vp, sz, vp]
+    lib.paged_attn_decode.restype = ci
+    lib.paged_attn_decode_partition_size.argtypes = [ci] * 9
+    lib.paged_attn_decode_partition_size.restype = ci
+    lib.paged_attn_decode_workspace_bytes.argtypes = [ci] * 9
+    lib.paged_attn_decode_workspace_bytes.restype = sz
+    lib.kv_cache_write.argtypes = [vp, vp, vp, vp, vp] + [ci] * 6 + [vp]
+    lib.kv_cache_write.restype = ci
+    lib.paged_kv_gather.argtypes = [vp] * 6 + [ci] * 8 + [vp]
+    lib.paged_kv_gather.restype = ci
+    return lib
+
+
+_lib = _load_library()
+
+
+class PagedKVError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        super().__init__(f"{fn}: {paged_kv_status_string(status)} (status {status})")
+        self.status = status
+
+
+def paged_kv_status_string(status: int) -> str:
+    return _lib.paged_kv_status_string(int(status)).decode()
+
+
+def _check(fn: str, status: int) -> None:
+    if status != 0:
+        raise PagedKVError(fn, status)
+
+
+def _dev(t: torch.Tensor, name: str) -> int:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on a GPU device, got {t.device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t.data_ptr()
+
+
+def _stream(device) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype not in _TORCH_DTYPES:
+        raise TypeError(f"unsupported element dtype {t.dtype}")
+    return _TORCH_DTYPES[t.dtype]
+
+
+def paged_attn_decode_partition_size(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
+                                     max_blocks_per_seq, max_context_len=0, partition_size=0,
+                                     dtype=PAGED_KV_BF16) -> int:
+    r = _lib.paged_attn_decode_partition_size(num_seqs, num_q_heads, num_kv_heads, head_dim,
+                                              block_size, max_blocks_per_seq, max_context_len,
+                                              partition_size, dtype)
+    if r < 0:
+        raise PagedKVError("paged_attn_decode_partition_size", -r)
+    return r
+
+
+def paged_attn_decode_workspace_bytes(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
+                                      max_blocks_per_seq, max_context_len=0, partition_size=0,
+                                      dtype=PAGED_KV_BF16) -> int:
+    r = _lib.paged_attn_decode_workspace_bytes(num_seqs, num_q_heads, num_kv_heads, head_dim,
+                                               block_size, max_blocks_per_seq, max_context_len,
+                                               partition_size, dtype)
+    if r == ctypes.c_size_t(-1).value:
+        raise PagedKVError("paged_attn_decode_workspace_bytes", 2)
+    return r
+
+
+def paged_attn_decode(query: torch.Tensor, key_cache: torch.Tensor, value_cache: torch.Tensor,
+                      block_tables: torch.Tensor, context_lens: torch.Tensor, scale: float,
+                      out: torch.Tensor, *, max_context_len: int = 0, partition_size: int = 0,
+                      workspace: torch.Tensor | None = None) -> torch.Tensor:
+    """Decode attention over a paged KV cache (see paged_attn_decode in
+    include/paged_kv.h).  query/out [S, Hq, D]; key_cache/value_cache
+    [num_blocks, block_size, Hkv, D]; block_tables [S, max_blocks] int32;
+    context_lens [S] int32.  A workspace of the required size is allocated
+    with torch when none is given."""
+    S, Hq, D = query.shape
+    nb, bs, Hkv, D2 = key_cache.shape
+    if D2 != D or tuple(value_cache.shape) != tuple(key_cache.shape):
+        raise ValueError("query / key_cache / value_cache shapes disagree")
+    if tuple(out.shape) != (S, Hq, D) or out.dtype != query.dtype:
+        raise ValueError("out must match query's shape and dtype")
+    if key_cache.dtype != query.dtype or value_cache.dtype != query.dtype:
+        raise TypeError("query, caches and out must share one dtype")
+    if block_tables.dtype != torch.int32 or context_lens.dtype != torch.int32:
+        raise TypeError("block_tables and context_lens must be int32")
+    if block_tables.dim() != 2 or block_tables.shape[0] != S or tuple(context_lens.shape) != (S,):
+        raise ValueError("block_tables must be [S, max_blocks] and context_lens [S]")
+    dt = _dtype_code(query)
+    mb = block_tables.shape[1]
+    need = paged_attn_decode_workspace_bytes(S, Hq, Hkv, D, bs, mb, max_context_len,
+                                             partition_size, dt)
+    ws_ptr, ws_bytes = None, 0
+    if need > 0:
+        if workspace is None:
+            workspace = torch.empty(need, dtype=torch.uint8, device=query.device)
+        ws_ptr, ws_bytes = _dev(workspace, "workspace"), workspace.numel() * workspace.element_size()
+    status = _lib.paged_attn_decode(
+        _dev(query, "query"), _dev(key_cache, "key_cache"), _dev(value_cache, "value_cache"),
+        _dev(block_tables, "block_tables"), _dev(context_lens, "context_lens"),
+        ctypes.c_float(scale), _dev(out, "out"), S, Hq, Hkv, D, bs, nb, mb, max_context_len,
+        partition_size, dt, ws_ptr, ws_bytes, _stream(query.device))
+    _check("paged_attn_decode", status)
+    return out
+
+
+def kv_cache_write(key: torch.Tensor, value: torch.Tensor, slot_mapping: torch.Tensor,
+                   key_cache: torch.Tensor, value_cache: torch.Tensor) -> None:
+    """Store key[t] / value[t] ([T, Hkv, D]) in the pool cell slot_mapping[t]."""
+    T, Hkv, D = key.shape
+    nb, bs, Hkv2, D2 = key_cache.shape
+    if (Hkv2, D2) != (Hkv, D) or tuple(value.shape) != tuple(key.shape) or \
+            tuple(value_cache.shape) != tuple(key_cache.shape):
+        raise ValueError("key/value and cache shapes disagree")
+    if not (key.dtype == value.dtype == key_cache.dtype == value_cache.dtype):
+        raise TypeError("key, value and the caches must share one dtype")
+    if slot_mapping.dtype != torch.int32 or tuple(slot_mapping.shape) != (T,):
+        raise ValueError("slot_mapping must be int32 [T]")
+    status = _lib.kv_cache_write(
+        _dev(key, "key"), _dev(value, "value"), _dev(slot_mapping, "slot_mapping"),
+        _dev(key_cache, "key_cache"), _dev(value_cache, "value_cache"), T, Hkv, D, bs, nb,
+        _dtype_code(key), _stream(key.device))
+    _check("kv_cache_write", status)
+
+
+def paged_kv_gather(key_cache: torch.Tensor, value_cache: torch.Tensor,
+                    block_tables: torch.Tensor, context_lens: torch.Tensor, out_key: torch.Tensor,
+                    out_value: torch.Tensor) -> None:
+    """Materialise each sequence's K/V through its block table into
+    out_key/out_value [S, max_context_len, Hkv, D]."""
+    nb, bs, Hkv, D = key_cache.shape
+    S, mb = block_tables.shape
+    if out_key.dim() != 4 or out_key.shape[0] != S or tuple(out_key.shape[2:]) != (Hkv, D) or \
+            tuple(out_value.shape) != tuple(out_key.shape):
+        raise ValueError("out_key/out_value must be [S, max_context_len, Hkv, D]")
+    if block_tables.dtype != torch.int32 or context_lens.dtype != torch.int32:
+        raise TypeError("block_tables and context_lens must be int32")
+    status = _lib.paged_kv_gather(
+        _dev(key_cache, "key_cache"), _dev(value_cache, "value_cache"),
+        _dev(block_tables, "block_tables"), _dev(context_lens, "context_lens"),
+        _dev(out_key, "out_key"), _dev(out_value, "out_value"), S, Hkv, D, bs, nb, mb,
+        out_key.shape[1], _dtype_code(key_cache), _stream(key_cache.device))
+    _check("paged_kv_gather", status)

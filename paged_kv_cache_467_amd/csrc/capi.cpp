@@ -1,0 +1,247 @@
+// C ABI of the paged-attention decode library: host-side argument checks,
+// the choice of context partition, workspace sizing and kernel launches on
+// the caller's stream.  Nothing here reads device memory or allocates.
+
+#include "../../include/paged_kv.h"
+
+#include <hip/hip_runtime.h>
+
+#include <limits.h>
+#include <math.h>
+#include <stdint.h>
+
+#include "decode.h"
+
+namespace {
+
+// Aim for about eight decode workgroups per compute unit (256 CUs) before
+// splitting contexts any further; never split below this many tokens.
+constexpr int kTargetWorkgroups = 2048;
+constexpr int kMinSplitTokens = 256;
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool aligned4(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
+bool pow2(int x) { return x > 0 && (x & (x - 1)) == 0; }
+int log2i(int x) {
+    int r = 0;
+    while ((1 << r) < x) ++r;
+    return r;
+}
+int elem_bytes(int dtype) { return dtype == PAGED_KV_F32 ? 4 : 2; }
+int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
+
+struct Plan {
+    int status;
+    int max_context_len;
+    int partition_size;
+    int num_partitions;
+};
+
+// Shape checks shared by the decode entry points, and the partition choice.
+Plan plan_decode(int num_seqs, int num_q_heads, int num_kv_heads, int head_dim, int block_size,
+                 int max_blocks_per_seq, int max_context_len, int partition_size, int dtype) {
+    Plan pl{PAGED_KV_OK, 0, 0, 1};
+    if (dtype != PAGED_KV_F32 && dtype != PAGED_KV_F16 && dtype != PAGED_KV_BF16) {
+        pl.status = PAGED_KV_ERR_UNSUPPORTED;
+        return pl;
+    }
+    if (num_seqs < 0 || num_q_heads < 1 || num_kv_heads < 1 || max_blocks_per_seq < 1 ||
+        max_context_len < 0 || partition_size < 0 || num_q_heads % num_kv_heads != 0) {
+        pl.status = PAGED_KV_ERR_BAD_SHAPE;
+        return pl;
+    }
+    const int group = num_q_heads / num_kv_heads;
+    if (!(head_dim == 64 || head_dim == 128 || head_dim == 256) ||
+        !(group == 1 || group == 2 || group == 4 || group == 8) || !pow2(block_size) ||
+        block_size > 256) {
+        pl.status = PAGED_KV_ERR_UNSUPPORTED;
+        return pl;
+    }
+    const int64_t table_tokens = (int64_t)max_blocks_per_seq * block_size;
+    if (table_tokens > INT_MAX) {
+        pl.status = PAGED_KV_ERR_BAD_SHAPE;
+        return pl;
+    }
+    const int max_ctx = max_context_len == 0 ? (int)table_tokens : max_context_len;
+    if (max_ctx > table_tokens) {
+        pl.status = PAGED_KV_ERR_BAD_SHAPE;
+        return pl;
+    }
+    const int align = block_size > 16 ? block_size : 16;
+    const int64_t max_part = (int64_t)pkv::kBtLds * block_size;
+    int64_t P;
+    if (partition_size > 0) {
+        if (partition_size % 16 != 0 || partition_size % block_size != 0 ||
+            partition_size > max_part) {
+            pl.status = PAGED_KV_ERR_BAD_SHAPE;
+            return pl;
+        }
+        P = partition_size;
+    } else {
+        const int64_t units = (int64_t)num_seqs * num_kv_heads;
+        int64_t parts = units > 0 ? (kTargetWorkgroups + units - 1) / units : 1;
+        const int64_t most = (max_ctx + kMinSplitTokens - 1) / kMinSplitTokens;
+        if (parts > most) parts = most;
+        if (parts < 1) parts = 1;
+        P = round_up((max_ctx + parts - 1) / parts, align);
+        if (P < align) P = align;
+        if (P > max_part) P = max_part;
+    }
+    const int64_t nparts = max_ctx == 0 ? 1 : (max_ctx + P - 1) / P;
+    if ((int64_t)num_seqs * num_kv_heads * nparts > INT_MAX ||
+        (int64_t)num_seqs * num_q_heads > INT_MAX) {
+        pl.status = PAGED_KV_ERR_BAD_SHAPE;
+        return pl;
+    }
+    pl.max_context_len = max_ctx;
+    pl.partition_size = (int)P;
+    pl.num_partitions = (int)nparts;
+    return pl;
+}
+
+size_t partial_floats(int num_seqs, int num_q_heads) {
+    return round_up((int64_t)num_seqs * num_q_heads, 4);  // keeps the o array 16-byte aligned
+}
+
+size_t workspace_for(const Plan &pl, int num_seqs, int num_q_heads, int head_dim) {
+    if (pl.num_partitions <= 1) return 0;
+    const size_t n = partial_floats(num_seqs, num_q_heads) * pl.num_partitions;
+    return n * (2 + (size_t)head_dim) * sizeof(float);
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *paged_kv_status_string(int status) {
+    switch (status) {
+        case PAGED_KV_OK: return "ok";
+        case PAGED_KV_ERR_NULL_POINTER: return "null pointer";
+        case PAGED_KV_ERR_BAD_SHAPE: return "bad shape, size or alignment";
+        case PAGED_KV_ERR_UNSUPPORTED: return "unsupported dtype or shape";
+        case PAGED_KV_ERR_WORKSPACE: return "workspace missing or too small";
+        case PAGED_KV_ERR_HIP: return "HIP runtime error";
+        default: return "unknown status";
+    }
+}
+
+int paged_attn_decode_partition_size(int num_seqs, int num_q_heads, int num_kv_heads,
+                                     int head_dim, int block_size, int max_blocks_per_seq,
+                                     int max_context_len, int partition_size, int dtype) {
+    const Plan pl = plan_decode(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
+                                max_blocks_per_seq, max_context_len, partition_size, dtype);
+    return pl.status == PAGED_KV_OK ? pl.partition_size : -pl.status;
+}
+
+size_t paged_attn_decode_workspace_bytes(int num_seqs, int num_q_heads, int num_kv_heads,
+                                         int head_dim, int block_size, int max_blocks_per_seq,
+                                         int max_context_len, int partition_size, int dtype) {
+    const Plan pl = plan_decode(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
+                                max_blocks_per_seq, max_context_len, partition_size, dtype);
+    if (pl.status != PAGED_KV_OK) return (size_t)-1;
+    return workspace_for(pl, num_seqs, num_q_heads, head_dim);
+}
+
+int paged_attn_decode(const void *query, const void *key_cache, const void *value_cache,
+                      const int32_t *block_tables, const int32_t *context_lens, float scale,
+                      void *out, int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
+                      int block_size, int num_blocks, int max_blocks_per_seq,
+                      int max_context_len, int partition_size, int dtype, void *workspace,
+                      size_t workspace_bytes, void *stream) {
+    const Plan pl = plan_decode(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
+                                max_blocks_per_seq, max_context_len, partition_size, dtype);
+    if (pl.status != PAGED_KV_OK) return pl.status;
+    if (num_blocks < 1 || !isfinite(scale)) return PAGED_KV_ERR_BAD_SHAPE;
+    if (num_seqs == 0) return PAGED_KV_OK;
+    if (!query || !key_cache || !value_cache || !block_tables || !context_lens || !out)
+        return PAGED_KV_ERR_NULL_POINTER;
+    if (!aligned16(query) || !aligned16(key_cache) || !aligned16(value_cache) ||
+        !aligned16(out) || !aligned4(block_tables) || !aligned4(context_lens))
+        return PAGED_KV_ERR_BAD_SHAPE;
+    const size_t need = workspace_for(pl, num_seqs, num_q_heads, head_dim);
+    if (need > 0 && (!workspace || workspace_bytes < need || !aligned16(workspace)))
+        return PAGED_KV_ERR_WORKSPACE;
+
+    const int e = elem_bytes(dtype);
+    pkv::DecodeParams p;
+    p.query = query;
+    p.key_cache = static_cast<const char *>(key_cache);
+    p.value_cache = static_cast<const char *>(value_cache);
+    p.block_tables = block_tables;
+    p.context_lens = context_lens;
+    p.out = out;
+    const size_t nph = partial_floats(num_seqs, num_q_heads) * pl.num_partitions;
+    float *ws = static_cast<float *>(workspace);
+    p.part_max = need ? ws : nullptr;
+    p.part_sum = need ? ws + nph : nullptr;
+    p.part_out = need ? ws + 2 * nph : nullptr;
+    p.scale_log2 = (float)((double)scale * 1.4426950408889634);  // scale * log2(e)
+    p.num_seqs = num_seqs;
+    p.num_q_heads = num_q_heads;
+    p.num_kv_heads = num_kv_heads;
+    p.block_size = block_size;
+    p.block_shift = log2i(block_size);
+    p.num_blocks = num_blocks;
+    p.max_blocks_per_seq = max_blocks_per_seq;
+    p.max_context_len = pl.max_context_len;
+    p.partition_size = pl.partition_size;
+    p.num_partitions = pl.num_partitions;
+    p.row_stride_bytes = num_kv_heads * head_dim * e;
+    p.block_stride_bytes = (int64_t)block_size * p.row_stride_bytes;
+
+    const int group = num_q_heads / num_kv_heads;
+    const int kernel = pkv::decode_kernel_choice(dtype, head_dim, group);
+    const hipError_t err = pkv::launch_decode(p, dtype, head_dim, group, kernel,
+                                              static_cast<hipStream_t>(stream));
+    return err == hipSuccess ? PAGED_KV_OK : PAGED_KV_ERR_HIP;
+}
+
+int kv_cache_write(const void *key, const void *value, const int32_t *slot_mapping,
+                   void *key_cache, void *value_cache, int num_tokens, int num_kv_heads,
+                   int head_dim, int block_size, int num_blocks, int dtype, void *stream) {
+    if (dtype != PAGED_KV_F32 && dtype != PAGED_KV_F16 && dtype != PAGED_KV_BF16)
+        return PAGED_KV_ERR_UNSUPPORTED;
+    if (num_tokens < 0 || num_kv_heads < 1 || head_dim < 1 || block_size < 1 || num_blocks < 1)
+        return PAGED_KV_ERR_BAD_SHAPE;
+    const int64_t row = (int64_t)num_kv_heads * head_dim * elem_bytes(dtype);
+    if (row % 16 != 0 || row > INT_MAX) return PAGED_KV_ERR_BAD_SHAPE;
+    if (num_tokens == 0) return PAGED_KV_OK;
+    if (!key || !value || !slot_mapping || !key_cache || !value_cache)
+        return PAGED_KV_ERR_NULL_POINTER;
+    if (!aligned16(key) || !aligned16(value) || !aligned16(key_cache) ||
+        !aligned16(value_cache) || !aligned4(slot_mapping))
+        return PAGED_KV_ERR_BAD_SHAPE;
+    const hipError_t err =
+        pkv::launch_kv_cache_write(key, value, slot_mapping, key_cache, value_cache, num_tokens,
+                                   (int)row, (int64_t)num_blocks * block_size,
+                                   static_cast<hipStream_t>(stream));
+    return err == hipSuccess ? PAGED_KV_OK : PAGED_KV_ERR_HIP;
+}
+
+int paged_kv_gather(const void *key_cache, const void *value_cache,
+                    const int32_t *block_tables, const int32_t *context_lens, void *out_key,
+                    void *out_value, int num_seqs, int num_kv_heads, int head_dim,
+                    int block_size, int num_blocks, int max_blocks_per_seq,
+                    int max_context_len, int dtype, void *stream) {
+    if (dtype != PAGED_KV_F32 && dtype != PAGED_KV_F16 && dtype != PAGED_KV_BF16)
+        return PAGED_KV_ERR_UNSUPPORTED;
+    if (num_seqs < 0 || num_seqs > 65535 || num_kv_heads < 1 || head_dim < 1 ||
+        !pow2(block_size) || num_blocks < 1 || max_blocks_per_seq < 1 || max_context_len < 0 ||
+        (int64_t)max_context_len > (int64_t)max_blocks_per_seq * block_size)
+        return PAGED_KV_ERR_BAD_SHAPE;
+    const int64_t row = (int64_t)num_kv_heads * head_dim * elem_bytes(dtype);
+    if (row % 16 != 0 || row * block_size > INT_MAX) return PAGED_KV_ERR_BAD_SHAPE;
+    if (num_seqs == 0 || max_context_len == 0) return PAGED_KV_OK;
+    if (!key_cache || !value_cache || !block_tables || !context_lens || !out_key || !out_value)
+        return PAGED_KV_ERR_NULL_POINTER;
+    if (!aligned16(key_cache) || !aligned16(value_cache) || !aligned16(out_key) ||
+        !aligned16(out_value) || !aligned4(block_tables) || !aligned4(context_lens))
+        return PAGED_KV_ERR_BAD_SHAPE;
+    const hipError_t err = pkv::launch_paged_kv_gather(
+        key_cache, value_cache, block_tables, context_lens, out_key, out_value, num_seqs,
+        max_blocks_per_seq, block_size, num_blocks, max_context_len, (int)row,
+        elem_bytes(dtype), static_cast<hipStream_t>(stream));
+    return err == hipSuccess ? PAGED_KV_OK : PAGED_KV_ERR_HIP;
+}
+
+}  // extern "C"

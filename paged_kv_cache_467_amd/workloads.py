@@ -45,10 +45,10 @@ def f32_to_bits(x: np.ndarray, dtype: str) -> np.ndarray:
     if dtype == "f16":
         return x.astype(np.float16).view(np.uint16)
     if dtype == "bf16":
-        u = x.view(np.uint32).astype(np.uint64)
-        # round half to even on the 16 dropped bits (inputs are finite)
-        u = u + 0x7FFF + ((u >> 16) & 1)
-        return (u >> 16).astype(np.uint16)
+        u = x.view(np.uint32)
+        # round half to even on the 16 dropped bits (finite inputs: no overflow)
+        u = u + np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1))
+        return (u >> np.uint32(16)).astype(np.uint16)
     raise ValueError(dtype)
 
 
@@ -142,10 +142,11 @@ def _normal_bits(rng: np.random.Generator, shape, dtype: str) -> np.ndarray:
 
 
 def _assemble(name, dtype, rng, *, S, Hq, Hkv, D, bs, lens, tables, num_blocks,
-              max_blocks, scale, poison, seed, meta=None, keys_identical=False):
+              max_blocks, scale, poison, seed, meta=None, keys_identical=False, values=True):
     """Fill the pool rows that block tables reach, poison or zero the rest,
     draw queries and the new tokens, and derive slot_mapping for a write of
-    one new token per sequence at position L_s - 1."""
+    one new token per sequence at position L_s - 1.  With values=False the
+    pool arrays are left empty (shape (0,)): only the structure is built."""
     sd = storage_dtype(dtype)
     lens = np.asarray(lens, dtype=np.int32)
     bt = np.asarray(tables, dtype=np.int32)
@@ -157,9 +158,13 @@ def _assemble(name, dtype, rng, *, S, Hq, Hkv, D, bs, lens, tables, num_blocks,
     referenced = np.array(sorted(referenced), dtype=np.int64)
 
     fill = NAN_BITS[dtype] if poison else sd(0)
-    key_cache = np.full((num_blocks, bs, Hkv, D), fill, dtype=sd)
-    value_cache = np.full((num_blocks, bs, Hkv, D), fill, dtype=sd)
-    if len(referenced):
+    if not values:
+        key_cache = value_cache = np.zeros((0,), dtype=sd)
+        poison = keys_identical = False
+    else:
+        key_cache = np.full((num_blocks, bs, Hkv, D), fill, dtype=sd)
+        value_cache = np.full((num_blocks, bs, Hkv, D), fill, dtype=sd)
+    if values and len(referenced):
         key_cache[referenced] = _normal_bits(rng, (len(referenced), bs, Hkv, D), dtype)
         value_cache[referenced] = _normal_bits(rng, (len(referenced), bs, Hkv, D), dtype)
     if poison:
@@ -226,8 +231,10 @@ WORKLOADS = ("tiny_f32", "llama3_8b_gqa_bf16", "llama13b_mha_f16",
              "long_context_bf16", "shared_prefix_bf16")
 
 
-def make_workload(name: str, seed: int | None = None, poison: bool = False) -> DecodeBatch:
-    """Build one of the five named workloads (seed defaults to 46700 + index)."""
+def make_workload(name: str, seed: int | None = None, poison: bool = False,
+                  values: bool = True) -> DecodeBatch:
+    """Build one of the five named workloads (seed defaults to 46700 + index).
+    values=False builds only lengths, tables and slots (no pool contents)."""
     idx = WORKLOADS.index(name)
     seed = 46700 + idx + 1 if seed is None else seed
     rng = np.random.default_rng(seed)
@@ -238,28 +245,28 @@ def make_workload(name: str, seed: int | None = None, poison: bool = False) -> D
         tables_pool = pool
         return _assemble(name, "f32", rng, S=S, Hq=Hq, Hkv=Hkv, D=D, bs=bs, lens=lens,
                          tables=tables, num_blocks=tables_pool, max_blocks=mb,
-                         scale=1.0 / math.sqrt(64), poison=poison, seed=seed)
+                         scale=1.0 / math.sqrt(64), poison=poison, seed=seed, values=values)
     if name == "llama3_8b_gqa_bf16":
         S, Hq, Hkv, D, bs, mb = 256, 32, 8, 128, 16, 40
         lens = rng.integers(512, 640, size=S, endpoint=True)
         tables, pool = _deal_tables(rng, lens, bs, mb)
         return _assemble(name, "bf16", rng, S=S, Hq=Hq, Hkv=Hkv, D=D, bs=bs, lens=lens,
                          tables=tables, num_blocks=pool, max_blocks=mb,
-                         scale=1.0 / math.sqrt(D), poison=poison, seed=seed)
+                         scale=1.0 / math.sqrt(D), poison=poison, seed=seed, values=values)
     if name == "llama13b_mha_f16":
         S, Hq, Hkv, D, bs, mb = 50, 40, 40, 128, 16, 128
         lens = rng.integers(1, 2048, size=S, endpoint=True)
         tables, pool = _deal_tables(rng, lens, bs, mb)
         return _assemble(name, "f16", rng, S=S, Hq=Hq, Hkv=Hkv, D=D, bs=bs, lens=lens,
                          tables=tables, num_blocks=pool, max_blocks=mb,
-                         scale=1.0 / math.sqrt(D), poison=poison, seed=seed)
+                         scale=1.0 / math.sqrt(D), poison=poison, seed=seed, values=values)
     if name == "long_context_bf16":
         S, Hq, Hkv, D, bs, mb = 8, 32, 8, 128, 32, 1024
         lens = rng.integers(24576, 32768, size=S, endpoint=True)
         tables, pool = _deal_tables(rng, lens, bs, mb)
         return _assemble(name, "bf16", rng, S=S, Hq=Hq, Hkv=Hkv, D=D, bs=bs, lens=lens,
                          tables=tables, num_blocks=pool, max_blocks=mb,
-                         scale=1.0 / math.sqrt(D), poison=poison, seed=seed)
+                         scale=1.0 / math.sqrt(D), poison=poison, seed=seed, values=values)
     if name == "shared_prefix_bf16":
         S, Hq, Hkv, D, bs = 64, 32, 8, 128, 16
         prefix_blocks = 125                     # 2000 tokens
@@ -281,7 +288,7 @@ def make_workload(name: str, seed: int | None = None, poison: bool = False) -> D
         lens = prefix_blocks * bs + suffix
         return _assemble(name, "bf16", rng, S=S, Hq=Hq, Hkv=Hkv, D=D, bs=bs, lens=lens,
                          tables=tables, num_blocks=pool, max_blocks=mb,
-                         scale=1.0 / math.sqrt(D), poison=poison, seed=seed,
+                         scale=1.0 / math.sqrt(D), poison=poison, seed=seed, values=values,
                          meta={"prefix_blocks": prefix_blocks})
     raise ValueError(name)
 

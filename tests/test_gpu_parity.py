@@ -1,0 +1,253 @@
+"""GPU parity: the HIP library, called through its C ABI (via the thin
+binding), against the CPU oracle on the same seeded inputs.
+
+Bars: kv_cache_write and paged_kv_gather bit-exact; decode attention within
+max-abs 2e-3 (f32) or max-abs 2e-2 and normwise relative 1e-2 (f16/bf16),
+with fp32 accumulation on the GPU.
+"""
+import functools
+import sys
+
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+pytestmark = pytest.mark.gpu
+
+import oracle  # noqa: E402
+from paged_kv_cache_467_amd import tensors, workloads as W  # noqa: E402
+
+
+def _say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def B():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from paged_kv_cache_467_amd import binding
+    return binding
+
+
+DEV = "cuda:0"
+TOL = {"f32": (2e-3, None), "f16": (2e-2, 1e-2), "bf16": (2e-2, 1e-2)}
+
+
+def check_close(got, ref, dtype, what=""):
+    got = np.asarray(got, dtype=np.float64)
+    assert got.shape == ref.shape
+    assert np.all(np.isfinite(got)), f"{what}: non-finite output"
+    err = np.abs(got - ref).max() if got.size else 0.0
+    nrm = np.linalg.norm(ref)
+    rel = np.linalg.norm(got - ref) / nrm if nrm > 0 else 0.0
+    amax, rmax = TOL[dtype]
+    _say(f"  {what}: max|err| {err:.3e}  normwise rel {rel:.3e}")
+    assert err <= amax, f"{what}: max abs error {err}"
+    if rmax is not None:
+        assert rel <= rmax, f"{what}: normwise relative error {rel}"
+
+
+def run_decode(B, batch, d=None, partition_size=0, max_context_len=None):
+    d = d or tensors.device_batch(batch, DEV)
+    mcl = batch.max_context_len if max_context_len is None else max_context_len
+    B.paged_attn_decode(d.query, d.key_cache, d.value_cache, d.block_tables, d.context_lens,
+                        batch.scale, d.out, max_context_len=mcl, partition_size=partition_size)
+    torch.cuda.synchronize()
+    return tensors.to_host_bits(d.out)
+
+
+@functools.lru_cache(maxsize=None)
+def workload(name):
+    return W.make_workload(name, poison=True)
+
+
+@functools.lru_cache(maxsize=None)
+def oracle_out(name):
+    return oracle.decode_batch(workload(name))
+
+
+# ------------------------------------------------------------ cache write
+@pytest.mark.parametrize("name", ["tiny_f32", "llama13b_mha_f16", "shared_prefix_bf16"])
+def test_kv_cache_write_bit_exact(B, name):
+    _say(f"kv_cache_write {name}")
+    b = workload(name)
+    d = tensors.device_batch(b, DEV)
+    B.kv_cache_write(d.new_key, d.new_value, d.slot_mapping, d.key_cache, d.value_cache)
+    torch.cuda.synchronize()
+    ref = b.copy()
+    oracle.write_batch(ref)
+    assert np.array_equal(tensors.to_host_bits(d.key_cache).view(np.uint8),
+                          ref.key_cache.view(np.uint8))
+    assert np.array_equal(tensors.to_host_bits(d.value_cache).view(np.uint8),
+                          ref.value_cache.view(np.uint8))
+
+
+@pytest.mark.parametrize("dtype,Hkv,D", [("f32", 2, 64), ("f16", 4, 128), ("bf16", 1, 256)])
+def test_kv_cache_write_skips_invalid_slots(B, dtype, Hkv, D):
+    _say(f"kv_cache_write invalid slots {dtype} Hkv={Hkv} D={D}")
+    b = W.make_custom(61, dtype=dtype, num_seqs=6, num_q_heads=Hkv, num_kv_heads=Hkv,
+                      head_dim=D, block_size=8, context_lens=(1, 8, 9, 20, 3, 30))
+    nslots = b.num_blocks * b.block_size
+    b.slot_mapping[1] = -1
+    b.slot_mapping[3] = nslots          # one past the end: ignored
+    b.slot_mapping[4] = -7
+    d = tensors.device_batch(b, DEV)
+    B.kv_cache_write(d.new_key, d.new_value, d.slot_mapping, d.key_cache, d.value_cache)
+    torch.cuda.synchronize()
+    ref = b.copy()
+    ref.slot_mapping[3] = -1            # the oracle's contract covers negatives only
+    oracle.write_batch(ref)
+    assert np.array_equal(tensors.to_host_bits(d.key_cache).view(np.uint8),
+                          ref.key_cache.view(np.uint8))
+    assert np.array_equal(tensors.to_host_bits(d.value_cache).view(np.uint8),
+                          ref.value_cache.view(np.uint8))
+
+
+# ----------------------------------------------------------------- gather
+@pytest.mark.parametrize("name,nseq", [("tiny_f32", 4), ("llama13b_mha_f16", 6),
+                                       ("shared_prefix_bf16", 8), ("long_context_bf16", 1)])
+def test_gather_bit_exact(B, name, nseq):
+    _say(f"paged_kv_gather {name} first {nseq} sequences")
+    b = workload(name)
+    bt = np.ascontiguousarray(b.block_tables[:nseq])
+    cl = np.ascontiguousarray(b.context_lens[:nseq])
+    maxL = int(cl.max())
+    rk, rv = oracle.paged_kv_gather(b.key_cache, b.value_cache, bt, cl, maxL, b.dtype,
+                                    fill=W.NAN_BITS[b.dtype])
+    kc = tensors.to_device(b.key_cache, b.dtype, DEV)
+    vc = tensors.to_device(b.value_cache, b.dtype, DEV)
+    ok = tensors.to_device(np.full(rk.shape, W.NAN_BITS[b.dtype], dtype=rk.dtype), b.dtype, DEV)
+    ov = tensors.to_device(np.full(rv.shape, W.NAN_BITS[b.dtype], dtype=rv.dtype), b.dtype, DEV)
+    B.paged_kv_gather(kc, vc, tensors.int32(bt, DEV), tensors.int32(cl, DEV), ok, ov)
+    torch.cuda.synchronize()
+    assert np.array_equal(tensors.to_host_bits(ok).view(np.uint8), rk.view(np.uint8))
+    assert np.array_equal(tensors.to_host_bits(ov).view(np.uint8), rv.view(np.uint8))
+
+
+# ---------------------------------------------------------- decode parity
+@pytest.mark.parametrize("name", W.WORKLOADS)
+def test_decode_workload(B, name):
+    _say(f"decode {name} (full size, poisoned pool)")
+    b = workload(name)
+    got = run_decode(B, b)
+    check_close(tensors.widen(got, b.dtype), oracle_out(name), b.dtype, name)
+
+
+@pytest.mark.parametrize("name", ["llama13b_mha_f16", "shared_prefix_bf16", "llama3_8b_gqa_bf16"])
+def test_decode_step_write_then_attend(B, name):
+    """One decode step: write each sequence's new token at position L-1,
+    then attend over L tokens (the new query sees its own key)."""
+    _say(f"step (write + decode) {name}")
+    b = workload(name)
+    d = tensors.device_batch(b, DEV)
+    B.kv_cache_write(d.new_key, d.new_value, d.slot_mapping, d.key_cache, d.value_cache)
+    got = run_decode(B, b, d)
+    ref = b.copy()
+    oracle.write_batch(ref)
+    check_close(tensors.widen(got, b.dtype), oracle.decode_batch(ref), b.dtype, name)
+
+
+@functools.lru_cache(maxsize=None)
+def medium(dtype="bf16", G=4, D=128, bs=16, seed=71):
+    lens = (1, 15, 16, 17, 100, 255, 256, 257, 600, 1000, 1500)
+    return W.make_custom(seed, dtype=dtype, num_seqs=len(lens), num_q_heads=2 * G,
+                         num_kv_heads=2, head_dim=D, block_size=bs, context_lens=lens,
+                         extra_blocks=20, poison=True)
+
+
+@pytest.mark.parametrize("bs", [16, 32])
+@pytest.mark.parametrize("P", [0, 32, 64, 256, 512, 1024, 2048])
+def test_decode_partition_sizes(B, P, bs):
+    if P and P % bs:
+        pytest.skip("partition size must be a multiple of the block size")
+    _say(f"decode forced partition_size={P} block_size={bs}")
+    b = medium(bs=bs)
+    got = run_decode(B, b, partition_size=P)
+    check_close(tensors.widen(got, b.dtype), oracle.decode_batch(b), b.dtype, f"P={P}")
+
+
+SHAPES = [(dt, D, G, bs) for dt in ("f32", "f16", "bf16") for D in (64, 128, 256)
+          for G in (1, 2, 4, 8) for bs in (1, 8, 16, 32)]
+
+
+@pytest.mark.parametrize("dtype,D,G,bs", SHAPES)
+def test_decode_shapes(B, dtype, D, G, bs):
+    lens = (1, bs + 1, 3 * bs + 5, 77, 300)
+    b = W.make_custom(1000 + D + 10 * G + bs, dtype=dtype, num_seqs=len(lens), num_q_heads=G * 2,
+                      num_kv_heads=2, head_dim=D, block_size=bs, context_lens=lens,
+                      extra_blocks=5, poison=True)
+    ref = oracle.decode_batch(b)
+    for P in (0, max(16, bs) * 2):
+        got = run_decode(B, b, partition_size=P)
+        check_close(tensors.widen(got, dtype), ref, dtype, f"{dtype} D={D} G={G} bs={bs} P={P}")
+
+
+def test_context_len_one_is_exactly_v(B):
+    for dtype, G in (("bf16", 4), ("f16", 1), ("f32", 2)):
+        b = W.make_custom(81, dtype=dtype, num_seqs=5, num_q_heads=2 * G, num_kv_heads=2,
+                          head_dim=128, block_size=16, context_lens=(1,) * 5, poison=True)
+        got = run_decode(B, b)
+        for s in range(5):
+            v = b.value_cache[b.block_tables[s, 0], 0]          # [Hkv, D] bits
+            for h in range(2 * G):
+                assert np.array_equal(got[s, h].view(np.uint8), v[h // G].view(np.uint8))
+
+
+def test_block_permutation_bit_identical(B):
+    b = medium()
+    p = W.permute_blocks(b, 5)
+    assert np.array_equal(run_decode(B, b).view(np.uint16), run_decode(B, p).view(np.uint16))
+    for P in (64, 256):
+        assert np.array_equal(run_decode(B, b, partition_size=P).view(np.uint16),
+                              run_decode(B, p, partition_size=P).view(np.uint16))
+
+
+def test_poison_bit_identical(B):
+    kw = dict(dtype="f16", num_seqs=6, num_q_heads=8, num_kv_heads=2, head_dim=128,
+              block_size=16, context_lens=(1, 5, 16, 31, 200, 511), extra_blocks=9,
+              max_blocks_per_seq=40)
+    clean = W.make_custom(91, poison=False, **kw)
+    dirty = W.make_custom(91, poison=True, **kw)
+    for P in (0, 64):
+        a = run_decode(B, clean, partition_size=P)
+        c = run_decode(B, dirty, partition_size=P)
+        assert np.array_equal(a, c)
+        assert np.all(np.isfinite(tensors.widen(c, "f16")))
+
+
+def test_deterministic(B):
+    b = workload("long_context_bf16")
+    d = tensors.device_batch(b, DEV)
+    first = run_decode(B, b, d)
+    for _ in range(3):
+        assert np.array_equal(run_decode(B, b, d), first)
+
+
+def test_empty_context_gives_zeros(B):
+    for P in (0, 32):
+        b = W.make_custom(95, dtype="bf16", num_seqs=3, num_q_heads=8, num_kv_heads=2,
+                          head_dim=128, block_size=16, context_lens=(0, 40, 0), poison=True)
+        got = tensors.widen(run_decode(B, b, partition_size=P), "bf16")
+        assert np.all(got[0] == 0) and np.all(got[2] == 0)
+        check_close(got[1:2], oracle.decode_batch(b)[1:2], "bf16", f"empty P={P}")
+
+
+def test_invalid_device_values_give_nan(B):
+    """Lengths above max_context_len or negative, and table entries outside
+    the pool, are caught by the kernels: that sequence's output is NaN and
+    the others are unaffected."""
+    b = W.make_custom(97, dtype="bf16", num_seqs=4, num_q_heads=8, num_kv_heads=2,
+                      head_dim=128, block_size=16, context_lens=(20, 40, 60, 33),
+                      max_blocks_per_seq=8, poison=True)
+    ref = oracle.decode_batch(b)
+    bad = b.copy()
+    bad.context_lens[0] = 65          # above max_context_len = 64
+    bad.block_tables[1, 1] = b.num_blocks + 3
+    bad.context_lens[3] = -5
+    for P in (0, 16):
+        got = tensors.widen(run_decode(B, bad, partition_size=P, max_context_len=64), "bf16")
+        assert np.all(np.isnan(got[0])) and np.all(np.isnan(got[1])) and np.all(np.isnan(got[3]))
+        check_close(got[2:3], ref[2:3], "bf16", f"valid neighbour P={P}")
