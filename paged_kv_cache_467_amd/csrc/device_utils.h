@@ -21,8 +21,13 @@ struct F32 {
     static constexpr int kBytes = 4;
     static constexpr int kPerChunk = 4;
     __device__ static inline void widen(const u32x4 &c, float *v) {
+        // element copied to a scalar first: a bit cast straight from the
+        // vector element lvalue reads element 0 with this compiler
 #pragma unroll
-        for (int i = 0; i < 4; ++i) v[i] = __builtin_bit_cast(float, c[i]);
+        for (int i = 0; i < 4; ++i) {
+            const uint32_t w = c[i];
+            v[i] = __builtin_bit_cast(float, w);
+        }
     }
     __device__ static inline void store(void *base, int64_t i, float x) {
         static_cast<float *>(base)[i] = x;
