@@ -14,9 +14,13 @@
 
 namespace {
 
-// Aim for about eight decode workgroups per compute unit (256 CUs) before
-// splitting contexts any further; never split below this many tokens.
-constexpr int kTargetWorkgroups = 2048;
+// Aim for about two decode workgroups (of up to 8 waves) per compute unit
+// (256 CUs) before splitting contexts any further; never split below this
+// many tokens.
+#ifndef PKV_TARGET_WORKGROUPS
+#define PKV_TARGET_WORKGROUPS 512
+#endif
+constexpr int kTargetWorkgroups = PKV_TARGET_WORKGROUPS;
 constexpr int kMinSplitTokens = 256;
 
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
@@ -35,12 +39,26 @@ struct Plan {
     int max_context_len;
     int partition_size;
     int num_partitions;
+    int heads_per_group;  // kv heads per decode workgroup (one wave each)
 };
+
+// Kv heads per workgroup: the largest power of two up to PKV_HEADS_PER_GROUP
+// that divides num_kv_heads.
+#ifndef PKV_HEADS_PER_GROUP
+#define PKV_HEADS_PER_GROUP 4
+#endif
+static_assert(PKV_HEADS_PER_GROUP >= 1 && PKV_HEADS_PER_GROUP <= pkv::kMaxDecodeWaves,
+              "heads per group");
+int heads_per_group_for(int num_kv_heads) {
+    for (int h = PKV_HEADS_PER_GROUP; h > 1; h /= 2)
+        if (num_kv_heads % h == 0) return h;
+    return 1;
+}
 
 // Shape checks shared by the decode entry points, and the partition choice.
 Plan plan_decode(int num_seqs, int num_q_heads, int num_kv_heads, int head_dim, int block_size,
                  int max_blocks_per_seq, int max_context_len, int partition_size, int dtype) {
-    Plan pl{PAGED_KV_OK, 0, 0, 1};
+    Plan pl{PAGED_KV_OK, 0, 0, 1, 1};
     if (dtype != PAGED_KV_F32 && dtype != PAGED_KV_F16 && dtype != PAGED_KV_BF16) {
         pl.status = PAGED_KV_ERR_UNSUPPORTED;
         return pl;
@@ -78,7 +96,7 @@ Plan plan_decode(int num_seqs, int num_q_heads, int num_kv_heads, int head_dim, 
         }
         P = partition_size;
     } else {
-        const int64_t units = (int64_t)num_seqs * num_kv_heads;
+        const int64_t units = (int64_t)num_seqs * (num_kv_heads / heads_per_group_for(num_kv_heads));
         int64_t parts = units > 0 ? (kTargetWorkgroups + units - 1) / units : 1;
         const int64_t most = (max_ctx + kMinSplitTokens - 1) / kMinSplitTokens;
         if (parts > most) parts = most;
@@ -96,6 +114,7 @@ Plan plan_decode(int num_seqs, int num_q_heads, int num_kv_heads, int head_dim, 
     pl.max_context_len = max_ctx;
     pl.partition_size = (int)P;
     pl.num_partitions = (int)nparts;
+    pl.heads_per_group = heads_per_group_for(num_kv_heads);
     return pl;
 }
 
@@ -163,6 +182,8 @@ int paged_attn_decode(const void *query, const void *key_cache, const void *valu
         return PAGED_KV_ERR_WORKSPACE;
 
     const int e = elem_bytes(dtype);
+    // The kernels address a block's rows with 32-bit offsets.
+    if ((int64_t)block_size * num_kv_heads * head_dim * e > INT_MAX) return PAGED_KV_ERR_BAD_SHAPE;
     pkv::DecodeParams p;
     p.query = query;
     p.key_cache = static_cast<const char *>(key_cache);
@@ -186,6 +207,8 @@ int paged_attn_decode(const void *query, const void *key_cache, const void *valu
     p.max_context_len = pl.max_context_len;
     p.partition_size = pl.partition_size;
     p.num_partitions = pl.num_partitions;
+    p.heads_per_group = pl.heads_per_group;
+    p.num_head_groups = num_kv_heads / pl.heads_per_group;
     p.row_stride_bytes = num_kv_heads * head_dim * e;
     p.block_stride_bytes = (int64_t)block_size * p.row_stride_bytes;
 

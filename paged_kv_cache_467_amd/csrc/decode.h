@@ -9,9 +9,10 @@ namespace pkv {
 // Block ids of one context partition are staged in LDS; a partition may span
 // at most this many blocks.
 constexpr int kBtLds = 1024;
-// Workgroup shape of the decode kernels: 4 waves of 64 lanes.
-constexpr int kDecodeThreads = 256;
-constexpr int kDecodeWaves = kDecodeThreads / 64;
+// A decode workgroup has one wave of 64 lanes per kv head of its group, at
+// most this many.
+constexpr int kMaxDecodeWaves = 8;
+constexpr int kMaxDecodeThreads = kMaxDecodeWaves * 64;
 
 struct DecodeParams {
     const void *query;          // [S, Hq, D]
@@ -34,6 +35,8 @@ struct DecodeParams {
     int max_context_len;        // every valid context_len is <= this
     int partition_size;         // tokens per partition
     int num_partitions;         // P_max = ceil(max_context_len / partition_size)
+    int heads_per_group;        // kv heads (= waves) per workgroup
+    int num_head_groups;        // num_kv_heads / heads_per_group
     int64_t block_stride_bytes; // bs * Hkv * D * elem bytes
     int row_stride_bytes;       // Hkv * D * elem bytes
 };

@@ -10,13 +10,23 @@
 // only name this as segmented attention over scattered blocks
 // ("23.1 vLLM：高吞吐推理框架原理与部署", §二.2 step 3).
 //
-// Work decomposition: one workgroup of 4 waves per (sequence, kv head,
-// context partition).  The workgroup first stages the partition's block ids
-// in LDS (checking each against the pool size), then its waves take 16-token
-// tiles of the partition in turn.  Each wave keeps its own online-softmax
-// state (running max m, running sum l, fp32 output accumulator) for the G
-// query heads that share the kv head, so every K/V byte is read once for all
-// G heads.  At the end the four waves are merged through LDS.
+// Work decomposition: one workgroup per (sequence, group of kv heads,
+// context partition), one wave per kv head of the group.  The workgroup
+// stages the partition's block ids in LDS once (checking each against the
+// pool size); then every wave walks the whole partition for its kv head, one
+// tile of at most 16 tokens at a time, keeping the online-softmax state
+// (running max m, running sum l, fp32 output accumulator) of the G query
+// heads that share that kv head, so every K/V byte is read once for all G
+// heads.  The waves of a workgroup read the same token rows side by side (a
+// block of all kv heads is one contiguous stretch of the pool), and a wave's
+// result needs no merge with other waves.  K/V tiles are loaded DEPTH - 1
+// tiles ahead of the one being consumed, with non-temporal loads.
+//
+// Addressing: tiles never cross a 16-token boundary, so with block_size >= 16
+// a tile lies in one block and its base address is wave-uniform (block id
+// read once from LDS into a scalar register); each lane adds a fixed offset.
+// Smaller blocks and the last, partial tile of a partition use per-lane
+// addresses with bounds guards.
 //
 // Two per-tile inner loops:
 //  * decode_mfma_kernel (f16/bf16, G >= 2): the scores of a 16-token tile for
@@ -27,8 +37,11 @@
 //    is accumulated with fp32 FMAs.
 //  * decode_valu_kernel (all dtypes, any G): each row of head_dim elements is
 //    spread over head_dim * bytes / 16 lanes, 16 bytes each; scores are dot
-//    products reduced across those lanes with DPP.
-// Loads of the next tile are issued before the current tile is consumed.
+//    products (packed 16-bit dot instructions for f16/bf16, fp32 FMAs for
+//    f32) reduced across those lanes with DPP.
+// Online softmax: the running max only moves when some score of the tile
+// exceeds it; each lane checks its own scores, and the cross-lane max
+// reduction and the rescale of l and the accumulator run only when one did.
 
 #include "decode.h"
 #include "device_utils.h"
@@ -38,8 +51,15 @@
 namespace pkv {
 namespace {
 
+// K/V tiles held in registers per wave: one being consumed, the rest in flight.
+#ifndef PKV_TILE_DEPTH
+#define PKV_TILE_DEPTH 2
+#endif
+constexpr int kDepth = PKV_TILE_DEPTH;
+
 struct WorkItem {
-    int s, kvh, part;
+    int s, kvh0, part;  // sequence, first kv head of the workgroup, partition
+    int kvh;            // this wave's kv head
     int context_len;
     int tok_begin, tok_end;  // this partition's token range [begin, end)
     bool bad_len;            // context_len < 0 or > max_context_len
@@ -48,13 +68,12 @@ struct WorkItem {
 __device__ inline WorkItem work_item(const DecodeParams &p) {
     WorkItem w;
     const int id = blockIdx.x;
-    // kv head fastest: consecutive workgroups go to consecutive XCDs, so all
-    // workgroups of one kv head (which share any shared-prefix blocks) land
-    // on the same XCD and its L2 when num_kv_heads is a multiple of 8.
-    w.kvh = id % p.num_kv_heads;
-    const int rest = id / p.num_kv_heads;
+    const int hg = id % p.num_head_groups;
+    const int rest = id / p.num_head_groups;
     w.part = rest % p.num_partitions;
     w.s = rest / p.num_partitions;
+    w.kvh0 = hg * p.heads_per_group;
+    w.kvh = w.kvh0 + (int)(threadIdx.x / kWave);
     w.context_len = p.context_lens[w.s];
     w.bad_len = w.context_len < 0 || w.context_len > p.max_context_len;
     w.tok_begin = w.part * p.partition_size;
@@ -71,7 +90,7 @@ __device__ inline bool stage_block_table(const DecodeParams &p, const WorkItem &
     const int b1 = (w.tok_end - 1) >> p.block_shift;
     const int32_t *row = p.block_tables + (int64_t)w.s * p.max_blocks_per_seq;
     int bad = 0;
-    for (int i = threadIdx.x; i <= b1 - b0; i += kDecodeThreads) {
+    for (int i = threadIdx.x; i <= b1 - b0; i += blockDim.x) {
         int id = row[b0 + i];
         if (id < 0 || id >= p.num_blocks) {
             bad = 1;
@@ -91,55 +110,27 @@ __device__ inline int64_t row_offset(const DecodeParams &p, const int32_t *bt_ld
     return (int64_t)blk * p.block_stride_bytes + (int64_t)(off * p.row_stride_bytes + head_bytes);
 }
 
-// Output of a workgroup that reads nothing: zeros for an empty sequence, NaN
-// for an invalid one.
-template <class T, int D, int G>
-__device__ void store_constant(const DecodeParams &p, const WorkItem &w, bool nan) {
-    for (int i = threadIdx.x; i < G * D; i += kDecodeThreads) {
-        const int g = i / D, d = i % D;
-        const int64_t o = ((int64_t)w.s * p.num_q_heads + w.kvh * G + g) * D + d;
-        if (nan)
-            T::store_nan(p.out, o);
-        else
-            T::store(p.out, o, 0.0f);
-    }
+// Byte offset of the row of token t0 (kv head 0) for a wave-uniform t0 when
+// block_size >= 16: the block id goes through a scalar register, so the
+// address arithmetic is scalar.
+__device__ inline int64_t uniform_row_offset(const DecodeParams &p, const int32_t *bt_lds, int b0,
+                                             int t0) {
+    const int blk = __builtin_amdgcn_readfirstlane(bt_lds[(t0 >> p.block_shift) - b0]);
+    const int off = t0 & (p.block_size - 1);
+    return (int64_t)blk * p.block_stride_bytes + (int64_t)off * p.row_stride_bytes;
 }
 
-// Merges the per-wave states in LDS and writes either the final output (no
-// split) or this partition's partial (m, l, unnormalised o).
+// Output of a workgroup that reads nothing: zeros for an empty sequence, NaN
+// for an invalid one; covers every query head of the workgroup's kv heads.
 template <class T, int D, int G>
-__device__ void merge_waves(const DecodeParams &p, const WorkItem &w, const float (*mw)[G],
-                            const float (*lw)[G], const float (*ow)[G][D], bool bad) {
-    const bool split = p.num_partitions > 1;
-    for (int i = threadIdx.x; i < G * D; i += kDecodeThreads) {
-        const int g = i / D, d = i % D;
-        float M = mw[0][g];
-#pragma unroll
-        for (int v = 1; v < kDecodeWaves; ++v) M = fmaxf(M, mw[v][g]);
-        float Ls = 0.0f, O = 0.0f;
-        if (M != -INFINITY) {
-#pragma unroll
-            for (int v = 0; v < kDecodeWaves; ++v) {
-                const float f = fast_exp2(mw[v][g] - M);  // 0 for a wave that saw no token
-                Ls += lw[v][g] * f;
-                O += ow[v][g][d] * f;
-            }
-        }
-        const int h = w.kvh * G + g;
-        if (!split) {
-            const int64_t o = ((int64_t)w.s * p.num_q_heads + h) * D + d;
-            if (bad)
-                T::store_nan(p.out, o);
-            else
-                T::store(p.out, o, Ls > 0.0f ? O / Ls : 0.0f);
-        } else {
-            const int64_t ph = ((int64_t)w.s * p.num_q_heads + h) * p.num_partitions + w.part;
-            p.part_out[ph * D + d] = bad ? NAN : O;
-            if (d == 0) {
-                p.part_max[ph] = bad ? 0.0f : M;
-                p.part_sum[ph] = bad ? NAN : Ls;
-            }
-        }
+__device__ void store_constant(const DecodeParams &p, const WorkItem &w, bool nan) {
+    const int n = p.heads_per_group * G * D;
+    const int64_t base = ((int64_t)w.s * p.num_q_heads + (int64_t)w.kvh0 * G) * D;
+    for (int i = threadIdx.x; i < n; i += blockDim.x) {
+        if (nan)
+            T::store_nan(p.out, base + i);
+        else
+            T::store(p.out, base + i, 0.0f);
     }
 }
 
@@ -147,51 +138,113 @@ __device__ void merge_waves(const DecodeParams &p, const WorkItem &w, const floa
 // has then already written whatever it owes).
 template <class T, int D, int G>
 __device__ bool prologue(const DecodeParams &p, const WorkItem &w) {
-    const bool split = p.num_partitions > 1;
     if (w.bad_len || w.tok_begin >= w.context_len) {
         // Without a split this workgroup owns the output (zeros when L == 0,
         // NaN when L is invalid).  With a split the reduce kernel owns it.
-        if (!split) store_constant<T, D, G>(p, w, w.bad_len);
+        if (p.num_partitions == 1) store_constant<T, D, G>(p, w, w.bad_len);
         return false;
     }
     return true;
 }
 
+// Writes one wave's result for query head h: the 16-byte chunk of output
+// elements starting at d0 (T::kPerChunk of them), from fp32 accumulators acc
+// (unnormalised), with the head's final running max m and sum l.  Without a
+// split the normalised output is stored in the output dtype; with a split
+// the partial (m, l, acc) is.
+template <class T, int D>
+__device__ inline void write_result(const DecodeParams &p, const WorkItem &w, int h, int d0,
+                                    const float *acc, float m, float l, bool bad,
+                                    bool write_ml) {
+    constexpr int EPC = T::kPerChunk;
+    if (p.num_partitions == 1) {
+        const int64_t o = ((int64_t)w.s * p.num_q_heads + h) * D + d0;
+        u32x4 c;
+        if (bad) {
+            c = u32x4{T::kNanPair, T::kNanPair, T::kNanPair, T::kNanPair};
+        } else {
+            const float inv = l > 0.0f ? 1.0f / l : 0.0f;
+            float v[EPC];
+#pragma unroll
+            for (int e = 0; e < EPC; ++e) v[e] = acc[e] * inv;
+            c = T::narrow_chunk(v);
+        }
+        store16(static_cast<char *>(p.out) + o * T::kBytes, c);
+    } else {
+        const int64_t ph = ((int64_t)w.s * p.num_q_heads + h) * p.num_partitions + w.part;
+        float *po = p.part_out + ph * D + d0;
+#pragma unroll
+        for (int e = 0; e < EPC; e += 4) {
+            u32x4 c;
+#pragma unroll
+            for (int k = 0; k < 4; ++k)
+                c[k] = bad ? 0x7FC00000u : __builtin_bit_cast(uint32_t, acc[e + k]);
+            store16(po + e, c);
+        }
+        if (write_ml) {
+            p.part_max[ph] = bad ? 0.0f : m;
+            p.part_sum[ph] = bad ? NAN : l;
+        }
+    }
+}
+
+// Runs the tile pipeline of one wave: tiles [0, ntiles), of which the first
+// nfull are complete; load(t, slot, full) fills register slot `slot` with
+// tile t, consume(t, slot, full) folds it into the softmax state.  Slots are
+// compile-time indices after unrolling, so the buffers stay in registers.
+template <int DEPTH, class Load, class Consume>
+__device__ inline void run_tiles(int ntiles, int nfull, Load &&load, Consume &&consume) {
+#pragma unroll
+    for (int j = 0; j < DEPTH - 1; ++j)
+        if (j < ntiles) load(j, j, j < nfull);
+    for (int t0 = 0; t0 < ntiles; t0 += DEPTH) {
+#pragma unroll
+        for (int j = 0; j < DEPTH; ++j) {
+            const int t = t0 + j;
+            if (t < ntiles) {
+                const int ahead = t + DEPTH - 1;
+                if (ahead < ntiles) load(ahead, (j + DEPTH - 1) % DEPTH, ahead < nfull);
+                consume(t, j, t < nfull);
+            }
+        }
+    }
+}
+
 // ------------------------------------------------------------------------
 // VALU kernel
 // ------------------------------------------------------------------------
-template <class T, int D, int G>
-__global__ __launch_bounds__(kDecodeThreads) void decode_valu_kernel(DecodeParams p) {
+template <class T, int D, int G, bool BT>
+__global__ __launch_bounds__(kMaxDecodeThreads) void decode_valu_kernel(DecodeParams p) {
     constexpr int EPC = T::kPerChunk;   // elements per 16-byte chunk
     constexpr int CPR = D / EPC;        // lanes holding one row
     constexpr int TPI = kWave / CPR;    // tokens per load instruction
-    constexpr int NL = 4;               // loads per lane per tile (K and V each)
-    constexpr int TILE = TPI * NL;      // tokens per tile
-    static_assert(CPR >= 1 && CPR <= 64 && kWave % CPR == 0, "row layout");
+    constexpr int NL = TPI <= 4 ? 4 : 16 / TPI;  // loads per lane per tile (K and V each)
+    constexpr int TILE = TPI * NL;      // tokens per tile: 4, 8 or 16, divides 16
+    static_assert(CPR >= 4 && CPR <= 64 && kWave % CPR == 0, "row layout");
+    static_assert(16 % TILE == 0, "tiles must not cross a 16-token boundary");
+    // wide rows or many fp32 accumulators: no room for a second tile
+    constexpr int DEPTH = (D >= 256 || G * EPC >= 32) ? 1 : kDepth;
 
     __shared__ int32_t bt_lds[kBtLds];
-    __shared__ float mw[kDecodeWaves][G];
-    __shared__ float lw[kDecodeWaves][G];
-    __shared__ float ow[kDecodeWaves][G][D];
 
     const WorkItem w = work_item(p);
     if (!prologue<T, D, G>(p, w)) return;
     const bool bad = stage_block_table(p, w, bt_lds);
     const int b0 = w.tok_begin >> p.block_shift;
 
-    const int wave = threadIdx.x / kWave;
     const int lane = threadIdx.x % kWave;
     const int tg = lane / CPR;  // token slot within a load
     const int c = lane % CPR;   // 16-byte chunk of the row
     const int head_bytes = w.kvh * D * T::kBytes + c * 16;
+    // offset of this lane's chunk from the row of the tile's first token
+    const uint32_t lane_off = (uint32_t)(tg * p.row_stride_bytes + head_bytes);
+    const uint32_t step_off = (uint32_t)(TPI * p.row_stride_bytes);  // per load of a tile
 
-    float q[G][EPC];
+    u32x4 q[G];
 #pragma unroll
-    for (int g = 0; g < G; ++g) {
-        const int64_t qo = (((int64_t)w.s * p.num_q_heads + w.kvh * G + g) * D + c * EPC) *
-                           T::kBytes;
-        T::widen(load16(static_cast<const char *>(p.query) + qo), q[g]);
-    }
+    for (int g = 0; g < G; ++g)
+        q[g] = load16(static_cast<const char *>(p.query) +
+                      (((int64_t)w.s * p.num_q_heads + w.kvh * G + g) * D + c * EPC) * T::kBytes);
 
     float m[G], l[G], acc[G][EPC];
 #pragma unroll
@@ -202,99 +255,102 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_valu_kernel(DecodeParam
         for (int e = 0; e < EPC; ++e) acc[g][e] = 0.0f;
     }
 
-    const int ntiles = bad ? 0 : (w.tok_end - w.tok_begin + TILE - 1) / TILE;
-    u32x4 kb[NL], vb[NL];
-    auto load_tile = [&](int tile, u32x4 *kd, u32x4 *vd) {
+    const int span = w.tok_end - w.tok_begin;
+    const int ntiles = bad ? 0 : (span + TILE - 1) / TILE;
+    const int nfull = bad ? 0 : span / TILE;
+    u32x4 kbuf[DEPTH][NL], vbuf[DEPTH][NL];
+
+    auto load = [&](int tile, int slot, bool full) {
+        const int t0 = w.tok_begin + tile * TILE;
 #pragma unroll
-        for (int i = 0; i < NL; ++i) {
-            const int t = w.tok_begin + tile * TILE + i * TPI + tg;
-            if (t < w.tok_end) {
-                const int64_t o = row_offset(p, bt_lds, b0, t, head_bytes);
-                kd[i] = load16(p.key_cache + o);
-                vd[i] = load16(p.value_cache + o);
+        for (int j = 0; j < DEPTH; ++j) {
+            if (j != slot) continue;
+            if (BT && full) {
+                const int64_t base = uniform_row_offset(p, bt_lds, b0, t0);
+                const char *kb = p.key_cache + base;
+                const char *vb = p.value_cache + base;
+#pragma unroll
+                for (int i = 0; i < NL; ++i) {
+                    kbuf[j][i] = load16_stream(kb + (lane_off + i * step_off));
+                    vbuf[j][i] = load16_stream(vb + (lane_off + i * step_off));
+                }
             } else {
-                kd[i] = u32x4{0, 0, 0, 0};
-                vd[i] = u32x4{0, 0, 0, 0};
+#pragma unroll
+                for (int i = 0; i < NL; ++i) {
+                    const int t = t0 + i * TPI + tg;
+                    if (t < w.tok_end) {
+                        const int64_t o = row_offset(p, bt_lds, b0, t, head_bytes);
+                        kbuf[j][i] = load16_stream(p.key_cache + o);
+                        vbuf[j][i] = load16_stream(p.value_cache + o);
+                    } else {
+                        kbuf[j][i] = u32x4{0, 0, 0, 0};
+                        vbuf[j][i] = u32x4{0, 0, 0, 0};
+                    }
+                }
             }
         }
     };
 
-    int tile = wave;
-    if (tile < ntiles) load_tile(tile, kb, vb);
-    for (; tile < ntiles; tile += kDecodeWaves) {
-        u32x4 kn[NL], vn[NL];
-        const int next = tile + kDecodeWaves;
-        if (next < ntiles) load_tile(next, kn, vn);
-
-        float sc[NL][G];
+    auto consume = [&](int tile, int slot, bool full) {
 #pragma unroll
-        for (int i = 0; i < NL; ++i) {
-            float k[EPC];
-            T::widen(kb[i], k);
-            const bool valid = w.tok_begin + tile * TILE + i * TPI + tg < w.tok_end;
+        for (int j = 0; j < DEPTH; ++j) {
+            if (j != slot) continue;
+            const int t0 = w.tok_begin + tile * TILE;
+            float sc[NL][G];
+            bool up = false;
 #pragma unroll
-            for (int g = 0; g < G; ++g) {
-                float d = 0.0f;
+            for (int i = 0; i < NL; ++i) {
+                const bool valid = full || t0 + i * TPI + tg < w.tok_end;
 #pragma unroll
-                for (int e = 0; e < EPC; ++e) d = fmaf(q[g][e], k[e], d);
-                d = group_sum<CPR>(d);
-                sc[i][g] = valid ? d * p.scale_log2 : -INFINITY;
+                for (int g = 0; g < G; ++g) {
+                    const float d = group_sum<CPR>(T::dot_chunk(q[g], kbuf[j][i], 0.0f));
+                    sc[i][g] = valid ? d * p.scale_log2 : -INFINITY;
+                    up |= sc[i][g] > m[g];
+                }
+            }
+            if (__builtin_amdgcn_ballot_w64(up) != 0) {
+#pragma unroll
+                for (int g = 0; g < G; ++g) {
+                    float x = sc[0][g];
+#pragma unroll
+                    for (int i = 1; i < NL; ++i) x = vmax(x, sc[i][g]);
+                    const float mn = vmax(m[g], across_groups_max<CPR>(x));
+                    const float alpha = fast_exp2(m[g] - mn);  // 0 on the first tile
+                    m[g] = mn;
+                    l[g] *= alpha;
+#pragma unroll
+                    for (int e = 0; e < EPC; ++e) acc[g][e] *= alpha;
+                }
+            }
+#pragma unroll
+            for (int i = 0; i < NL; ++i) {
+                float v[EPC];
+                T::widen(vbuf[j][i], v);
+#pragma unroll
+                for (int g = 0; g < G; ++g) {
+                    const float pr = fast_exp2(sc[i][g] - m[g]);
+                    l[g] += pr;
+#pragma unroll
+                    for (int e = 0; e < EPC; ++e) acc[g][e] = fmaf(pr, v[e], acc[g][e]);
+                }
             }
         }
-#pragma unroll
-        for (int g = 0; g < G; ++g) {
-            float mt = sc[0][g];
-#pragma unroll
-            for (int i = 1; i < NL; ++i) mt = fmaxf(mt, sc[i][g]);
-            mt = across_groups_max<CPR>(mt);
-            const float mn = fmaxf(m[g], mt);
-            const float alpha = fast_exp2(m[g] - mn);
-            m[g] = mn;
-            l[g] *= alpha;
-#pragma unroll
-            for (int e = 0; e < EPC; ++e) acc[g][e] *= alpha;
-        }
-#pragma unroll
-        for (int i = 0; i < NL; ++i) {
-            float v[EPC];
-            T::widen(vb[i], v);
-#pragma unroll
-            for (int g = 0; g < G; ++g) {
-                const float pr = fast_exp2(sc[i][g] - m[g]);
-                l[g] += pr;
-#pragma unroll
-                for (int e = 0; e < EPC; ++e) acc[g][e] = fmaf(pr, v[e], acc[g][e]);
-            }
-        }
-#pragma unroll
-        for (int i = 0; i < NL; ++i) {
-            kb[i] = kn[i];
-            vb[i] = vn[i];
-        }
-    }
+    };
 
-    // Combine the token groups of the wave, then the waves.
+    run_tiles<DEPTH>(ntiles, nfull, load, consume);
+
+    // Combine the token groups of the wave: l and acc over the TPI groups.
 #pragma unroll
     for (int g = 0; g < G; ++g) {
         l[g] = across_groups_sum<CPR>(l[g]);
 #pragma unroll
         for (int e = 0; e < EPC; ++e) acc[g][e] = across_groups_sum<CPR>(acc[g][e]);
     }
-    if (lane == 0) {
-#pragma unroll
-        for (int g = 0; g < G; ++g) {
-            mw[wave][g] = m[g];
-            lw[wave][g] = l[g];
-        }
-    }
     if (tg == 0) {
 #pragma unroll
         for (int g = 0; g < G; ++g)
-#pragma unroll
-            for (int e = 0; e < EPC; ++e) ow[wave][g][c * EPC + e] = acc[g][e];
+            write_result<T, D>(p, w, w.kvh * G + g, c * EPC, acc[g], m[g], l[g], bad, c == 0);
     }
-    __syncthreads();
-    merge_waves<T, D, G>(p, w, mw, lw, ow, bad);
 }
 
 // ------------------------------------------------------------------------
@@ -318,8 +374,8 @@ __device__ inline f32x4 mfma16x16x32<F16>(const u32x4 &a, const u32x4 &b, const 
 // lane l receives result rows 4 * (l / 16) + r, r = 0..3, of column l % 16.
 // Any pairing of k values works as long as A and B use the same one, so the
 // k-group of lane l in step ks is 16-byte chunk (l / 16) + 4 * ks of a row.
-template <class T, int D, int G>
-__global__ __launch_bounds__(kDecodeThreads) void decode_mfma_kernel(DecodeParams p) {
+template <class T, int D, int G, bool BT>
+__global__ __launch_bounds__(kMaxDecodeThreads) void decode_mfma_kernel(DecodeParams p) {
     static_assert(T::kBytes == 2, "MFMA path is for 16-bit element types");
     static_assert(G == 2 || G == 4 || G == 8, "group size");
     constexpr int KS = D / 32;        // MFMA k-steps per tile
@@ -327,13 +383,14 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_mfma_kernel(DecodeParam
     constexpr int TPI = kWave / CPR;  // tokens per V load instruction
     constexpr int NV = 16 / TPI;      // V loads per lane per tile
     constexpr int TILE = 16;
+    constexpr int HW = G < 4 ? G : 4;  // heads among a lane's four result rows
+    constexpr int DEPTH = D >= 256 ? 1 : kDepth;  // wide rows: no room for a second tile
 
     __shared__ int32_t bt_lds[kBtLds];
-    __shared__ float pex[kDecodeWaves][TILE][G];  // softmax weights of the tile
-    __shared__ float aex[kDecodeWaves][G];        // rescale factors of the tile
-    __shared__ float mw[kDecodeWaves][G];
-    __shared__ float lw[kDecodeWaves][G];
-    __shared__ float ow[kDecodeWaves][G][D];
+    // softmax weights of the tile (16-byte aligned: read and written as f32x4)
+    __shared__ __attribute__((aligned(16))) float pex[kMaxDecodeWaves][TILE][G];
+    __shared__ float aex[kMaxDecodeWaves][G];  // rescale factors, then final m
+    __shared__ float lex[kMaxDecodeWaves][G];  // final l
 
     const WorkItem w = work_item(p);
     if (!prologue<T, D, G>(p, w)) return;
@@ -349,6 +406,13 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_mfma_kernel(DecodeParam
     const int vtg = lane / CPR;
     const int vc = lane % CPR;
     const int head_bytes = w.kvh * D * 2;
+    // offsets from the row of the tile's first token
+    const uint32_t k_off = (uint32_t)(kt * p.row_stride_bytes + head_bytes + 16 * rg);
+    const uint32_t v_off = (uint32_t)(vtg * p.row_stride_bytes + head_bytes + 16 * vc);
+    const uint32_t v_step = (uint32_t)(TPI * p.row_stride_bytes);
+    // row group rg holds heads 4 * rg .. 4 * rg + HW - 1; groups with
+    // 4 * rg >= G hold copies of those rows
+    const bool owns_rows = 4 * rg < G;
 
     // A operand: query head (kt % G) of this kv head's group
     u32x4 qa[KS];
@@ -371,87 +435,122 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_mfma_kernel(DecodeParam
 #pragma unroll
         for (int e = 0; e < 8; ++e) acc[g][e] = 0.0f;
 
-    const int ntiles = bad ? 0 : (w.tok_end - w.tok_begin + TILE - 1) / TILE;
-    auto load_tile = [&](int tile, u32x4 *kd, u32x4 *vd) {
-        const int base = w.tok_begin + tile * TILE;
-        {
-            const int t = base + kt;
-            if (t < w.tok_end) {
-                const char *row = p.key_cache + row_offset(p, bt_lds, b0, t, head_bytes);
+    const int span = w.tok_end - w.tok_begin;
+    const int ntiles = bad ? 0 : (span + TILE - 1) / TILE;
+    const int nfull = bad ? 0 : span / TILE;
+    u32x4 kbuf[DEPTH][KS], vbuf[DEPTH][NV];
+
+    auto load = [&](int tile, int slot, bool full) {
+        const int t0 = w.tok_begin + tile * TILE;
 #pragma unroll
-                for (int ks = 0; ks < KS; ++ks) kd[ks] = load16(row + 16 * (rg + 4 * ks));
+        for (int j = 0; j < DEPTH; ++j) {
+            if (j != slot) continue;
+            if (BT && full) {
+                const int64_t base = uniform_row_offset(p, bt_lds, b0, t0);
+                const char *kb = p.key_cache + base;
+                const char *vb = p.value_cache + base;
+#pragma unroll
+                for (int ks = 0; ks < KS; ++ks)
+                    kbuf[j][ks] = load16_stream(kb + (k_off + 64 * ks));
+#pragma unroll
+                for (int i = 0; i < NV; ++i) vbuf[j][i] = load16_stream(vb + (v_off + i * v_step));
             } else {
+                const int t = t0 + kt;
+                if (t < w.tok_end) {
+                    const char *row = p.key_cache + row_offset(p, bt_lds, b0, t, head_bytes);
 #pragma unroll
-                for (int ks = 0; ks < KS; ++ks) kd[ks] = u32x4{0, 0, 0, 0};
+                    for (int ks = 0; ks < KS; ++ks)
+                        kbuf[j][ks] = load16_stream(row + 16 * (rg + 4 * ks));
+                } else {
+#pragma unroll
+                    for (int ks = 0; ks < KS; ++ks) kbuf[j][ks] = u32x4{0, 0, 0, 0};
+                }
+#pragma unroll
+                for (int i = 0; i < NV; ++i) {
+                    const int tv = t0 + i * TPI + vtg;
+                    if (tv < w.tok_end)
+                        vbuf[j][i] = load16_stream(
+                            p.value_cache + row_offset(p, bt_lds, b0, tv, head_bytes) + 16 * vc);
+                    else
+                        vbuf[j][i] = u32x4{0, 0, 0, 0};
+                }
             }
-        }
-#pragma unroll
-        for (int i = 0; i < NV; ++i) {
-            const int t = base + i * TPI + vtg;
-            if (t < w.tok_end)
-                vd[i] = load16(p.value_cache + row_offset(p, bt_lds, b0, t, head_bytes) + 16 * vc);
-            else
-                vd[i] = u32x4{0, 0, 0, 0};
         }
     };
 
-    u32x4 kb[KS], vb[NV];
-    int tile = wave;
-    if (tile < ntiles) load_tile(tile, kb, vb);
-    for (; tile < ntiles; tile += kDecodeWaves) {
-        u32x4 kn[KS], vn[NV];
-        const int next = tile + kDecodeWaves;
-        if (next < ntiles) load_tile(next, kn, vn);
-
-        f32x4 s = {0.0f, 0.0f, 0.0f, 0.0f};
+    auto consume = [&](int tile, int slot, bool full) {
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) s = mfma16x16x32<T>(qa[ks], kb[ks], s);
-
-        const bool valid = w.tok_begin + tile * TILE + kt < w.tok_end;
+        for (int j = 0; j < DEPTH; ++j) {
+            if (j != slot) continue;
+            f32x4 s = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const float sc = valid ? s[r] * p.scale_log2 : -INFINITY;
-            const float mt = group_max<16>(sc);  // over the 16 tokens of the tile
-            const float mn = fmaxf(m[r], mt);
-            const float alpha = fast_exp2(m[r] - mn);
-            const float pr = fast_exp2(sc - mn);
-            m[r] = mn;
-            l[r] = l[r] * alpha + pr;
-            const int head = 4 * rg + r;
-            if (head < G) {
-                pex[wave][kt][head] = pr;
-                if (kt == 0) aex[wave][head] = alpha;
+            for (int ks = 0; ks < KS; ++ks) s = mfma16x16x32<T>(qa[ks], kbuf[j][ks], s);
+
+            const bool valid = full || w.tok_begin + tile * TILE + kt < w.tok_end;
+            float sc[4];
+            bool up = false;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                sc[r] = valid ? s[r] * p.scale_log2 : -INFINITY;
+                up |= sc[r] > m[r];
             }
+            // Every head is held by some lane, so "no lane's score exceeds its
+            // row's max" means no head's max moves in this tile.
+            const bool rescale = __builtin_amdgcn_ballot_w64(up) != 0;
+            if (rescale) {
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const float mn = vmax(m[r], group_max<16>(sc[r]));  // 16 tokens of the tile
+                    const float alpha = fast_exp2(m[r] - mn);          // 0 on the first tile
+                    m[r] = mn;
+                    l[r] *= alpha;
+                    if (r < HW && owns_rows && kt == 0) aex[wave][4 * rg + r] = alpha;
+                }
+            }
+            float pr[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                pr[r] = fast_exp2(sc[r] - m[r]);
+                l[r] += pr[r];
+            }
+            if (owns_rows) {
+                if constexpr (HW == 4) {
+                    *reinterpret_cast<f32x4 *>(&pex[wave][kt][4 * rg]) =
+                        f32x4{pr[0], pr[1], pr[2], pr[3]};
+                } else {
+#pragma unroll
+                    for (int r = 0; r < HW; ++r) pex[wave][kt][4 * rg + r] = pr[r];
+                }
+            }
+            // The weights were written by this wave; LDS executes a wave's
+            // accesses in order, so only compiler ordering must be kept.
+            __builtin_amdgcn_wave_barrier();
+            if (rescale) {
+                float alpha[G];
+#pragma unroll
+                for (int g = 0; g < G; ++g) alpha[g] = aex[wave][g];
+#pragma unroll
+                for (int g = 0; g < G; ++g)
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) acc[g][e] *= alpha[g];
+            }
+#pragma unroll
+            for (int i = 0; i < NV; ++i) {
+                float v[8];
+                T::widen(vbuf[j][i], v);
+                float pw[G];
+#pragma unroll
+                for (int g = 0; g < G; ++g) pw[g] = pex[wave][i * TPI + vtg][g];
+#pragma unroll
+                for (int g = 0; g < G; ++g)
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) acc[g][e] = fmaf(pw[g], v[e], acc[g][e]);
+            }
+            __builtin_amdgcn_wave_barrier();
         }
-        // The weights were written by this wave; LDS executes a wave's
-        // accesses in order, so only compiler ordering must be kept.
-        __builtin_amdgcn_wave_barrier();
+    };
 
-        float alpha[G];
-#pragma unroll
-        for (int g = 0; g < G; ++g) alpha[g] = aex[wave][g];
-#pragma unroll
-        for (int g = 0; g < G; ++g)
-#pragma unroll
-            for (int e = 0; e < 8; ++e) acc[g][e] *= alpha[g];
-#pragma unroll
-        for (int i = 0; i < NV; ++i) {
-            float v[8];
-            T::widen(vb[i], v);
-            float pw[G];
-#pragma unroll
-            for (int g = 0; g < G; ++g) pw[g] = pex[wave][i * TPI + vtg][g];
-#pragma unroll
-            for (int g = 0; g < G; ++g)
-#pragma unroll
-                for (int e = 0; e < 8; ++e) acc[g][e] = fmaf(pw[g], v[e], acc[g][e]);
-        }
-        __builtin_amdgcn_wave_barrier();
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) kb[ks] = kn[ks];
-#pragma unroll
-        for (int i = 0; i < NV; ++i) vb[i] = vn[i];
-    }
+    run_tiles<DEPTH>(ntiles, nfull, load, consume);
 
     // l: sum over the 16 tokens of each row; acc: over the value token slots.
 #pragma unroll
@@ -460,24 +559,20 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_mfma_kernel(DecodeParam
     for (int g = 0; g < G; ++g)
 #pragma unroll
         for (int e = 0; e < 8; ++e) acc[g][e] = across_groups_sum<CPR>(acc[g][e]);
-    if (kt == 0) {
+    if (kt == 0 && owns_rows) {
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int head = 4 * rg + r;
-            if (head < G) {
-                mw[wave][head] = m[r];
-                lw[wave][head] = l[r];
-            }
+        for (int r = 0; r < HW; ++r) {
+            aex[wave][4 * rg + r] = m[r];
+            lex[wave][4 * rg + r] = l[r];
         }
     }
+    __builtin_amdgcn_wave_barrier();
     if (vtg == 0) {
 #pragma unroll
         for (int g = 0; g < G; ++g)
-#pragma unroll
-            for (int e = 0; e < 8; ++e) ow[wave][g][vc * 8 + e] = acc[g][e];
+            write_result<T, D>(p, w, w.kvh * G + g, vc * 8, acc[g], aex[wave][g], lex[wave][g],
+                               bad, vc == 0);
     }
-    __syncthreads();
-    merge_waves<T, D, G>(p, w, mw, lw, ow, bad);
 }
 
 // ------------------------------------------------------------------------
@@ -514,21 +609,29 @@ __global__ __launch_bounds__(kReduceThreads) void decode_reduce_kernel(DecodePar
     }
 }
 
-template <class T, int D, int G>
-hipError_t launch_typed(const DecodeParams &p, int kernel, hipStream_t stream) {
-    const unsigned grid = (unsigned)((int64_t)p.num_seqs * p.num_kv_heads * p.num_partitions);
-    if (kernel == 1) {
-        if constexpr (T::kBytes == 2 && G >= 2) {
-            hipLaunchKernelGGL((decode_mfma_kernel<T, D, G>), dim3(grid), dim3(kDecodeThreads), 0,
-                               stream, p);
-        } else {
-            return hipErrorInvalidValue;
-        }
+template <class T, int D, int G, bool BT>
+hipError_t launch_main(const DecodeParams &p, int kernel, hipStream_t stream) {
+    const unsigned grid =
+        (unsigned)((int64_t)p.num_seqs * p.num_head_groups * p.num_partitions);
+    const unsigned threads = (unsigned)(p.heads_per_group * kWave);
+    // 16-bit types with grouped queries take the MFMA kernel, everything else
+    // the VALU kernel (decode_kernel_choice); only those pairs are built.
+    if constexpr (T::kBytes == 2 && G >= 2) {
+        if (kernel != 1) return hipErrorInvalidValue;
+        hipLaunchKernelGGL((decode_mfma_kernel<T, D, G, BT>), dim3(grid), dim3(threads), 0,
+                           stream, p);
     } else {
-        hipLaunchKernelGGL((decode_valu_kernel<T, D, G>), dim3(grid), dim3(kDecodeThreads), 0,
+        if (kernel != 0) return hipErrorInvalidValue;
+        hipLaunchKernelGGL((decode_valu_kernel<T, D, G, BT>), dim3(grid), dim3(threads), 0,
                            stream, p);
     }
-    hipError_t e = hipGetLastError();
+    return hipGetLastError();
+}
+
+template <class T, int D, int G>
+hipError_t launch_typed(const DecodeParams &p, int kernel, hipStream_t stream) {
+    hipError_t e = p.block_size >= 16 ? launch_main<T, D, G, true>(p, kernel, stream)
+                                      : launch_main<T, D, G, false>(p, kernel, stream);
     if (e != hipSuccess) return e;
     if (p.num_partitions > 1) {
         hipLaunchKernelGGL((decode_reduce_kernel<T, D>), dim3(p.num_seqs * p.num_q_heads),
@@ -571,6 +674,7 @@ int decode_kernel_choice(int dtype, int head_dim, int group) {
 
 hipError_t launch_decode(const DecodeParams &p, int dtype, int head_dim, int group, int kernel,
                          hipStream_t stream) {
+    if (p.heads_per_group < 1 || p.heads_per_group > kMaxDecodeWaves) return hipErrorInvalidValue;
     switch (dtype) {
         case 0: return launch_t<F32>(p, head_dim, group, kernel, stream);
         case 1: return launch_t<F16>(p, head_dim, group, kernel, stream);
