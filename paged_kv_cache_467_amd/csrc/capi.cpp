@@ -14,14 +14,13 @@
 
 namespace {
 
-// Aim for about two decode workgroups (of up to 8 waves) per compute unit
-// (256 CUs) before splitting contexts any further; never split below this
-// many tokens.
-#ifndef PKV_TARGET_WORKGROUPS
-#define PKV_TARGET_WORKGROUPS 512
-#endif
-constexpr int kTargetWorkgroups = PKV_TARGET_WORKGROUPS;
+// Context partitions: contexts are split only when the batch has too few
+// (sequence, kv-head group) units to give every resident decode workgroup
+// slot one; the split then aims to fill the slots once.  Never split below
+// this many tokens.  When the device cannot be queried (no GPU), assume
+// 256 compute units holding three workgroups each.
 constexpr int kMinSplitTokens = 256;
+constexpr int kFallbackResidentWorkgroups = 768;
 
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 bool aligned4(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
@@ -96,8 +95,13 @@ Plan plan_decode(int num_seqs, int num_q_heads, int num_kv_heads, int head_dim, 
         }
         P = partition_size;
     } else {
-        const int64_t units = (int64_t)num_seqs * (num_kv_heads / heads_per_group_for(num_kv_heads));
-        int64_t parts = units > 0 ? (kTargetWorkgroups + units - 1) / units : 1;
+        const int hpg = heads_per_group_for(num_kv_heads);
+        const int64_t units = (int64_t)num_seqs * (num_kv_heads / hpg);
+        int64_t slots = pkv::decode_resident_workgroups(dtype, head_dim, group, block_size, hpg);
+        if (slots <= 0) slots = kFallbackResidentWorkgroups;
+        // enough units for half the slots or more: no split; otherwise the
+        // largest split that still fits every workgroup in one round
+        int64_t parts = units > 0 && 2 * units < slots ? slots / units : 1;
         const int64_t most = (max_ctx + kMinSplitTokens - 1) / kMinSplitTokens;
         if (parts > most) parts = most;
         if (parts < 1) parts = 1;

@@ -48,6 +48,8 @@
 
 #include <math.h>
 
+#include <atomic>
+
 namespace pkv {
 namespace {
 
@@ -577,35 +579,98 @@ __global__ __launch_bounds__(kMaxDecodeThreads) void decode_mfma_kernel(DecodePa
 
 // ------------------------------------------------------------------------
 // Cross-partition reduce: out = sum_p 2^(m_p - M) o_p / sum_p 2^(m_p - M) l_p
+// with M = max_p m_p.  One wave per (sequence, query head): the lanes split
+// the partitions for M and the denominator, then each lane owns head_dim / 64
+// output elements and walks the partitions with several loads in flight.
 // ------------------------------------------------------------------------
 constexpr int kReduceThreads = 64;
 
 template <class T, int D>
 __global__ __launch_bounds__(kReduceThreads) void decode_reduce_kernel(DecodeParams p) {
+    constexpr int EL = D / kReduceThreads;  // output elements per lane: 1, 2 or 4
+    constexpr int UNROLL = 8;
     const int sh = blockIdx.x;
+    const int lane = threadIdx.x;
     const int s = sh / p.num_q_heads;
     const int L = p.context_lens[s];
-    const int64_t obase = (int64_t)sh * D;
+    const int64_t obase = (int64_t)sh * D + lane * EL;
     if (L < 0 || L > p.max_context_len) {
-        for (int d = threadIdx.x; d < D; d += kReduceThreads) T::store_nan(p.out, obase + d);
+#pragma unroll
+        for (int e = 0; e < EL; ++e) T::store_nan(p.out, obase + e);
         return;
     }
     if (L == 0) {
-        for (int d = threadIdx.x; d < D; d += kReduceThreads) T::store(p.out, obase + d, 0.0f);
+#pragma unroll
+        for (int e = 0; e < EL; ++e) T::store(p.out, obase + e, 0.0f);
         return;
     }
     const int nparts = (L + p.partition_size - 1) / p.partition_size;
     const int64_t pbase = (int64_t)sh * p.num_partitions;
+    const float *pm = p.part_max + pbase;
+    const float *ps = p.part_sum + pbase;
     float M = -INFINITY;
-    for (int q = 0; q < nparts; ++q) M = fmaxf(M, p.part_max[pbase + q]);
+    for (int q = lane; q < nparts; q += kReduceThreads) M = vmax(M, pm[q]);
+    M = group_max<kReduceThreads>(M);
     float Ls = 0.0f;
-    for (int q = 0; q < nparts; ++q) Ls += p.part_sum[pbase + q] * fast_exp2(p.part_max[pbase + q] - M);
+    for (int q = lane; q < nparts; q += kReduceThreads) Ls += ps[q] * fast_exp2(pm[q] - M);
+    Ls = group_sum<kReduceThreads>(Ls);
     const float inv = 1.0f / Ls;
-    for (int d = threadIdx.x; d < D; d += kReduceThreads) {
-        float O = 0.0f;
-        for (int q = 0; q < nparts; ++q)
-            O += p.part_out[(pbase + q) * D + d] * fast_exp2(p.part_max[pbase + q] - M);
-        T::store(p.out, obase + d, O * inv);
+
+    const float *po = p.part_out + pbase * D + lane * EL;
+    float o[EL];
+#pragma unroll
+    for (int e = 0; e < EL; ++e) o[e] = 0.0f;
+    for (int q0 = 0; q0 < nparts; q0 += UNROLL) {
+        float v[UNROLL][EL], wq[UNROLL];
+#pragma unroll
+        for (int u = 0; u < UNROLL; ++u) {
+            // past the last partition: reread partition 0 (in bounds, finite) with weight 0
+            const int q = q0 + u < nparts ? q0 + u : 0;
+            wq[u] = q0 + u < nparts ? fast_exp2(pm[q] - M) : 0.0f;
+#pragma unroll
+            for (int e = 0; e < EL; ++e) v[u][e] = po[(int64_t)q * D + e];
+        }
+#pragma unroll
+        for (int u = 0; u < UNROLL; ++u)
+#pragma unroll
+            for (int e = 0; e < EL; ++e) o[e] = fmaf(wq[u], v[u][e], o[e]);
+    }
+#pragma unroll
+    for (int e = 0; e < EL; ++e) T::store(p.out, obase + e, o[e] * inv);
+}
+
+// Workgroups of this kernel instance one compute unit holds at once.
+template <class T, int D, int G, bool BT>
+int blocks_per_cu(int threads) {
+    int n = 0;
+    hipError_t e;
+    if constexpr (T::kBytes == 2 && G >= 2)
+        e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
+            &n, reinterpret_cast<const void *>(&decode_mfma_kernel<T, D, G, BT>), threads, 0);
+    else
+        e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
+            &n, reinterpret_cast<const void *>(&decode_valu_kernel<T, D, G, BT>), threads, 0);
+    return e == hipSuccess ? n : 0;
+}
+
+template <class T, int D>
+int blocks_per_cu_d(int group, bool bt, int threads) {
+    switch (group) {
+        case 1: return bt ? blocks_per_cu<T, D, 1, true>(threads) : blocks_per_cu<T, D, 1, false>(threads);
+        case 2: return bt ? blocks_per_cu<T, D, 2, true>(threads) : blocks_per_cu<T, D, 2, false>(threads);
+        case 4: return bt ? blocks_per_cu<T, D, 4, true>(threads) : blocks_per_cu<T, D, 4, false>(threads);
+        case 8: return bt ? blocks_per_cu<T, D, 8, true>(threads) : blocks_per_cu<T, D, 8, false>(threads);
+        default: return 0;
+    }
+}
+
+template <class T>
+int blocks_per_cu_t(int head_dim, int group, bool bt, int threads) {
+    switch (head_dim) {
+        case 64: return blocks_per_cu_d<T, 64>(group, bt, threads);
+        case 128: return blocks_per_cu_d<T, 128>(group, bt, threads);
+        case 256: return blocks_per_cu_d<T, 256>(group, bt, threads);
+        default: return 0;
     }
 }
 
@@ -670,6 +735,42 @@ int decode_kernel_choice(int dtype, int head_dim, int group) {
     // Grouped queries of a 16-bit type make each tile a real contraction
     // (G heads x head_dim x 16 tokens): MFMA.  Otherwise plain FMAs.
     return (dtype != 0 && group >= 2) ? 1 : 0;
+}
+
+int decode_resident_workgroups(int dtype, int head_dim, int group, int block_size,
+                               int heads_per_group) {
+    // Occupancy depends only on the kernel instance and the workgroup size;
+    // cache it per (dtype, head_dim, group, block_size >= 16, heads_per_group).
+    static std::atomic<int> cache[3][3][4][2][4];
+    static std::atomic<int> cus{0};
+    const int di = dtype, hi = head_dim == 64 ? 0 : head_dim == 128 ? 1 : 2;
+    const int gi = group == 1 ? 0 : group == 2 ? 1 : group == 4 ? 2 : 3;
+    const int bi = block_size >= 16 ? 1 : 0;
+    const int wi = heads_per_group == 1 ? 0 : heads_per_group == 2 ? 1 : heads_per_group == 4 ? 2 : 3;
+    if (di < 0 || di > 2) return 0;
+    int n_cu = cus.load(std::memory_order_relaxed);
+    if (n_cu == 0) {
+        int dev = 0;
+        if (hipGetDevice(&dev) != hipSuccess ||
+            hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+            n_cu = 0;
+        if (n_cu > 0) cus.store(n_cu, std::memory_order_relaxed);
+    }
+    int per_cu = cache[di][hi][gi][bi][wi].load(std::memory_order_relaxed);
+    if (per_cu == 0) {
+        const int threads = heads_per_group * kWave;
+        switch (dtype) {
+            case 0: per_cu = blocks_per_cu_t<F32>(head_dim, group, bi, threads); break;
+            case 1: per_cu = blocks_per_cu_t<F16>(head_dim, group, bi, threads); break;
+            default: per_cu = blocks_per_cu_t<BF16>(head_dim, group, bi, threads); break;
+        }
+        if (per_cu > 0) cache[di][hi][gi][bi][wi].store(per_cu, std::memory_order_relaxed);
+    }
+    if (n_cu <= 0 || per_cu <= 0) {
+        (void)hipGetLastError();  // no device here: clear the error
+        return 0;
+    }
+    return n_cu * per_cu;
 }
 
 hipError_t launch_decode(const DecodeParams &p, int dtype, int head_dim, int group, int kernel,
