@@ -62,9 +62,10 @@ def measured_traffic(workload: str):
     return float(tot.group(1))
 
 
-def cpu_baseline(workload: str, batch_values):
-    """The fp64 CPU oracle on this host's cores, on the whole batch (median
-    of three runs)."""
+def cpu_baseline(workload: str, batch_values, budget_s: float = 10.0):
+    """The fp64 CPU oracle on this host's cores, on the whole batch, repeated
+    until about budget_s seconds have passed (at least three runs; median),
+    plus one single-thread run of the same batch for reference."""
     import oracle
 
     b = batch_values
@@ -72,19 +73,30 @@ def cpu_baseline(workload: str, batch_values):
     threads = len(os.sched_getaffinity(0))
     orc.set_threads(threads)
     times = []
-    for _ in range(3):
+    start = time.perf_counter()
+    while len(times) < 3 or (time.perf_counter() - start < budget_s and len(times) < 200):
         t0 = time.perf_counter()
         orc.decode_batch(b)
         times.append(time.perf_counter() - t0)
     t = statistics.median(times)
+    orc.set_threads(1)
+    t0 = time.perf_counter()
+    orc.decode_batch(b)
+    t1 = time.perf_counter() - t0
+    used = threads
+    orc.set_threads(threads)
+    byt = b.decode_algorithmic_bytes()
     return {
-        "value": round(b.decode_algorithmic_bytes() / t / 1e9, 3),
+        "value": round(byt / t / 1e9, 3),
         "unit": "GB/s",
-        "cores": orc.max_threads(),
+        "cores": used,
         "kind": "oracle",
-        "sample": f"whole {workload} batch ({b.num_seqs} seqs), fp64 decode attention, "
-                  f"median of 3 runs of {t:.3f} s",
+        "sample": f"whole {workload} batch ({b.num_seqs} seqs, {int(b.context_lens.sum())} "
+                  f"context tokens), fp64 decode attention, median of {len(times)} runs "
+                  f"of {t:.4f} s on {used} threads",
         "seq_per_s": round(b.num_seqs / t, 1),
+        "single_thread": {"value": round(byt / t1 / 1e9, 3), "unit": "GB/s",
+                          "seconds": round(t1, 4)},
         "cpu_model": _cpu_model(),
     }
 

@@ -14,13 +14,19 @@
 
 namespace {
 
-// Context partitions: contexts are split only when the batch has too few
-// (sequence, kv-head group) units to give every resident decode workgroup
-// slot one; the split then aims to fill the slots once.  Never split below
-// this many tokens.  When the device cannot be queried (no GPU), assume
-// 256 compute units holding three workgroups each.
+// Context partitions.  HBM reads run fastest on this part with about eight
+// streaming waves per compute unit: more concurrent streams lower DRAM
+// efficiency, fewer leave bandwidth unused.  So the decode aims for
+// 8 / heads_per_group workgroups per compute unit (never more than fit).
+// Contexts are not split when the batch already has that many (sequence,
+// kv-head group) units; otherwise the split aims to reach it in one round.
+// A partition holds between kMinSplitTokens and kMaxAutoTokens tokens, so
+// that one very long context cannot hold up the whole launch.  When the
+// device cannot be queried (no GPU), assume 256 compute units.
 constexpr int kMinSplitTokens = 256;
-constexpr int kFallbackResidentWorkgroups = 768;
+constexpr int kMaxAutoTokens = 1024;
+constexpr int kTargetWavesPerCu = 8;
+constexpr int kFallbackComputeUnits = 256;
 
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 bool aligned4(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
@@ -97,15 +103,23 @@ Plan plan_decode(int num_seqs, int num_q_heads, int num_kv_heads, int head_dim, 
     } else {
         const int hpg = heads_per_group_for(num_kv_heads);
         const int64_t units = (int64_t)num_seqs * (num_kv_heads / hpg);
-        int64_t slots = pkv::decode_resident_workgroups(dtype, head_dim, group, block_size, hpg);
-        if (slots <= 0) slots = kFallbackResidentWorkgroups;
-        // enough units for half the slots or more: no split; otherwise the
-        // largest split that still fits every workgroup in one round
-        int64_t parts = units > 0 && 2 * units < slots ? slots / units : 1;
-        const int64_t most = (max_ctx + kMinSplitTokens - 1) / kMinSplitTokens;
-        if (parts > most) parts = most;
-        if (parts < 1) parts = 1;
-        P = round_up((max_ctx + parts - 1) / parts, align);
+        const pkv::DeviceOccupancy occ =
+            pkv::decode_occupancy(dtype, head_dim, group, block_size, hpg);
+        int64_t per_cu = kTargetWavesPerCu / hpg;
+        if (occ.workgroups_per_cu > 0 && per_cu > occ.workgroups_per_cu)
+            per_cu = occ.workgroups_per_cu;
+        if (per_cu < 1) per_cu = 1;
+        const int64_t target =
+            (occ.compute_units > 0 ? occ.compute_units : kFallbackComputeUnits) * per_cu;
+        if (units >= target || max_ctx <= kMinSplitTokens) {
+            P = max_ctx;  // enough units already, or nothing worth splitting
+        } else {
+            const int64_t parts = units > 0 ? target / units : 1;
+            P = (max_ctx + parts - 1) / parts;
+            if (P > kMaxAutoTokens) P = kMaxAutoTokens;
+            if (P < kMinSplitTokens) P = kMinSplitTokens;
+        }
+        P = round_up(P, align);
         if (P < align) P = align;
         if (P > max_part) P = max_part;
     }

@@ -44,10 +44,14 @@ struct DecodeParams {
 // dtype codes match paged_kv_dtype; kernel = 0 VALU, 1 MFMA.
 hipError_t launch_decode(const DecodeParams &p, int dtype, int head_dim, int group, int kernel,
                          hipStream_t stream);
-// Decode workgroups the current device holds at once for this shape
-// (compute units x resident workgroups per unit), or 0 when unknown.
-int decode_resident_workgroups(int dtype, int head_dim, int group, int block_size,
-                               int heads_per_group);
+// Compute units of the current device and decode workgroups of this shape
+// one of them holds at once; 0 where unknown (no device).
+struct DeviceOccupancy {
+    int compute_units;
+    int workgroups_per_cu;
+};
+DeviceOccupancy decode_occupancy(int dtype, int head_dim, int group, int block_size,
+                                 int heads_per_group);
 // Which decode kernel launch_decode uses for this shape.
 int decode_kernel_choice(int dtype, int head_dim, int group);
 

@@ -737,17 +737,18 @@ int decode_kernel_choice(int dtype, int head_dim, int group) {
     return (dtype != 0 && group >= 2) ? 1 : 0;
 }
 
-int decode_resident_workgroups(int dtype, int head_dim, int group, int block_size,
-                               int heads_per_group) {
+DeviceOccupancy decode_occupancy(int dtype, int head_dim, int group, int block_size,
+                                 int heads_per_group) {
     // Occupancy depends only on the kernel instance and the workgroup size;
     // cache it per (dtype, head_dim, group, block_size >= 16, heads_per_group).
     static std::atomic<int> cache[3][3][4][2][4];
     static std::atomic<int> cus{0};
-    const int di = dtype, hi = head_dim == 64 ? 0 : head_dim == 128 ? 1 : 2;
+    DeviceOccupancy r{0, 0};
+    if (dtype < 0 || dtype > 2) return r;
+    const int hi = head_dim == 64 ? 0 : head_dim == 128 ? 1 : 2;
     const int gi = group == 1 ? 0 : group == 2 ? 1 : group == 4 ? 2 : 3;
     const int bi = block_size >= 16 ? 1 : 0;
     const int wi = heads_per_group == 1 ? 0 : heads_per_group == 2 ? 1 : heads_per_group == 4 ? 2 : 3;
-    if (di < 0 || di > 2) return 0;
     int n_cu = cus.load(std::memory_order_relaxed);
     if (n_cu == 0) {
         int dev = 0;
@@ -756,21 +757,20 @@ int decode_resident_workgroups(int dtype, int head_dim, int group, int block_siz
             n_cu = 0;
         if (n_cu > 0) cus.store(n_cu, std::memory_order_relaxed);
     }
-    int per_cu = cache[di][hi][gi][bi][wi].load(std::memory_order_relaxed);
-    if (per_cu == 0) {
+    int per_cu = cache[dtype][hi][gi][bi][wi].load(std::memory_order_relaxed);
+    if (per_cu == 0 && n_cu > 0) {
         const int threads = heads_per_group * kWave;
         switch (dtype) {
             case 0: per_cu = blocks_per_cu_t<F32>(head_dim, group, bi, threads); break;
             case 1: per_cu = blocks_per_cu_t<F16>(head_dim, group, bi, threads); break;
             default: per_cu = blocks_per_cu_t<BF16>(head_dim, group, bi, threads); break;
         }
-        if (per_cu > 0) cache[di][hi][gi][bi][wi].store(per_cu, std::memory_order_relaxed);
+        if (per_cu > 0) cache[dtype][hi][gi][bi][wi].store(per_cu, std::memory_order_relaxed);
     }
-    if (n_cu <= 0 || per_cu <= 0) {
-        (void)hipGetLastError();  // no device here: clear the error
-        return 0;
-    }
-    return n_cu * per_cu;
+    if (n_cu <= 0 || per_cu <= 0) (void)hipGetLastError();  // no device here: clear the error
+    r.compute_units = n_cu > 0 ? n_cu : 0;
+    r.workgroups_per_cu = per_cu > 0 ? per_cu : 0;
+    return r;
 }
 
 hipError_t launch_decode(const DecodeParams &p, int dtype, int head_dim, int group, int kernel,
