@@ -13,7 +13,9 @@
  * Conventions shared by every entry point:
  *  - All array arguments are DEVICE pointers, owned by the caller, dense and
  *    row-major, 16-byte aligned.  The library never allocates memory and
- *    keeps no state between calls; entry points are re-entrant.
+ *    keeps no state between calls besides a cache of the device's compute
+ *    unit count and of kernel occupancies, filled on first use; entry points
+ *    are re-entrant.
  *  - Element data are one dtype per call (paged_kv_dtype); index arrays are
  *    int32.
  *  - Every call is asynchronous on `stream` (a hipStream_t; NULL means the
@@ -78,7 +80,10 @@ const char *paged_kv_status_string(int status);
  *   max_context_len  upper bound on every context_lens[s]; 0 means
  *                max_blocks_per_seq * block_size.  It sizes the split into
  *                context partitions and the workspace.
- *   partition_size   tokens per context partition; 0 picks one.  An
+ *   partition_size   tokens per context partition; 0 picks one from the
+ *                shape and the current device (its compute units and the
+ *                decode kernel's occupancy), so query the split and the
+ *                workspace size on the device that will run the decode.  An
  *                explicit value must be a positive multiple of 16 and of
  *                block_size with partition_size / block_size <= 1024.
  *   workspace, workspace_bytes  device scratch of at least
@@ -93,7 +98,8 @@ const char *paged_kv_status_string(int status);
  * [0, num_blocks), gets NaN in every output element; nothing out of range
  * is read.
  * Pool size: num_blocks * block_size * num_kv_heads * head_dim may exceed
- * 2^31 elements (64-bit addressing).
+ * 2^31 elements (64-bit addressing); one block, block_size * num_kv_heads *
+ * head_dim elements, must fit in 2^31 - 1 bytes (else PAGED_KV_ERR_BAD_SHAPE).
  */
 int paged_attn_decode(const void *query, const void *key_cache, const void *value_cache,
                       const int32_t *block_tables, const int32_t *context_lens, float scale,

@@ -20,7 +20,8 @@
 // heads.  The waves of a workgroup read the same token rows side by side (a
 // block of all kv heads is one contiguous stretch of the pool), and a wave's
 // result needs no merge with other waves.  K/V tiles are loaded DEPTH - 1
-// tiles ahead of the one being consumed, with non-temporal loads.
+// tiles ahead of the one being consumed (DEPTH per kernel below), with
+// non-temporal loads.
 //
 // Addressing: tiles never cross a 16-token boundary, so with block_size >= 16
 // a tile lies in one block and its base address is wave-uniform (block id
@@ -53,11 +54,14 @@
 namespace pkv {
 namespace {
 
-// K/V tiles held in registers per wave: one being consumed, the rest in flight.
-#ifndef PKV_TILE_DEPTH
-#define PKV_TILE_DEPTH 2
-#endif
-constexpr int kDepth = PKV_TILE_DEPTH;
+// K/V tiles held in registers per wave: one being consumed, the rest in
+// flight.  HBM reads on this part are fastest with about 32 KB in flight per
+// compute unit; with 8 waves per unit the MFMA kernel stays closest to that
+// loading each tile just before it is consumed (measured 2% faster than one
+// tile ahead), while the VALU kernel's longer per-tile work pays for one
+// tile of look-ahead.
+constexpr int kMfmaDepth = 1;
+constexpr int kValuDepth = 2;
 
 struct WorkItem {
     int s, kvh0, part;  // sequence, first kv head of the workgroup, partition
@@ -220,12 +224,13 @@ __global__ __launch_bounds__(kMaxDecodeThreads) void decode_valu_kernel(DecodePa
     constexpr int EPC = T::kPerChunk;   // elements per 16-byte chunk
     constexpr int CPR = D / EPC;        // lanes holding one row
     constexpr int TPI = kWave / CPR;    // tokens per load instruction
-    constexpr int NL = TPI <= 4 ? 4 : 16 / TPI;  // loads per lane per tile (K and V each)
-    constexpr int TILE = TPI * NL;      // tokens per tile: 4, 8 or 16, divides 16
+    // loads per lane per tile (K and V each); fewer with many fp32 accumulators
+    constexpr int NL = TPI > 4 ? 16 / TPI : G * EPC >= 32 ? 2 : 4;
+    constexpr int TILE = TPI * NL;      // tokens per tile: 2 to 16, divides 16
     static_assert(CPR >= 4 && CPR <= 64 && kWave % CPR == 0, "row layout");
     static_assert(16 % TILE == 0, "tiles must not cross a 16-token boundary");
     // wide rows or many fp32 accumulators: no room for a second tile
-    constexpr int DEPTH = (D >= 256 || G * EPC >= 32) ? 1 : kDepth;
+    constexpr int DEPTH = (D >= 256 || G * EPC >= 32) ? 1 : kValuDepth;
 
     __shared__ int32_t bt_lds[kBtLds];
 
@@ -386,7 +391,7 @@ __global__ __launch_bounds__(kMaxDecodeThreads) void decode_mfma_kernel(DecodePa
     constexpr int NV = 16 / TPI;      // V loads per lane per tile
     constexpr int TILE = 16;
     constexpr int HW = G < 4 ? G : 4;  // heads among a lane's four result rows
-    constexpr int DEPTH = D >= 256 ? 1 : kDepth;  // wide rows: no room for a second tile
+    constexpr int DEPTH = kMfmaDepth;
 
     __shared__ int32_t bt_lds[kBtLds];
     // softmax weights of the tile (16-byte aligned: read and written as f32x4)

@@ -185,6 +185,24 @@ def test_decode_shapes(B, dtype, D, G, bs):
         check_close(tensors.widen(got, dtype), ref, dtype, f"{dtype} D={D} G={G} bs={bs} P={P}")
 
 
+# kv-head counts that give 1, 2 or 4 kv heads per decode workgroup and one
+# or several workgroups per sequence
+HEAD_GROUPS = [("bf16", 1, 4), ("f16", 3, 1), ("bf16", 6, 2), ("f16", 8, 8), ("bf16", 12, 4),
+               ("f32", 16, 1), ("f16", 40, 1), ("f32", 4, 8), ("bf16", 16, 8)]
+
+
+@pytest.mark.parametrize("dtype,Hkv,G", HEAD_GROUPS)
+def test_decode_head_groups(B, dtype, Hkv, G):
+    lens = (3, 16, 47, 160, 333)
+    b = W.make_custom(2000 + Hkv * 10 + G, dtype=dtype, num_seqs=len(lens),
+                      num_q_heads=Hkv * G, num_kv_heads=Hkv, head_dim=128, block_size=16,
+                      context_lens=lens, extra_blocks=4, poison=True)
+    ref = oracle.decode_batch(b)
+    for P in (0, 64):
+        got = run_decode(B, b, partition_size=P)
+        check_close(tensors.widen(got, dtype), ref, dtype, f"{dtype} Hkv={Hkv} G={G} P={P}")
+
+
 def test_context_len_one_is_exactly_v(B):
     for dtype, G in (("bf16", 4), ("f16", 1), ("f32", 2)):
         b = W.make_custom(81, dtype=dtype, num_seqs=5, num_q_heads=2 * G, num_kv_heads=2,
