@@ -149,6 +149,29 @@ int kv_cache_write(const void *key, const void *value, const int32_t *slot_mappi
                    int head_dim, int block_size, int num_blocks, int dtype, void *stream);
 
 /*
+ * Copy-on-write block copy: before a sequence writes into a block that other
+ * sequences still reference (a shared prompt prefix, parallel samples or
+ * beams), the block is copied to a block of the sequence's own
+ * ("23.1 vLLM：高吞吐推理框架原理与部署", §二.3).
+ *
+ * For each pair i < num_pairs with src = block_mapping[2 * i] and
+ * dst = block_mapping[2 * i + 1]: all block_size slots of all kv heads of
+ * physical block dst, in both key_cache and value_cache, become a bit copy
+ * of block src.
+ *   key_cache, value_cache  [num_blocks, block_size, num_kv_heads, head_dim],
+ *                updated in place
+ *   block_mapping [num_pairs, 2] int32 (src, dst), device memory
+ * Device-side values: a pair whose src or dst is outside [0, num_blocks)
+ * copies nothing.  Pairs run in parallel: a dst that appears twice, or that
+ * is also a src in the same call, leaves an unspecified result.
+ * One block (block_size * num_kv_heads * head_dim elements) must be a
+ * multiple of 16 bytes and at most 4 GiB (else PAGED_KV_ERR_BAD_SHAPE).
+ */
+int paged_kv_copy_blocks(void *key_cache, void *value_cache, const int32_t *block_mapping,
+                         int num_pairs, int num_kv_heads, int head_dim, int block_size,
+                         int num_blocks, int dtype, void *stream);
+
+/*
  * Materialise each sequence's logical K/V through its block table (the
  * addressing of paged_attn_decode, as a bit copy); used to check the
  * addressing on its own.

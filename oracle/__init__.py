@@ -43,6 +43,7 @@ class Oracle:
             "oracle_paged_attention_decode_partitioned": [vp, vp, vp, vp, vp, cf] + [ci] * 8 + [vp],
             "oracle_kv_cache_write": [vp, vp, vp, vp, vp] + [ci] * 5,
             "oracle_paged_kv_gather": [vp, vp, vp, vp, vp, vp] + [ci] * 7,
+            "oracle_copy_blocks": [vp, vp, vp] + [ci] * 5,
             "oracle_elements_to_double": [vp, ctypes.c_int64, ci, vp],
             "oracle_set_threads": [ci],
             "oracle_max_threads": [],
@@ -117,6 +118,15 @@ class Oracle:
                                         _ptr(out_k), _ptr(out_v), S, Hkv, D, bs, bt.shape[1],
                                         int(max_context_len), _code(dtype))
         return out_k, out_v
+
+    def copy_blocks(self, key_cache, value_cache, block_mapping, dtype):
+        """Copy-on-write block copy, in place: for each (src, dst) row of
+        block_mapping, in order, block dst of both pools becomes a copy of
+        block src; a negative id skips the row."""
+        nb, bs, Hkv, D = key_cache.shape
+        bm = np.ascontiguousarray(block_mapping, dtype=np.int32).reshape(-1, 2)
+        self.lib.oracle_copy_blocks(_ptr(key_cache), _ptr(value_cache), _ptr(bm), bm.shape[0],
+                                    Hkv, D, bs, _code(dtype))
 
     # ---- conveniences on a workloads.DecodeBatch ----
     def decode_batch(self, batch, *, return_weights=False):

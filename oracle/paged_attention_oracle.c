@@ -30,6 +30,11 @@
  *    nothing ("大模型推理框架VLLM-0.7.3源码", §2.1 on slot_mapping).
  *  - Gather: materialise each sequence's logical K/V through its block
  *    table (the same addressing, as a bit copy).
+ *  - Block copy: copy-on-write of shared blocks -- before a sequence writes
+ *    into a block it shares with others, the block's contents are copied to
+ *    a block of its own ("23.1 vLLM：高吞吐推理框架原理与部署", §二.3).  Each
+ *    (src, dst) pair copies every slot of physical block src to block dst,
+ *    in both pools; a negative id skips the pair.
  *
  * Element types: f32 (code 0), f16 (code 1, IEEE binary16), bf16 (code 2,
  * the upper half of a binary32).  Inputs are read as stored bits and widened
@@ -314,5 +319,26 @@ void oracle_paged_kv_gather(const void *key_cache, const void *value_cache,
             memcpy((char *)out_v + dst * element_bytes(dtype),
                    (const char *)value_cache + src * element_bytes(dtype), row_bytes);
         }
+    }
+}
+
+/*
+ * block_mapping: [num_pairs, 2] int32 (src, dst).  Pairs are applied in
+ * order; a pair with a negative src or dst copies nothing.
+ */
+void oracle_copy_blocks(void *key_cache, void *value_cache, const int32_t *block_mapping,
+                        int num_pairs, int num_kv_heads, int head_dim, int block_size, int dtype)
+{
+    const size_t block_bytes =
+        (size_t)block_size * num_kv_heads * head_dim * element_bytes(dtype);
+    for (int i = 0; i < num_pairs; ++i) {
+        const int src = block_mapping[2 * i];
+        const int dst = block_mapping[2 * i + 1];
+        if (src < 0 || dst < 0)
+            continue;
+        memmove((char *)key_cache + (size_t)dst * block_bytes,
+                (const char *)key_cache + (size_t)src * block_bytes, block_bytes);
+        memmove((char *)value_cache + (size_t)dst * block_bytes,
+                (const char *)value_cache + (size_t)src * block_bytes, block_bytes);
     }
 }

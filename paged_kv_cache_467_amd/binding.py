@@ -27,6 +27,7 @@ EXPORTED = (
     "paged_attn_decode_workspace_bytes",
     "kv_cache_write",
     "paged_kv_gather",
+    "paged_kv_copy_blocks",
 )
 
 
@@ -49,6 +50,8 @@ def _load_library(path: str = LIBRARY) -> ctypes.CDLL:
     lib.kv_cache_write.restype = ci
     lib.paged_kv_gather.argtypes = [vp] * 6 + [ci] * 8 + [vp]
     lib.paged_kv_gather.restype = ci
+    lib.paged_kv_copy_blocks.argtypes = [vp] * 3 + [ci] * 6 + [vp]
+    lib.paged_kv_copy_blocks.restype = ci
     return lib
 
 
@@ -188,3 +191,21 @@ def paged_kv_gather(key_cache: torch.Tensor, value_cache: torch.Tensor,
         _dev(out_key, "out_key"), _dev(out_value, "out_value"), S, Hkv, D, bs, nb, mb,
         out_key.shape[1], _dtype_code(key_cache), _stream(key_cache.device))
     _check("paged_kv_gather", status)
+
+
+def paged_kv_copy_blocks(key_cache: torch.Tensor, value_cache: torch.Tensor,
+                         block_mapping: torch.Tensor) -> None:
+    """Copy-on-write block copy: for each (src, dst) row of block_mapping
+    ([num_pairs, 2] int32), block dst of both pools becomes a copy of block
+    src (see paged_kv_copy_blocks in include/paged_kv.h)."""
+    nb, bs, Hkv, D = key_cache.shape
+    if tuple(value_cache.shape) != tuple(key_cache.shape) or value_cache.dtype != key_cache.dtype:
+        raise ValueError("key_cache and value_cache must share shape and dtype")
+    if block_mapping.dtype != torch.int32 or block_mapping.dim() != 2 or \
+            block_mapping.shape[1] != 2:
+        raise ValueError("block_mapping must be int32 [num_pairs, 2]")
+    status = _lib.paged_kv_copy_blocks(
+        _dev(key_cache, "key_cache"), _dev(value_cache, "value_cache"),
+        _dev(block_mapping, "block_mapping"), block_mapping.shape[0], Hkv, D, bs, nb,
+        _dtype_code(key_cache), _stream(key_cache.device))
+    _check("paged_kv_copy_blocks", status)

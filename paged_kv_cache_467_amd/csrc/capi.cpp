@@ -259,6 +259,26 @@ int kv_cache_write(const void *key, const void *value, const int32_t *slot_mappi
     return err == hipSuccess ? PAGED_KV_OK : PAGED_KV_ERR_HIP;
 }
 
+int paged_kv_copy_blocks(void *key_cache, void *value_cache, const int32_t *block_mapping,
+                         int num_pairs, int num_kv_heads, int head_dim, int block_size,
+                         int num_blocks, int dtype, void *stream) {
+    if (dtype != PAGED_KV_F32 && dtype != PAGED_KV_F16 && dtype != PAGED_KV_BF16)
+        return PAGED_KV_ERR_UNSUPPORTED;
+    if (num_pairs < 0 || num_pairs > 0x7fffffff / 2 || num_kv_heads < 1 || head_dim < 1 ||
+        block_size < 1 || num_blocks < 1)
+        return PAGED_KV_ERR_BAD_SHAPE;
+    const int64_t block_bytes = (int64_t)block_size * num_kv_heads * head_dim * elem_bytes(dtype);
+    if (block_bytes % 16 != 0 || block_bytes / 65536 > 65535) return PAGED_KV_ERR_BAD_SHAPE;
+    if (num_pairs == 0) return PAGED_KV_OK;
+    if (!key_cache || !value_cache || !block_mapping) return PAGED_KV_ERR_NULL_POINTER;
+    if (!aligned16(key_cache) || !aligned16(value_cache) || !aligned4(block_mapping))
+        return PAGED_KV_ERR_BAD_SHAPE;
+    const hipError_t err = pkv::launch_copy_blocks(key_cache, value_cache, block_mapping,
+                                                   num_pairs, block_bytes, num_blocks,
+                                                   static_cast<hipStream_t>(stream));
+    return err == hipSuccess ? PAGED_KV_OK : PAGED_KV_ERR_HIP;
+}
+
 int paged_kv_gather(const void *key_cache, const void *value_cache,
                     const int32_t *block_tables, const int32_t *context_lens, void *out_key,
                     void *out_value, int num_seqs, int num_kv_heads, int head_dim,

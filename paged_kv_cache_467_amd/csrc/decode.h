@@ -59,6 +59,10 @@ hipError_t launch_kv_cache_write(const void *key, const void *value, const int32
                                  void *key_cache, void *value_cache, int num_tokens,
                                  int row_bytes, int64_t num_slots, hipStream_t stream);
 
+hipError_t launch_copy_blocks(void *key_cache, void *value_cache, const int32_t *block_mapping,
+                              int num_pairs, int64_t block_bytes, int num_blocks,
+                              hipStream_t stream);
+
 hipError_t launch_paged_kv_gather(const void *key_cache, const void *value_cache,
                                   const int32_t *block_tables, const int32_t *context_lens,
                                   void *out_key, void *out_value, int num_seqs,

@@ -152,6 +152,10 @@ __device__ inline u32x4 load16_stream(const void *p) {
 __device__ inline void store16(void *p, const u32x4 &v) {
     *reinterpret_cast<u32x4 *>(p) = v;
 }
+// Streaming (non-temporal) 16-byte vector store, for data not read again soon.
+__device__ inline void store16_stream(void *p, const u32x4 &v) {
+    __builtin_nontemporal_store(v, reinterpret_cast<u32x4 *>(p));
+}
 
 // ------------------------------------------------------------------ DPP
 // dpp_ctrl encodings (GFX9 DPP): quad_perm [1,0,3,2] swaps neighbours,

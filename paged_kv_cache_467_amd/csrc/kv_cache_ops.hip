@@ -9,7 +9,13 @@
 // sequence's logical tokens are read through its block table
 // ("大模型推理框架 vllm 源码解析 一", §三 pseudo-code) into a dense array.
 //
-// Both are bit copies done with 16-byte vector loads and stores.
+// Block copy: copy-on-write of a shared block -- before a sequence writes
+// into a block that other sequences still reference, the block's contents
+// go to a block of its own ("23.1 vLLM：高吞吐推理框架原理与部署", §二.3);
+// each (src, dst) pair copies all block_size slots of every kv head, in both
+// pools.
+//
+// All three are bit copies done with 16-byte vector loads and stores.
 
 #include "decode.h"
 #include "device_utils.h"
@@ -73,7 +79,48 @@ __global__ __launch_bounds__(kCopyThreads) void paged_kv_gather_kernel(
     }
 }
 
+// Block copy: grid (pair, pool, chunk of up to kCopyChunkBytes of the block).
+// A pair whose src or dst is outside [0, num_blocks) copies nothing.  Every
+// byte is touched once, so loads and stores are non-temporal.
+constexpr int kCopyChunkBytes = 64 * 1024;
+constexpr int kCopyUnroll = 4;
+
+__global__ __launch_bounds__(kCopyThreads) void copy_blocks_kernel(
+    char *__restrict__ key_cache, char *__restrict__ value_cache,
+    const int32_t *__restrict__ block_mapping, int64_t block_bytes, int num_blocks) {
+    const int pair = blockIdx.x;
+    const int src = block_mapping[2 * pair];
+    const int dst = block_mapping[2 * pair + 1];
+    if (src < 0 || src >= num_blocks || dst < 0 || dst >= num_blocks) return;
+    char *pool = blockIdx.y == 0 ? key_cache : value_cache;
+    const int64_t begin = (int64_t)blockIdx.z * kCopyChunkBytes;
+    const int64_t end = begin + kCopyChunkBytes < block_bytes ? begin + kCopyChunkBytes : block_bytes;
+    const char *from = pool + (int64_t)src * block_bytes;
+    char *to = pool + (int64_t)dst * block_bytes;
+    constexpr int kStep = kCopyThreads * 16;
+    int64_t b = begin + threadIdx.x * 16;
+    for (; b + (kCopyUnroll - 1) * kStep < end; b += kCopyUnroll * kStep) {
+        u32x4 v[kCopyUnroll];
+#pragma unroll
+        for (int u = 0; u < kCopyUnroll; ++u) v[u] = load16_stream(from + b + u * kStep);
+#pragma unroll
+        for (int u = 0; u < kCopyUnroll; ++u) store16_stream(to + b + u * kStep, v[u]);
+    }
+    for (; b < end; b += kStep) store16_stream(to + b, load16_stream(from + b));
+}
+
 }  // namespace
+
+hipError_t launch_copy_blocks(void *key_cache, void *value_cache, const int32_t *block_mapping,
+                              int num_pairs, int64_t block_bytes, int num_blocks,
+                              hipStream_t stream) {
+    if (num_pairs == 0) return hipSuccess;
+    const unsigned chunks = (unsigned)((block_bytes + kCopyChunkBytes - 1) / kCopyChunkBytes);
+    hipLaunchKernelGGL(copy_blocks_kernel, dim3(num_pairs, 2, chunks), dim3(kCopyThreads), 0,
+                       stream, static_cast<char *>(key_cache), static_cast<char *>(value_cache),
+                       block_mapping, block_bytes, num_blocks);
+    return hipGetLastError();
+}
 
 hipError_t launch_kv_cache_write(const void *key, const void *value, const int32_t *slot_mapping,
                                  void *key_cache, void *value_cache, int num_tokens,

@@ -11,6 +11,7 @@ import numpy as np
 import torch
 
 TORCH_DTYPE = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}
+ELEM_BYTES = {"f32": 4, "f16": 2, "bf16": 2}
 
 
 def to_device(bits: np.ndarray, dtype: str, device) -> torch.Tensor:

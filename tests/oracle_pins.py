@@ -335,10 +335,41 @@ def pin_linear_in_values(orc):
     assert np.abs(run(v1 + v2) - (run(v1) + run(v2))).max() <= 1e-12
 
 
+def pin_copy_blocks(orc):
+    """Copy-on-write block copy ("23.1 vLLM", §二.3): after copying (src, dst)
+    pairs, block dst of each pool holds block src's bits and every other
+    block is untouched -- checked against numpy fancy indexing on a pool whose
+    every element encodes its own position, and a negative id skips a pair."""
+    rng = np.random.default_rng(17)
+    for dtype, nb, bs, Hkv, D in (("bf16", 40, 16, 2, 8), ("f32", 12, 4, 3, 4)):
+        n = nb * bs * Hkv * D
+        kc = np.arange(n, dtype=np.uint32).reshape(nb, bs, Hkv, D)
+        vc = (kc + n).astype(np.uint32)
+        if dtype != "f32":
+            kc = (kc % 65521).astype(np.uint16)
+            vc = ((vc * 7) % 65521).astype(np.uint16)
+        else:
+            kc = kc.view(np.float32)
+            vc = vc.view(np.float32)
+        perm = rng.permutation(nb)
+        npairs = nb // 3
+        pairs = np.stack([perm[:npairs], perm[npairs:2 * npairs]], axis=1).astype(np.int32)
+        pairs[1] = (-1, pairs[1, 1])
+        k2, v2 = kc.copy(), vc.copy()
+        orc.copy_blocks(k2, v2, pairs, dtype)
+        keep = pairs[:, 0] >= 0
+        ek, ev = kc.copy(), vc.copy()
+        ek[pairs[keep, 1]] = kc[pairs[keep, 0]]
+        ev[pairs[keep, 1]] = vc[pairs[keep, 0]]
+        assert np.array_equal(k2.view(np.uint8), ek.view(np.uint8))
+        assert np.array_equal(v2.view(np.uint8), ev.view(np.uint8))
+        assert np.array_equal(k2[pairs[1, 1]].view(np.uint8), kc[pairs[1, 1]].view(np.uint8))
+
+
 ALL_PINS = [
     pin_element_decode, pin_addressing_worked_example, pin_shared_prefix_blocks,
     pin_write_gather_roundtrip, pin_decode_vs_sdpa, pin_tiny_workload_vs_sdpa,
     pin_context_len_one, pin_identical_keys, pin_two_token_logistic, pin_weights_sum_to_one,
     pin_block_permutation, pin_gqa_equals_mha, pin_split_merge, pin_poison_unreferenced,
-    pin_large_scores, pin_empty_context, pin_linear_in_values,
+    pin_large_scores, pin_empty_context, pin_linear_in_values, pin_copy_blocks,
 ]

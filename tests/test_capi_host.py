@@ -35,13 +35,15 @@ def lib():
     lib.paged_attn_decode_workspace_bytes.restype = sz
     lib.kv_cache_write.argtypes = [vp, vp, vp, vp, vp] + [ci] * 6 + [vp]
     lib.paged_kv_gather.argtypes = [vp] * 6 + [ci] * 8 + [vp]
+    lib.paged_kv_copy_blocks.argtypes = [vp] * 3 + [ci] * 6 + [vp]
     return lib
 
 
 def test_header_declares_the_entry_points():
     assert declared_functions() == sorted([
         "paged_kv_status_string", "paged_attn_decode", "paged_attn_decode_partition_size",
-        "paged_attn_decode_workspace_bytes", "kv_cache_write", "paged_kv_gather"])
+        "paged_attn_decode_workspace_bytes", "kv_cache_write", "paged_kv_gather",
+        "paged_kv_copy_blocks"])
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -132,3 +134,15 @@ def test_kv_cache_write_rejects(lib, args, status):
 ])
 def test_gather_rejects(lib, args, status):
     assert lib.paged_kv_gather(*args) == status
+
+
+@pytest.mark.parametrize("args,status", [
+    ((P, P, P, 4, 8, 128, 16, 64, 7, None), UNSUPPORTED),
+    ((P, P, P, -1, 8, 128, 16, 64, 2, None), BAD_SHAPE),
+    ((P, P, P, 4, 1, 2, 1, 64, 2, None), BAD_SHAPE),          # 4-byte block
+    ((P, None, P, 4, 8, 128, 16, 64, 2, None), NULLPTR),
+    ((P + 8, P, P, 4, 8, 128, 16, 64, 2, None), BAD_SHAPE),   # cache misaligned
+    ((None, None, None, 0, 8, 128, 16, 64, 2, None), OK),     # nothing to copy
+])
+def test_copy_blocks_rejects(lib, args, status):
+    assert lib.paged_kv_copy_blocks(*args) == status

@@ -106,6 +106,70 @@ def test_kv_cache_write_skips_invalid_slots(B, dtype, Hkv, D):
                           ref.value_cache.view(np.uint8))
 
 
+# ------------------------------------------------------------- block copy
+def _random_pool_bits(rng, nb, bs, Hkv, D, dtype):
+    word = np.uint32 if dtype == "f32" else np.uint16
+    info = np.iinfo(word)
+    k = rng.integers(0, info.max, size=(nb, bs, Hkv, D), dtype=word, endpoint=True)
+    v = rng.integers(0, info.max, size=(nb, bs, Hkv, D), dtype=word, endpoint=True)
+    if dtype == "f32":
+        k, v = k.view(np.float32), v.view(np.float32)
+    return k, v
+
+
+@pytest.mark.parametrize("dtype,nb,bs,Hkv,D,npairs", [
+    ("bf16", 300, 16, 8, 128, 64), ("f16", 120, 32, 2, 64, 40), ("f32", 64, 8, 3, 64, 20),
+    ("bf16", 40, 256, 8, 128, 12), ("f16", 50, 1, 1, 64, 25)])
+def test_copy_blocks_bit_exact(B, dtype, nb, bs, Hkv, D, npairs):
+    """Copy-on-write block copy against the oracle on random bit patterns
+    (NaNs and infinities included), with pairs the kernel must skip."""
+    _say(f"paged_kv_copy_blocks {dtype} nb={nb} bs={bs} Hkv={Hkv} D={D} pairs={npairs}")
+    rng = np.random.default_rng(nb + bs + npairs)
+    kc, vc = _random_pool_bits(rng, nb, bs, Hkv, D, dtype)
+    perm = rng.permutation(nb)
+    pairs = np.stack([perm[:npairs], perm[npairs:2 * npairs]], axis=1).astype(np.int32)
+    pairs[0, 0] = -3          # skipped: negative source
+    pairs[2, 1] = nb          # skipped: destination past the pool
+    pairs[3, 0] = nb + 100    # skipped: source past the pool
+    dk = tensors.to_device(kc, dtype, DEV)
+    dv = tensors.to_device(vc, dtype, DEV)
+    B.paged_kv_copy_blocks(dk, dv, tensors.int32(pairs, DEV))
+    torch.cuda.synchronize()
+    ref_pairs = pairs.copy()
+    ref_pairs[2:4] = -1       # the oracle's contract covers negatives only
+    rk, rv = kc.copy(), vc.copy()
+    oracle.copy_blocks(rk, rv, ref_pairs, dtype)
+    assert np.array_equal(tensors.to_host_bits(dk).view(np.uint8), rk.view(np.uint8))
+    assert np.array_equal(tensors.to_host_bits(dv).view(np.uint8), rv.view(np.uint8))
+
+
+def test_copy_then_write_then_decode(B):
+    """Copy-on-write in a decode step: a sequence forks from a shared last
+    block; the shared block is copied, the fork's new token goes into the
+    copy, and both sequences decode correctly (the other sequence still sees
+    the original block)."""
+    _say("copy-on-write fork step")
+    b = W.make_custom(131, dtype="bf16", num_seqs=2, num_q_heads=8, num_kv_heads=2,
+                      head_dim=128, block_size=16, context_lens=(40, 40), extra_blocks=6)
+    # sequence 1 shares sequence 0's blocks; its last (partial) block is forked
+    shared_last = b.block_tables[0, 2]
+    fresh = int(np.setdiff1d(np.arange(b.num_blocks), b.block_tables[:, :3].ravel())[0])
+    b.block_tables[1, :3] = b.block_tables[0, :3]
+    b.block_tables[1, 2] = fresh
+    b.context_lens[:] = (39, 40)            # sequence 1 appends token 39 into its copy
+    b.slot_mapping[:] = (-1, fresh * 16 + 39 % 16)
+    pairs = np.array([[shared_last, fresh]], dtype=np.int32)
+    d = tensors.device_batch(b, DEV)
+    B.paged_kv_copy_blocks(d.key_cache, d.value_cache, tensors.int32(pairs, DEV))
+    B.kv_cache_write(d.new_key, d.new_value, d.slot_mapping, d.key_cache, d.value_cache)
+    got = run_decode(B, b, d)
+    ref = b.copy()
+    oracle.copy_blocks(ref.key_cache, ref.value_cache, pairs, "bf16")
+    oracle.write_batch(ref)
+    assert np.array_equal(tensors.to_host_bits(d.key_cache), ref.key_cache)
+    check_close(tensors.widen(got, "bf16"), oracle.decode_batch(ref), "bf16", "cow fork")
+
+
 # ----------------------------------------------------------------- gather
 @pytest.mark.parametrize("name,nseq", [("tiny_f32", 4), ("llama13b_mha_f16", 6),
                                        ("shared_prefix_bf16", 8), ("long_context_bf16", 1)])

@@ -46,6 +46,12 @@ MUTANTS = {
                        "        double m = x[0];"),
     # split merge: rescale factor with the wrong sign
     "merge_sign": ("const double c = exp(m_p[p] - M) / total;", "const double c = exp(M - m_p[p]) / total;"),
+    # block copy: source and destination swapped
+    "copy_direction": ("const int src = block_mapping[2 * i];\n        const int dst = block_mapping[2 * i + 1];",
+                       "const int src = block_mapping[2 * i + 1];\n        const int dst = block_mapping[2 * i];"),
+    # block copy: value pool filled from the key pool
+    "copy_v_from_k": ("memmove((char *)value_cache + (size_t)dst * block_bytes,\n                (const char *)value_cache",
+                      "memmove((char *)value_cache + (size_t)dst * block_bytes,\n                (const char *)key_cache"),
     # gather: value rows taken from the key pool
     "gather_v_from_k": ("memcpy((char *)out_v + dst * element_bytes(dtype),\n                   (const char *)value_cache",
                         "memcpy((char *)out_v + dst * element_bytes(dtype),\n                   (const char *)key_cache"),
