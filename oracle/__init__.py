@@ -44,6 +44,7 @@ class Oracle:
             "oracle_kv_cache_write": [vp, vp, vp, vp, vp] + [ci] * 5,
             "oracle_paged_kv_gather": [vp, vp, vp, vp, vp, vp] + [ci] * 7,
             "oracle_copy_blocks": [vp, vp, vp] + [ci] * 5,
+            "oracle_paged_attention_prefill": [vp] * 6 + [cf] + [ci] * 7 + [vp],
             "oracle_elements_to_double": [vp, ctypes.c_int64, ci, vp],
             "oracle_set_threads": [ci],
             "oracle_max_threads": [],
@@ -118,6 +119,25 @@ class Oracle:
                                         _ptr(out_k), _ptr(out_v), S, Hkv, D, bs, bt.shape[1],
                                         int(max_context_len), _code(dtype))
         return out_k, out_v
+
+    def paged_attention_prefill(self, query, key_cache, value_cache, block_tables,
+                                context_lens, query_start, scale, dtype):
+        """Multi-token causal attention over the paged cache; returns fp64
+        [total_q, Hq, D].  Row i of sequence s sits at position
+        context_lens[s] - q_len_s + i and attends over positions 0 .. that."""
+        total_q, Hq, D = query.shape
+        nb, bs, Hkv, D2 = key_cache.shape
+        assert D2 == D
+        bt = np.ascontiguousarray(block_tables, dtype=np.int32)
+        cl = np.ascontiguousarray(context_lens, dtype=np.int32)
+        qs = np.ascontiguousarray(query_start, dtype=np.int32)
+        S = bt.shape[0]
+        assert qs.shape == (S + 1,) and qs[-1] == total_q
+        out = np.zeros((total_q, Hq, D), dtype=np.float64)
+        self.lib.oracle_paged_attention_prefill(
+            _ptr(query), _ptr(key_cache), _ptr(value_cache), _ptr(bt), _ptr(cl), _ptr(qs),
+            ctypes.c_float(scale), S, Hq, Hkv, D, bs, bt.shape[1], _code(dtype), _ptr(out))
+        return out
 
     def copy_blocks(self, key_cache, value_cache, block_mapping, dtype):
         """Copy-on-write block copy, in place: for each (src, dst) row of

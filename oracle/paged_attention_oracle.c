@@ -30,6 +30,15 @@
  *    nothing ("大模型推理框架VLLM-0.7.3源码", §2.1 on slot_mapping).
  *  - Gather: materialise each sequence's logical K/V through its block
  *    table (the same addressing, as a bit copy).
+ *  - Multi-token (chunked-prefill) attention: a sequence adds q_len new
+ *    tokens at once (a prompt, or a chunk of one, processed together with
+ *    decoding sequences in one batch: "23.1 vLLM：高吞吐推理框架原理与部署",
+ *    §二.2 and continuous batching; "大模型推理框架VLLM-0.7.3源码", §3.2).
+ *    Their keys and values are already in the pool at positions
+ *    L - q_len .. L - 1 of the sequence, and new token i (position
+ *    L - q_len + i) attends over positions 0 .. L - q_len + i -- every
+ *    earlier token and itself, never a later one (causal).  With q_len = 1
+ *    this is the decode above.
  *  - Block copy: copy-on-write of shared blocks -- before a sequence writes
  *    into a block it shares with others, the block's contents are copied to
  *    a block of its own ("23.1 vLLM：高吞吐推理框架原理与部署", §二.3).  Each
@@ -340,5 +349,74 @@ void oracle_copy_blocks(void *key_cache, void *value_cache, const int32_t *block
                 (const char *)key_cache + (size_t)src * block_bytes, block_bytes);
         memmove((char *)value_cache + (size_t)dst * block_bytes,
                 (const char *)value_cache + (size_t)src * block_bytes, block_bytes);
+    }
+}
+
+/*
+ * Multi-token attention.  query and out: [total_q, num_q_heads, head_dim],
+ * the new tokens of all sequences one after another; query_start[num_seqs+1]
+ * gives sequence s its rows query_start[s] .. query_start[s+1] - 1 (q_len).
+ * context_lens[s] = L counts every cached token of s including its q_len new
+ * ones.  Row i of sequence s attends over positions 0 .. L - q_len + i.
+ * A sequence with q_len > L writes NaN rows (out is fp64 here).
+ */
+void oracle_paged_attention_prefill(const void *query, const void *key_cache,
+                                    const void *value_cache, const int32_t *block_tables,
+                                    const int32_t *context_lens, const int32_t *query_start,
+                                    float scale, int num_seqs, int num_q_heads, int num_kv_heads,
+                                    int head_dim, int block_size, int max_blocks_per_seq,
+                                    int dtype, double *out)
+{
+    const int group = num_q_heads / num_kv_heads;
+    const int64_t total_q = query_start[num_seqs];
+    const int64_t units = total_q * num_q_heads;
+#pragma omp parallel for schedule(dynamic, 4)
+    for (int64_t unit = 0; unit < units; ++unit) {
+        const int64_t row = unit / num_q_heads; /* global new-token index */
+        const int h = (int)(unit % num_q_heads);
+        int s = 0;
+        while (query_start[s + 1] <= row)
+            ++s;
+        const int q_len = query_start[s + 1] - query_start[s];
+        const int i = (int)(row - query_start[s]);
+        const int context_len = context_lens[s];
+        const int kv_head = h / group;
+        const int32_t *blocks = block_tables + (int64_t)s * max_blocks_per_seq;
+        const int64_t q0 = (row * num_q_heads + h) * head_dim;
+        double *o = out + unit * head_dim;
+        if (q_len > context_len) {
+            for (int d = 0; d < head_dim; ++d)
+                o[d] = NAN;
+            continue;
+        }
+        const int position = context_len - q_len + i;
+        const int n = position + 1; /* positions 0 .. position */
+
+        double *x = (double *)malloc(sizeof(double) * (size_t)n);
+        for (int j = 0; j < n; ++j) {
+            const int64_t k0 = pool_row(blocks[j / block_size], j % block_size, kv_head,
+                                        block_size, num_kv_heads, head_dim);
+            double dot = 0.0;
+            for (int d = 0; d < head_dim; ++d)
+                dot += element(query, q0 + d, dtype) * element(key_cache, k0 + d, dtype);
+            x[j] = (double)scale * dot;
+        }
+        double m = x[0];
+        for (int j = 1; j < n; ++j)
+            if (x[j] > m)
+                m = x[j];
+        double sum = 0.0;
+        for (int j = 0; j < n; ++j)
+            sum += exp(x[j] - m);
+        for (int d = 0; d < head_dim; ++d)
+            o[d] = 0.0;
+        for (int j = 0; j < n; ++j) {
+            const double w = exp(x[j] - m) / sum;
+            const int64_t v0 = pool_row(blocks[j / block_size], j % block_size, kv_head,
+                                        block_size, num_kv_heads, head_dim);
+            for (int d = 0; d < head_dim; ++d)
+                o[d] += w * element(value_cache, v0 + d, dtype);
+        }
+        free(x);
     }
 }

@@ -314,6 +314,106 @@ def make_custom(seed: int, *, dtype="f32", num_seqs=2, num_q_heads=2, num_kv_hea
                      poison=poison, seed=seed, keys_identical=keys_identical)
 
 
+@dataclass
+class PrefillBatch:
+    """Multi-token (chunked-prefill) inputs: a paged pool whose sequences
+    already hold their q_len new tokens at positions L - q_len .. L - 1, and
+    the queries of those new tokens, all sequences one after another
+    (``query_start[s] .. query_start[s+1] - 1`` are sequence s's rows)."""
+
+    base: DecodeBatch                # pool, tables, context_lens (L includes the new tokens)
+    query: np.ndarray                # [total_q, Hq, D] bits
+    query_start: np.ndarray          # [S + 1] int32
+
+    def __getattr__(self, name):
+        # pool, shapes and lengths come from the decode batch underneath
+        if name in ("base", "query", "query_start"):
+            raise AttributeError(name)
+        return getattr(self.base, name)
+
+    @property
+    def query_lens(self) -> np.ndarray:
+        return np.diff(self.query_start).astype(np.int32)
+
+    @property
+    def total_q(self) -> int:
+        return int(self.query_start[-1])
+
+    @property
+    def max_query_len(self) -> int:
+        return int(self.query_lens.max()) if self.base.num_seqs else 0
+
+    def copy(self) -> "PrefillBatch":
+        return PrefillBatch(self.base.copy(), self.query.copy(), self.query_start.copy())
+
+    def flops(self) -> int:
+        """Causal attention FLOPs: new token i of sequence s scores and
+        averages L - q_len + i + 1 positions, 4 * head_dim flops each, for
+        every query head."""
+        total = 0
+        for L, q in zip(self.base.context_lens.astype(np.int64), self.query_lens.astype(np.int64)):
+            if 0 < q <= L:
+                total += int(q * (L - q) + q * (q + 1) // 2)
+        return total * self.base.num_q_heads * 4 * self.base.head_dim
+
+    def algorithmic_bytes(self) -> int:
+        """Each sequence's K/V rows once, the queries read, the outputs
+        written, block-table entries and the two length arrays."""
+        b = self.base
+        e = b.elem_bytes
+        L = b.context_lens.astype(np.int64)
+        kv = int(L.sum()) * b.num_kv_heads * b.head_dim * e * 2
+        qo = 2 * self.total_q * b.num_q_heads * b.head_dim * e
+        bt = int(np.sum((L + b.block_size - 1) // b.block_size)) * 4
+        return kv + qo + bt + 4 * (2 * b.num_seqs + 1)
+
+
+def make_prefill(seed: int, *, dtype="bf16", num_q_heads=8, num_kv_heads=2, head_dim=128,
+                 block_size=16, context_lens=(40, 17), query_lens=(8, 17), extra_blocks=3,
+                 pool_factor=1.0, poison=False, scale=None, values=True,
+                 name=None) -> PrefillBatch:
+    """A multi-token batch: sequence s holds context_lens[s] tokens, the last
+    query_lens[s] of them new (their queries are drawn here, their K/V are
+    already in the pool).  Blocks are dealt as for make_custom."""
+    rng = np.random.default_rng(seed)
+    lens = np.asarray(context_lens, dtype=np.int64)
+    qlens = np.asarray(query_lens, dtype=np.int64)
+    assert lens.shape == qlens.shape
+    need = [(int(L) + block_size - 1) // block_size for L in lens]
+    mb = max(1, max(need))
+    tables, pool = _deal_tables(rng, lens, block_size, mb, pool_factor=pool_factor,
+                                min_pool=sum(need) + max(1, extra_blocks))
+    if scale is None:
+        scale = 1.0 / math.sqrt(head_dim)
+    base = _assemble(name or f"prefill{seed}", dtype, rng, S=len(lens), Hq=num_q_heads,
+                     Hkv=num_kv_heads, D=head_dim, bs=block_size, lens=lens, tables=tables,
+                     num_blocks=pool, max_blocks=mb, scale=scale, poison=poison, seed=seed,
+                     values=values)
+    qs = np.zeros(len(lens) + 1, dtype=np.int32)
+    qs[1:] = np.cumsum(qlens)
+    query = _normal_bits(rng, (int(qs[-1]), num_q_heads, head_dim), dtype)
+    return PrefillBatch(base, query, qs)
+
+
+PREFILL_WORKLOADS = ("llama3_8b_chunked_prefill_bf16",)
+
+
+def make_prefill_workload(name: str, seed: int | None = None, poison: bool = False,
+                          values: bool = True) -> PrefillBatch:
+    """Chunked prefill on the Llama-3-8B shape: 16 prompts of 1024..2048
+    tokens whose last 512 tokens are processed as one chunk (the earlier ones
+    already cached), 32 query / 8 kv heads, head_dim 128, block_size 16,
+    bf16."""
+    if name != "llama3_8b_chunked_prefill_bf16":
+        raise ValueError(name)
+    seed = 46710 if seed is None else seed
+    rng = np.random.default_rng(seed)
+    lens = rng.integers(1024, 2048, size=16, endpoint=True)
+    return make_prefill(seed, dtype="bf16", num_q_heads=32, num_kv_heads=8, head_dim=128,
+                        block_size=16, context_lens=lens, query_lens=np.full(16, 512),
+                        pool_factor=1.5, poison=poison, values=values, name=name)
+
+
 def permute_blocks(batch: DecodeBatch, seed: int) -> DecodeBatch:
     """Relabel physical blocks by a random permutation pi: pool row b moves
     to pi[b] and every table entry b becomes pi[b].  The logical contents of

@@ -366,10 +366,102 @@ def pin_copy_blocks(orc):
         assert np.array_equal(k2[pairs[1, 1]].view(np.uint8), kc[pairs[1, 1]].view(np.uint8))
 
 
+# ------------------------------------------------------ multi-token (prefill)
+PREFILL_SHAPES = [
+    # seed, dtype, Hq, Hkv, D, bs, context lens, query lens
+    (51, "f32", 4, 2, 8, 4, (9, 20, 5), (3, 20, 1)),
+    (52, "bf16", 8, 2, 64, 16, (40, 17, 33), (8, 17, 1)),
+    (53, "f16", 6, 6, 16, 1, (12, 7), (5, 7)),
+    (54, "bf16", 4, 1, 32, 32, (70, 64), (35, 2)),
+]
+
+
+def _prefill(seed, dt, Hq, Hkv, D, bs, lens, qlens):
+    return W.make_prefill(seed, dtype=dt, num_q_heads=Hq, num_kv_heads=Hkv, head_dim=D,
+                          block_size=bs, context_lens=lens, query_lens=qlens)
+
+
+def _run_prefill(orc, b, key_cache=None, value_cache=None):
+    return orc.paged_attention_prefill(
+        b.query, b.key_cache if key_cache is None else key_cache,
+        b.value_cache if value_cache is None else value_cache, b.block_tables, b.context_lens,
+        b.query_start, b.scale, b.dtype)
+
+
+def pin_prefill_vs_sdpa(orc):
+    """Multi-token causal attention against torch's CPU fp64
+    scaled_dot_product_attention on K/V gathered with numpy indexing, with an
+    explicit mask: new token i (position L - q + i) sees positions <= its own."""
+    import torch
+    import torch.nn.functional as F
+
+    for args in PREFILL_SHAPES:
+        b = _prefill(*args)
+        got = _run_prefill(orc, b)
+        kc, vc = _f64(b.key_cache, b.dtype), _f64(b.value_cache, b.dtype)
+        q = _f64(b.query, b.dtype)
+        for s in range(b.num_seqs):
+            L, q0, q1 = int(b.context_lens[s]), int(b.query_start[s]), int(b.query_start[s + 1])
+            nq = q1 - q0
+            blocks = b.block_tables[s, :(L + b.block_size - 1) // b.block_size]
+            k = kc[blocks].reshape(-1, b.num_kv_heads, b.head_dim)[:L]
+            v = vc[blocks].reshape(-1, b.num_kv_heads, b.head_dim)[:L]
+            mask = np.arange(L)[None, :] <= (L - nq + np.arange(nq))[:, None]
+            o = F.scaled_dot_product_attention(
+                torch.from_numpy(q[q0:q1]).permute(1, 0, 2)[None].contiguous(),
+                torch.from_numpy(k).permute(1, 0, 2)[None].contiguous(),
+                torch.from_numpy(v).permute(1, 0, 2)[None].contiguous(),
+                attn_mask=torch.from_numpy(mask), scale=float(b.scale), enable_gqa=True)
+            ref = o[0].permute(1, 0, 2).numpy()
+            err = np.abs(got[q0:q1] - ref).max()
+            assert err <= 1e-12 * max(1.0, np.abs(ref).max()), (args[0], s, err)
+
+
+def pin_prefill_one_token_is_decode(orc):
+    """With one new token per sequence the multi-token attention is the
+    decode attention."""
+    b = W.make_custom(61, dtype="bf16", num_seqs=3, num_q_heads=8, num_kv_heads=2, head_dim=32,
+                      block_size=16, context_lens=(5, 33, 16))
+    qs = np.arange(4, dtype=np.int32)
+    got = orc.paged_attention_prefill(b.query, b.key_cache, b.value_cache, b.block_tables,
+                                      b.context_lens, qs, b.scale, b.dtype)
+    assert np.abs(got - orc.decode_batch(b)).max() <= 1e-14
+
+
+def pin_prefill_causal(orc):
+    """The first token of a whole prompt (q_len = L) sees only itself, so its
+    output is exactly its own V row; changing the K/V row of the last
+    position changes only the last new token's output (bit for bit)."""
+    b = _prefill(55, "f16", 4, 2, 16, 4, (6, 11), (6, 4))
+    got = _run_prefill(orc, b)
+    v0 = _f64(b.value_cache[b.block_tables[0, 0], 0], b.dtype)        # [Hkv, D]
+    assert np.array_equal(got[0], np.repeat(v0, 2, axis=0))
+    kc, vc = b.key_cache.copy(), b.value_cache.copy()
+    for s in range(b.num_seqs):
+        L = int(b.context_lens[s])
+        blk, off = b.block_tables[s, (L - 1) // b.block_size], (L - 1) % b.block_size
+        kc[blk, off] = W.f32_to_bits(np.full(kc[blk, off].shape, 3.0, np.float32), b.dtype)
+        vc[blk, off] = W.f32_to_bits(np.full(vc[blk, off].shape, -5.0, np.float32), b.dtype)
+    moved = _run_prefill(orc, b, kc, vc)
+    last = b.query_start[1:] - 1
+    keep = np.setdiff1d(np.arange(b.total_q), last)
+    assert np.array_equal(moved[keep], got[keep])
+    assert np.all(np.abs(moved[last] - got[last]).max(axis=(1, 2)) > 1e-3)
+
+
+def pin_prefill_block_permutation(orc):
+    b = _prefill(56, "bf16", 8, 2, 16, 4, (30, 13), (10, 13))
+    p = W.permute_blocks(b.base, 3)
+    pb = W.PrefillBatch(p, b.query, b.query_start)
+    assert np.array_equal(_run_prefill(orc, b), _run_prefill(orc, pb))
+
+
 ALL_PINS = [
     pin_element_decode, pin_addressing_worked_example, pin_shared_prefix_blocks,
     pin_write_gather_roundtrip, pin_decode_vs_sdpa, pin_tiny_workload_vs_sdpa,
     pin_context_len_one, pin_identical_keys, pin_two_token_logistic, pin_weights_sum_to_one,
     pin_block_permutation, pin_gqa_equals_mha, pin_split_merge, pin_poison_unreferenced,
     pin_large_scores, pin_empty_context, pin_linear_in_values, pin_copy_blocks,
+    pin_prefill_vs_sdpa, pin_prefill_one_token_is_decode, pin_prefill_causal,
+    pin_prefill_block_permutation,
 ]

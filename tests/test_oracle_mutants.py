@@ -46,6 +46,12 @@ MUTANTS = {
                        "        double m = x[0];"),
     # split merge: rescale factor with the wrong sign
     "merge_sign": ("const double c = exp(m_p[p] - M) / total;", "const double c = exp(M - m_p[p]) / total;"),
+    # multi-token: causal bound off by one (a new token does not see itself)
+    "prefill_causal_off_by_one": ("const int n = position + 1; /* positions 0 .. position */",
+                                  "const int n = position > 0 ? position : 1;"),
+    # multi-token: new token i placed at position i instead of L - q_len + i
+    "prefill_position": ("const int position = context_len - q_len + i;",
+                         "const int position = i;"),
     # block copy: source and destination swapped
     "copy_direction": ("const int src = block_mapping[2 * i];\n        const int dst = block_mapping[2 * i + 1];",
                        "const int src = block_mapping[2 * i + 1];\n        const int dst = block_mapping[2 * i];"),
