@@ -186,6 +186,100 @@ def bench_copy_blocks(args) -> int:
     return 0
 
 
+MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "f16": 2500.0}
+
+
+def bench_prefill(args) -> int:
+    """Multi-token (chunked-prefill) attention: each of 16 prompts of
+    1024..2048 tokens has its last 512 tokens as new queries.  The work is a
+    real contraction, so the roofline is the MFMA peak; `value` counts only
+    the causally needed attention FLOPs."""
+    import numpy as np
+    import torch
+
+    import oracle
+    from paged_kv_cache_467_amd import binding, tensors, workloads as W
+
+    name = "llama3_8b_chunked_prefill_bf16"
+    dev = torch.device("cuda:0")
+    b = W.make_prefill_workload(name, values=False)
+    dt = tensors.TORCH_DTYPE[b.dtype]
+    pool_shape = (b.num_blocks, b.block_size, b.num_kv_heads, b.head_dim)
+    copies = [(torch.randn(pool_shape, device=dev).to(dt), torch.randn(pool_shape, device=dev).to(dt))
+              for _ in range(max(1, args.copies))]
+    query = torch.randn((b.total_q, b.num_q_heads, b.head_dim), device=dev).to(dt)
+    out = torch.empty_like(query)
+    bt = tensors.int32(b.block_tables, dev)
+    cl = tensors.int32(b.context_lens, dev)
+    qs = tensors.int32(b.query_start, dev)
+
+    def step(i):
+        kc, vc = copies[i % len(copies)]
+        binding.paged_attn_prefill(query, kc, vc, bt, cl, qs, b.scale, out,
+                                   max_query_len=b.max_query_len,
+                                   max_context_len=b.base.max_context_len)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    events = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for i, (a, z) in enumerate(events):
+        a.record()
+        step(args.warmup + i)
+        z.record()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    ms = [a.elapsed_time(z) for a, z in events]
+    avg = sum(ms) / len(ms)
+    flops = b.flops()
+    tflops = flops / (avg * 1e-3) / 1e12
+    peak = MFMA_PEAK_TFLOPS[b.dtype]
+    result = {
+        "metric": "chunked-prefill paged attention: achieved TFLOP/s (% of MFMA peak)",
+        "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(elapsed * 1e3 / args.steps, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": b.dtype,
+        "data": "synthetic",
+        "config": {"workload": name, "num_seqs": b.num_seqs, "new_tokens": b.total_q,
+                   "context_len_range": [int(b.context_lens.min()), int(b.context_lens.max())],
+                   "num_q_heads": b.num_q_heads, "num_kv_heads": b.num_kv_heads,
+                   "head_dim": b.head_dim, "block_size": b.block_size, "pool_copies": len(copies)},
+        "prefill_ms": round(avg, 5),
+        "new_tokens_per_s": round(b.total_q / (avg * 1e-3), 1),
+        "algorithmic_bytes_per_launch": b.algorithmic_bytes(),
+        "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": peak,
+                     "unit": "TFLOP/s", "frac": round(tflops / peak, 4), "traffic": None,
+                     "kernel": "paged_attn_prefill", "flops_per_launch": flops},
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        # one sequence of the workload (512 new tokens), timed on all host threads
+        host = W.make_prefill_workload(name)
+        s = int(np.argmin(host.context_lens))
+        q0, q1 = int(host.query_start[s]), int(host.query_start[s + 1])
+        sub = W.PrefillBatch(host.base, host.query[q0:q1],
+                             np.array([0] * (s + 1) + [q1 - q0] * (host.num_seqs - s), np.int32))
+        orc = oracle.default()
+        orc.set_threads(len(os.sched_getaffinity(0)))
+        times = []
+        while len(times) < 3 or sum(times) < 5.0:
+            t1 = time.perf_counter()
+            orc.paged_attention_prefill(sub.query, sub.key_cache, sub.value_cache,
+                                        sub.block_tables, sub.context_lens, sub.query_start,
+                                        sub.scale, sub.dtype)
+            times.append(time.perf_counter() - t1)
+        t = statistics.median(times)
+        result["cpu_baseline"] = {
+            "value": round(sub.flops() / t / 1e12, 6), "unit": "TFLOP/s",
+            "cores": orc.max_threads(), "kind": "oracle",
+            "sample": f"sequence {s} of the workload ({q1 - q0} new tokens, context "
+                      f"{int(host.context_lens[s])}), fp64, median of {len(times)} runs of {t:.3f} s"}
+    print(json.dumps(result), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -195,9 +289,10 @@ def main() -> int:
     ap.add_argument("--copies", type=int, default=4, help="pool copies rotated across steps")
     ap.add_argument("--partition-size", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--op", choices=("decode", "copy_blocks"), default="decode",
+    ap.add_argument("--op", choices=("decode", "copy_blocks", "prefill"), default="decode",
                     help="decode: the decode step (default); copy_blocks: the copy-on-write "
-                         "block copy on the same pool")
+                         "block copy on the same pool; prefill: multi-token attention on the "
+                         "chunked-prefill workload")
     ap.add_argument("--pairs", type=int, default=2048, help="block pairs per copy_blocks step")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="also run one plain device copy of this many MiB (counter calibration)")
@@ -221,6 +316,8 @@ def main() -> int:
     torch.manual_seed(0)
     if args.op == "copy_blocks":
         return bench_copy_blocks(args)
+    if args.op == "prefill":
+        return bench_prefill(args)
     b = W.make_workload(args.workload, values=False)
     dt = tensors.TORCH_DTYPE[b.dtype]
     S, Hq, Hkv, D, bs = b.num_seqs, b.num_q_heads, b.num_kv_heads, b.head_dim, b.block_size

@@ -38,6 +38,9 @@
 extern "C" {
 #endif
 
+/* Entry points are the library's only exported symbols. */
+#define PAGED_KV_API __attribute__((visibility("default")))
+
 typedef enum {
     PAGED_KV_F32 = 0,  /* IEEE binary32 */
     PAGED_KV_F16 = 1,  /* IEEE binary16 */
@@ -54,7 +57,7 @@ typedef enum {
 } paged_kv_status;
 
 /* Human-readable name of a status code (static storage, never NULL). */
-const char *paged_kv_status_string(int status);
+PAGED_KV_API const char *paged_kv_status_string(int status);
 
 /*
  * Decode attention over a paged KV cache.
@@ -101,12 +104,12 @@ const char *paged_kv_status_string(int status);
  * 2^31 elements (64-bit addressing); one block, block_size * num_kv_heads *
  * head_dim elements, must fit in 2^31 - 1 bytes (else PAGED_KV_ERR_BAD_SHAPE).
  */
-int paged_attn_decode(const void *query, const void *key_cache, const void *value_cache,
-                      const int32_t *block_tables, const int32_t *context_lens, float scale,
-                      void *out, int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
-                      int block_size, int num_blocks, int max_blocks_per_seq,
-                      int max_context_len, int partition_size, int dtype, void *workspace,
-                      size_t workspace_bytes, void *stream);
+PAGED_KV_API int paged_attn_decode(
+    const void *query, const void *key_cache, const void *value_cache,
+    const int32_t *block_tables, const int32_t *context_lens, float scale, void *out,
+    int num_seqs, int num_q_heads, int num_kv_heads, int head_dim, int block_size,
+    int num_blocks, int max_blocks_per_seq, int max_context_len, int partition_size, int dtype,
+    void *workspace, size_t workspace_bytes, void *stream);
 
 /*
  * The context partition size paged_attn_decode uses for these arguments
@@ -114,9 +117,9 @@ int paged_attn_decode(const void *query, const void *key_cache, const void *valu
  * code when the arguments are invalid.  A partition size >= max_context_len
  * means no split: one pass writes out directly.
  */
-int paged_attn_decode_partition_size(int num_seqs, int num_q_heads, int num_kv_heads,
-                                     int head_dim, int block_size, int max_blocks_per_seq,
-                                     int max_context_len, int partition_size, int dtype);
+PAGED_KV_API int paged_attn_decode_partition_size(
+    int num_seqs, int num_q_heads, int num_kv_heads, int head_dim, int block_size,
+    int max_blocks_per_seq, int max_context_len, int partition_size, int dtype);
 
 /*
  * Bytes of workspace paged_attn_decode needs for these arguments (0 when the
@@ -124,9 +127,9 @@ int paged_attn_decode_partition_size(int num_seqs, int num_q_heads, int num_kv_h
  * partials are fp32: per (sequence, query head, partition) a running max, a
  * running sum and head_dim unnormalised output values.
  */
-size_t paged_attn_decode_workspace_bytes(int num_seqs, int num_q_heads, int num_kv_heads,
-                                         int head_dim, int block_size, int max_blocks_per_seq,
-                                         int max_context_len, int partition_size, int dtype);
+PAGED_KV_API size_t paged_attn_decode_workspace_bytes(
+    int num_seqs, int num_q_heads, int num_kv_heads, int head_dim, int block_size,
+    int max_blocks_per_seq, int max_context_len, int partition_size, int dtype);
 
 /*
  * Store new tokens' keys and values in the paged pool.
@@ -144,9 +147,55 @@ size_t paged_attn_decode_workspace_bytes(int num_seqs, int num_q_heads, int num_
  * row (unspecified which).  Writing into a block that several sequences
  * share is the caller's responsibility (copy it first).
  */
-int kv_cache_write(const void *key, const void *value, const int32_t *slot_mapping,
-                   void *key_cache, void *value_cache, int num_tokens, int num_kv_heads,
-                   int head_dim, int block_size, int num_blocks, int dtype, void *stream);
+PAGED_KV_API int kv_cache_write(
+    const void *key, const void *value, const int32_t *slot_mapping, void *key_cache,
+    void *value_cache, int num_tokens, int num_kv_heads, int head_dim, int block_size,
+    int num_blocks, int dtype, void *stream);
+
+/*
+ * Multi-token (chunked-prefill) attention over a paged KV cache.
+ *
+ * Sequence s holds L = context_lens[s] tokens in the pool, the last q_len of
+ * which are new: a prompt, or a chunk of one, processed in the same batch as
+ * decoding sequences ("23.1 vLLM：高吞吐推理框架原理与部署", §二.2;
+ * "大模型推理框架VLLM-0.7.3源码", §3.2).  Their keys and values are already
+ * in the pool (kv_cache_write), and their queries are rows
+ * query_start[s] .. query_start[s+1] - 1 of query (q_len of them).  New
+ * token i sits at position L - q_len + i and attends over positions
+ * 0 .. L - q_len + i of its sequence -- every earlier token and itself:
+ *   x_j = scale * dot(query[row, h, :], key_cache[block, offset, h / G, :]),
+ *   out[row, h, :] = sum_j softmax(x)_j * value_cache[block, offset, h / G, :],
+ * with position j at block block_tables[s][j / block_size], offset
+ * j % block_size ("大模型推理框架 vllm 源码解析 一", §三).  With q_len = 1
+ * this is paged_attn_decode.  Accumulation is fp32 (the weights enter the
+ * value product rounded to the element type); out is rounded to nearest
+ * even.
+ *
+ * Arguments:
+ *   query, out     [total_q, num_q_heads, head_dim]
+ *   key_cache, value_cache  [num_blocks, block_size, num_kv_heads, head_dim]
+ *   block_tables   [num_seqs, max_blocks_per_seq] int32
+ *   context_lens   [num_seqs] int32, L including the new tokens
+ *   query_start    [num_seqs + 1] int32, non-decreasing, query_start[0] = 0,
+ *                  query_start[num_seqs] = total_q
+ *   max_query_len  upper bound on every q_len (sizes the grid)
+ *   max_context_len  upper bound on every L; 0 means
+ *                  max_blocks_per_seq * block_size
+ * Supported: dtype f16, bf16 (f32: PAGED_KV_ERR_UNSUPPORTED); head_dim 64,
+ * 128, 256; num_q_heads / num_kv_heads in {1, 2, 4, 8}; block_size a power
+ * of two in [1, 256].  No workspace; nothing is allocated.
+ * Device-side values: a sequence with q_len > L or L > max_context_len gets
+ * NaN rows; a table entry outside [0, num_blocks) makes the rows that read
+ * it NaN; rows past max_query_len are not written, nor are the rows of a
+ * sequence whose query_start range leaves [0, total_q] or decreases.
+ * Nothing out of range is read or written.
+ */
+PAGED_KV_API int paged_attn_prefill(
+    const void *query, const void *key_cache, const void *value_cache,
+    const int32_t *block_tables, const int32_t *context_lens, const int32_t *query_start,
+    float scale, void *out, int num_seqs, int total_q, int num_q_heads, int num_kv_heads,
+    int head_dim, int block_size, int num_blocks, int max_blocks_per_seq, int max_query_len,
+    int max_context_len, int dtype, void *stream);
 
 /*
  * Copy-on-write block copy: before a sequence writes into a block that other
@@ -167,9 +216,9 @@ int kv_cache_write(const void *key, const void *value, const int32_t *slot_mappi
  * One block (block_size * num_kv_heads * head_dim elements) must be a
  * multiple of 16 bytes and at most 4 GiB (else PAGED_KV_ERR_BAD_SHAPE).
  */
-int paged_kv_copy_blocks(void *key_cache, void *value_cache, const int32_t *block_mapping,
-                         int num_pairs, int num_kv_heads, int head_dim, int block_size,
-                         int num_blocks, int dtype, void *stream);
+PAGED_KV_API int paged_kv_copy_blocks(
+    void *key_cache, void *value_cache, const int32_t *block_mapping, int num_pairs,
+    int num_kv_heads, int head_dim, int block_size, int num_blocks, int dtype, void *stream);
 
 /*
  * Materialise each sequence's logical K/V through its block table (the
@@ -180,11 +229,11 @@ int paged_kv_copy_blocks(void *key_cache, void *value_cache, const int32_t *bloc
  * j; later positions are left untouched.  A table entry outside
  * [0, num_blocks) fills the rows it would supply with NaN.
  */
-int paged_kv_gather(const void *key_cache, const void *value_cache,
-                    const int32_t *block_tables, const int32_t *context_lens, void *out_key,
-                    void *out_value, int num_seqs, int num_kv_heads, int head_dim,
-                    int block_size, int num_blocks, int max_blocks_per_seq,
-                    int max_context_len, int dtype, void *stream);
+PAGED_KV_API int paged_kv_gather(
+    const void *key_cache, const void *value_cache, const int32_t *block_tables,
+    const int32_t *context_lens, void *out_key, void *out_value, int num_seqs, int num_kv_heads,
+    int head_dim, int block_size, int num_blocks, int max_blocks_per_seq, int max_context_len,
+    int dtype, void *stream);
 
 #ifdef __cplusplus
 }

@@ -28,6 +28,7 @@ EXPORTED = (
     "kv_cache_write",
     "paged_kv_gather",
     "paged_kv_copy_blocks",
+    "paged_attn_prefill",
 )
 
 
@@ -52,6 +53,8 @@ def _load_library(path: str = LIBRARY) -> ctypes.CDLL:
     lib.paged_kv_gather.restype = ci
     lib.paged_kv_copy_blocks.argtypes = [vp] * 3 + [ci] * 6 + [vp]
     lib.paged_kv_copy_blocks.restype = ci
+    lib.paged_attn_prefill.argtypes = [vp] * 6 + [cf, vp] + [ci] * 11 + [vp]
+    lib.paged_attn_prefill.restype = ci
     return lib
 
 
@@ -209,3 +212,37 @@ def paged_kv_copy_blocks(key_cache: torch.Tensor, value_cache: torch.Tensor,
         _dev(block_mapping, "block_mapping"), block_mapping.shape[0], Hkv, D, bs, nb,
         _dtype_code(key_cache), _stream(key_cache.device))
     _check("paged_kv_copy_blocks", status)
+
+
+def paged_attn_prefill(query: torch.Tensor, key_cache: torch.Tensor, value_cache: torch.Tensor,
+                       block_tables: torch.Tensor, context_lens: torch.Tensor,
+                       query_start: torch.Tensor, scale: float, out: torch.Tensor, *,
+                       max_query_len: int, max_context_len: int = 0) -> torch.Tensor:
+    """Multi-token causal attention of each sequence's new tokens over the
+    paged cache (see paged_attn_prefill in include/paged_kv.h).  query/out
+    [total_q, Hq, D]; query_start [S + 1] int32; context_lens [S] int32
+    counts the new tokens too."""
+    total_q, Hq, D = query.shape
+    nb, bs, Hkv, D2 = key_cache.shape
+    S = context_lens.shape[0]
+    if D2 != D or tuple(value_cache.shape) != tuple(key_cache.shape):
+        raise ValueError("query / key_cache / value_cache shapes disagree")
+    if tuple(out.shape) != (total_q, Hq, D) or out.dtype != query.dtype:
+        raise ValueError("out must match query's shape and dtype")
+    if key_cache.dtype != query.dtype or value_cache.dtype != query.dtype:
+        raise TypeError("query, caches and out must share one dtype")
+    for t, name in ((block_tables, "block_tables"), (context_lens, "context_lens"),
+                    (query_start, "query_start")):
+        if t.dtype != torch.int32:
+            raise TypeError(f"{name} must be int32")
+    if block_tables.dim() != 2 or block_tables.shape[0] != S or \
+            tuple(query_start.shape) != (S + 1,):
+        raise ValueError("block_tables must be [S, max_blocks] and query_start [S + 1]")
+    status = _lib.paged_attn_prefill(
+        _dev(query, "query"), _dev(key_cache, "key_cache"), _dev(value_cache, "value_cache"),
+        _dev(block_tables, "block_tables"), _dev(context_lens, "context_lens"),
+        _dev(query_start, "query_start"), ctypes.c_float(scale), _dev(out, "out"), S, total_q,
+        Hq, Hkv, D, bs, nb, block_tables.shape[1], max_query_len, max_context_len,
+        _dtype_code(query), _stream(query.device))
+    _check("paged_attn_prefill", status)
+    return out

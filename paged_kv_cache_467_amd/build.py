@@ -6,12 +6,13 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIBRARY = os.path.join(HERE, "libpaged_kv.so")
-SOURCES = ["paged_attention_decode.hip", "kv_cache_ops.hip", "capi.cpp"]
+SOURCES = ["paged_attention_decode.hip", "paged_attention_prefill.hip", "kv_cache_ops.hip",
+           "capi.cpp"]
 ARCH = os.environ.get("PAGED_KV_ARCH", "gfx950")
 
 FLAGS = [
     "-O3", "-std=c++17", "-fPIC", "-shared", f"--offload-arch={ARCH}",
-    "-Wall", "-Wno-unused-command-line-argument",
+    "-Wall", "-Wno-unused-command-line-argument", "-fvisibility=hidden",
     # no packed fp32 instructions in generated device code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
 ]

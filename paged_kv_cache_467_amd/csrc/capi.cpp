@@ -11,6 +11,7 @@
 #include <stdint.h>
 
 #include "decode.h"
+#include "prefill.h"
 
 namespace {
 
@@ -256,6 +257,68 @@ int kv_cache_write(const void *key, const void *value, const int32_t *slot_mappi
         pkv::launch_kv_cache_write(key, value, slot_mapping, key_cache, value_cache, num_tokens,
                                    (int)row, (int64_t)num_blocks * block_size,
                                    static_cast<hipStream_t>(stream));
+    return err == hipSuccess ? PAGED_KV_OK : PAGED_KV_ERR_HIP;
+}
+
+int paged_attn_prefill(const void *query, const void *key_cache, const void *value_cache,
+                       const int32_t *block_tables, const int32_t *context_lens,
+                       const int32_t *query_start, float scale, void *out, int num_seqs,
+                       int total_q, int num_q_heads, int num_kv_heads, int head_dim,
+                       int block_size, int num_blocks, int max_blocks_per_seq,
+                       int max_query_len, int max_context_len, int dtype, void *stream) {
+    if (dtype == PAGED_KV_F32) return PAGED_KV_ERR_UNSUPPORTED;
+    if (dtype != PAGED_KV_F16 && dtype != PAGED_KV_BF16) return PAGED_KV_ERR_UNSUPPORTED;
+    if (num_seqs < 0 || total_q < 0 || num_q_heads < 1 || num_kv_heads < 1 ||
+        num_q_heads % num_kv_heads != 0 || num_blocks < 1 || max_blocks_per_seq < 1 ||
+        max_query_len < 0 || max_context_len < 0)
+        return PAGED_KV_ERR_BAD_SHAPE;
+    const int group = num_q_heads / num_kv_heads;
+    if (!(head_dim == 64 || head_dim == 128 || head_dim == 256) ||
+        !(group == 1 || group == 2 || group == 4 || group == 8) || !pow2(block_size) ||
+        block_size > 256)
+        return PAGED_KV_ERR_UNSUPPORTED;
+    const int64_t table_tokens = (int64_t)max_blocks_per_seq * block_size;
+    if (table_tokens > INT_MAX) return PAGED_KV_ERR_BAD_SHAPE;
+    const int max_ctx = max_context_len == 0 ? (int)table_tokens : max_context_len;
+    if (max_ctx > table_tokens || !isfinite(scale)) return PAGED_KV_ERR_BAD_SHAPE;
+    const int e = elem_bytes(dtype);
+    if ((int64_t)block_size * num_kv_heads * head_dim * e > INT_MAX) return PAGED_KV_ERR_BAD_SHAPE;
+    const int rpb = pkv::prefill_rows_per_block();
+    const int64_t row_blocks = ((int64_t)max_query_len * group + rpb - 1) / rpb;
+    if ((int64_t)num_seqs * num_kv_heads * row_blocks > INT_MAX) return PAGED_KV_ERR_BAD_SHAPE;
+    if (num_seqs == 0 || total_q == 0 || max_query_len == 0) return PAGED_KV_OK;
+    if (!query || !key_cache || !value_cache || !block_tables || !context_lens ||
+        !query_start || !out)
+        return PAGED_KV_ERR_NULL_POINTER;
+    if (!aligned16(query) || !aligned16(key_cache) || !aligned16(value_cache) ||
+        !aligned16(out) || !aligned4(block_tables) || !aligned4(context_lens) ||
+        !aligned4(query_start))
+        return PAGED_KV_ERR_BAD_SHAPE;
+    pkv::PrefillParams p;
+    p.query = query;
+    p.key_cache = static_cast<const char *>(key_cache);
+    p.value_cache = static_cast<const char *>(value_cache);
+    p.block_tables = block_tables;
+    p.context_lens = context_lens;
+    p.query_start = query_start;
+    p.out = out;
+    p.scale_log2 = (float)((double)scale * 1.4426950408889634);  // scale * log2(e)
+    p.num_seqs = num_seqs;
+    p.total_q = total_q;
+    p.num_q_heads = num_q_heads;
+    p.num_kv_heads = num_kv_heads;
+    p.group = group;
+    p.block_size = block_size;
+    p.block_shift = log2i(block_size);
+    p.num_blocks = num_blocks;
+    p.max_blocks_per_seq = max_blocks_per_seq;
+    p.max_query_len = max_query_len;
+    p.max_context_len = max_ctx;
+    p.row_blocks = (int)row_blocks;
+    p.row_stride_bytes = num_kv_heads * head_dim * e;
+    p.block_stride_bytes = (int64_t)block_size * p.row_stride_bytes;
+    const hipError_t err =
+        pkv::launch_prefill(p, dtype, head_dim, static_cast<hipStream_t>(stream));
     return err == hipSuccess ? PAGED_KV_OK : PAGED_KV_ERR_HIP;
 }
 

@@ -1,0 +1,40 @@
+// Internal interface between the C ABI (capi.cpp) and the multi-token
+// (chunked-prefill) attention kernel.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pkv {
+
+struct PrefillParams {
+    const void *query;            // [total_q, Hq, D]
+    const char *key_cache;        // [num_blocks, bs, Hkv, D]
+    const char *value_cache;      // [num_blocks, bs, Hkv, D]
+    const int32_t *block_tables;  // [S, max_blocks_per_seq]
+    const int32_t *context_lens;  // [S]
+    const int32_t *query_start;   // [S + 1]
+    void *out;                    // [total_q, Hq, D]
+    float scale_log2;             // scale * log2(e)
+    int num_seqs;
+    int total_q;
+    int num_q_heads;
+    int num_kv_heads;
+    int group;                    // num_q_heads / num_kv_heads
+    int block_size;
+    int block_shift;              // log2(block_size)
+    int num_blocks;
+    int max_blocks_per_seq;
+    int max_query_len;            // rows of a sequence beyond this are not computed
+    int max_context_len;          // every valid context_len is <= this
+    int row_blocks;               // ceil(max_query_len * group / rows per workgroup)
+    int64_t block_stride_bytes;   // bs * Hkv * D * elem bytes
+    int row_stride_bytes;         // Hkv * D * elem bytes
+};
+
+// Query rows (new token, query head) one prefill workgroup covers.
+int prefill_rows_per_block();
+// dtype codes match paged_kv_dtype (f16 and bf16 only).
+hipError_t launch_prefill(const PrefillParams &p, int dtype, int head_dim, hipStream_t stream);
+
+}  // namespace pkv

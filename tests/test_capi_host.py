@@ -17,7 +17,8 @@ OK, NULLPTR, BAD_SHAPE, UNSUPPORTED, WORKSPACE, HIP = range(6)
 def declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(\w+)\s*\(", text, flags=re.M)))
+    return sorted(set(re.findall(r"^\s*PAGED_KV_API\s+(?:const\s+)?\w+\s*\*?\s*(\w+)\s*\(", text,
+                                 flags=re.M)))
 
 
 @pytest.fixture(scope="module")
@@ -36,6 +37,7 @@ def lib():
     lib.kv_cache_write.argtypes = [vp, vp, vp, vp, vp] + [ci] * 6 + [vp]
     lib.paged_kv_gather.argtypes = [vp] * 6 + [ci] * 8 + [vp]
     lib.paged_kv_copy_blocks.argtypes = [vp] * 3 + [ci] * 6 + [vp]
+    lib.paged_attn_prefill.argtypes = [vp] * 6 + [cf, vp] + [ci] * 11 + [vp]
     return lib
 
 
@@ -43,7 +45,18 @@ def test_header_declares_the_entry_points():
     assert declared_functions() == sorted([
         "paged_kv_status_string", "paged_attn_decode", "paged_attn_decode_partition_size",
         "paged_attn_decode_workspace_bytes", "kv_cache_write", "paged_kv_gather",
-        "paged_kv_copy_blocks"])
+        "paged_kv_copy_blocks", "paged_attn_prefill"])
+
+
+def test_library_exports_only_the_entry_points():
+    """Internal C++ functions stay hidden: the dynamic symbol table holds the
+    declared entry points and nothing else of the library's own."""
+    import subprocess
+    out = subprocess.run(["nm", "-D", "--defined-only", LIBRARY], capture_output=True,
+                         text=True, check=True).stdout
+    names = {ln.split()[-1] for ln in out.splitlines() if " T " in ln}
+    assert set(declared_functions()) <= names
+    assert not [n for n in names if "pkv" in n], sorted(names)
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -146,3 +159,32 @@ def test_gather_rejects(lib, args, status):
 ])
 def test_copy_blocks_rejects(lib, args, status):
     assert lib.paged_kv_copy_blocks(*args) == status
+
+
+def prefill(lib, **kw):
+    a = dict(query=P, key_cache=P, value_cache=P, block_tables=P, context_lens=P,
+             query_start=P, scale=0.125, out=P, num_seqs=4, total_q=40, num_q_heads=8,
+             num_kv_heads=2, head_dim=128, block_size=16, num_blocks=64,
+             max_blocks_per_seq=8, max_query_len=16, max_context_len=0, dtype=2, stream=None)
+    a.update(kw)
+    return lib.paged_attn_prefill(*a.values())
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dtype=0), UNSUPPORTED),                      # f32 has no prefill kernel
+    (dict(dtype=9), UNSUPPORTED),
+    (dict(head_dim=96), UNSUPPORTED),
+    (dict(num_q_heads=6, num_kv_heads=4), BAD_SHAPE),
+    (dict(num_q_heads=48, num_kv_heads=2), UNSUPPORTED),  # group 24
+    (dict(block_size=12), UNSUPPORTED),
+    (dict(max_context_len=129), BAD_SHAPE),            # more than the table holds
+    (dict(scale=float("inf")), BAD_SHAPE),
+    (dict(total_q=-1), BAD_SHAPE),
+    (dict(query=None), NULLPTR),
+    (dict(query_start=P + 2), BAD_SHAPE),              # misaligned
+    (dict(out=P + 8), BAD_SHAPE),
+    (dict(num_seqs=0, query=None), OK),                # nothing to do
+    (dict(max_query_len=0, query=None), OK),
+])
+def test_prefill_rejects(lib, kw, status):
+    assert prefill(lib, **kw) == status
