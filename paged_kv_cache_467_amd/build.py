@@ -15,6 +15,9 @@ FLAGS = [
     "-Wall", "-Wno-unused-command-line-argument", "-fvisibility=hidden",
     # no packed fp32 instructions in generated device code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # MFMA results in arch VGPRs: the prefill kernel's accumulators are also
+    # rescaled by VALU code, and in AGPRs every loop iteration copied them
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
 ]
 
 

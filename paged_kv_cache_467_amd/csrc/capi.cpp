@@ -283,7 +283,7 @@ int paged_attn_prefill(const void *query, const void *key_cache, const void *val
     if (max_ctx > table_tokens || !isfinite(scale)) return PAGED_KV_ERR_BAD_SHAPE;
     const int e = elem_bytes(dtype);
     if ((int64_t)block_size * num_kv_heads * head_dim * e > INT_MAX) return PAGED_KV_ERR_BAD_SHAPE;
-    const int rpb = pkv::prefill_rows_per_block();
+    const int rpb = pkv::prefill_rows_per_block(head_dim);
     const int64_t row_blocks = ((int64_t)max_query_len * group + rpb - 1) / rpb;
     if ((int64_t)num_seqs * num_kv_heads * row_blocks > INT_MAX) return PAGED_KV_ERR_BAD_SHAPE;
     if (num_seqs == 0 || total_q == 0 || max_query_len == 0) return PAGED_KV_OK;

@@ -12,22 +12,28 @@
 // With q_len new tokens and G query heads per kv head, each kv head serves
 // q_len * G query rows: both products are real contractions, so both run on
 // MFMA.  Work decomposition: one workgroup of 4 waves per (sequence, kv
-// head, block of 64 rows), row r = (new token r / G, query head r % G);
-// each wave owns 16 rows.  The workgroup walks the positions its rows can
-// see in 16-token tiles, staged in LDS (double-buffered, one barrier per
-// tile) and shared by its 4 waves:
-//  * K rows are stored as they are ([token][d], rows padded against bank
-//    conflicts); V rows are stored transposed ([d][token]).
+// head, block of rows), row r = (new token r / G, query head r % G); each
+// wave owns MB blocks of 16 rows (32 rows for head_dim <= 128, 16 for 256),
+// so that every K/V operand read from LDS serves MB blocks.  The workgroup
+// walks the positions its rows can see in 32-token tiles, staged in LDS as
+// they lie in the pool ([token][d], rows padded by 16 bytes against bank
+// conflicts), double-buffered with one barrier per tile and shared by its 4
+// waves:
 //  * Scores are computed transposed, S^T = K Q^T, with
-//    v_mfma_f32_16x16x32: A = K (lane l: token l % 16, 8 consecutive d of
-//    k-group l / 16), B = Q^T from registers (lane l: row l % 16, same d).
-//    The result leaves lane l holding tokens 4 * (l / 16) + 0..3 of row
-//    l % 16 -- exactly the B-operand layout of v_mfma_f32_16x16x16 with the
-//    tokens as k, so after the online softmax the weights P^T feed the value
-//    product O^T = V^T P^T straight from registers (A = V^T from LDS: lane l,
-//    d = l % 16 of a 16-wide d block, 4 consecutive tokens).
-//  * The accumulator O^T leaves lane l holding 4 consecutive d of row
-//    l % 16, so each lane owns one row's running max, sum and rescale.
+//    v_mfma_f32_16x16x32 per 16-token half: A = K (lane l: token l % 16, 8
+//    consecutive d of k-group l / 16), B = Q^T from registers (lane l: row
+//    l % 16, same d).  Lane l then holds tokens 4 (l / 16) + 0..3 of each
+//    half for row l % 16, and owns that row's running max, sum and rescale.
+//  * The value product O^T = V^T P^T also uses v_mfma_f32_16x16x32, with
+//    k-group g of the 32 tokens being {4g .. 4g+3} of the first half and
+//    {16+4g .. 16+4g+3} of the second -- what each lane already holds of P^T
+//    after the softmax, so the weights feed the MFMA from registers.  The
+//    matching V^T operand (lane l: d = l % 16 of a 16-wide block, the same 8
+//    tokens) comes from the row-major V tile through ds_read_b64_tr_b16:
+//    within a group of 16 lanes, lane i receives element i % 4 of the 8-byte
+//    vectors addressed by lanes 4e + i / 4 (e = 0..3), so lane 16g + 4r + c
+//    addresses V[4g + r][4c ..] and lane 16g + i receives V[4g + 0..3][i].
+//  * The accumulator O^T leaves lane l holding 4 consecutive d of row l % 16.
 // Causal masking: position t is masked for a row whose position is below t;
 // tiles past a wave's last row position are skipped by that wave.
 
@@ -42,12 +48,17 @@ namespace {
 
 constexpr int kPrefillThreads = 256;
 constexpr int kPrefillWaves = kPrefillThreads / 64;
-constexpr int kRowsPerWave = 16;
-constexpr int kRowsPerBlock = kPrefillWaves * kRowsPerWave;  // 64
-constexpr int kTile = 16;                                     // tokens per tile
+constexpr int kTile = 32;  // tokens per tile: two 16-token halves
+constexpr int kXcds = 8;   // accelerator complex dies of the MI355X, each with its own L2
+
+// 16-row blocks per wave: two share each K/V operand read; head_dim 256
+// keeps one (its accumulators and query operands double).
+__host__ __device__ constexpr int blocks_per_wave(int D) { return D >= 256 ? 1 : 2; }
+__host__ __device__ constexpr int rows_per_workgroup(int D) {
+    return kPrefillWaves * 16 * blocks_per_wave(D);
+}
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
-typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
 
 template <class T>
 __device__ inline f32x4 mfma_k32(const u32x4 &a, const u32x4 &b, const f32x4 &c);
@@ -60,20 +71,6 @@ template <>
 __device__ inline f32x4 mfma_k32<F16>(const u32x4 &a, const u32x4 &b, const f32x4 &c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a),
                                                   __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
-}
-
-// 16x16x16: a, b each hold 4 consecutive k values (two 32-bit words)
-template <class T>
-__device__ inline f32x4 mfma_k16(uint64_t a, uint64_t b, const f32x4 &c);
-template <>
-__device__ inline f32x4 mfma_k16<BF16>(uint64_t a, uint64_t b, const f32x4 &c) {
-    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4, a),
-                                                     __builtin_bit_cast(s16x4, b), c, 0, 0, 0);
-}
-template <>
-__device__ inline f32x4 mfma_k16<F16>(uint64_t a, uint64_t b, const f32x4 &c) {
-    return __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(f16x4, a),
-                                                 __builtin_bit_cast(f16x4, b), c, 0, 0, 0);
 }
 
 // Round one weight in [0, 1] to the element type (nearest even).
@@ -89,26 +86,48 @@ __device__ inline uint32_t narrow_weight<F16>(float x) {
     return __builtin_bit_cast(uint16_t, (_Float16)x);
 }
 
-template <class T, int D>
+// Transposing 8-byte LDS read (see the layout note at the top of the file).
+__device__ inline uint64_t lds_read_tr16(const uint16_t *p) {
+    const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (s16x4 __attribute__((address_space(3))) *)(p));
+    return __builtin_bit_cast(uint64_t, v);
+}
+
+template <class T, int D, bool BT>
 __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(PrefillParams p) {
     static_assert(T::kBytes == 2, "MFMA path is for 16-bit element types");
+    constexpr int MB = blocks_per_wave(D);
+    constexpr int RPB = rows_per_workgroup(D);
     constexpr int KS = D / 32;            // k-steps of the score MFMA
     constexpr int DB = D / 16;            // 16-wide d blocks of the value MFMA
-    constexpr int KSTR = D + 8;           // K tile row stride in elements (+16 bytes)
-    constexpr int VSTR = kTile + 4;       // V^T row stride in elements (+8 bytes)
+    constexpr int RSTR = D + 8;           // tile row stride in elements (+16 bytes)
     constexpr int CHUNKS = kTile * D / 8;  // 16-byte chunks per tile and tensor
     constexpr int CPT = (CHUNKS + kPrefillThreads - 1) / kPrefillThreads;  // per thread
     constexpr int CPRW = D / 8;           // chunks per token row
 
-    __shared__ __attribute__((aligned(16))) uint16_t ks_lds[2][kTile * KSTR];
-    __shared__ __attribute__((aligned(16))) uint16_t vt_lds[2][D * VSTR];
+    __shared__ __attribute__((aligned(16))) uint16_t k_lds[2][kTile * RSTR];
+    __shared__ __attribute__((aligned(16))) uint16_t v_lds[2][kTile * RSTR];
 
     // ---- work item
+    // Workgroups go to the 8 XCDs round-robin.  All row blocks of one
+    // (sequence, kv head) unit read the same K/V, so they get ids 8 apart:
+    // the same XCD, dispatched together, sharing that XCD's L2.
     const int nrb = p.row_blocks;
-    const int rb = blockIdx.x % nrb;
-    const int rest = blockIdx.x / nrb;
-    const int kvh = rest % p.num_kv_heads;
-    const int s = rest / p.num_kv_heads;
+    const int n_units = p.num_seqs * p.num_kv_heads;
+    const int full = n_units / kXcds * kXcds;  // units placed XCD by XCD
+    const int id = blockIdx.x;
+    int unit, rb;
+    if (id < full * nrb) {
+        const int k = id / kXcds;
+        rb = k % nrb;
+        unit = (k / nrb) * kXcds + id % kXcds;
+    } else {
+        const int r = id - full * nrb;
+        unit = full + r / nrb;
+        rb = r % nrb;
+    }
+    const int kvh = unit % p.num_kv_heads;
+    const int s = unit / p.num_kv_heads;
     const int G = p.group;
     const int qs0 = p.query_start[s];
     const int qs1 = p.query_start[s + 1];
@@ -116,76 +135,114 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(PrefillParams 
     if (qs0 < 0 || qs1 > p.total_q || qs1 < qs0) return;  // rows not identifiable: nothing written
     const int q_len = qs1 - qs0;
     const int nrows = (q_len < p.max_query_len ? q_len : p.max_query_len) * G;
-    const int row0 = rb * kRowsPerBlock;
+    const int row0 = rb * RPB;
     if (row0 >= nrows) return;
     const bool bad_len = L < q_len || L > p.max_context_len;
 
     const int wave = threadIdx.x / kWave;
     const int lane = threadIdx.x % kWave;
-    const int lrow = lane & 15;   // this lane's row within the wave's 16
+    const int lrow = lane & 15;   // this lane's row within each 16-row block
     const int kg = lane >> 4;     // k-group / token group
-    const int row = row0 + wave * kRowsPerWave + lrow;
-    const bool row_ok = row < nrows;
-    const int tok = row / G;            // new token index within the sequence
-    const int head = kvh * G + row % G;
-    const int64_t qrow = (int64_t)qs0 + tok;
-    const int pos = L - q_len + tok;     // this row's position
+    const int w_first = row0 + wave * 16 * MB;
+    bool row_ok[MB];
+    int pos[MB];        // the row's position; -1 for a row past the end (sees nothing)
+    int64_t obase[MB];  // element offset of the row's output / query
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) {
+        const int row = w_first + 16 * mb + lrow;
+        row_ok[mb] = row < nrows;
+        const int tok = row / G;
+        pos[mb] = row_ok[mb] ? L - q_len + tok : -1;
+        obase[mb] = (((int64_t)qs0 + tok) * p.num_q_heads + kvh * G + row % G) * D;
+    }
 
     if (bad_len) {
-        if (row_ok) {
-            const int64_t o = (qrow * p.num_q_heads + head) * D;
-            for (int d = kg * 4; d < D; d += 16)
-                *reinterpret_cast<uint64_t *>(static_cast<char *>(p.out) + (o + d) * 2) =
-                    ((uint64_t)T::kNanPair << 32) | T::kNanPair;
-        }
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+            if (row_ok[mb])
+                for (int d = kg * 4; d < D; d += 16)
+                    *reinterpret_cast<uint64_t *>(static_cast<char *>(p.out) +
+                                                  (obase[mb] + d) * 2) =
+                        ((uint64_t)T::kNanPair << 32) | T::kNanPair;
         return;
     }
 
     // positions the workgroup's rows can see: 0 .. pmax (the last valid row's)
-    const int last_row = (row0 + kRowsPerBlock < nrows ? row0 + kRowsPerBlock : nrows) - 1;
+    const int last_row = (row0 + RPB < nrows ? row0 + RPB : nrows) - 1;
     const int pmax = L - q_len + last_row / G;
     const int ntiles = pmax / kTile + 1;
-    // this wave's rows: positions wave_pmin .. wave_pmax (none if the wave has no row)
-    const int w_first = row0 + wave * kRowsPerWave;
-    const int w_last = (w_first + kRowsPerWave < nrows ? w_first + kRowsPerWave : nrows) - 1;
+    const int w_last = (w_first + 16 * MB < nrows ? w_first + 16 * MB : nrows) - 1;
     const bool wave_active = w_first < nrows;
     const int wave_pmax = L - q_len + w_last / G;
-    const int wave_pmin = L - q_len + w_first / G;
+    // tiles ending at or below this position need no causal mask
+    const int wave_pmin = w_first + 16 * MB <= nrows ? L - q_len + w_first / G : -1;
 
     // B operand of the score MFMA: Q^T, lane = row, 16-byte chunk kg + 4 * ks
-    u32x4 qb[KS];
-    {
-        const char *qp = static_cast<const char *>(p.query) + ((qrow * p.num_q_heads + head) * D) * 2;
+    u32x4 qb[MB][KS];
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) {
+        const char *qp = static_cast<const char *>(p.query) + obase[mb] * 2;
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks)
-            qb[ks] = row_ok ? load16(qp + 16 * (kg + 4 * ks)) : u32x4{0, 0, 0, 0};
+            qb[mb][ks] = row_ok[mb] ? load16(qp + 16 * (kg + 4 * ks)) : u32x4{0, 0, 0, 0};
     }
 
-    // cooperative tile loader: thread -> (token of the tile, 16-byte chunk)
+    // cooperative tile loader: thread -> (token of the tile, 16-byte chunk).
+    // With block_size >= 16 each 16-token half of a tile lies in one block:
+    // its id is a uniform (scalar) load and each thread adds a fixed offset;
+    // the half a chunk falls in is the same for a whole wave.
     const int32_t *bt_row = p.block_tables + (int64_t)s * p.max_blocks_per_seq;
     const int64_t head_off = (int64_t)kvh * D * 2;
     int bad = 0;
     u32x4 kreg[CPT], vreg[CPT];
+    uint32_t chunk_off[CPT];  // offset of the thread's chunk from its half's first row
+#pragma unroll
+    for (int c = 0; c < CPT; ++c) {
+        const int idx = threadIdx.x + c * kPrefillThreads;
+        chunk_off[c] = (uint32_t)(((idx / CPRW) % 16) * p.row_stride_bytes + head_off +
+                                  (idx % CPRW) * 16);
+    }
     auto load_tile = [&](int tile) {
+        const int t0 = tile * kTile;
+        int64_t half_base[2] = {0, 0};
+        if constexpr (BT) {
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const int th = t0 + 16 * h;
+                if (th <= pmax) {
+                    int blk = __builtin_amdgcn_readfirstlane(bt_row[th >> p.block_shift]);
+                    if (blk < 0 || blk >= p.num_blocks) {
+                        bad = 1;
+                        blk = 0;
+                    }
+                    half_base[h] = (int64_t)blk * p.block_stride_bytes +
+                                   (int64_t)(th & (p.block_size - 1)) * p.row_stride_bytes;
+                }
+            }
+        }
 #pragma unroll
         for (int c = 0; c < CPT; ++c) {
             const int idx = threadIdx.x + c * kPrefillThreads;
             const int tt = idx / CPRW;
-            const int ch = idx % CPRW;
-            const int t = tile * kTile + tt;
+            const int t = t0 + tt;
             kreg[c] = u32x4{0, 0, 0, 0};
             vreg[c] = u32x4{0, 0, 0, 0};
             if (idx < CHUNKS && t <= pmax) {
-                int blk = bt_row[t >> p.block_shift];
-                if (blk < 0 || blk >= p.num_blocks) {
-                    bad = 1;
+                int64_t o;
+                if constexpr (BT) {
+                    o = half_base[tt / 16] + chunk_off[c];
                 } else {
-                    const int64_t o = (int64_t)blk * p.block_stride_bytes +
-                                      (int64_t)(t & (p.block_size - 1)) * p.row_stride_bytes +
-                                      head_off + ch * 16;
-                    kreg[c] = load16_stream(p.key_cache + o);
-                    vreg[c] = load16_stream(p.value_cache + o);
+                    int blk = bt_row[t >> p.block_shift];
+                    if (blk < 0 || blk >= p.num_blocks) {
+                        bad = 1;
+                        blk = 0;
+                    }
+                    o = (int64_t)blk * p.block_stride_bytes +
+                        (int64_t)(t & (p.block_size - 1)) * p.row_stride_bytes + head_off +
+                        (idx % CPRW) * 16;
                 }
+                kreg[c] = load16_stream(p.key_cache + o);
+                vreg[c] = load16_stream(p.value_cache + o);
             }
         }
     };
@@ -194,118 +251,157 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(PrefillParams 
         for (int c = 0; c < CPT; ++c) {
             const int idx = threadIdx.x + c * kPrefillThreads;
             if (idx >= CHUNKS) continue;
-            const int tt = idx / CPRW;
-            const int ch = idx % CPRW;
-            *reinterpret_cast<u32x4 *>(&ks_lds[buf][tt * KSTR + ch * 8]) = kreg[c];
-            // transpose V: element e of the chunk is d = 8 ch + e
-#pragma unroll
-            for (int w = 0; w < 4; ++w) {
-                const uint32_t word = vreg[c][w];
-                vt_lds[buf][(ch * 8 + 2 * w) * VSTR + tt] = (uint16_t)(word & 0xFFFFu);
-                vt_lds[buf][(ch * 8 + 2 * w + 1) * VSTR + tt] = (uint16_t)(word >> 16);
-            }
+            const int e = (idx / CPRW) * RSTR + (idx % CPRW) * 8;
+            *reinterpret_cast<u32x4 *>(&k_lds[buf][e]) = kreg[c];
+            *reinterpret_cast<u32x4 *>(&v_lds[buf][e]) = vreg[c];
         }
     };
 
-    float m = -INFINITY, lsum = 0.0f;  // this lane's row (partial sum over its 4 tokens per tile)
-    f32x4 acc[DB];
+    float m[MB], lsum[MB];  // this lane's rows; lsum is the lane's share of the row sum
+    f32x4 acc[MB][DB];
 #pragma unroll
-    for (int b = 0; b < DB; ++b) acc[b] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    for (int mb = 0; mb < MB; ++mb) {
+        m[mb] = -INFINITY;
+        lsum[mb] = 0.0f;
+#pragma unroll
+        for (int b = 0; b < DB; ++b) acc[mb][b] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    }
+    // this lane's V^T addresses inside a tile (half 0); half 1 is 16 rows down
+    const int vt_elem = (4 * kg + lrow / 4) * RSTR + 4 * (lrow % 4);
 
     load_tile(0);
     store_tile(0);
     __syncthreads();
     for (int tile = 0; tile < ntiles; ++tile) {
         const int buf = tile & 1;
-        if (tile + 1 < ntiles) load_tile(tile + 1);
         const int t0 = tile * kTile;
+        bool prefetched = false;
         if (wave_active && t0 <= wave_pmax) {
-            // S^T tile: lane holds tokens t0 + 4 kg + r of its row
-            f32x4 st = {0.0f, 0.0f, 0.0f, 0.0f};
+            const uint16_t *kt = k_lds[buf];
+            const uint16_t *vt = v_lds[buf];
+            // S^T for both halves and every row block
+            f32x4 st[MB][2];
 #pragma unroll
-            for (int ks = 0; ks < KS; ++ks) {
-                const u32x4 a =
-                    *reinterpret_cast<const u32x4 *>(&ks_lds[buf][lrow * KSTR + (kg + 4 * ks) * 8]);
-                st = mfma_k32<T>(a, qb[ks], st);
-            }
-            float sc[4];
-            const bool need_mask = t0 + kTile - 1 > wave_pmin || !row_ok;
+            for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int t = t0 + 4 * kg + r;
-                const bool vis = !need_mask || (row_ok && t <= pos);
-                sc[r] = vis ? st[r] * p.scale_log2 : -INFINITY;
-            }
-            float mt = vmax(vmax(sc[0], sc[1]), vmax(sc[2], sc[3]));
-            mt = vmax(mt, __shfl_xor(mt, 16));
-            mt = vmax(mt, __shfl_xor(mt, 32));  // row max over the 16 tokens
-            if (__builtin_amdgcn_ballot_w64(mt > m) != 0) {
-                const float mn = vmax(m, mt);
-                const float alpha = mn == -INFINITY ? 1.0f : fast_exp2(m - mn);
-                m = mn;
-                lsum *= alpha;
+                for (int u = 0; u < 2; ++u) st[mb][u] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-                for (int b = 0; b < DB; ++b) acc[b] *= alpha;
-            }
-            const float mref = m == -INFINITY ? 0.0f : m;  // rows that saw nothing: weights 0
-            float pr[4];
+            for (int u = 0; u < 2; ++u) {
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                pr[r] = fast_exp2(sc[r] - mref);
-                lsum += pr[r];
+                for (int ks = 0; ks < KS; ++ks) {
+                    const u32x4 a = *reinterpret_cast<const u32x4 *>(
+                        &kt[(16 * u + lrow) * RSTR + (kg + 4 * ks) * 8]);
+#pragma unroll
+                    for (int mb = 0; mb < MB; ++mb) st[mb][u] = mfma_k32<T>(a, qb[mb][ks], st[mb][u]);
+                }
             }
-            const uint64_t pb =
-                (uint64_t)(narrow_weight<T>(pr[0]) | (narrow_weight<T>(pr[1]) << 16)) |
-                ((uint64_t)(narrow_weight<T>(pr[2]) | (narrow_weight<T>(pr[3]) << 16)) << 32);
+            // the next tile's loads, issued once this tile's K operands are in registers
+            if (tile + 1 < ntiles) load_tile(tile + 1);
+            prefetched = true;
+            const bool need_mask = t0 + kTile - 1 > wave_pmin;  // wave-uniform
+            u32x4 pb[MB];
+#pragma unroll
+            for (int mb = 0; mb < MB; ++mb) {
+                float sc[2][4];
+#pragma unroll
+                for (int u = 0; u < 2; ++u)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) sc[u][r] = st[mb][u][r] * p.scale_log2;
+                if (need_mask) {
+                    const int first = t0 + 4 * kg;  // this lane's first token of half 0
+#pragma unroll
+                    for (int u = 0; u < 2; ++u)
+#pragma unroll
+                        for (int r = 0; r < 4; ++r)
+                            if (first + 16 * u + r > pos[mb]) sc[u][r] = -INFINITY;
+                }
+                float mt = vmax(vmax(vmax(sc[0][0], sc[0][1]), vmax(sc[0][2], sc[0][3])),
+                                vmax(vmax(sc[1][0], sc[1][1]), vmax(sc[1][2], sc[1][3])));
+                mt = vmax(mt, __shfl_xor(mt, 16));
+                mt = vmax(mt, __shfl_xor(mt, 32));  // row max over the 32 tokens
+                if (__builtin_amdgcn_ballot_w64(mt > m[mb]) != 0) {
+                    const float mn = vmax(m[mb], mt);
+                    const float alpha = mn == -INFINITY ? 1.0f : fast_exp2(m[mb] - mn);
+                    m[mb] = mn;
+                    lsum[mb] *= alpha;
+#pragma unroll
+                    for (int b = 0; b < DB; ++b) acc[mb][b] *= alpha;
+                }
+                const float mref = m[mb] == -INFINITY ? 0.0f : m[mb];  // rows that saw nothing
+                uint32_t w[4];
+#pragma unroll
+                for (int u = 0; u < 2; ++u) {
+                    float pr[4];
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        pr[r] = fast_exp2(sc[u][r] - mref);
+                        lsum[mb] += pr[r];
+                    }
+                    w[2 * u] = narrow_weight<T>(pr[0]) | (narrow_weight<T>(pr[1]) << 16);
+                    w[2 * u + 1] = narrow_weight<T>(pr[2]) | (narrow_weight<T>(pr[3]) << 16);
+                }
+                pb[mb] = u32x4{w[0], w[1], w[2], w[3]};
+            }
 #pragma unroll
             for (int b = 0; b < DB; ++b) {
-                const uint64_t a = *reinterpret_cast<const uint64_t *>(
-                    &vt_lds[buf][(b * 16 + lrow) * VSTR + 4 * kg]);
-                acc[b] = mfma_k16<T>(a, pb, acc[b]);
+                const uint64_t lo = lds_read_tr16(vt + vt_elem + 16 * b);
+                const uint64_t hi = lds_read_tr16(vt + vt_elem + 16 * RSTR + 16 * b);
+                const u32x4 a = u32x4{(uint32_t)lo, (uint32_t)(lo >> 32), (uint32_t)hi,
+                                      (uint32_t)(hi >> 32)};
+#pragma unroll
+                for (int mb = 0; mb < MB; ++mb) acc[mb][b] = mfma_k32<T>(a, pb[mb], acc[mb][b]);
             }
         }
+        if (!prefetched && tile + 1 < ntiles) load_tile(tile + 1);
         if (tile + 1 < ntiles) store_tile(buf ^ 1);
         __syncthreads();
     }
     bad = __syncthreads_or(bad);
 
-    // row sum over the 4 token groups; the lane's accumulator holds d = 16 b + 4 kg + r
-    lsum += __shfl_xor(lsum, 16);
-    lsum += __shfl_xor(lsum, 32);
-    if (!row_ok) return;
-    const float inv = lsum > 0.0f ? 1.0f / lsum : 0.0f;
-    char *op = static_cast<char *>(p.out) + ((qrow * p.num_q_heads + head) * D) * 2;
+    // row sums over the 4 token groups; the accumulator holds d = 16 b + 4 kg + r
 #pragma unroll
-    for (int b = 0; b < DB; ++b) {
-        uint64_t v;
-        if (bad) {
-            v = ((uint64_t)T::kNanPair << 32) | T::kNanPair;
-        } else {
-            float o4[8] = {acc[b][0] * inv, acc[b][1] * inv, acc[b][2] * inv, acc[b][3] * inv,
-                           0.0f, 0.0f, 0.0f, 0.0f};
-            const u32x4 c = T::narrow_chunk(o4);
-            v = (uint64_t)c[0] | ((uint64_t)c[1] << 32);
-        }
-        *reinterpret_cast<uint64_t *>(op + (b * 16 + 4 * kg) * 2) = v;
+    for (int mb = 0; mb < MB; ++mb) {
+        lsum[mb] += __shfl_xor(lsum[mb], 16);
+        lsum[mb] += __shfl_xor(lsum[mb], 32);
     }
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) {
+        if (!row_ok[mb]) continue;
+        const float inv = lsum[mb] > 0.0f ? 1.0f / lsum[mb] : 0.0f;
+        char *op = static_cast<char *>(p.out) + obase[mb] * 2;
+#pragma unroll
+        for (int b = 0; b < DB; ++b) {
+            uint64_t v;
+            if (bad) {
+                v = ((uint64_t)T::kNanPair << 32) | T::kNanPair;
+            } else {
+                float o4[8] = {acc[mb][b][0] * inv, acc[mb][b][1] * inv, acc[mb][b][2] * inv,
+                               acc[mb][b][3] * inv, 0.0f, 0.0f, 0.0f, 0.0f};
+                const u32x4 c = T::narrow_chunk(o4);
+                v = (uint64_t)c[0] | ((uint64_t)c[1] << 32);
+            }
+            *reinterpret_cast<uint64_t *>(op + (b * 16 + 4 * kg) * 2) = v;
+        }
+    }
+}
+
+template <class T, int D>
+void launch_d(const PrefillParams &p, hipStream_t stream) {
+    const unsigned grid = (unsigned)((int64_t)p.num_seqs * p.num_kv_heads * p.row_blocks);
+    if (p.block_size >= 16)
+        hipLaunchKernelGGL((prefill_kernel<T, D, true>), dim3(grid), dim3(kPrefillThreads), 0,
+                           stream, p);
+    else
+        hipLaunchKernelGGL((prefill_kernel<T, D, false>), dim3(grid), dim3(kPrefillThreads), 0,
+                           stream, p);
 }
 
 template <class T>
 hipError_t launch_t(const PrefillParams &p, int head_dim, hipStream_t stream) {
-    const unsigned grid = (unsigned)((int64_t)p.num_seqs * p.num_kv_heads * p.row_blocks);
     switch (head_dim) {
-        case 64:
-            hipLaunchKernelGGL((prefill_kernel<T, 64>), dim3(grid), dim3(kPrefillThreads), 0,
-                               stream, p);
-            break;
-        case 128:
-            hipLaunchKernelGGL((prefill_kernel<T, 128>), dim3(grid), dim3(kPrefillThreads), 0,
-                               stream, p);
-            break;
-        case 256:
-            hipLaunchKernelGGL((prefill_kernel<T, 256>), dim3(grid), dim3(kPrefillThreads), 0,
-                               stream, p);
-            break;
+        case 64: launch_d<T, 64>(p, stream); break;
+        case 128: launch_d<T, 128>(p, stream); break;
+        case 256: launch_d<T, 256>(p, stream); break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
@@ -313,7 +409,7 @@ hipError_t launch_t(const PrefillParams &p, int head_dim, hipStream_t stream) {
 
 }  // namespace
 
-int prefill_rows_per_block() { return kRowsPerBlock; }
+int prefill_rows_per_block(int head_dim) { return rows_per_workgroup(head_dim); }
 
 hipError_t launch_prefill(const PrefillParams &p, int dtype, int head_dim, hipStream_t stream) {
     switch (dtype) {

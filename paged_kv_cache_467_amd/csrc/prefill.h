@@ -33,7 +33,7 @@ struct PrefillParams {
 };
 
 // Query rows (new token, query head) one prefill workgroup covers.
-int prefill_rows_per_block();
+int prefill_rows_per_block(int head_dim);
 // dtype codes match paged_kv_dtype (f16 and bf16 only).
 hipError_t launch_prefill(const PrefillParams &p, int dtype, int head_dim, hipStream_t stream);
 
