@@ -302,7 +302,10 @@ int paged_attn_prefill(const void *query, const void *key_cache, const void *val
     p.context_lens = context_lens;
     p.query_start = query_start;
     p.out = out;
-    p.scale_log2 = (float)((double)scale * 1.4426950408889634);  // scale * log2(e)
+    // scale * dot(q, k) == |scale| * dot(-q, k) exactly, so the kernel keeps
+    // a non-negative score scale and flips the query's sign bits instead
+    p.score_scale = (float)(fabs((double)scale) * 1.4426950408889634);  // |scale| * log2(e)
+    p.negate_query = scale < 0.0f;
     p.num_seqs = num_seqs;
     p.total_q = total_q;
     p.num_q_heads = num_q_heads;

@@ -73,18 +73,46 @@ __device__ inline f32x4 mfma_k32<F16>(const u32x4 &a, const u32x4 &b, const f32x
                                                   __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
 }
 
-// Round one weight in [0, 1] to the element type (nearest even).
+// Round two weights in [0, 1] to the element type (nearest even) and pack
+// them into one word, the first in the low half.
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 template <class T>
-__device__ inline uint32_t narrow_weight(float x);
+__device__ inline uint32_t narrow_pair(float a, float b);
 template <>
-__device__ inline uint32_t narrow_weight<BF16>(float x) {
-    const uint32_t u = __builtin_bit_cast(uint32_t, x);
-    return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+__device__ inline uint32_t narrow_pair<BF16>(float a, float b) {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a, b}, bf16x2));
 }
 template <>
-__device__ inline uint32_t narrow_weight<F16>(float x) {
-    return __builtin_bit_cast(uint16_t, (_Float16)x);
+__device__ inline uint32_t narrow_pair<F16>(float a, float b) {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a, b}, f16x2));
 }
+
+// Maximum (sum) over lanes l, l ^ 16, l ^ 32 and l ^ 48 -- the four token
+// groups holding one row -- with the gfx950 lane-swap instructions rather
+// than LDS permutes: swapping a value with itself across 32-lane (16-lane)
+// halves leaves each lane holding its own value in one result and its
+// partner's in the other.  (The results are copied out as scalars: clang
+// reads element 0 for a bit cast of an indexed vector element.)
+template <bool MAX>
+__device__ inline float row_reduce4(float x) {
+    uint32_t u = __builtin_bit_cast(uint32_t, x);
+    const auto a = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    const uint32_t a0 = a[0], a1 = a[1];
+    const float x0 = __builtin_bit_cast(float, a0), x1 = __builtin_bit_cast(float, a1);
+    x = MAX ? vmax(x0, x1) : x0 + x1;
+    u = __builtin_bit_cast(uint32_t, x);
+    const auto b = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+    const uint32_t b0 = b[0], b1 = b[1];
+    const float y0 = __builtin_bit_cast(float, b0), y1 = __builtin_bit_cast(float, b1);
+    return MAX ? vmax(y0, y1) : y0 + y1;
+}
+
+// The running max of a row is only moved (and the row's sum and
+// accumulator rescaled) once a tile's max exceeds it by more than this many
+// binary orders of magnitude: until then the weights stay below 2^8, well
+// inside fp32 and the 16-bit weight formats, and the result is the same
+// softmax up to rounding.
+constexpr float kRescaleSlack = 8.0f;
 
 // Transposing 8-byte LDS read (see the layout note at the top of the file).
 __device__ inline uint64_t lds_read_tr16(const uint16_t *p) {
@@ -104,6 +132,7 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(PrefillParams 
     constexpr int CHUNKS = kTile * D / 8;  // 16-byte chunks per tile and tensor
     constexpr int CPT = (CHUNKS + kPrefillThreads - 1) / kPrefillThreads;  // per thread
     constexpr int CPRW = D / 8;           // chunks per token row
+    static_assert(CHUNKS % kPrefillThreads == 0, "every thread loads whole chunks");
 
     __shared__ __attribute__((aligned(16))) uint16_t k_lds[2][kTile * RSTR];
     __shared__ __attribute__((aligned(16))) uint16_t v_lds[2][kTile * RSTR];
@@ -186,6 +215,12 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(PrefillParams 
         for (int ks = 0; ks < KS; ++ks)
             qb[mb][ks] = row_ok[mb] ? load16(qp + 16 * (kg + 4 * ks)) : u32x4{0, 0, 0, 0};
     }
+    if (p.negate_query) {
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) qb[mb][ks] ^= 0x80008000u;  // both sign bits
+    }
 
     // cooperative tile loader: thread -> (token of the tile, 16-byte chunk).
     // With block_size >= 16 each 16-token half of a tile lies in one block:
@@ -202,6 +237,15 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(PrefillParams 
         chunk_off[c] = (uint32_t)(((idx / CPRW) % 16) * p.row_stride_bytes + head_off +
                                   (idx % CPRW) * 16);
     }
+    // the 16-token half of a tile that chunk c of this thread falls in: the
+    // same for the whole wave
+    const int wave_s = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    auto half_of = [&](int c) {
+        if constexpr (16 * CPRW >= kPrefillThreads)
+            return c * kPrefillThreads / (16 * CPRW);
+        else
+            return (wave_s * kWave + c * kPrefillThreads) / (16 * CPRW);
+    };
     auto load_tile = [&](int tile) {
         const int t0 = tile * kTile;
         int64_t half_base[2] = {0, 0};
@@ -220,40 +264,45 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(PrefillParams 
                 }
             }
         }
+        // Every chunk is loaded, so that the loads issue back to back; a
+        // token past pmax reads an in-bounds cell (block 0 for a half past
+        // pmax, the same block otherwise, or token pmax with per-token ids)
+        // and is zeroed when the tile is stored.
 #pragma unroll
         for (int c = 0; c < CPT; ++c) {
-            const int idx = threadIdx.x + c * kPrefillThreads;
-            const int tt = idx / CPRW;
-            const int t = t0 + tt;
-            kreg[c] = u32x4{0, 0, 0, 0};
-            vreg[c] = u32x4{0, 0, 0, 0};
-            if (idx < CHUNKS && t <= pmax) {
-                int64_t o;
-                if constexpr (BT) {
-                    o = half_base[tt / 16] + chunk_off[c];
-                } else {
-                    int blk = bt_row[t >> p.block_shift];
-                    if (blk < 0 || blk >= p.num_blocks) {
-                        bad = 1;
-                        blk = 0;
-                    }
-                    o = (int64_t)blk * p.block_stride_bytes +
-                        (int64_t)(t & (p.block_size - 1)) * p.row_stride_bytes + head_off +
-                        (idx % CPRW) * 16;
+            int64_t o;
+            if constexpr (BT) {
+                o = half_base[half_of(c)] + chunk_off[c];
+            } else {
+                const int idx = threadIdx.x + c * kPrefillThreads;
+                const int t = min(t0 + idx / CPRW, pmax);
+                int blk = bt_row[t >> p.block_shift];
+                if (blk < 0 || blk >= p.num_blocks) {
+                    bad = 1;
+                    blk = 0;
                 }
-                kreg[c] = load16_stream(p.key_cache + o);
-                vreg[c] = load16_stream(p.value_cache + o);
+                o = (int64_t)blk * p.block_stride_bytes +
+                    (int64_t)(t & (p.block_size - 1)) * p.row_stride_bytes + head_off +
+                    (idx % CPRW) * 16;
             }
+            kreg[c] = load16_stream(p.key_cache + o);
+            vreg[c] = load16_stream(p.value_cache + o);
         }
     };
-    auto store_tile = [&](int buf) {
+    auto store_tile = [&](int buf, int tile) {
+        const int t0 = tile * kTile;
+        const bool partial = t0 + kTile - 1 > pmax;  // workgroup-uniform
 #pragma unroll
         for (int c = 0; c < CPT; ++c) {
             const int idx = threadIdx.x + c * kPrefillThreads;
-            if (idx >= CHUNKS) continue;
             const int e = (idx / CPRW) * RSTR + (idx % CPRW) * 8;
-            *reinterpret_cast<u32x4 *>(&k_lds[buf][e]) = kreg[c];
-            *reinterpret_cast<u32x4 *>(&v_lds[buf][e]) = vreg[c];
+            u32x4 kv = kreg[c], vv = vreg[c];
+            if (partial && t0 + idx / CPRW > pmax) {
+                kv = u32x4{0, 0, 0, 0};
+                vv = u32x4{0, 0, 0, 0};
+            }
+            *reinterpret_cast<u32x4 *>(&k_lds[buf][e]) = kv;
+            *reinterpret_cast<u32x4 *>(&v_lds[buf][e]) = vv;
         }
     };
 
@@ -270,7 +319,7 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(PrefillParams 
     const int vt_elem = (4 * kg + lrow / 4) * RSTR + 4 * (lrow % 4);
 
     load_tile(0);
-    store_tile(0);
+    store_tile(0, 0);
     __syncthreads();
     for (int tile = 0; tile < ntiles; ++tile) {
         const int buf = tile & 1;
@@ -299,16 +348,18 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(PrefillParams 
             if (tile + 1 < ntiles) load_tile(tile + 1);
             prefetched = true;
             const bool need_mask = t0 + kTile - 1 > wave_pmin;  // wave-uniform
+            const int first = t0 + 4 * kg;  // this lane's first token of half 0
+            const float c = p.score_scale;
             u32x4 pb[MB];
 #pragma unroll
             for (int mb = 0; mb < MB; ++mb) {
+                // raw scores; the scale (>= 0) enters with the exponent
                 float sc[2][4];
 #pragma unroll
                 for (int u = 0; u < 2; ++u)
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) sc[u][r] = st[mb][u][r] * p.scale_log2;
+                    for (int r = 0; r < 4; ++r) sc[u][r] = st[mb][u][r];
                 if (need_mask) {
-                    const int first = t0 + 4 * kg;  // this lane's first token of half 0
 #pragma unroll
                     for (int u = 0; u < 2; ++u)
 #pragma unroll
@@ -317,9 +368,9 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(PrefillParams 
                 }
                 float mt = vmax(vmax(vmax(sc[0][0], sc[0][1]), vmax(sc[0][2], sc[0][3])),
                                 vmax(vmax(sc[1][0], sc[1][1]), vmax(sc[1][2], sc[1][3])));
-                mt = vmax(mt, __shfl_xor(mt, 16));
-                mt = vmax(mt, __shfl_xor(mt, 32));  // row max over the 32 tokens
-                if (__builtin_amdgcn_ballot_w64(mt > m[mb]) != 0) {
+                mt = row_reduce4<true>(mt);                              // row max over the 32 tokens
+                mt = mt == -INFINITY ? -INFINITY : mt * c;      // scaled (log2 domain)
+                if (__builtin_amdgcn_ballot_w64(mt > m[mb] + kRescaleSlack) != 0) {
                     const float mn = vmax(m[mb], mt);
                     const float alpha = mn == -INFINITY ? 1.0f : fast_exp2(m[mb] - mn);
                     m[mb] = mn;
@@ -327,18 +378,30 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(PrefillParams 
 #pragma unroll
                     for (int b = 0; b < DB; ++b) acc[mb][b] *= alpha;
                 }
-                const float mref = m[mb] == -INFINITY ? 0.0f : m[mb];  // rows that saw nothing
+                const float nref = m[mb] == -INFINITY ? 0.0f : -m[mb];  // rows that saw nothing
+                float arg[2][4];
+#pragma unroll
+                for (int u = 0; u < 2; ++u)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) arg[u][r] = __builtin_fmaf(sc[u][r], c, nref);
+                if (need_mask) {  // a zero scale turns a masked score into NaN above
+#pragma unroll
+                    for (int u = 0; u < 2; ++u)
+#pragma unroll
+                        for (int r = 0; r < 4; ++r)
+                            if (first + 16 * u + r > pos[mb]) arg[u][r] = -INFINITY;
+                }
                 uint32_t w[4];
 #pragma unroll
                 for (int u = 0; u < 2; ++u) {
                     float pr[4];
 #pragma unroll
                     for (int r = 0; r < 4; ++r) {
-                        pr[r] = fast_exp2(sc[u][r] - mref);
+                        pr[r] = fast_exp2(arg[u][r]);
                         lsum[mb] += pr[r];
                     }
-                    w[2 * u] = narrow_weight<T>(pr[0]) | (narrow_weight<T>(pr[1]) << 16);
-                    w[2 * u + 1] = narrow_weight<T>(pr[2]) | (narrow_weight<T>(pr[3]) << 16);
+                    w[2 * u] = narrow_pair<T>(pr[0], pr[1]);
+                    w[2 * u + 1] = narrow_pair<T>(pr[2], pr[3]);
                 }
                 pb[mb] = u32x4{w[0], w[1], w[2], w[3]};
             }
@@ -353,7 +416,7 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(PrefillParams 
             }
         }
         if (!prefetched && tile + 1 < ntiles) load_tile(tile + 1);
-        if (tile + 1 < ntiles) store_tile(buf ^ 1);
+        if (tile + 1 < ntiles) store_tile(buf ^ 1, tile + 1);
         __syncthreads();
     }
     bad = __syncthreads_or(bad);
@@ -361,8 +424,7 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(PrefillParams 
     // row sums over the 4 token groups; the accumulator holds d = 16 b + 4 kg + r
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) {
-        lsum[mb] += __shfl_xor(lsum[mb], 16);
-        lsum[mb] += __shfl_xor(lsum[mb], 32);
+        lsum[mb] = row_reduce4<false>(lsum[mb]);
     }
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) {

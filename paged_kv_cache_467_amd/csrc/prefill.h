@@ -15,7 +15,8 @@ struct PrefillParams {
     const int32_t *context_lens;  // [S]
     const int32_t *query_start;   // [S + 1]
     void *out;                    // [total_q, Hq, D]
-    float scale_log2;             // scale * log2(e)
+    float score_scale;            // |scale| * log2(e)
+    int negate_query;             // scale < 0: the query enters with its sign flipped
     int num_seqs;
     int total_q;
     int num_q_heads;

@@ -168,3 +168,15 @@ def test_prefill_rows_past_max_query_len_untouched(B):
     assert np.all(wide[8:20] == 7.0)           # rows 8.. of sequence 0 not written
     check_close(wide[:8], ref[:8], "first rows")
     check_close(wide[20:], ref[20:], "second sequence")
+
+
+@pytest.mark.parametrize("scale", [0.0, -0.0884, 3.0, -3.0])
+def test_prefill_scale_sign_and_range(B, scale):
+    """A zero scale (uniform weights), negative scales (the query's sign is
+    flipped inside the kernel) and scales large enough that the weights span
+    hundreds of binary orders of magnitude: a running max reduced over the
+    wrong lanes would overflow here."""
+    b = W.make_prefill(3601, dtype="bf16", num_q_heads=8, num_kv_heads=2, head_dim=128,
+                       block_size=16, context_lens=(70, 200, 33), query_lens=(70, 64, 1),
+                       poison=True, scale=scale)
+    check_close(tensors.widen(run_prefill(B, b), "bf16"), ref_prefill(b), f"scale={scale}")
