@@ -50,6 +50,9 @@ constexpr int kPrefillThreads = 256;
 constexpr int kPrefillWaves = kPrefillThreads / 64;
 constexpr int kTile = 32;  // tokens per tile: two 16-token halves
 constexpr int kXcds = 8;   // accelerator complex dies of the MI355X, each with its own L2
+// Word 3 of a raw buffer resource on gfx9-family parts (32-bit data format):
+// loads past the stated size return zero.
+constexpr int kBufferConfig = 0x00020000;
 
 // 16-row blocks per wave: two share each K/V operand read; head_dim 256
 // keeps one (its accumulators and query operands double).
@@ -246,6 +249,22 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(PrefillParams 
         else
             return (wave_s * kWave + c * kPrefillThreads) / (16 * CPRW);
     };
+    // Block ids of the two halves of the next tile to load, fetched one tile
+    // ahead with a vector (buffer) load, so that they are in registers when
+    // the tile's loads are issued: a scalar load there would stall the wave
+    // (its wait also covers every outstanding LDS access).  A half past pmax
+    // takes pmax's block; its tokens are zeroed when the tile is stored.
+    const __amdgpu_buffer_rsrc_t bt_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<int32_t *>(bt_row), 0, p.max_blocks_per_seq * 4, kBufferConfig);
+    int next_id[2] = {0, 0};
+    auto fetch_ids = [&](int tile) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const int th = min(tile * kTile + 16 * h, pmax);
+            next_id[h] = __builtin_amdgcn_raw_buffer_load_b32(bt_rsrc, (th >> p.block_shift) * 4,
+                                                              0, 0);
+        }
+    };
     auto load_tile = [&](int tile) {
         const int t0 = tile * kTile;
         int64_t half_base[2] = {0, 0};
@@ -253,15 +272,13 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(PrefillParams 
 #pragma unroll
             for (int h = 0; h < 2; ++h) {
                 const int th = t0 + 16 * h;
-                if (th <= pmax) {
-                    int blk = __builtin_amdgcn_readfirstlane(bt_row[th >> p.block_shift]);
-                    if (blk < 0 || blk >= p.num_blocks) {
-                        bad = 1;
-                        blk = 0;
-                    }
-                    half_base[h] = (int64_t)blk * p.block_stride_bytes +
-                                   (int64_t)(th & (p.block_size - 1)) * p.row_stride_bytes;
+                int blk = __builtin_amdgcn_readfirstlane(next_id[h]);
+                if (blk < 0 || blk >= p.num_blocks) {
+                    bad = 1;
+                    blk = 0;
                 }
+                half_base[h] = (int64_t)blk * p.block_stride_bytes +
+                               (int64_t)(th & (p.block_size - 1)) * p.row_stride_bytes;
             }
         }
         // Every chunk is loaded, so that the loads issue back to back; a
@@ -288,21 +305,26 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(PrefillParams 
             kreg[c] = load16_stream(p.key_cache + o);
             vreg[c] = load16_stream(p.value_cache + o);
         }
+        if constexpr (BT) fetch_ids(tile + 1);  // past the last tile: pmax's block again
     };
     auto store_tile = [&](int buf, int tile) {
         const int t0 = tile * kTile;
-        const bool partial = t0 + kTile - 1 > pmax;  // workgroup-uniform
 #pragma unroll
         for (int c = 0; c < CPT; ++c) {
             const int idx = threadIdx.x + c * kPrefillThreads;
             const int e = (idx / CPRW) * RSTR + (idx % CPRW) * 8;
-            u32x4 kv = kreg[c], vv = vreg[c];
-            if (partial && t0 + idx / CPRW > pmax) {
-                kv = u32x4{0, 0, 0, 0};
-                vv = u32x4{0, 0, 0, 0};
+            *reinterpret_cast<u32x4 *>(&k_lds[buf][e]) = kreg[c];
+            *reinterpret_cast<u32x4 *>(&v_lds[buf][e]) = vreg[c];
+        }
+        if (t0 + kTile - 1 > pmax) {  // the last tile: overwrite tokens past pmax
+#pragma unroll
+            for (int c = 0; c < CPT; ++c) {
+                const int idx = threadIdx.x + c * kPrefillThreads;
+                if (t0 + idx / CPRW <= pmax) continue;
+                const int e = (idx / CPRW) * RSTR + (idx % CPRW) * 8;
+                *reinterpret_cast<u32x4 *>(&k_lds[buf][e]) = u32x4{0, 0, 0, 0};
+                *reinterpret_cast<u32x4 *>(&v_lds[buf][e]) = u32x4{0, 0, 0, 0};
             }
-            *reinterpret_cast<u32x4 *>(&k_lds[buf][e]) = kv;
-            *reinterpret_cast<u32x4 *>(&v_lds[buf][e]) = vv;
         }
     };
 
@@ -318,6 +340,7 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(PrefillParams 
     // this lane's V^T addresses inside a tile (half 0); half 1 is 16 rows down
     const int vt_elem = (4 * kg + lrow / 4) * RSTR + 4 * (lrow % 4);
 
+    if constexpr (BT) fetch_ids(0);
     load_tile(0);
     store_tile(0, 0);
     __syncthreads();
