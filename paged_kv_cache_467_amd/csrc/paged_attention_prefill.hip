@@ -16,9 +16,9 @@
 // wave owns MB blocks of 16 rows (32 rows for head_dim <= 128, 16 for 256),
 // so that every K/V operand read from LDS serves MB blocks.  The workgroup
 // walks the positions its rows can see in 32-token tiles, staged in LDS as
-// they lie in the pool ([token][d], rows padded by 16 bytes against bank
-// conflicts), double-buffered with one barrier per tile and shared by its 4
-// waves:
+// they lie in the pool ([token][d]; K rows padded by 16 bytes and V rows
+// by 32, so that neither operand read meets a bank conflict),
+// double-buffered with one barrier per tile and shared by its 4 waves:
 //  * Scores are computed transposed, S^T = K Q^T, with
 //    v_mfma_f32_16x16x32 per 16-token half: A = K (lane l: token l % 16, 8
 //    consecutive d of k-group l / 16), B = Q^T from registers (lane l: row
@@ -131,14 +131,20 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(PrefillParams 
     constexpr int RPB = rows_per_workgroup(D);
     constexpr int KS = D / 32;            // k-steps of the score MFMA
     constexpr int DB = D / 16;            // 16-wide d blocks of the value MFMA
-    constexpr int RSTR = D + 8;           // tile row stride in elements (+16 bytes)
+    // Tile row strides in elements.  The score operand reads 16 rows x 16
+    // bytes per pass: a 16-byte pad puts those rows 4 banks apart.  The
+    // transposing value reads take 8 rows x 32 bytes per pass: a 32-byte pad
+    // puts them 8 banks apart.  Either way no two lanes of a pass share a
+    // bank (with 32 or with 64 four-byte banks).
+    constexpr int KSTR = D + 8;
+    constexpr int VSTR = D + 16;
     constexpr int CHUNKS = kTile * D / 8;  // 16-byte chunks per tile and tensor
     constexpr int CPT = (CHUNKS + kPrefillThreads - 1) / kPrefillThreads;  // per thread
     constexpr int CPRW = D / 8;           // chunks per token row
     static_assert(CHUNKS % kPrefillThreads == 0, "every thread loads whole chunks");
 
-    __shared__ __attribute__((aligned(16))) uint16_t k_lds[2][kTile * RSTR];
-    __shared__ __attribute__((aligned(16))) uint16_t v_lds[2][kTile * RSTR];
+    __shared__ __attribute__((aligned(16))) uint16_t k_lds[2][kTile * KSTR];
+    __shared__ __attribute__((aligned(16))) uint16_t v_lds[2][kTile * VSTR];
 
     // ---- work item
     // Workgroups go to the 8 XCDs round-robin.  All row blocks of one
@@ -312,18 +318,18 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(PrefillParams 
 #pragma unroll
         for (int c = 0; c < CPT; ++c) {
             const int idx = threadIdx.x + c * kPrefillThreads;
-            const int e = (idx / CPRW) * RSTR + (idx % CPRW) * 8;
-            *reinterpret_cast<u32x4 *>(&k_lds[buf][e]) = kreg[c];
-            *reinterpret_cast<u32x4 *>(&v_lds[buf][e]) = vreg[c];
+            const int row = idx / CPRW, col = (idx % CPRW) * 8;
+            *reinterpret_cast<u32x4 *>(&k_lds[buf][row * KSTR + col]) = kreg[c];
+            *reinterpret_cast<u32x4 *>(&v_lds[buf][row * VSTR + col]) = vreg[c];
         }
         if (t0 + kTile - 1 > pmax) {  // the last tile: overwrite tokens past pmax
 #pragma unroll
             for (int c = 0; c < CPT; ++c) {
                 const int idx = threadIdx.x + c * kPrefillThreads;
                 if (t0 + idx / CPRW <= pmax) continue;
-                const int e = (idx / CPRW) * RSTR + (idx % CPRW) * 8;
-                *reinterpret_cast<u32x4 *>(&k_lds[buf][e]) = u32x4{0, 0, 0, 0};
-                *reinterpret_cast<u32x4 *>(&v_lds[buf][e]) = u32x4{0, 0, 0, 0};
+                const int row = idx / CPRW, col = (idx % CPRW) * 8;
+                *reinterpret_cast<u32x4 *>(&k_lds[buf][row * KSTR + col]) = u32x4{0, 0, 0, 0};
+                *reinterpret_cast<u32x4 *>(&v_lds[buf][row * VSTR + col]) = u32x4{0, 0, 0, 0};
             }
         }
     };
@@ -338,7 +344,7 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(PrefillParams 
         for (int b = 0; b < DB; ++b) acc[mb][b] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
     }
     // this lane's V^T addresses inside a tile (half 0); half 1 is 16 rows down
-    const int vt_elem = (4 * kg + lrow / 4) * RSTR + 4 * (lrow % 4);
+    const int vt_elem = (4 * kg + lrow / 4) * VSTR + 4 * (lrow % 4);
 
     if constexpr (BT) fetch_ids(0);
     load_tile(0);
@@ -362,7 +368,7 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(PrefillParams 
 #pragma unroll
                 for (int ks = 0; ks < KS; ++ks) {
                     const u32x4 a = *reinterpret_cast<const u32x4 *>(
-                        &kt[(16 * u + lrow) * RSTR + (kg + 4 * ks) * 8]);
+                        &kt[(16 * u + lrow) * KSTR + (kg + 4 * ks) * 8]);
 #pragma unroll
                     for (int mb = 0; mb < MB; ++mb) st[mb][u] = mfma_k32<T>(a, qb[mb][ks], st[mb][u]);
                 }
@@ -431,7 +437,7 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(PrefillParams 
 #pragma unroll
             for (int b = 0; b < DB; ++b) {
                 const uint64_t lo = lds_read_tr16(vt + vt_elem + 16 * b);
-                const uint64_t hi = lds_read_tr16(vt + vt_elem + 16 * RSTR + 16 * b);
+                const uint64_t hi = lds_read_tr16(vt + vt_elem + 16 * VSTR + 16 * b);
                 const u32x4 a = u32x4{(uint32_t)lo, (uint32_t)(lo >> 32), (uint32_t)hi,
                                       (uint32_t)(hi >> 32)};
 #pragma unroll
