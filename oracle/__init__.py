@@ -44,6 +44,7 @@ class Oracle:
             "oracle_kv_cache_write": [vp, vp, vp, vp, vp] + [ci] * 5,
             "oracle_paged_kv_gather": [vp, vp, vp, vp, vp, vp] + [ci] * 7,
             "oracle_copy_blocks": [vp, vp, vp] + [ci] * 5,
+            "oracle_swap_blocks": [vp, vp, ci, vp, vp, ci, vp] + [ci] * 5,
             "oracle_paged_attention_prefill": [vp] * 6 + [cf] + [ci] * 7 + [vp],
             "oracle_elements_to_double": [vp, ctypes.c_int64, ci, vp],
             "oracle_set_threads": [ci],
@@ -146,6 +147,19 @@ class Oracle:
         nb, bs, Hkv, D = key_cache.shape
         bm = np.ascontiguousarray(block_mapping, dtype=np.int32).reshape(-1, 2)
         self.lib.oracle_copy_blocks(_ptr(key_cache), _ptr(value_cache), _ptr(bm), bm.shape[0],
+                                    Hkv, D, bs, _code(dtype))
+
+    def swap_blocks(self, src_key, src_value, dst_key, dst_value, block_mapping, dtype):
+        """Block swap between two pool pairs of the same block shape (device
+        to host, or back): for each (from, to) row of block_mapping, block to
+        of dst_key/dst_value becomes a copy of block from of src_key/src_value;
+        a row with an id outside its pool is skipped.  dst is updated in
+        place."""
+        ns, bs, Hkv, D = src_key.shape
+        assert dst_key.shape[1:] == src_key.shape[1:] and dst_value.shape == dst_key.shape
+        bm = np.ascontiguousarray(block_mapping, dtype=np.int32).reshape(-1, 2)
+        self.lib.oracle_swap_blocks(_ptr(src_key), _ptr(src_value), ns, _ptr(dst_key),
+                                    _ptr(dst_value), dst_key.shape[0], _ptr(bm), bm.shape[0],
                                     Hkv, D, bs, _code(dtype))
 
     # ---- conveniences on a workloads.DecodeBatch ----

@@ -44,6 +44,15 @@
  *    a block of its own ("23.1 vLLM：高吞吐推理框架原理与部署", §二.3).  Each
  *    (src, dst) pair copies every slot of physical block src to block dst,
  *    in both pools; a negative id skips the pair.
+ *  - Block swap: when GPU memory runs short the scheduler preempts a
+ *    sequence and moves its KV blocks out to CPU memory rather than
+ *    refusing work, and a swapped sequence goes back to running first once
+ *    memory allows ("大模型推理框架 vllm 源码解析 一", §三; the size of the
+ *    CPU swap area is a serving option, §四; "大模型推理框架VLLM-0.7.3源码",
+ *    §2.2 on the swapped queue).  Each (from, to) pair copies block `from`
+ *    of a source pool pair to block `to` of a destination pool pair of the
+ *    same block shape; swap-out and swap-in differ only in which pools are
+ *    which.
  *
  * Element types: f32 (code 0), f16 (code 1, IEEE binary16), bf16 (code 2,
  * the upper half of a binary32).  Inputs are read as stored bits and widened
@@ -349,6 +358,29 @@ void oracle_copy_blocks(void *key_cache, void *value_cache, const int32_t *block
                 (const char *)key_cache + (size_t)src * block_bytes, block_bytes);
         memmove((char *)value_cache + (size_t)dst * block_bytes,
                 (const char *)value_cache + (size_t)src * block_bytes, block_bytes);
+    }
+}
+
+/*
+ * Block swap between two pool pairs of the same block shape (device to host
+ * or host to device).  block_mapping holds (from, to) pairs; a pair with an
+ * id outside its pool copies nothing.
+ */
+void oracle_swap_blocks(const void *src_key, const void *src_value, int num_src_blocks,
+                        void *dst_key, void *dst_value, int num_dst_blocks,
+                        const int32_t *block_mapping, int num_pairs, int num_kv_heads,
+                        int head_dim, int block_size, int dtype)
+{
+    const size_t bytes = (size_t)block_size * num_kv_heads * head_dim * element_bytes(dtype);
+    for (int i = 0; i < num_pairs; ++i) {
+        const int from = block_mapping[2 * i];
+        const int to = block_mapping[2 * i + 1];
+        if (from < 0 || from >= num_src_blocks || to < 0 || to >= num_dst_blocks)
+            continue;
+        memcpy((char *)dst_key + (size_t)to * bytes, (const char *)src_key + (size_t)from * bytes,
+               bytes);
+        memcpy((char *)dst_value + (size_t)to * bytes,
+               (const char *)src_value + (size_t)from * bytes, bytes);
     }
 }
 

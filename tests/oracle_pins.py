@@ -366,6 +366,48 @@ def pin_copy_blocks(orc):
         assert np.array_equal(k2[pairs[1, 1]].view(np.uint8), kc[pairs[1, 1]].view(np.uint8))
 
 
+def _position_pools(dtype, nb, bs, Hkv, D, salt):
+    """Two pools whose every element encodes its own position (and the pool)."""
+    n = nb * bs * Hkv * D
+    kc = np.arange(n, dtype=np.uint32).reshape(nb, bs, Hkv, D) * 3 + salt
+    vc = kc + 1
+    if dtype != "f32":
+        return (kc % 65521).astype(np.uint16), (vc % 65521).astype(np.uint16)
+    return kc.view(np.float32), vc.view(np.float32)
+
+
+def pin_swap_blocks(orc):
+    """Block swap (preemption to CPU memory and back: "大模型推理框架 vllm 源码
+    解析 一", §三; "大模型推理框架VLLM-0.7.3源码", §2.2): swap-out equals numpy
+    fancy-index assignment from the device pools into the host pools, leaves
+    every other host block as it was and skips pairs with an id outside
+    either pool; swapping back into other device blocks (the inverse pairs)
+    restores the original bits there."""
+    rng = np.random.default_rng(23)
+    for dtype, nb, nh, bs, Hkv, D in (("bf16", 30, 12, 16, 2, 8), ("f32", 9, 5, 4, 3, 4)):
+        dk, dv = _position_pools(dtype, nb, bs, Hkv, D, 0)
+        hk, hv = _position_pools(dtype, nh, bs, Hkv, D, 7)
+        n = min(nb, nh) - 2
+        pairs = np.stack([rng.permutation(nb)[:n], rng.permutation(nh)[:n]], axis=1)
+        pairs = np.concatenate([pairs, [[-1, 0], [nb, 1], [0, nh], [1, -3]]]).astype(np.int32)
+        hk2, hv2 = hk.copy(), hv.copy()
+        orc.swap_blocks(dk, dv, hk2, hv2, pairs, dtype)
+        ek, ev = hk.copy(), hv.copy()
+        ek[pairs[:n, 1]] = dk[pairs[:n, 0]]
+        ev[pairs[:n, 1]] = dv[pairs[:n, 0]]
+        assert np.array_equal(hk2.view(np.uint8), ek.view(np.uint8))
+        assert np.array_equal(hv2.view(np.uint8), ev.view(np.uint8))
+        # back in, to a relabelled set of device blocks of a clobbered pool
+        dest = rng.permutation(nb)[:n]
+        back = np.stack([pairs[:n, 1], dest], axis=1).astype(np.int32)
+        rk, rv = np.zeros_like(dk), np.zeros_like(dv)
+        orc.swap_blocks(hk2, hv2, rk, rv, back, dtype)
+        assert np.array_equal(rk[dest].view(np.uint8), dk[pairs[:n, 0]].view(np.uint8))
+        assert np.array_equal(rv[dest].view(np.uint8), dv[pairs[:n, 0]].view(np.uint8))
+        untouched = np.setdiff1d(np.arange(nb), dest)
+        assert not rk[untouched].any() and not rv[untouched].any()
+
+
 # ------------------------------------------------------ multi-token (prefill)
 PREFILL_SHAPES = [
     # seed, dtype, Hq, Hkv, D, bs, context lens, query lens
@@ -462,6 +504,7 @@ ALL_PINS = [
     pin_context_len_one, pin_identical_keys, pin_two_token_logistic, pin_weights_sum_to_one,
     pin_block_permutation, pin_gqa_equals_mha, pin_split_merge, pin_poison_unreferenced,
     pin_large_scores, pin_empty_context, pin_linear_in_values, pin_copy_blocks,
+    pin_swap_blocks,
     pin_prefill_vs_sdpa, pin_prefill_one_token_is_decode, pin_prefill_causal,
     pin_prefill_block_permutation,
 ]

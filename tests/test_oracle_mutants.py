@@ -58,6 +58,14 @@ MUTANTS = {
     # block copy: value pool filled from the key pool
     "copy_v_from_k": ("memmove((char *)value_cache + (size_t)dst * block_bytes,\n                (const char *)value_cache",
                       "memmove((char *)value_cache + (size_t)dst * block_bytes,\n                (const char *)key_cache"),
+    # block swap: pair read the wrong way round
+    "swap_direction": ("const int from = block_mapping[2 * i];\n        const int to = block_mapping[2 * i + 1];",
+                       "const int from = block_mapping[2 * i + 1];\n        const int to = block_mapping[2 * i];"),
+    # block swap: value pool filled from the key pool
+    "swap_v_from_k": ("(const char *)src_value + (size_t)from * bytes",
+                      "(const char *)src_key + (size_t)from * bytes"),
+    # block swap: off-by-one range check (reads one block past the source)
+    "swap_range": ("from >= num_src_blocks", "from > num_src_blocks"),
     # gather: value rows taken from the key pool
     "gather_v_from_k": ("memcpy((char *)out_v + dst * element_bytes(dtype),\n                   (const char *)value_cache",
                         "memcpy((char *)out_v + dst * element_bytes(dtype),\n                   (const char *)key_cache"),
