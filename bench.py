@@ -186,6 +186,116 @@ def bench_copy_blocks(args) -> int:
     return 0
 
 
+# MI355X host link: PCIe 5.0 x16, 32 GT/s on each of 16 lanes = 64 GB/s per
+# direction before encoding and packet overheads.
+HOST_LINK_PEAK_GBPS = 64.0
+
+
+def bench_swap(args) -> int:
+    """Block swap between the workload's device pools and pinned host pools:
+    each step moves --pairs random device blocks of both pools out to host
+    blocks (swap_out) or back (swap_in).  Reported as bytes moved over the
+    host link (each block of both pools once) over the kernel time; the
+    runtime's own copy of the same number of contiguous bytes between the
+    same kinds of memory is measured beside it."""
+    import numpy as np
+    import torch
+
+    import oracle
+    from paged_kv_cache_467_amd import binding, tensors, workloads as W
+
+    out = args.op == "swap_out"
+    dev = torch.device("cuda:0")
+    b = W.make_workload(args.workload, values=False)
+    dt = tensors.TORCH_DTYPE[b.dtype]
+    blk = (b.block_size, b.num_kv_heads, b.head_dim)
+    block_bytes = b.block_size * b.num_kv_heads * b.head_dim * tensors.ELEM_BYTES[b.dtype]
+    rng = np.random.default_rng(46791)
+    npairs = min(args.pairs, b.num_blocks)
+    dev_ids = rng.permutation(b.num_blocks)[:npairs]
+    host_ids = rng.permutation(npairs)
+    pairs = np.stack([dev_ids, host_ids] if out else [host_ids, dev_ids], axis=1).astype(np.int32)
+    kc = torch.randn((b.num_blocks,) + blk, device=dev).to(dt)
+    vc = torch.randn((b.num_blocks,) + blk, device=dev).to(dt)
+    hk = torch.empty((npairs,) + blk, dtype=dt, pin_memory=True)
+    hv = torch.empty((npairs,) + blk, dtype=dt, pin_memory=True)
+    hk.copy_(kc[:npairs].cpu())
+    hv.copy_(vc[:npairs].cpu())
+    mapping = tensors.int32(pairs, dev)
+
+    def step(_):
+        if out:
+            binding.paged_kv_swap_out(kc, vc, hk, hv, mapping)
+        else:
+            binding.paged_kv_swap_in(hk, hv, kc, vc, mapping)
+
+    def timed(fn, steps, warmup):
+        for i in range(warmup):
+            fn(i)
+        torch.cuda.synchronize()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(steps)]
+        t0 = time.perf_counter()
+        for i, (a, z) in enumerate(ev):
+            a.record()
+            fn(warmup + i)
+            z.record()
+        torch.cuda.synchronize()
+        return time.perf_counter() - t0, sum(a.elapsed_time(z) for a, z in ev) / steps
+
+    elapsed, avg = timed(step, args.steps, args.warmup)
+    byt = 2 * npairs * block_bytes
+    achieved = byt / (avg * 1e-3) / 1e9
+    # the runtime's DMA copy of the same bytes, contiguous, same direction
+    flat_dev = kc.view(-1)[:hk.numel()]
+    flat_host = hk.view(-1)
+
+    def dma(_):
+        if out:
+            flat_host.copy_(flat_dev, non_blocking=True)
+        else:
+            flat_dev.copy_(flat_host, non_blocking=True)
+    _, dma_ms = timed(dma, max(5, args.steps // 4), 2)
+    dma_gbps = (flat_host.numel() * flat_host.element_size()) / (dma_ms * 1e-3) / 1e9
+    direction = "device to host" if out else "host to device"
+    result = {
+        "metric": f"KV block {args.op.replace('_', '-')}: achieved host-link GB/s",
+        "value": round(achieved, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(elapsed * 1e3 / args.steps, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": b.dtype,
+        "data": "synthetic",
+        "config": {"workload": f"{args.op} of {npairs} random blocks of the {args.workload} pool, "
+                               f"{direction} (pinned)",
+                   "pairs": npairs, "block_bytes": block_bytes, "num_blocks": b.num_blocks},
+        "swap_ms": round(avg, 5),
+        "runtime_dma_copy_GBps": round(dma_gbps, 2),
+        "roofline": {"bound": "host_link", "achieved": round(achieved, 2),
+                     "peak": HOST_LINK_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(achieved / HOST_LINK_PEAK_GBPS, 4), "traffic": None,
+                     "kernel": f"paged_kv_{args.op}", "algorithmic_bytes_per_launch": byt},
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        sd = np.float32 if b.dtype == "f32" else np.uint16
+        # filled, so that every page is real memory (untouched zeros would all
+        # read one shared page)
+        host_pool = [np.full((npairs,) + blk, 1, dtype=sd) for _ in range(2)]
+        dev_pool = [np.full((b.num_blocks,) + blk, 2, dtype=sd) for _ in range(2)]
+        src, dst = (dev_pool, host_pool) if out else (host_pool, dev_pool)
+        times = []
+        while len(times) < 3 or sum(times) < 2.0:
+            t1 = time.perf_counter()
+            oracle.swap_blocks(src[0], src[1], dst[0], dst[1], pairs, b.dtype)
+            times.append(time.perf_counter() - t1)
+        t = statistics.median(times)
+        result["cpu_baseline"] = {"value": round(byt / t / 1e9, 3), "unit": "GB/s", "cores": 1,
+                                  "kind": "oracle",
+                                  "sample": f"the same {npairs} pairs between host arrays, "
+                                            f"median of {len(times)} runs"}
+    print(json.dumps(result), flush=True)
+    return 0
+
+
 MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "f16": 2500.0}
 
 
@@ -289,10 +399,12 @@ def main() -> int:
     ap.add_argument("--copies", type=int, default=4, help="pool copies rotated across steps")
     ap.add_argument("--partition-size", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--op", choices=("decode", "copy_blocks", "prefill"), default="decode",
+    ap.add_argument("--op", choices=("decode", "copy_blocks", "prefill", "swap_out", "swap_in"),
+                    default="decode",
                     help="decode: the decode step (default); copy_blocks: the copy-on-write "
                          "block copy on the same pool; prefill: multi-token attention on the "
-                         "chunked-prefill workload")
+                         "chunked-prefill workload; swap_out / swap_in: block swap between the "
+                         "pool and pinned host memory")
     ap.add_argument("--pairs", type=int, default=2048, help="block pairs per copy_blocks step")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="also run one plain device copy of this many MiB (counter calibration)")
@@ -314,6 +426,8 @@ def main() -> int:
         return 1
     dev = torch.device("cuda:0")
     torch.manual_seed(0)
+    if args.op in ("swap_out", "swap_in"):
+        return bench_swap(args)
     if args.op == "copy_blocks":
         return bench_copy_blocks(args)
     if args.op == "prefill":

@@ -53,7 +53,8 @@ typedef enum {
     PAGED_KV_ERR_BAD_SHAPE = 2,    /* sizes inconsistent, out of range or misaligned */
     PAGED_KV_ERR_UNSUPPORTED = 3,  /* valid but not implemented (dtype, head_dim, ...) */
     PAGED_KV_ERR_WORKSPACE = 4,    /* workspace missing or smaller than required */
-    PAGED_KV_ERR_HIP = 5           /* the HIP runtime reported an error */
+    PAGED_KV_ERR_HIP = 5,          /* the HIP runtime reported an error */
+    PAGED_KV_ERR_HOST_MEMORY = 6   /* a host buffer is not pinned, device-mapped memory */
 } paged_kv_status;
 
 /* Human-readable name of a status code (static storage, never NULL). */
@@ -219,6 +220,45 @@ PAGED_KV_API int paged_attn_prefill(
 PAGED_KV_API int paged_kv_copy_blocks(
     void *key_cache, void *value_cache, const int32_t *block_mapping, int num_pairs,
     int num_kv_heads, int head_dim, int block_size, int num_blocks, int dtype, void *stream);
+
+/*
+ * Block swap for preemption: when GPU memory runs short the scheduler moves
+ * a preempted sequence's KV blocks out to CPU memory instead of refusing
+ * work, and brings them back (into whatever device blocks are free) when
+ * the sequence resumes ("大模型推理框架 vllm 源码解析 一", §三, and the CPU
+ * swap-space option of §四; "大模型推理框架VLLM-0.7.3源码", §2.2 on the swapped
+ * queue).
+ *
+ * Swap-out: for each pair i < num_pairs with from = block_mapping[2 * i]
+ * (device block) and to = block_mapping[2 * i + 1] (host block), all
+ * block_size slots of all kv heads of host block `to`, in both host pools,
+ * become a bit copy of device block `from`.  Swap-in is the reverse: from is
+ * a host block and to a device block.
+ *   key_cache, value_cache  device pools [num_blocks, block_size,
+ *                num_kv_heads, head_dim]
+ *   host_key_cache, host_value_cache  host pools [num_host_blocks,
+ *                block_size, num_kv_heads, head_dim] in pinned, device-mapped
+ *                host memory (hipHostMalloc, or a pinned torch tensor); any
+ *                other host memory returns PAGED_KV_ERR_HOST_MEMORY and
+ *                enqueues nothing.  The kernel reads or writes it directly
+ *                over the host link.
+ *   block_mapping [num_pairs, 2] int32 (from, to), device memory
+ * The destination pools are updated in place; the caller keeps the host
+ * pools alive and unmodified until the stream has passed the call.
+ * Device-side values: a pair with an id outside its pool copies nothing.
+ * Pairs run in parallel: a `to` that appears twice leaves an unspecified
+ * result.  One block must be a multiple of 16 bytes and at most 4 GiB (else
+ * PAGED_KV_ERR_BAD_SHAPE).
+ */
+PAGED_KV_API int paged_kv_swap_out(
+    const void *key_cache, const void *value_cache, void *host_key_cache,
+    void *host_value_cache, const int32_t *block_mapping, int num_pairs, int num_kv_heads,
+    int head_dim, int block_size, int num_blocks, int num_host_blocks, int dtype, void *stream);
+
+PAGED_KV_API int paged_kv_swap_in(
+    const void *host_key_cache, const void *host_value_cache, void *key_cache,
+    void *value_cache, const int32_t *block_mapping, int num_pairs, int num_kv_heads,
+    int head_dim, int block_size, int num_blocks, int num_host_blocks, int dtype, void *stream);
 
 /*
  * Materialise each sequence's logical K/V through its block table (the

@@ -29,6 +29,8 @@ EXPORTED = (
     "paged_kv_gather",
     "paged_kv_copy_blocks",
     "paged_attn_prefill",
+    "paged_kv_swap_out",
+    "paged_kv_swap_in",
 )
 
 
@@ -55,6 +57,9 @@ def _load_library(path: str = LIBRARY) -> ctypes.CDLL:
     lib.paged_kv_copy_blocks.restype = ci
     lib.paged_attn_prefill.argtypes = [vp] * 6 + [cf, vp] + [ci] * 11 + [vp]
     lib.paged_attn_prefill.restype = ci
+    for name in ("paged_kv_swap_out", "paged_kv_swap_in"):
+        getattr(lib, name).argtypes = [vp] * 5 + [ci] * 7 + [vp]
+        getattr(lib, name).restype = ci
     return lib
 
 
@@ -81,6 +86,18 @@ def _dev(t: torch.Tensor, name: str) -> int:
         raise TypeError(f"{name} must be a torch.Tensor")
     if t.device.type != "cuda":
         raise ValueError(f"{name} must be on a GPU device, got {t.device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t.data_ptr()
+
+
+def _host(t: torch.Tensor, name: str) -> int:
+    """Host pools are CPU tensors; the library itself checks that they are
+    pinned (torch's pin_memory=True) and returns an error otherwise."""
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cpu":
+        raise ValueError(f"{name} must be a (pinned) CPU tensor, got {t.device}")
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
     return t.data_ptr()
@@ -246,3 +263,51 @@ def paged_attn_prefill(query: torch.Tensor, key_cache: torch.Tensor, value_cache
         _dtype_code(query), _stream(query.device))
     _check("paged_attn_prefill", status)
     return out
+
+
+def _swap_shapes(dev_key, dev_value, host_key, host_value, block_mapping):
+    nb, bs, Hkv, D = dev_key.shape
+    for t in (dev_value, host_key, host_value):
+        if tuple(t.shape[1:]) != (bs, Hkv, D) or t.dtype != dev_key.dtype:
+            raise ValueError("the four pools must share block shape and dtype")
+    if tuple(dev_value.shape) != tuple(dev_key.shape) or \
+            tuple(host_value.shape) != tuple(host_key.shape):
+        raise ValueError("key and value pools must share their shape")
+    if block_mapping.dtype != torch.int32 or block_mapping.dim() != 2 or \
+            block_mapping.shape[1] != 2:
+        raise ValueError("block_mapping must be an int32 tensor of shape [num_pairs, 2]")
+    return nb, bs, Hkv, D, host_key.shape[0]
+
+
+def paged_kv_swap_out(key_cache: torch.Tensor, value_cache: torch.Tensor,
+                      host_key_cache: torch.Tensor, host_value_cache: torch.Tensor,
+                      block_mapping: torch.Tensor) -> None:
+    """Swap-out: for each (device block, host block) row of block_mapping
+    ([num_pairs, 2] int32, on the GPU), the host block of both pinned host
+    pools becomes a copy of the device block (see paged_kv_swap_out in
+    include/paged_kv.h).  Asynchronous on the current stream."""
+    nb, bs, Hkv, D, nh = _swap_shapes(key_cache, value_cache, host_key_cache,
+                                      host_value_cache, block_mapping)
+    status = _lib.paged_kv_swap_out(
+        _dev(key_cache, "key_cache"), _dev(value_cache, "value_cache"),
+        _host(host_key_cache, "host_key_cache"), _host(host_value_cache, "host_value_cache"),
+        _dev(block_mapping, "block_mapping"), block_mapping.shape[0], Hkv, D, bs, nb, nh,
+        _dtype_code(key_cache), _stream(key_cache.device))
+    _check("paged_kv_swap_out", status)
+
+
+def paged_kv_swap_in(host_key_cache: torch.Tensor, host_value_cache: torch.Tensor,
+                     key_cache: torch.Tensor, value_cache: torch.Tensor,
+                     block_mapping: torch.Tensor) -> None:
+    """Swap-in: for each (host block, device block) row of block_mapping
+    ([num_pairs, 2] int32, on the GPU), the device block of both pools
+    becomes a copy of the host block (see paged_kv_swap_in in
+    include/paged_kv.h).  Asynchronous on the current stream."""
+    nb, bs, Hkv, D, nh = _swap_shapes(key_cache, value_cache, host_key_cache,
+                                      host_value_cache, block_mapping)
+    status = _lib.paged_kv_swap_in(
+        _host(host_key_cache, "host_key_cache"), _host(host_value_cache, "host_value_cache"),
+        _dev(key_cache, "key_cache"), _dev(value_cache, "value_cache"),
+        _dev(block_mapping, "block_mapping"), block_mapping.shape[0], Hkv, D, bs, nb, nh,
+        _dtype_code(key_cache), _stream(key_cache.device))
+    _check("paged_kv_swap_in", status)

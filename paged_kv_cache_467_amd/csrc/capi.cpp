@@ -159,6 +159,7 @@ const char *paged_kv_status_string(int status) {
         case PAGED_KV_ERR_UNSUPPORTED: return "unsupported dtype or shape";
         case PAGED_KV_ERR_WORKSPACE: return "workspace missing or too small";
         case PAGED_KV_ERR_HIP: return "HIP runtime error";
+        case PAGED_KV_ERR_HOST_MEMORY: return "host buffer is not pinned, device-mapped memory";
         default: return "unknown status";
     }
 }
@@ -339,10 +340,77 @@ int paged_kv_copy_blocks(void *key_cache, void *value_cache, const int32_t *bloc
     if (!key_cache || !value_cache || !block_mapping) return PAGED_KV_ERR_NULL_POINTER;
     if (!aligned16(key_cache) || !aligned16(value_cache) || !aligned4(block_mapping))
         return PAGED_KV_ERR_BAD_SHAPE;
-    const hipError_t err = pkv::launch_copy_blocks(key_cache, value_cache, block_mapping,
-                                                   num_pairs, block_bytes, num_blocks,
+    const hipError_t err = pkv::launch_copy_blocks(key_cache, value_cache, num_blocks, key_cache,
+                                                   value_cache, num_blocks, block_mapping,
+                                                   num_pairs, block_bytes,
                                                    static_cast<hipStream_t>(stream));
     return err == hipSuccess ? PAGED_KV_OK : PAGED_KV_ERR_HIP;
+}
+
+namespace {
+
+// The device address of pinned, device-mapped host memory (hipHostMalloc, or
+// a pinned torch tensor), or nullptr for any other pointer.
+void *host_device_view(const void *host) {
+    hipPointerAttribute_t attr;
+    if (hipPointerGetAttributes(&attr, host) != hipSuccess) {
+        (void)hipGetLastError();  // an unknown pointer is an answer, not a failure
+        return nullptr;
+    }
+    return attr.type == hipMemoryTypeHost ? attr.devicePointer : nullptr;
+}
+
+// Shared checks and launch of both swap directions; device_to_host picks
+// which pools are the source.
+int swap_blocks(const void *dev_key, const void *dev_value, const void *host_key,
+                const void *host_value, const int32_t *block_mapping, int num_pairs,
+                int num_kv_heads, int head_dim, int block_size, int num_blocks,
+                int num_host_blocks, int dtype, void *stream, bool device_to_host) {
+    if (dtype != PAGED_KV_F32 && dtype != PAGED_KV_F16 && dtype != PAGED_KV_BF16)
+        return PAGED_KV_ERR_UNSUPPORTED;
+    if (num_pairs < 0 || num_pairs > 0x7fffffff / 2 || num_kv_heads < 1 || head_dim < 1 ||
+        block_size < 1 || num_blocks < 1 || num_host_blocks < 1)
+        return PAGED_KV_ERR_BAD_SHAPE;
+    const int64_t block_bytes = (int64_t)block_size * num_kv_heads * head_dim * elem_bytes(dtype);
+    if (block_bytes % 16 != 0 || block_bytes / 65536 > 65535) return PAGED_KV_ERR_BAD_SHAPE;
+    if (num_pairs == 0) return PAGED_KV_OK;
+    if (!dev_key || !dev_value || !host_key || !host_value || !block_mapping)
+        return PAGED_KV_ERR_NULL_POINTER;
+    if (!aligned16(dev_key) || !aligned16(dev_value) || !aligned16(host_key) ||
+        !aligned16(host_value) || !aligned4(block_mapping))
+        return PAGED_KV_ERR_BAD_SHAPE;
+    void *hk = host_device_view(host_key);
+    void *hv = host_device_view(host_value);
+    if (!hk || !hv) return PAGED_KV_ERR_HOST_MEMORY;
+    const hipStream_t st = static_cast<hipStream_t>(stream);
+    const hipError_t err =
+        device_to_host
+            ? pkv::launch_copy_blocks(dev_key, dev_value, num_blocks, hk, hv, num_host_blocks,
+                                      block_mapping, num_pairs, block_bytes, st)
+            : pkv::launch_copy_blocks(hk, hv, num_host_blocks, const_cast<void *>(dev_key),
+                                      const_cast<void *>(dev_value), num_blocks, block_mapping,
+                                      num_pairs, block_bytes, st);
+    return err == hipSuccess ? PAGED_KV_OK : PAGED_KV_ERR_HIP;
+}
+
+}  // namespace
+
+int paged_kv_swap_out(const void *key_cache, const void *value_cache, void *host_key_cache,
+                      void *host_value_cache, const int32_t *block_mapping, int num_pairs,
+                      int num_kv_heads, int head_dim, int block_size, int num_blocks,
+                      int num_host_blocks, int dtype, void *stream) {
+    return swap_blocks(key_cache, value_cache, host_key_cache, host_value_cache, block_mapping,
+                       num_pairs, num_kv_heads, head_dim, block_size, num_blocks,
+                       num_host_blocks, dtype, stream, true);
+}
+
+int paged_kv_swap_in(const void *host_key_cache, const void *host_value_cache,
+                     void *key_cache, void *value_cache, const int32_t *block_mapping,
+                     int num_pairs, int num_kv_heads, int head_dim, int block_size,
+                     int num_blocks, int num_host_blocks, int dtype, void *stream) {
+    return swap_blocks(key_cache, value_cache, host_key_cache, host_value_cache, block_mapping,
+                       num_pairs, num_kv_heads, head_dim, block_size, num_blocks,
+                       num_host_blocks, dtype, stream, false);
 }
 
 int paged_kv_gather(const void *key_cache, const void *value_cache,

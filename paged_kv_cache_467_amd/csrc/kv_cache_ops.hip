@@ -79,24 +79,30 @@ __global__ __launch_bounds__(kCopyThreads) void paged_kv_gather_kernel(
     }
 }
 
-// Block copy: grid (pair, pool, chunk of up to kCopyChunkBytes of the block).
-// A pair whose src or dst is outside [0, num_blocks) copies nothing.  Every
-// byte is touched once, so loads and stores are non-temporal.
+// Block copy from one pool pair into another of the same block shape (one
+// pool pair for a copy-on-write copy; device and pinned host pools for a
+// swap): grid (pair, pool, chunk of up to kCopyChunkBytes of the block).  A
+// pair whose from or to id leaves its pool copies nothing.  Every byte is
+// touched once, so loads and stores are non-temporal.
 constexpr int kCopyChunkBytes = 64 * 1024;
 constexpr int kCopyUnroll = 4;
 
+struct BlockCopy {
+    const char *src_key, *src_value;
+    char *dst_key, *dst_value;
+    int num_src_blocks, num_dst_blocks;
+};
+
 __global__ __launch_bounds__(kCopyThreads) void copy_blocks_kernel(
-    char *__restrict__ key_cache, char *__restrict__ value_cache,
-    const int32_t *__restrict__ block_mapping, int64_t block_bytes, int num_blocks) {
+    BlockCopy c, const int32_t *__restrict__ block_mapping, int64_t block_bytes) {
     const int pair = blockIdx.x;
     const int src = block_mapping[2 * pair];
     const int dst = block_mapping[2 * pair + 1];
-    if (src < 0 || src >= num_blocks || dst < 0 || dst >= num_blocks) return;
-    char *pool = blockIdx.y == 0 ? key_cache : value_cache;
+    if (src < 0 || src >= c.num_src_blocks || dst < 0 || dst >= c.num_dst_blocks) return;
     const int64_t begin = (int64_t)blockIdx.z * kCopyChunkBytes;
     const int64_t end = begin + kCopyChunkBytes < block_bytes ? begin + kCopyChunkBytes : block_bytes;
-    const char *from = pool + (int64_t)src * block_bytes;
-    char *to = pool + (int64_t)dst * block_bytes;
+    const char *from = (blockIdx.y == 0 ? c.src_key : c.src_value) + (int64_t)src * block_bytes;
+    char *to = (blockIdx.y == 0 ? c.dst_key : c.dst_value) + (int64_t)dst * block_bytes;
     constexpr int kStep = kCopyThreads * 16;
     int64_t b = begin + threadIdx.x * 16;
     for (; b + (kCopyUnroll - 1) * kStep < end; b += kCopyUnroll * kStep) {
@@ -111,14 +117,17 @@ __global__ __launch_bounds__(kCopyThreads) void copy_blocks_kernel(
 
 }  // namespace
 
-hipError_t launch_copy_blocks(void *key_cache, void *value_cache, const int32_t *block_mapping,
-                              int num_pairs, int64_t block_bytes, int num_blocks,
+hipError_t launch_copy_blocks(const void *src_key, const void *src_value, int num_src_blocks,
+                              void *dst_key, void *dst_value, int num_dst_blocks,
+                              const int32_t *block_mapping, int num_pairs, int64_t block_bytes,
                               hipStream_t stream) {
     if (num_pairs == 0) return hipSuccess;
     const unsigned chunks = (unsigned)((block_bytes + kCopyChunkBytes - 1) / kCopyChunkBytes);
+    const BlockCopy c{static_cast<const char *>(src_key), static_cast<const char *>(src_value),
+                      static_cast<char *>(dst_key), static_cast<char *>(dst_value),
+                      num_src_blocks, num_dst_blocks};
     hipLaunchKernelGGL(copy_blocks_kernel, dim3(num_pairs, 2, chunks), dim3(kCopyThreads), 0,
-                       stream, static_cast<char *>(key_cache), static_cast<char *>(value_cache),
-                       block_mapping, block_bytes, num_blocks);
+                       stream, c, block_mapping, block_bytes);
     return hipGetLastError();
 }
 
