@@ -33,10 +33,11 @@ if ROOT not in sys.path:
 METRIC = "paged decode attention: achieved HBM GB/s (% of peak) + sequences/sec per layer"
 HBM_PEAK_GBPS = 8000.0
 PROFILES = os.path.join(ROOT, "profiles")
+# what decides the decode kernels and their launch (the partition choice)
 DECODE_SOURCES = ["paged_kv_cache_467_amd/csrc/paged_attention_decode.hip",
                   "paged_kv_cache_467_amd/csrc/device_utils.h",
                   "paged_kv_cache_467_amd/csrc/decode.h",
-                  "paged_kv_cache_467_amd/csrc/capi.cpp"]
+                  "paged_kv_cache_467_amd/csrc/decode_plan.cpp"]
 
 
 def decode_source_hash() -> str:

@@ -1,6 +1,7 @@
-// C ABI of the paged-attention decode library: host-side argument checks,
-// the choice of context partition, workspace sizing and kernel launches on
-// the caller's stream.  Nothing here reads device memory or allocates.
+// C ABI of the paged-KV library: host-side argument checks and kernel
+// launches on the caller's stream (the decode's partition choice and
+// workspace sizing are in decode_plan.cpp).  Nothing here reads device
+// memory or allocates.
 
 #include "../../include/paged_kv.h"
 
@@ -11,23 +12,10 @@
 #include <stdint.h>
 
 #include "decode.h"
+#include "kv_ops.h"
 #include "prefill.h"
 
 namespace {
-
-// Context partitions.  HBM reads run fastest on this part with about eight
-// streaming waves per compute unit: more concurrent streams lower DRAM
-// efficiency, fewer leave bandwidth unused.  So the decode aims for
-// 8 / heads_per_group workgroups per compute unit (never more than fit).
-// Contexts are not split when the batch already has that many (sequence,
-// kv-head group) units; otherwise the split aims to reach it in one round.
-// A partition holds between kMinSplitTokens and kMaxAutoTokens tokens, so
-// that one very long context cannot hold up the whole launch.  When the
-// device cannot be queried (no GPU), assume 256 compute units.
-constexpr int kMinSplitTokens = 256;
-constexpr int kMaxAutoTokens = 1024;
-constexpr int kTargetWavesPerCu = 8;
-constexpr int kFallbackComputeUnits = 256;
 
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 bool aligned4(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
@@ -38,114 +26,6 @@ int log2i(int x) {
     return r;
 }
 int elem_bytes(int dtype) { return dtype == PAGED_KV_F32 ? 4 : 2; }
-int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
-
-struct Plan {
-    int status;
-    int max_context_len;
-    int partition_size;
-    int num_partitions;
-    int heads_per_group;  // kv heads per decode workgroup (one wave each)
-};
-
-// Kv heads per workgroup: the largest power of two up to PKV_HEADS_PER_GROUP
-// that divides num_kv_heads.
-#ifndef PKV_HEADS_PER_GROUP
-#define PKV_HEADS_PER_GROUP 4
-#endif
-static_assert(PKV_HEADS_PER_GROUP >= 1 && PKV_HEADS_PER_GROUP <= pkv::kMaxDecodeWaves,
-              "heads per group");
-int heads_per_group_for(int num_kv_heads) {
-    for (int h = PKV_HEADS_PER_GROUP; h > 1; h /= 2)
-        if (num_kv_heads % h == 0) return h;
-    return 1;
-}
-
-// Shape checks shared by the decode entry points, and the partition choice.
-Plan plan_decode(int num_seqs, int num_q_heads, int num_kv_heads, int head_dim, int block_size,
-                 int max_blocks_per_seq, int max_context_len, int partition_size, int dtype) {
-    Plan pl{PAGED_KV_OK, 0, 0, 1, 1};
-    if (dtype != PAGED_KV_F32 && dtype != PAGED_KV_F16 && dtype != PAGED_KV_BF16) {
-        pl.status = PAGED_KV_ERR_UNSUPPORTED;
-        return pl;
-    }
-    if (num_seqs < 0 || num_q_heads < 1 || num_kv_heads < 1 || max_blocks_per_seq < 1 ||
-        max_context_len < 0 || partition_size < 0 || num_q_heads % num_kv_heads != 0) {
-        pl.status = PAGED_KV_ERR_BAD_SHAPE;
-        return pl;
-    }
-    const int group = num_q_heads / num_kv_heads;
-    if (!(head_dim == 64 || head_dim == 128 || head_dim == 256) ||
-        !(group == 1 || group == 2 || group == 4 || group == 8) || !pow2(block_size) ||
-        block_size > 256) {
-        pl.status = PAGED_KV_ERR_UNSUPPORTED;
-        return pl;
-    }
-    const int64_t table_tokens = (int64_t)max_blocks_per_seq * block_size;
-    if (table_tokens > INT_MAX) {
-        pl.status = PAGED_KV_ERR_BAD_SHAPE;
-        return pl;
-    }
-    const int max_ctx = max_context_len == 0 ? (int)table_tokens : max_context_len;
-    if (max_ctx > table_tokens) {
-        pl.status = PAGED_KV_ERR_BAD_SHAPE;
-        return pl;
-    }
-    const int align = block_size > 16 ? block_size : 16;
-    const int64_t max_part = (int64_t)pkv::kBtLds * block_size;
-    int64_t P;
-    if (partition_size > 0) {
-        if (partition_size % 16 != 0 || partition_size % block_size != 0 ||
-            partition_size > max_part) {
-            pl.status = PAGED_KV_ERR_BAD_SHAPE;
-            return pl;
-        }
-        P = partition_size;
-    } else {
-        const int hpg = heads_per_group_for(num_kv_heads);
-        const int64_t units = (int64_t)num_seqs * (num_kv_heads / hpg);
-        const pkv::DeviceOccupancy occ =
-            pkv::decode_occupancy(dtype, head_dim, group, block_size, hpg);
-        int64_t per_cu = kTargetWavesPerCu / hpg;
-        if (occ.workgroups_per_cu > 0 && per_cu > occ.workgroups_per_cu)
-            per_cu = occ.workgroups_per_cu;
-        if (per_cu < 1) per_cu = 1;
-        const int64_t target =
-            (occ.compute_units > 0 ? occ.compute_units : kFallbackComputeUnits) * per_cu;
-        if (units >= target || max_ctx <= kMinSplitTokens) {
-            P = max_ctx;  // enough units already, or nothing worth splitting
-        } else {
-            const int64_t parts = units > 0 ? target / units : 1;
-            P = (max_ctx + parts - 1) / parts;
-            if (P > kMaxAutoTokens) P = kMaxAutoTokens;
-            if (P < kMinSplitTokens) P = kMinSplitTokens;
-        }
-        P = round_up(P, align);
-        if (P < align) P = align;
-        if (P > max_part) P = max_part;
-    }
-    const int64_t nparts = max_ctx == 0 ? 1 : (max_ctx + P - 1) / P;
-    if ((int64_t)num_seqs * num_kv_heads * nparts > INT_MAX ||
-        (int64_t)num_seqs * num_q_heads > INT_MAX) {
-        pl.status = PAGED_KV_ERR_BAD_SHAPE;
-        return pl;
-    }
-    pl.max_context_len = max_ctx;
-    pl.partition_size = (int)P;
-    pl.num_partitions = (int)nparts;
-    pl.heads_per_group = heads_per_group_for(num_kv_heads);
-    return pl;
-}
-
-size_t partial_floats(int num_seqs, int num_q_heads) {
-    return round_up((int64_t)num_seqs * num_q_heads, 4);  // keeps the o array 16-byte aligned
-}
-
-size_t workspace_for(const Plan &pl, int num_seqs, int num_q_heads, int head_dim) {
-    if (pl.num_partitions <= 1) return 0;
-    const size_t n = partial_floats(num_seqs, num_q_heads) * pl.num_partitions;
-    return n * (2 + (size_t)head_dim) * sizeof(float);
-}
 
 }  // namespace
 
@@ -167,7 +47,7 @@ const char *paged_kv_status_string(int status) {
 int paged_attn_decode_partition_size(int num_seqs, int num_q_heads, int num_kv_heads,
                                      int head_dim, int block_size, int max_blocks_per_seq,
                                      int max_context_len, int partition_size, int dtype) {
-    const Plan pl = plan_decode(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
+    const pkv::DecodePlan pl = pkv::plan_decode(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
                                 max_blocks_per_seq, max_context_len, partition_size, dtype);
     return pl.status == PAGED_KV_OK ? pl.partition_size : -pl.status;
 }
@@ -175,10 +55,10 @@ int paged_attn_decode_partition_size(int num_seqs, int num_q_heads, int num_kv_h
 size_t paged_attn_decode_workspace_bytes(int num_seqs, int num_q_heads, int num_kv_heads,
                                          int head_dim, int block_size, int max_blocks_per_seq,
                                          int max_context_len, int partition_size, int dtype) {
-    const Plan pl = plan_decode(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
+    const pkv::DecodePlan pl = pkv::plan_decode(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
                                 max_blocks_per_seq, max_context_len, partition_size, dtype);
     if (pl.status != PAGED_KV_OK) return (size_t)-1;
-    return workspace_for(pl, num_seqs, num_q_heads, head_dim);
+    return pkv::decode_workspace_bytes(pl, num_seqs, num_q_heads, head_dim);
 }
 
 int paged_attn_decode(const void *query, const void *key_cache, const void *value_cache,
@@ -187,7 +67,7 @@ int paged_attn_decode(const void *query, const void *key_cache, const void *valu
                       int block_size, int num_blocks, int max_blocks_per_seq,
                       int max_context_len, int partition_size, int dtype, void *workspace,
                       size_t workspace_bytes, void *stream) {
-    const Plan pl = plan_decode(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
+    const pkv::DecodePlan pl = pkv::plan_decode(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
                                 max_blocks_per_seq, max_context_len, partition_size, dtype);
     if (pl.status != PAGED_KV_OK) return pl.status;
     if (num_blocks < 1 || !isfinite(scale)) return PAGED_KV_ERR_BAD_SHAPE;
@@ -197,7 +77,7 @@ int paged_attn_decode(const void *query, const void *key_cache, const void *valu
     if (!aligned16(query) || !aligned16(key_cache) || !aligned16(value_cache) ||
         !aligned16(out) || !aligned4(block_tables) || !aligned4(context_lens))
         return PAGED_KV_ERR_BAD_SHAPE;
-    const size_t need = workspace_for(pl, num_seqs, num_q_heads, head_dim);
+    const size_t need = pkv::decode_workspace_bytes(pl, num_seqs, num_q_heads, head_dim);
     if (need > 0 && (!workspace || workspace_bytes < need || !aligned16(workspace)))
         return PAGED_KV_ERR_WORKSPACE;
 
@@ -211,7 +91,7 @@ int paged_attn_decode(const void *query, const void *key_cache, const void *valu
     p.block_tables = block_tables;
     p.context_lens = context_lens;
     p.out = out;
-    const size_t nph = partial_floats(num_seqs, num_q_heads) * pl.num_partitions;
+    const size_t nph = pkv::decode_partial_floats(num_seqs, num_q_heads) * pl.num_partitions;
     float *ws = static_cast<float *>(workspace);
     p.part_max = need ? ws : nullptr;
     p.part_sum = need ? ws + nph : nullptr;

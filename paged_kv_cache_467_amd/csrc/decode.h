@@ -2,6 +2,7 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+#include <stddef.h>
 #include <stdint.h>
 
 namespace pkv {
@@ -55,22 +56,21 @@ DeviceOccupancy decode_occupancy(int dtype, int head_dim, int group, int block_s
 // Which decode kernel launch_decode uses for this shape.
 int decode_kernel_choice(int dtype, int head_dim, int group);
 
-hipError_t launch_kv_cache_write(const void *key, const void *value, const int32_t *slot_mapping,
-                                 void *key_cache, void *value_cache, int num_tokens,
-                                 int row_bytes, int64_t num_slots, hipStream_t stream);
-
-// Block copy from a source pool pair into a destination pool pair (the
-// same pair for copy-on-write; device and host pools for a swap).
-hipError_t launch_copy_blocks(const void *src_key, const void *src_value, int num_src_blocks,
-                              void *dst_key, void *dst_value, int num_dst_blocks,
-                              const int32_t *block_mapping, int num_pairs, int64_t block_bytes,
-                              hipStream_t stream);
-
-hipError_t launch_paged_kv_gather(const void *key_cache, const void *value_cache,
-                                  const int32_t *block_tables, const int32_t *context_lens,
-                                  void *out_key, void *out_value, int num_seqs,
-                                  int max_blocks_per_seq, int block_size, int num_blocks,
-                                  int max_context_len, int row_bytes, int elem_bytes,
-                                  hipStream_t stream);
+// Host-side plan of one decode launch (decode_plan.cpp): status, the
+// context bound, the partition size and count, and kv heads per workgroup.
+struct DecodePlan {
+    int status;
+    int max_context_len;
+    int partition_size;
+    int num_partitions;
+    int heads_per_group;  // kv heads per decode workgroup (one wave each)
+};
+DecodePlan plan_decode(int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
+                       int block_size, int max_blocks_per_seq, int max_context_len,
+                       int partition_size, int dtype);
+// Floats per partition in each split-scratch array (rounded for alignment),
+// and the workspace bytes the plan needs (0 without a split).
+size_t decode_partial_floats(int num_seqs, int num_q_heads);
+size_t decode_workspace_bytes(const DecodePlan &pl, int num_seqs, int num_q_heads, int head_dim);
 
 }  // namespace pkv

@@ -17,7 +17,7 @@
 //
 // All three are bit copies done with 16-byte vector loads and stores.
 
-#include "decode.h"
+#include "kv_ops.h"
 #include "device_utils.h"
 
 namespace pkv {

@@ -37,7 +37,6 @@
 // Causal masking: position t is masked for a row whose position is below t;
 // tiles past a wave's last row position are skipped by that wave.
 
-#include "decode.h"
 #include "device_utils.h"
 #include "prefill.h"
 
