@@ -45,6 +45,7 @@ class Oracle:
             "oracle_paged_kv_gather": [vp, vp, vp, vp, vp, vp] + [ci] * 7,
             "oracle_copy_blocks": [vp, vp, vp] + [ci] * 5,
             "oracle_swap_blocks": [vp, vp, ci, vp, vp, ci, vp] + [ci] * 5,
+            "oracle_prefix_block_hashes": [vp, ci, ci, ctypes.c_uint64, ctypes.c_uint64, vp],
             "oracle_paged_attention_prefill": [vp] * 6 + [cf] + [ci] * 7 + [vp],
             "oracle_elements_to_double": [vp, ctypes.c_int64, ci, vp],
             "oracle_set_threads": [ci],
@@ -161,6 +162,38 @@ class Oracle:
         self.lib.oracle_swap_blocks(_ptr(src_key), _ptr(src_value), ns, _ptr(dst_key),
                                     _ptr(dst_value), dst_key.shape[0], _ptr(bm), bm.shape[0],
                                     Hkv, D, bs, _code(dtype))
+
+    def prefix_block_hashes(self, tokens, block_size, seed, base):
+        """Chained prefix hashes of one token sequence, one per full block:
+        out[k] is the polynomial hash (mod 2^61 - 1, from ``seed``, Horner's
+        rule with ``base``, token t entering as t + 1) of the first
+        (k + 1) * block_size tokens.  Returns uint64 [len(tokens) // bs]."""
+        t = np.ascontiguousarray(tokens, dtype=np.int32)
+        out = np.zeros(t.size // block_size, dtype=np.uint64)
+        if out.size:
+            self.lib.oracle_prefix_block_hashes(_ptr(t), t.size, block_size, seed, base,
+                                                _ptr(out))
+        return out
+
+    @staticmethod
+    def prefix_match(block_hashes, block_start, cached):
+        """Longest cached prefix of each sequence.  block_hashes holds the
+        full-block hashes of all sequences, sequence s owning entries
+        block_start[s] .. block_start[s+1] - 1 in order; cached maps a hash
+        to the block that holds it.  Returns (blocks, lengths): lengths[s] =
+        the number of leading blocks of s whose hashes are all cached, and
+        blocks[block_start[s] + k] = cached[hash] for k < lengths[s] (-1
+        elsewhere)."""
+        blocks = np.full(len(block_hashes), -1, dtype=np.int32)
+        lengths = np.zeros(len(block_start) - 1, dtype=np.int32)
+        for s in range(len(block_start) - 1):
+            for i in range(int(block_start[s]), int(block_start[s + 1])):
+                h = int(block_hashes[i])
+                if h not in cached:
+                    break
+                blocks[i] = cached[h]
+                lengths[s] += 1
+        return blocks, lengths
 
     # ---- conveniences on a workloads.DecodeBatch ----
     def decode_batch(self, batch, *, return_weights=False):

@@ -44,6 +44,15 @@
  *    a block of its own ("23.1 vLLM：高吞吐推理框架原理与部署", §二.3).  Each
  *    (src, dst) pair copies every slot of physical block src to block dst,
  *    in both pools; a negative id skips the pair.
+ *  - Prefix hashing: requests whose token prefix is identical reuse the KV
+ *    blocks already computed for it; the prefix of each full block is
+ *    hashed, chained to everything before it, so that any change anywhere
+ *    in the prompt changes the hashes from that block on
+ *    ("大模型推理框架VLLM-0.7.3源码", §2.3 and §4.2).  The pages fix no hash
+ *    function; the one used here is the polynomial hash of the token
+ *    sequence modulo the prime 2^61 - 1, evaluated by Horner's rule from a
+ *    seed: h(empty) = seed, h(prefix, t) = h(prefix) * base + t + 1, and
+ *    full block k's hash is h of the first (k + 1) * block_size tokens.
  *  - Block swap: when GPU memory runs short the scheduler preempts a
  *    sequence and moves its KV blocks out to CPU memory rather than
  *    refusing work, and a swapped sequence goes back to running first once
@@ -381,6 +390,31 @@ void oracle_swap_blocks(const void *src_key, const void *src_value, int num_src_
                bytes);
         memcpy((char *)dst_value + (size_t)to * bytes,
                (const char *)src_value + (size_t)from * bytes, bytes);
+    }
+}
+
+/*
+ * Prefix hashes of one token sequence: out[k] = h(tokens[0 .. (k+1)*bs - 1])
+ * for every full block k (num_tokens / block_size of them), with
+ * h(empty) = seed mod P and h(prefix, t) = (h(prefix) * base + t + 1) mod P,
+ * P = 2^61 - 1, a token read as an unsigned 32-bit value.
+ */
+#define ORACLE_HASH_P ((((uint64_t)1) << 61) - 1)
+
+static uint64_t mulmod_p61(uint64_t a, uint64_t b)
+{
+    return (uint64_t)(((unsigned __int128)a * b) % ORACLE_HASH_P);
+}
+
+void oracle_prefix_block_hashes(const int32_t *tokens, int num_tokens, int block_size,
+                                uint64_t seed, uint64_t base, uint64_t *out)
+{
+    uint64_t h = seed % ORACLE_HASH_P;
+    for (int i = 0; i < num_tokens; ++i) {
+        h = (mulmod_p61(h, base % ORACLE_HASH_P) + (uint64_t)(uint32_t)tokens[i] + 1) %
+            ORACLE_HASH_P;
+        if ((i + 1) % block_size == 0)
+            out[i / block_size] = h;
     }
 }
 

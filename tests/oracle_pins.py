@@ -408,6 +408,69 @@ def pin_swap_blocks(orc):
         assert not rk[untouched].any() and not rv[untouched].any()
 
 
+P61 = (1 << 61) - 1
+
+
+def _hash_closed_form(tokens, n, seed, base):
+    """seed * base^n + sum_i (t_i + 1) * base^(n-1-i) mod 2^61 - 1 over the
+    first n tokens, with Python integers and modular powers (no Horner)."""
+    acc = (seed % P61) * pow(base, n, P61)
+    for i in range(n):
+        acc += (int(tokens[i]) % (1 << 32) + 1) * pow(base, n - 1 - i, P61)
+    return acc % P61
+
+
+def pin_prefix_hashes(orc):
+    """Prefix hashing for automatic prefix caching ("大模型推理框架VLLM-0.7.3源码",
+    §2.3 and §4.2): every full block's hash equals the closed form of the
+    polynomial hash of the prefix it ends; a trailing partial block has no
+    hash; a changed token changes the hash of its block and of every later
+    block, never an earlier one; two sequences that share a prefix share its
+    block hashes whatever follows; random distinct prefixes hash apart."""
+    rng = np.random.default_rng(31)
+    for bs, base, seed in ((16, 0x1C6A8B2F3E5D7093, 0), (4, 3, 12345), (1, P61 - 2, P61 + 7)):
+        n = 7 * bs + bs - 1
+        toks = rng.integers(0, 152064, size=n).astype(np.int32)
+        toks[2] = -5                                   # read as an unsigned 32-bit value
+        toks[min(5, n - 1)] = 0                        # token 0 still counts
+        h = orc.prefix_block_hashes(toks, bs, seed, base)
+        assert h.shape == (n // bs,) and h.dtype == np.uint64
+        for k in range(h.size):
+            assert int(h[k]) == _hash_closed_form(toks, (k + 1) * bs, seed, base), (bs, k)
+        i = 3 * bs + bs // 2
+        t2 = toks.copy()
+        t2[i] += 1
+        h2 = orc.prefix_block_hashes(t2, bs, seed, base)
+        kb = i // bs
+        assert np.array_equal(h2[:kb], h[:kb]) and np.all(h2[kb:] != h[kb:])
+    bs = 16
+    prefix = rng.integers(0, 50000, size=3 * bs).astype(np.int32)
+    a = np.concatenate([prefix, rng.integers(0, 50000, size=2 * bs).astype(np.int32)])
+    b = np.concatenate([prefix, rng.integers(0, 50000, size=bs + 5).astype(np.int32)])
+    ha = orc.prefix_block_hashes(a, bs, 0, 1000003)
+    hb = orc.prefix_block_hashes(b, bs, 0, 1000003)
+    assert hb.size == 4 and np.array_equal(ha[:3], hb[:3]) and ha[3] != hb[3]
+    hs = np.concatenate([orc.prefix_block_hashes(rng.integers(0, 50000, size=8 * bs), bs, 0,
+                                                 1000003) for _ in range(200)])
+    assert len(set(int(x) for x in hs)) == hs.size
+
+
+def pin_prefix_match(orc):
+    """The longest cached prefix: a sequence reuses its leading blocks while
+    their hashes are cached and stops at the first miss, even if later
+    blocks' hashes are cached too; a sequence whose first block differs
+    reuses nothing (a prefix hit needs the whole prefix to match,
+    "大模型推理框架VLLM-0.7.3源码", §4.2)."""
+    h = np.array([11, 12, 13, 14, 21, 12, 31, 32, 33], dtype=np.uint64)
+    start = np.array([0, 4, 6, 9], dtype=np.int32)
+    cached = {11: 5, 12: 6, 13: 7, 32: 9, 33: 8}
+    blocks, lengths = orc.prefix_match(h, start, cached)
+    assert list(lengths) == [3, 0, 0]
+    assert list(blocks) == [5, 6, 7, -1, -1, -1, -1, -1, -1]
+    blocks, lengths = orc.prefix_match(h, start, {**cached, 14: 2, 31: 4})
+    assert list(lengths) == [4, 0, 3] and list(blocks[6:]) == [4, 9, 8]
+
+
 # ------------------------------------------------------ multi-token (prefill)
 PREFILL_SHAPES = [
     # seed, dtype, Hq, Hkv, D, bs, context lens, query lens
@@ -504,7 +567,7 @@ ALL_PINS = [
     pin_context_len_one, pin_identical_keys, pin_two_token_logistic, pin_weights_sum_to_one,
     pin_block_permutation, pin_gqa_equals_mha, pin_split_merge, pin_poison_unreferenced,
     pin_large_scores, pin_empty_context, pin_linear_in_values, pin_copy_blocks,
-    pin_swap_blocks,
+    pin_swap_blocks, pin_prefix_hashes, pin_prefix_match,
     pin_prefill_vs_sdpa, pin_prefill_one_token_is_decode, pin_prefill_causal,
     pin_prefill_block_permutation,
 ]

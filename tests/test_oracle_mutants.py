@@ -66,6 +66,12 @@ MUTANTS = {
                       "(const char *)src_key + (size_t)from * bytes"),
     # block swap: off-by-one range check (reads one block past the source)
     "swap_range": ("from >= num_src_blocks", "from > num_src_blocks"),
+    # prefix hash: token t enters as t instead of t + 1
+    "hash_plus_one_dropped": ("+ (uint64_t)(uint32_t)tokens[i] + 1)", "+ (uint64_t)(uint32_t)tokens[i])"),
+    # prefix hash: a block's hash taken one token early
+    "hash_boundary": ("if ((i + 1) % block_size == 0)", "if ((i + 2) % block_size == 0)"),
+    # prefix hash: seed ignored
+    "hash_seed_ignored": ("uint64_t h = seed % ORACLE_HASH_P;", "uint64_t h = 0;"),
     # gather: value rows taken from the key pool
     "gather_v_from_k": ("memcpy((char *)out_v + dst * element_bytes(dtype),\n                   (const char *)value_cache",
                         "memcpy((char *)out_v + dst * element_bytes(dtype),\n                   (const char *)key_cache"),
