@@ -187,6 +187,98 @@ def bench_copy_blocks(args) -> int:
     return 0
 
 
+def bench_prefix_cache(args) -> int:
+    """Prefix caching on the shared-system-prompt workload: each step hashes
+    every full block of the 256 requests and looks up each request's
+    longest cached prefix in a table that holds the blocks of 16 earlier
+    requests and 400 000 other cached blocks (40% full).  value = tokens
+    handled per second; the roofline figure is the hash kernel's bytes
+    (tokens read, hashes written) over its own time."""
+    import numpy as np
+    import torch
+
+    import oracle
+    from paged_kv_cache_467_amd import binding, workloads as W
+
+    dev = torch.device("cuda:0")
+    b = W.make_prefix_workload("shared_system_prompt_rag")
+    i32 = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).to(dev)
+    toks, ts, bst = i32(b.tokens), i32(b.token_start), i32(b.block_start)
+    nb = b.total_blocks
+    hashes = torch.zeros(nb, dtype=torch.int64, device=dev)
+    binding.paged_kv_prefix_hash(toks, ts, bst, b.block_size, hashes)
+    cap_log2 = 20
+    tk, tb = binding.new_prefix_table(cap_log2, dev)
+    warm = hashes[:int(b.block_start[16])]
+    binding.paged_kv_prefix_insert(warm, torch.arange(warm.numel(), dtype=torch.int32, device=dev),
+                                   tk, tb)
+    rng = np.random.default_rng(46721)
+    filler = rng.integers(0, (1 << 61) - 1, size=400_000, dtype=np.int64)
+    binding.paged_kv_prefix_insert(torch.from_numpy(filler).to(dev),
+                                   torch.zeros(filler.size, dtype=torch.int32, device=dev), tk, tb)
+    mb = torch.full((nb,), -1, dtype=torch.int32, device=dev)
+    ml = torch.zeros(b.num_seqs, dtype=torch.int32, device=dev)
+    torch.cuda.synchronize()
+
+    def step(_):
+        binding.paged_kv_prefix_hash(toks, ts, bst, b.block_size, hashes)
+        binding.paged_kv_prefix_match(hashes, bst, tk, tb, mb, ml)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for e in ev:
+        e[0].record()
+        binding.paged_kv_prefix_hash(toks, ts, bst, b.block_size, hashes)
+        e[1].record()
+        binding.paged_kv_prefix_match(hashes, bst, tk, tb, mb, ml)
+        e[2].record()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    hash_ms = sum(e[0].elapsed_time(e[1]) for e in ev) / len(ev)
+    match_ms = sum(e[1].elapsed_time(e[2]) for e in ev) / len(ev)
+    ntok = len(b.tokens)
+    tok_per_s = ntok / ((hash_ms + match_ms) * 1e-3)
+    hash_bytes = ntok * 4 + nb * 8 + 2 * 4 * (b.num_seqs + 1)
+    achieved = hash_bytes / (hash_ms * 1e-3) / 1e9
+    matched = int(ml.sum().item())
+    result = {
+        "metric": "prefix-cache block hashing + longest-prefix lookup: tokens/s",
+        "value": round(tok_per_s, 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(elapsed * 1e3 / args.steps, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "int32",
+        "data": "synthetic",
+        "config": {"workload": b.name, "requests": b.num_seqs, "tokens": ntok,
+                   "block_size": b.block_size, "full_blocks": nb,
+                   "table_slots": 1 << cap_log2, "matched_blocks": matched},
+        "hash_ms": round(hash_ms, 5), "match_ms": round(match_ms, 5),
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBPS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None,
+                     "kernel": "paged_kv_prefix_hash", "algorithmic_bytes_per_launch": hash_bytes},
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        base = 0x1C6A8B2F3E5D7093  # the hash base the library documents
+        times = []
+        while len(times) < 3 or sum(times) < 2.0:
+            t1 = time.perf_counter()
+            ref = np.concatenate([oracle.prefix_block_hashes(b.seq_tokens(s), b.block_size, 0,
+                                                             base)
+                                  for s in range(b.num_seqs)])
+            cached = {int(h): i for i, h in enumerate(ref[:int(b.block_start[16])])}
+            oracle.prefix_match(ref, b.block_start, cached)
+            times.append(time.perf_counter() - t1)
+        t = statistics.median(times)
+        result["cpu_baseline"] = {"value": round(ntok / t, 1), "unit": "tokens/s", "cores": 1,
+                                  "kind": "oracle",
+                                  "sample": f"the whole workload (hash in C, match in Python), "
+                                            f"median of {len(times)} runs"}
+    print(json.dumps(result), flush=True)
+    return 0
+
+
 # MI355X host link: PCIe 5.0 x16, 32 GT/s on each of 16 lanes = 64 GB/s per
 # direction before encoding and packet overheads.
 HOST_LINK_PEAK_GBPS = 64.0
@@ -400,12 +492,14 @@ def main() -> int:
     ap.add_argument("--copies", type=int, default=4, help="pool copies rotated across steps")
     ap.add_argument("--partition-size", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--op", choices=("decode", "copy_blocks", "prefill", "swap_out", "swap_in"),
+    ap.add_argument("--op", choices=("decode", "copy_blocks", "prefill", "swap_out", "swap_in",
+                                     "prefix_cache"),
                     default="decode",
                     help="decode: the decode step (default); copy_blocks: the copy-on-write "
                          "block copy on the same pool; prefill: multi-token attention on the "
                          "chunked-prefill workload; swap_out / swap_in: block swap between the "
-                         "pool and pinned host memory")
+                         "pool and pinned host memory; prefix_cache: block hashing and "
+                         "cached-prefix lookup")
     ap.add_argument("--pairs", type=int, default=2048, help="block pairs per copy_blocks step")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="also run one plain device copy of this many MiB (counter calibration)")
@@ -429,6 +523,8 @@ def main() -> int:
     torch.manual_seed(0)
     if args.op in ("swap_out", "swap_in"):
         return bench_swap(args)
+    if args.op == "prefix_cache":
+        return bench_prefix_cache(args)
     if args.op == "copy_blocks":
         return bench_copy_blocks(args)
     if args.op == "prefill":

@@ -261,6 +261,77 @@ PAGED_KV_API int paged_kv_swap_in(
     int head_dim, int block_size, int num_blocks, int num_host_blocks, int dtype, void *stream);
 
 /*
+ * Prefix caching: requests whose token prefix is identical reuse the KV
+ * blocks already computed for it.  Each full block is identified by a hash
+ * of the block together with everything before it, so any change in a
+ * prompt changes the hashes from that block on and only whole identical
+ * prefixes hit ("大模型推理框架VLLM-0.7.3源码", §2.3 and §4.2; the shared
+ * system prompt of "23.1 vLLM：高吞吐推理框架原理与部署").
+ *
+ * The hash (the pages fix none): the polynomial hash of the token prefix
+ * modulo the prime P = 2^61 - 1, from a seed, by Horner's rule:
+ *   h(empty) = seed mod P,  h(prefix, t) = (h(prefix) * B + t + 1) mod P
+ * with B = PAGED_KV_PREFIX_HASH_BASE and each token read as an unsigned
+ * 32-bit value; full block k of a sequence hashes to h of the sequence's
+ * first (k + 1) * block_size tokens.  Every hash is below 2^61 - 1.  The seed
+ * keeps hashes of different namespaces (models, adapters) apart.
+ */
+#define PAGED_KV_PREFIX_HASH_BASE 0x1C6A8B2F3E5D7093ull
+/* The key of an empty slot of a prefix table: every key slot starts as this. */
+#define PAGED_KV_PREFIX_EMPTY_KEY 0xFFFFFFFFFFFFFFFFull
+
+/*
+ * Hashes of every full block of a batch of token sequences.
+ *   tokens       [total_tokens] int32, the sequences one after another
+ *   token_start  [num_seqs + 1] int32: sequence s holds tokens
+ *                token_start[s] .. token_start[s+1] - 1
+ *   block_start  [num_seqs + 1] int32: sequence s's hashes go to
+ *                block_hashes[block_start[s] ..] (prefix sums of the full-block
+ *                counts, computed by the caller)
+ *   block_hashes [total_blocks] uint64, written: block_hashes[block_start[s]
+ *                + k] for k < min(full blocks of s, block_start[s+1] -
+ *                block_start[s]); a trailing partial block has no hash and
+ *                other slots are left as they are
+ * All device memory.  Device-side values: a sequence whose token_start or
+ * block_start range leaves its array or decreases is skipped.
+ * block_size in [1, 4096].
+ */
+PAGED_KV_API int paged_kv_prefix_hash(
+    const int32_t *tokens, const int32_t *token_start, const int32_t *block_start, int num_seqs,
+    int total_tokens, int total_blocks, int block_size, uint64_t seed, uint64_t *block_hashes,
+    void *stream);
+
+/*
+ * Record cached blocks: entry i maps hashes[i] to physical block blocks[i]
+ * in an open-addressing table of 2^capacity_log2 slots (linear probing from
+ * slot hash mod capacity).  table_keys [capacity] uint64 (every slot starts
+ * as PAGED_KV_PREFIX_EMPTY_KEY), table_blocks [capacity] int32, caller-owned
+ * device memory, updated in place.  stored [num_entries] int32 (device,
+ * optional): 1 = inserted, 0 = the hash was already there (the block stored
+ * first stays), -1 = no free slot or not a hash value (>= 2^61 - 1).
+ * Entries run in parallel: two entries with one hash leave either block.
+ * capacity_log2 in [1, 30]; keep the table at most about half full.
+ */
+PAGED_KV_API int paged_kv_prefix_insert(
+    const uint64_t *hashes, const int32_t *blocks, int num_entries, uint64_t *table_keys,
+    int32_t *table_blocks, int capacity_log2, int32_t *stored, void *stream);
+
+/*
+ * The longest cached prefix of each sequence: matched_len[s] = the number of
+ * leading blocks of s (block_hashes[block_start[s]], [block_start[s] + 1],
+ * ...) whose hashes are all in the table, and matched_blocks[block_start[s]
+ * + k] = the cached block for k < matched_len[s] (the entries after are
+ * left as they are).  The walk stops at the first uncached block even when
+ * later hashes are cached.  All device memory; matched_blocks [total_blocks]
+ * int32, matched_len [num_seqs] int32.  A sequence whose block_start range
+ * leaves the array or decreases matches nothing.
+ */
+PAGED_KV_API int paged_kv_prefix_match(
+    const uint64_t *block_hashes, const int32_t *block_start, int num_seqs, int total_blocks,
+    const uint64_t *table_keys, const int32_t *table_blocks, int capacity_log2,
+    int32_t *matched_blocks, int32_t *matched_len, void *stream);
+
+/*
  * Materialise each sequence's logical K/V through its block table (the
  * addressing of paged_attn_decode, as a bit copy); used to check the
  * addressing on its own.

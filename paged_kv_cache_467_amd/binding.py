@@ -31,6 +31,9 @@ EXPORTED = (
     "paged_attn_prefill",
     "paged_kv_swap_out",
     "paged_kv_swap_in",
+    "paged_kv_prefix_hash",
+    "paged_kv_prefix_insert",
+    "paged_kv_prefix_match",
 )
 
 
@@ -59,6 +62,12 @@ def _load_library(path: str = LIBRARY) -> ctypes.CDLL:
     lib.paged_attn_prefill.restype = ci
     for name in ("paged_kv_swap_out", "paged_kv_swap_in"):
         getattr(lib, name).argtypes = [vp] * 5 + [ci] * 7 + [vp]
+        getattr(lib, name).restype = ci
+    u64 = ctypes.c_uint64
+    lib.paged_kv_prefix_hash.argtypes = [vp] * 3 + [ci] * 4 + [u64, vp, vp]
+    lib.paged_kv_prefix_insert.argtypes = [vp, vp, ci, vp, vp, ci, vp, vp]
+    lib.paged_kv_prefix_match.argtypes = [vp, vp, ci, ci, vp, vp, ci, vp, vp, vp]
+    for name in ("paged_kv_prefix_hash", "paged_kv_prefix_insert", "paged_kv_prefix_match"):
         getattr(lib, name).restype = ci
     return lib
 
@@ -311,3 +320,82 @@ def paged_kv_swap_in(host_key_cache: torch.Tensor, host_value_cache: torch.Tenso
         _dev(block_mapping, "block_mapping"), block_mapping.shape[0], Hkv, D, bs, nb, nh,
         _dtype_code(key_cache), _stream(key_cache.device))
     _check("paged_kv_swap_in", status)
+
+
+# ---- prefix caching (see paged_kv_prefix_* in include/paged_kv.h) ----
+# Hashes and table keys travel in int64 tensors holding the unsigned values
+# (a hash is below 2^61 - 1; an empty table slot reads as -1).
+PREFIX_EMPTY_KEY = -1
+
+
+def _int_tensor(t: torch.Tensor, dtype, name: str) -> int:
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    return _dev(t, name)
+
+
+def new_prefix_table(capacity_log2: int, device="cuda"):
+    """An empty prefix table of 2**capacity_log2 slots: (keys, blocks)."""
+    n = 1 << capacity_log2
+    return (torch.full((n,), PREFIX_EMPTY_KEY, dtype=torch.int64, device=device),
+            torch.full((n,), -1, dtype=torch.int32, device=device))
+
+
+def _capacity_log2(table_keys: torch.Tensor, table_blocks: torch.Tensor) -> int:
+    n = table_keys.numel()
+    if n < 2 or n & (n - 1) or table_blocks.numel() != n:
+        raise ValueError("the table needs a power-of-two number of slots (>= 2) in both arrays")
+    return n.bit_length() - 1
+
+
+def paged_kv_prefix_hash(tokens: torch.Tensor, token_start: torch.Tensor,
+                         block_start: torch.Tensor, block_size: int, block_hashes: torch.Tensor,
+                         seed: int = 0) -> None:
+    """Chained hashes of every full block of a batch of token sequences
+    (int32 tokens, int32 [S+1] token_start / block_start) into the int64
+    tensor block_hashes."""
+    S = token_start.numel() - 1
+    if S < 0 or block_start.numel() != S + 1:
+        raise ValueError("token_start and block_start need num_seqs + 1 entries")
+    status = _lib.paged_kv_prefix_hash(
+        _int_tensor(tokens, torch.int32, "tokens"),
+        _int_tensor(token_start, torch.int32, "token_start"),
+        _int_tensor(block_start, torch.int32, "block_start"), S, tokens.numel(),
+        block_hashes.numel(), block_size, int(seed) & ((1 << 64) - 1),
+        _int_tensor(block_hashes, torch.int64, "block_hashes"), _stream(tokens.device))
+    _check("paged_kv_prefix_hash", status)
+
+
+def paged_kv_prefix_insert(hashes: torch.Tensor, blocks: torch.Tensor, table_keys: torch.Tensor,
+                           table_blocks: torch.Tensor, stored: torch.Tensor | None = None) -> None:
+    """Record (hash -> block) entries in the table; optional int32 stored
+    receives 1 (inserted), 0 (already there) or -1 (no free slot)."""
+    if blocks.numel() != hashes.numel() or (stored is not None and stored.numel() != hashes.numel()):
+        raise ValueError("hashes, blocks and stored must have one entry each")
+    status = _lib.paged_kv_prefix_insert(
+        _int_tensor(hashes, torch.int64, "hashes"), _int_tensor(blocks, torch.int32, "blocks"),
+        hashes.numel(), _int_tensor(table_keys, torch.int64, "table_keys"),
+        _int_tensor(table_blocks, torch.int32, "table_blocks"),
+        _capacity_log2(table_keys, table_blocks),
+        None if stored is None else _int_tensor(stored, torch.int32, "stored"),
+        _stream(hashes.device))
+    _check("paged_kv_prefix_insert", status)
+
+
+def paged_kv_prefix_match(block_hashes: torch.Tensor, block_start: torch.Tensor,
+                          table_keys: torch.Tensor, table_blocks: torch.Tensor,
+                          matched_blocks: torch.Tensor, matched_len: torch.Tensor) -> None:
+    """Longest cached prefix of each sequence: matched_len [S] int32 and the
+    cached blocks in matched_blocks (int32, laid out like block_hashes)."""
+    S = block_start.numel() - 1
+    if S < 0 or matched_len.numel() != S or matched_blocks.numel() != block_hashes.numel():
+        raise ValueError("matched_len needs num_seqs entries, matched_blocks one per hash")
+    status = _lib.paged_kv_prefix_match(
+        _int_tensor(block_hashes, torch.int64, "block_hashes"),
+        _int_tensor(block_start, torch.int32, "block_start"), S, block_hashes.numel(),
+        _int_tensor(table_keys, torch.int64, "table_keys"),
+        _int_tensor(table_blocks, torch.int32, "table_blocks"),
+        _capacity_log2(table_keys, table_blocks),
+        _int_tensor(matched_blocks, torch.int32, "matched_blocks"),
+        _int_tensor(matched_len, torch.int32, "matched_len"), _stream(block_start.device))
+    _check("paged_kv_prefix_match", status)

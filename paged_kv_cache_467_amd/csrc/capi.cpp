@@ -14,6 +14,7 @@
 #include "decode.h"
 #include "kv_ops.h"
 #include "prefill.h"
+#include "prefix_cache.h"
 
 namespace {
 
@@ -316,6 +317,68 @@ int paged_kv_gather(const void *key_cache, const void *value_cache,
         key_cache, value_cache, block_tables, context_lens, out_key, out_value, num_seqs,
         max_blocks_per_seq, block_size, num_blocks, max_context_len, (int)row,
         elem_bytes(dtype), static_cast<hipStream_t>(stream));
+    return err == hipSuccess ? PAGED_KV_OK : PAGED_KV_ERR_HIP;
+}
+
+
+int paged_kv_prefix_hash(const int32_t *tokens, const int32_t *token_start,
+                         const int32_t *block_start, int num_seqs, int total_tokens,
+                         int total_blocks, int block_size, uint64_t seed, uint64_t *block_hashes,
+                         void *stream) {
+    if (num_seqs < 0 || num_seqs > 0x7fffffff - 1 || total_tokens < 0 || total_blocks < 0 ||
+        block_size < 1 || block_size > 4096)
+        return PAGED_KV_ERR_BAD_SHAPE;
+    if (num_seqs == 0) return PAGED_KV_OK;
+    if (!token_start || !block_start || (total_tokens > 0 && !tokens) ||
+        (total_blocks > 0 && !block_hashes))
+        return PAGED_KV_ERR_NULL_POINTER;
+    if (!aligned4(tokens) || !aligned4(token_start) || !aligned4(block_start) ||
+        (reinterpret_cast<uintptr_t>(block_hashes) & 7u) != 0)
+        return PAGED_KV_ERR_BAD_SHAPE;
+    // base^block_size mod 2^61 - 1, the factor that carries a hash over one block
+    const unsigned __int128 p = (((unsigned __int128)1) << 61) - 1;
+    unsigned __int128 m = 1;
+    for (int i = 0; i < block_size; ++i) m = m * PAGED_KV_PREFIX_HASH_BASE % p;
+    const hipError_t err = pkv::launch_prefix_hash(
+        tokens, token_start, block_start, num_seqs, total_tokens, total_blocks, block_size, seed,
+        PAGED_KV_PREFIX_HASH_BASE, (uint64_t)m, block_hashes, static_cast<hipStream_t>(stream));
+    return err == hipSuccess ? PAGED_KV_OK : PAGED_KV_ERR_HIP;
+}
+
+int paged_kv_prefix_insert(const uint64_t *hashes, const int32_t *blocks, int num_entries,
+                           uint64_t *table_keys, int32_t *table_blocks, int capacity_log2,
+                           int32_t *stored, void *stream) {
+    if (num_entries < 0 || capacity_log2 < 1 || capacity_log2 > 30) return PAGED_KV_ERR_BAD_SHAPE;
+    if (num_entries == 0) return PAGED_KV_OK;
+    if (!hashes || !blocks || !table_keys || !table_blocks) return PAGED_KV_ERR_NULL_POINTER;
+    if ((reinterpret_cast<uintptr_t>(hashes) & 7u) != 0 ||
+        (reinterpret_cast<uintptr_t>(table_keys) & 7u) != 0 || !aligned4(blocks) ||
+        !aligned4(table_blocks) || !aligned4(stored))
+        return PAGED_KV_ERR_BAD_SHAPE;
+    const hipError_t err =
+        pkv::launch_prefix_insert(hashes, blocks, num_entries, table_keys, table_blocks,
+                                  capacity_log2, stored, static_cast<hipStream_t>(stream));
+    return err == hipSuccess ? PAGED_KV_OK : PAGED_KV_ERR_HIP;
+}
+
+int paged_kv_prefix_match(const uint64_t *block_hashes, const int32_t *block_start,
+                          int num_seqs, int total_blocks, const uint64_t *table_keys,
+                          const int32_t *table_blocks, int capacity_log2, int32_t *matched_blocks,
+                          int32_t *matched_len, void *stream) {
+    if (num_seqs < 0 || num_seqs > 0x7fffffff - 1 || total_blocks < 0 || capacity_log2 < 1 ||
+        capacity_log2 > 30)
+        return PAGED_KV_ERR_BAD_SHAPE;
+    if (num_seqs == 0) return PAGED_KV_OK;
+    if (!block_start || !table_keys || !table_blocks || !matched_len ||
+        (total_blocks > 0 && (!block_hashes || !matched_blocks)))
+        return PAGED_KV_ERR_NULL_POINTER;
+    if ((reinterpret_cast<uintptr_t>(block_hashes) & 7u) != 0 ||
+        (reinterpret_cast<uintptr_t>(table_keys) & 7u) != 0 || !aligned4(block_start) ||
+        !aligned4(table_blocks) || !aligned4(matched_blocks) || !aligned4(matched_len))
+        return PAGED_KV_ERR_BAD_SHAPE;
+    const hipError_t err = pkv::launch_prefix_match(
+        block_hashes, block_start, num_seqs, total_blocks, table_keys, table_blocks, capacity_log2,
+        matched_blocks, matched_len, static_cast<hipStream_t>(stream));
     return err == hipSuccess ? PAGED_KV_OK : PAGED_KV_ERR_HIP;
 }
 

@@ -434,3 +434,68 @@ def permute_blocks(batch: DecodeBatch, seed: int) -> DecodeBatch:
     out.slot_mapping = new_sl.astype(np.int32)
     out.referenced_blocks = np.sort(pi[batch.referenced_blocks])
     return out
+
+
+# ---- prefix caching ----
+@dataclass
+class PrefixBatch:
+    """Token sequences for prefix-cache hashing: tokens one after another,
+    token_start [S+1] and block_start [S+1] (prefix sums of full-block
+    counts)."""
+    name: str
+    block_size: int
+    tokens: np.ndarray       # [T] int32
+    token_start: np.ndarray  # [S + 1] int32
+    block_start: np.ndarray  # [S + 1] int32
+    shared_blocks: int       # full blocks of the prompt every sequence starts with
+
+    @property
+    def num_seqs(self) -> int:
+        return len(self.token_start) - 1
+
+    @property
+    def total_blocks(self) -> int:
+        return int(self.block_start[-1])
+
+    def seq_tokens(self, s: int) -> np.ndarray:
+        return self.tokens[self.token_start[s]:self.token_start[s + 1]]
+
+
+def make_prefix_batch(seed: int, *, num_seqs=256, block_size=16, system_len=512,
+                      doc_len=1024, num_docs=8, doc_share=0.5, suffix=(64, 1024),
+                      vocab=152064, name="prefix") -> PrefixBatch:
+    """Requests that all begin with one system prompt of system_len tokens
+    (the pages' long shared system prompt); a doc_share fraction of them
+    then carry one of num_docs retrieved documents of doc_len tokens (the
+    RAG case, documents placed right after the prompt so that requests on
+    the same document share it), then a private suffix of U{suffix} tokens.
+    Token ids uniform in [0, vocab)."""
+    rng = np.random.default_rng(seed)
+    system = rng.integers(0, vocab, size=system_len).astype(np.int32)
+    docs = [rng.integers(0, vocab, size=doc_len).astype(np.int32) for _ in range(num_docs)]
+    seqs = []
+    for _ in range(num_seqs):
+        parts = [system]
+        if num_docs and rng.random() < doc_share:
+            parts.append(docs[int(rng.integers(0, num_docs))])
+        parts.append(rng.integers(0, vocab, size=int(rng.integers(suffix[0], suffix[1],
+                                                                   endpoint=True))
+                                  ).astype(np.int32))
+        seqs.append(np.concatenate(parts))
+    lens = np.array([len(x) for x in seqs], dtype=np.int64)
+    token_start = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    block_start = np.concatenate([[0], np.cumsum(lens // block_size)]).astype(np.int32)
+    return PrefixBatch(name, block_size, np.concatenate(seqs).astype(np.int32), token_start,
+                       block_start, system_len // block_size)
+
+
+PREFIX_WORKLOADS = ("shared_system_prompt_rag",)
+
+
+def make_prefix_workload(name: str) -> PrefixBatch:
+    """256 requests behind one 512-token system prompt, half of them with
+    one of 8 retrieved 1024-token documents, private suffixes of 64..1024
+    tokens, 16-token blocks."""
+    if name != "shared_system_prompt_rag":
+        raise ValueError(name)
+    return make_prefix_batch(46720, name=name)

@@ -40,6 +40,9 @@ def lib():
     lib.paged_attn_prefill.argtypes = [vp] * 6 + [cf, vp] + [ci] * 11 + [vp]
     for name in ("paged_kv_swap_out", "paged_kv_swap_in"):
         getattr(lib, name).argtypes = [vp] * 5 + [ci] * 7 + [vp]
+    lib.paged_kv_prefix_hash.argtypes = [vp] * 3 + [ci] * 4 + [ctypes.c_uint64, vp, vp]
+    lib.paged_kv_prefix_insert.argtypes = [vp, vp, ci, vp, vp, ci, vp, vp]
+    lib.paged_kv_prefix_match.argtypes = [vp, vp, ci, ci, vp, vp, ci, vp, vp, vp]
     return lib
 
 
@@ -47,7 +50,8 @@ def test_header_declares_the_entry_points():
     assert declared_functions() == sorted([
         "paged_kv_status_string", "paged_attn_decode", "paged_attn_decode_partition_size",
         "paged_attn_decode_workspace_bytes", "kv_cache_write", "paged_kv_gather",
-        "paged_kv_copy_blocks", "paged_attn_prefill", "paged_kv_swap_out", "paged_kv_swap_in"])
+        "paged_kv_copy_blocks", "paged_attn_prefill", "paged_kv_swap_out", "paged_kv_swap_in",
+        "paged_kv_prefix_hash", "paged_kv_prefix_insert", "paged_kv_prefix_match"])
 
 
 def test_library_exports_only_the_entry_points():
@@ -214,3 +218,44 @@ def prefill(lib, **kw):
 ])
 def test_prefill_rejects(lib, kw, status):
     assert prefill(lib, **kw) == status
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(block_size=0), BAD_SHAPE), (dict(block_size=5000), BAD_SHAPE),
+    (dict(num_seqs=-1), BAD_SHAPE), (dict(total_tokens=-4), BAD_SHAPE),
+    (dict(token_start=None), NULLPTR), (dict(block_hashes=None), NULLPTR),
+    (dict(block_hashes=P + 4), BAD_SHAPE), (dict(tokens=P + 2), BAD_SHAPE),
+    (dict(num_seqs=0, tokens=None, token_start=None, block_start=None, block_hashes=None), OK),
+])
+def test_prefix_hash_rejects(lib, kw, status):
+    a = dict(tokens=P, token_start=P, block_start=P, num_seqs=4, total_tokens=100,
+             total_blocks=6, block_size=16, seed=0, block_hashes=P, stream=None)
+    a.update(kw)
+    assert lib.paged_kv_prefix_hash(*a.values()) == status
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(capacity_log2=0), BAD_SHAPE), (dict(capacity_log2=31), BAD_SHAPE),
+    (dict(num_entries=-1), BAD_SHAPE), (dict(table_keys=None), NULLPTR),
+    (dict(hashes=P + 4), BAD_SHAPE), (dict(stored=P + 2), BAD_SHAPE),
+    (dict(num_entries=0, hashes=None, blocks=None, table_keys=None, table_blocks=None), OK),
+])
+def test_prefix_insert_rejects(lib, kw, status):
+    a = dict(hashes=P, blocks=P, num_entries=8, table_keys=P, table_blocks=P, capacity_log2=10,
+             stored=None, stream=None)
+    a.update(kw)
+    assert lib.paged_kv_prefix_insert(*a.values()) == status
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(capacity_log2=0), BAD_SHAPE), (dict(total_blocks=-1), BAD_SHAPE),
+    (dict(matched_len=None), NULLPTR), (dict(block_hashes=None), NULLPTR),
+    (dict(table_keys=P + 4), BAD_SHAPE),
+    (dict(num_seqs=0, block_hashes=None, block_start=None, table_keys=None, table_blocks=None,
+          matched_blocks=None, matched_len=None), OK),
+])
+def test_prefix_match_rejects(lib, kw, status):
+    a = dict(block_hashes=P, block_start=P, num_seqs=4, total_blocks=6, table_keys=P,
+             table_blocks=P, capacity_log2=10, matched_blocks=P, matched_len=P, stream=None)
+    a.update(kw)
+    assert lib.paged_kv_prefix_match(*a.values()) == status
