@@ -47,7 +47,6 @@ namespace {
 
 constexpr int kPrefillThreads = 256;
 constexpr int kPrefillWaves = kPrefillThreads / 64;
-constexpr int kTile = 32;  // tokens per tile: two 16-token halves
 constexpr int kXcds = 8;   // accelerator complex dies of the MI355X, each with its own L2
 // Word 3 of a raw buffer resource on gfx9-family parts (32-bit data format):
 // loads past the stated size return zero.
@@ -59,6 +58,10 @@ __host__ __device__ constexpr int blocks_per_wave(int D) { return D >= 256 ? 1 :
 __host__ __device__ constexpr int rows_per_workgroup(int D) {
     return kPrefillWaves * 16 * blocks_per_wave(D);
 }
+// Positions per tile (one barrier each): 64 -- four 16-token quarters, two
+// 32-token value-product groups -- and 32 for head_dim 256, whose tiles
+// would otherwise leave room in LDS for one workgroup per compute unit.
+__host__ __device__ constexpr int tile_tokens(int D) { return D >= 256 ? 32 : 64; }
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 
@@ -130,6 +133,9 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(PrefillParams 
     constexpr int RPB = rows_per_workgroup(D);
     constexpr int KS = D / 32;            // k-steps of the score MFMA
     constexpr int DB = D / 16;            // 16-wide d blocks of the value MFMA
+    constexpr int TT = tile_tokens(D);    // positions per tile
+    constexpr int NQ = TT / 16;           // 16-token quarters of a tile
+    constexpr int NG = TT / 32;           // 32-token groups of the value MFMA
     // Tile row strides in elements.  The score operand reads 16 rows x 16
     // bytes per pass: a 16-byte pad puts those rows 4 banks apart.  The
     // transposing value reads take 8 rows x 32 bytes per pass: a 32-byte pad
@@ -137,13 +143,13 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(PrefillParams 
     // bank (with 32 or with 64 four-byte banks).
     constexpr int KSTR = D + 8;
     constexpr int VSTR = D + 16;
-    constexpr int CHUNKS = kTile * D / 8;  // 16-byte chunks per tile and tensor
+    constexpr int CHUNKS = TT * D / 8;    // 16-byte chunks per tile and tensor
     constexpr int CPT = (CHUNKS + kPrefillThreads - 1) / kPrefillThreads;  // per thread
     constexpr int CPRW = D / 8;           // chunks per token row
     static_assert(CHUNKS % kPrefillThreads == 0, "every thread loads whole chunks");
 
-    __shared__ __attribute__((aligned(16))) uint16_t k_lds[2][kTile * KSTR];
-    __shared__ __attribute__((aligned(16))) uint16_t v_lds[2][kTile * VSTR];
+    __shared__ __attribute__((aligned(16))) uint16_t k_lds[2][TT * KSTR];
+    __shared__ __attribute__((aligned(16))) uint16_t v_lds[2][TT * VSTR];
 
     // ---- work item
     // Workgroups go to the 8 XCDs round-robin.  All row blocks of one
@@ -207,7 +213,7 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(PrefillParams 
     // positions the workgroup's rows can see: 0 .. pmax (the last valid row's)
     const int last_row = (row0 + RPB < nrows ? row0 + RPB : nrows) - 1;
     const int pmax = L - q_len + last_row / G;
-    const int ntiles = pmax / kTile + 1;
+    const int ntiles = pmax / TT + 1;
     const int w_last = (w_first + 16 * MB < nrows ? w_first + 16 * MB : nrows) - 1;
     const bool wave_active = w_first < nrows;
     const int wave_pmax = L - q_len + w_last / G;
@@ -231,22 +237,22 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(PrefillParams 
     }
 
     // cooperative tile loader: thread -> (token of the tile, 16-byte chunk).
-    // With block_size >= 16 each 16-token half of a tile lies in one block:
-    // its id is a uniform (scalar) load and each thread adds a fixed offset;
-    // the half a chunk falls in is the same for a whole wave.
+    // With block_size >= 16 each 16-token quarter of a tile lies in one
+    // block: its id is uniform (a scalar register) and each thread adds a
+    // fixed offset; the quarter a chunk falls in is the same for a whole wave.
     const int32_t *bt_row = p.block_tables + (int64_t)s * p.max_blocks_per_seq;
     const int64_t head_off = (int64_t)kvh * D * 2;
     int bad = 0;
     u32x4 kreg[CPT], vreg[CPT];
-    uint32_t chunk_off[CPT];  // offset of the thread's chunk from its half's first row
+    uint32_t chunk_off[CPT];  // offset of the thread's chunk from its quarter's first row
 #pragma unroll
     for (int c = 0; c < CPT; ++c) {
         const int idx = threadIdx.x + c * kPrefillThreads;
         chunk_off[c] = (uint32_t)(((idx / CPRW) % 16) * p.row_stride_bytes + head_off +
                                   (idx % CPRW) * 16);
     }
-    // the 16-token half of a tile that chunk c of this thread falls in: the
-    // same for the whole wave
+    // the 16-token quarter of a tile that chunk c of this thread falls in:
+    // the same for the whole wave
     const int wave_s = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     auto half_of = [&](int c) {
         if constexpr (16 * CPRW >= kPrefillThreads)
@@ -254,28 +260,28 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(PrefillParams 
         else
             return (wave_s * kWave + c * kPrefillThreads) / (16 * CPRW);
     };
-    // Block ids of the two halves of the next tile to load, fetched one tile
+    // Block ids of the quarters of the next tile to load, fetched one tile
     // ahead with a vector (buffer) load, so that they are in registers when
     // the tile's loads are issued: a scalar load there would stall the wave
-    // (its wait also covers every outstanding LDS access).  A half past pmax
-    // takes pmax's block; its tokens are zeroed when the tile is stored.
+    // (its wait also covers every outstanding LDS access).  A quarter past
+    // pmax takes pmax's block; its tokens are zeroed when the tile is stored.
     const __amdgpu_buffer_rsrc_t bt_rsrc = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<int32_t *>(bt_row), 0, p.max_blocks_per_seq * 4, kBufferConfig);
-    int next_id[2] = {0, 0};
+    int next_id[NQ];
     auto fetch_ids = [&](int tile) {
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            const int th = min(tile * kTile + 16 * h, pmax);
+        for (int h = 0; h < NQ; ++h) {
+            const int th = min(tile * TT + 16 * h, pmax);
             next_id[h] = __builtin_amdgcn_raw_buffer_load_b32(bt_rsrc, (th >> p.block_shift) * 4,
                                                               0, 0);
         }
     };
     auto load_tile = [&](int tile) {
-        const int t0 = tile * kTile;
-        int64_t half_base[2] = {0, 0};
+        const int t0 = tile * TT;
+        int64_t half_base[NQ] = {};
         if constexpr (BT) {
 #pragma unroll
-            for (int h = 0; h < 2; ++h) {
+            for (int h = 0; h < NQ; ++h) {
                 const int th = t0 + 16 * h;
                 int blk = __builtin_amdgcn_readfirstlane(next_id[h]);
                 if (blk < 0 || blk >= p.num_blocks) {
@@ -287,8 +293,9 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(PrefillParams 
             }
         }
         // Every chunk is loaded, so that the loads issue back to back; a
-        // token past pmax reads an in-bounds cell (block 0 for a half past
-        // pmax, the same block otherwise, or token pmax with per-token ids)
+        // token past pmax reads an in-bounds cell (pmax's block for a quarter
+        // past pmax, the same block otherwise, or token pmax with per-token
+        // ids)
         // and is zeroed when the tile is stored.
 #pragma unroll
         for (int c = 0; c < CPT; ++c) {
@@ -313,7 +320,7 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(PrefillParams 
         if constexpr (BT) fetch_ids(tile + 1);  // past the last tile: pmax's block again
     };
     auto store_tile = [&](int buf, int tile) {
-        const int t0 = tile * kTile;
+        const int t0 = tile * TT;
 #pragma unroll
         for (int c = 0; c < CPT; ++c) {
             const int idx = threadIdx.x + c * kPrefillThreads;
@@ -321,7 +328,7 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(PrefillParams 
             *reinterpret_cast<u32x4 *>(&k_lds[buf][row * KSTR + col]) = kreg[c];
             *reinterpret_cast<u32x4 *>(&v_lds[buf][row * VSTR + col]) = vreg[c];
         }
-        if (t0 + kTile - 1 > pmax) {  // the last tile: overwrite tokens past pmax
+        if (t0 + TT - 1 > pmax) {  // the last tile: overwrite tokens past pmax
 #pragma unroll
             for (int c = 0; c < CPT; ++c) {
                 const int idx = threadIdx.x + c * kPrefillThreads;
@@ -342,7 +349,7 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(PrefillParams 
 #pragma unroll
         for (int b = 0; b < DB; ++b) acc[mb][b] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
     }
-    // this lane's V^T addresses inside a tile (half 0); half 1 is 16 rows down
+    // this lane's V^T addresses inside a tile (quarter 0); quarter q is 16 q rows down
     const int vt_elem = (4 * kg + lrow / 4) * VSTR + 4 * (lrow % 4);
 
     if constexpr (BT) fetch_ids(0);
@@ -351,19 +358,19 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(PrefillParams 
     __syncthreads();
     for (int tile = 0; tile < ntiles; ++tile) {
         const int buf = tile & 1;
-        const int t0 = tile * kTile;
+        const int t0 = tile * TT;
         bool prefetched = false;
         if (wave_active && t0 <= wave_pmax) {
             const uint16_t *kt = k_lds[buf];
             const uint16_t *vt = v_lds[buf];
-            // S^T for both halves and every row block
-            f32x4 st[MB][2];
+            // S^T for every quarter and row block
+            f32x4 st[MB][NQ];
 #pragma unroll
             for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-                for (int u = 0; u < 2; ++u) st[mb][u] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+                for (int u = 0; u < NQ; ++u) st[mb][u] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-            for (int u = 0; u < 2; ++u) {
+            for (int u = 0; u < NQ; ++u) {
 #pragma unroll
                 for (int ks = 0; ks < KS; ++ks) {
                     const u32x4 a = *reinterpret_cast<const u32x4 *>(
@@ -375,28 +382,30 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(PrefillParams 
             // the next tile's loads, issued once this tile's K operands are in registers
             if (tile + 1 < ntiles) load_tile(tile + 1);
             prefetched = true;
-            const bool need_mask = t0 + kTile - 1 > wave_pmin;  // wave-uniform
-            const int first = t0 + 4 * kg;  // this lane's first token of half 0
+            const bool need_mask = t0 + TT - 1 > wave_pmin;  // wave-uniform
+            const int first = t0 + 4 * kg;  // this lane's first token of quarter 0
             const float c = p.score_scale;
-            u32x4 pb[MB];
+            u32x4 pb[MB][NG];
 #pragma unroll
             for (int mb = 0; mb < MB; ++mb) {
                 // raw scores; the scale (>= 0) enters with the exponent
-                float sc[2][4];
+                float sc[NQ][4];
 #pragma unroll
-                for (int u = 0; u < 2; ++u)
+                for (int u = 0; u < NQ; ++u)
 #pragma unroll
                     for (int r = 0; r < 4; ++r) sc[u][r] = st[mb][u][r];
                 if (need_mask) {
 #pragma unroll
-                    for (int u = 0; u < 2; ++u)
+                    for (int u = 0; u < NQ; ++u)
 #pragma unroll
                         for (int r = 0; r < 4; ++r)
                             if (first + 16 * u + r > pos[mb]) sc[u][r] = -INFINITY;
                 }
-                float mt = vmax(vmax(vmax(sc[0][0], sc[0][1]), vmax(sc[0][2], sc[0][3])),
-                                vmax(vmax(sc[1][0], sc[1][1]), vmax(sc[1][2], sc[1][3])));
-                mt = row_reduce4<true>(mt);                              // row max over the 32 tokens
+                float mt = -INFINITY;
+#pragma unroll
+                for (int u = 0; u < NQ; ++u)
+                    mt = vmax(mt, vmax(vmax(sc[u][0], sc[u][1]), vmax(sc[u][2], sc[u][3])));
+                mt = row_reduce4<true>(mt);                     // row max over the tile
                 mt = mt == -INFINITY ? -INFINITY : mt * c;      // scaled (log2 domain)
                 if (__builtin_amdgcn_ballot_w64(mt > m[mb] + kRescaleSlack) != 0) {
                     const float mn = vmax(m[mb], mt);
@@ -407,40 +416,47 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(PrefillParams 
                     for (int b = 0; b < DB; ++b) acc[mb][b] *= alpha;
                 }
                 const float nref = m[mb] == -INFINITY ? 0.0f : -m[mb];  // rows that saw nothing
-                float arg[2][4];
+                float arg[NQ][4];
 #pragma unroll
-                for (int u = 0; u < 2; ++u)
+                for (int u = 0; u < NQ; ++u)
 #pragma unroll
                     for (int r = 0; r < 4; ++r) arg[u][r] = __builtin_fmaf(sc[u][r], c, nref);
                 if (need_mask) {  // a zero scale turns a masked score into NaN above
 #pragma unroll
-                    for (int u = 0; u < 2; ++u)
+                    for (int u = 0; u < NQ; ++u)
 #pragma unroll
                         for (int r = 0; r < 4; ++r)
                             if (first + 16 * u + r > pos[mb]) arg[u][r] = -INFINITY;
                 }
-                uint32_t w[4];
+                uint32_t w[NQ][2];
 #pragma unroll
-                for (int u = 0; u < 2; ++u) {
+                for (int u = 0; u < NQ; ++u) {
                     float pr[4];
 #pragma unroll
                     for (int r = 0; r < 4; ++r) {
                         pr[r] = fast_exp2(arg[u][r]);
                         lsum[mb] += pr[r];
                     }
-                    w[2 * u] = narrow_pair<T>(pr[0], pr[1]);
-                    w[2 * u + 1] = narrow_pair<T>(pr[2], pr[3]);
+                    w[u][0] = narrow_pair<T>(pr[0], pr[1]);
+                    w[u][1] = narrow_pair<T>(pr[2], pr[3]);
                 }
-                pb[mb] = u32x4{w[0], w[1], w[2], w[3]};
+#pragma unroll
+                for (int g = 0; g < NG; ++g)
+                    pb[mb][g] = u32x4{w[2 * g][0], w[2 * g][1], w[2 * g + 1][0], w[2 * g + 1][1]};
             }
 #pragma unroll
-            for (int b = 0; b < DB; ++b) {
-                const uint64_t lo = lds_read_tr16(vt + vt_elem + 16 * b);
-                const uint64_t hi = lds_read_tr16(vt + vt_elem + 16 * VSTR + 16 * b);
-                const u32x4 a = u32x4{(uint32_t)lo, (uint32_t)(lo >> 32), (uint32_t)hi,
-                                      (uint32_t)(hi >> 32)};
+            for (int g = 0; g < NG; ++g) {
 #pragma unroll
-                for (int mb = 0; mb < MB; ++mb) acc[mb][b] = mfma_k32<T>(a, pb[mb], acc[mb][b]);
+                for (int b = 0; b < DB; ++b) {
+                    const uint16_t *vg = vt + vt_elem + 32 * g * VSTR + 16 * b;
+                    const uint64_t lo = lds_read_tr16(vg);
+                    const uint64_t hi = lds_read_tr16(vg + 16 * VSTR);
+                    const u32x4 a = u32x4{(uint32_t)lo, (uint32_t)(lo >> 32), (uint32_t)hi,
+                                          (uint32_t)(hi >> 32)};
+#pragma unroll
+                    for (int mb = 0; mb < MB; ++mb)
+                        acc[mb][b] = mfma_k32<T>(a, pb[mb][g], acc[mb][b]);
+                }
             }
         }
         if (!prefetched && tile + 1 < ntiles) load_tile(tile + 1);
