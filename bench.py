@@ -492,6 +492,9 @@ def main() -> int:
     ap.add_argument("--copies", type=int, default=4, help="pool copies rotated across steps")
     ap.add_argument("--partition-size", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--fused", action="store_true",
+                    help="time the decode step as one paged_attn_decode_write launch instead "
+                         "of kv_cache_write + paged_attn_decode")
     ap.add_argument("--op", choices=("decode", "copy_blocks", "prefill", "swap_out", "swap_in",
                                      "prefix_cache"),
                     default="decode",
@@ -554,11 +557,19 @@ def main() -> int:
 
     def step(i, ev=None):
         kc, vc = copies[i % len(copies)]
-        binding.kv_cache_write(new_key, new_value, sm, kc, vc)
+        if not args.fused:
+            binding.kv_cache_write(new_key, new_value, sm, kc, vc)
         if ev is not None:
             ev[0].record()
-        binding.paged_attn_decode(query, kc, vc, bt, cl, b.scale, out, max_context_len=max_ctx,
-                                  partition_size=args.partition_size, workspace=workspace)
+        if not args.fused:
+            binding.paged_attn_decode(query, kc, vc, bt, cl, b.scale, out,
+                                      max_context_len=max_ctx,
+                                      partition_size=args.partition_size, workspace=workspace)
+        else:
+            binding.paged_attn_decode_write(query, new_key, new_value, sm, kc, vc, bt, cl,
+                                            b.scale, out, max_context_len=max_ctx,
+                                            partition_size=args.partition_size,
+                                            workspace=workspace)
         if ev is not None:
             ev[1].record()
 
@@ -574,29 +585,37 @@ def main() -> int:
         step(i)
     torch.cuda.synchronize()
 
-    events = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-              for _ in range(args.steps)]
+    # The timed steps: the wall clock over K steps with nothing else on the
+    # stream (an event pair per step would add its own time to every step).
+    steps = args.steps
     torch.cuda.synchronize()
     t0 = time.perf_counter()
+    for i in range(steps):
+        step(args.warmup + i)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    ms_per_step = elapsed * 1e3 / steps
+
+    # Each launch on its own, between HIP events on the stream it runs on.
+    events = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(args.steps)]
     for i in range(args.steps):
         step(args.warmup + i, events[i])
     torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t0
-
-    ms_per_step = elapsed * 1e3 / args.steps
     decode_ms = [a.elapsed_time(z) for a, z in events]
     decode_avg_ms = sum(decode_ms) / len(decode_ms)
     b_dec = b.decode_algorithmic_bytes()
     b_step = b_dec + b.write_algorithmic_bytes()
-    achieved = b_dec / (decode_avg_ms * 1e-3) / 1e9
-    traffic = measured_traffic(args.workload)
+    b_launch = b_dec if not args.fused else b_step  # the timed launch's own bytes
+    achieved = b_launch / (decode_avg_ms * 1e-3) / 1e9
+    traffic = None if args.fused else measured_traffic(args.workload)
 
     result = {
         "metric": METRIC,
         "value": round(b_step / (ms_per_step * 1e-3) / 1e9, 2),
         "unit": "GB/s",
         "n_gpus": 1,
-        "steps": args.steps,
+        "steps": steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms_per_step, 5),
         "higher_is_better": True,
@@ -611,7 +630,10 @@ def main() -> int:
             "context_tokens": int(b.context_lens.sum()),
             "context_len_range": [int(b.context_lens.min()), int(b.context_lens.max())],
             "partition_size": P, "pool_copies": len(copies),
-            "step": "kv_cache_write of one token per sequence + paged_attn_decode",
+            "step": ("kv_cache_write of one token per sequence + paged_attn_decode"
+                     if not args.fused else
+                     "paged_attn_decode_write: one new token per sequence stored in the pool "
+                     "and the decode, in one launch"),
         },
         "seq_per_s_per_layer": round(S / (decode_avg_ms * 1e-3), 1),
         "decode_ms": round(decode_avg_ms, 5),
@@ -625,8 +647,8 @@ def main() -> int:
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBPS, 4),
             "traffic": traffic,
-            "kernel": "paged_attn_decode",
-            "algorithmic_bytes_per_launch": b_dec,
+            "kernel": "paged_attn_decode" if not args.fused else "paged_attn_decode_write",
+            "algorithmic_bytes_per_launch": b_launch,
         },
         "cpu_baseline": None,
     }

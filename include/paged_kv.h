@@ -113,6 +113,29 @@ PAGED_KV_API int paged_attn_decode(
     void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * One decode step in one launch: kv_cache_write of each sequence's new token
+ * followed by paged_attn_decode, with the same results (pool bits and
+ * output) as the two calls.  The worker writes each new token's K/V into its
+ * pool cell and the kernel then reads the sequence's history, the new token
+ * included ("大模型推理框架VLLM-0.7.3源码", §3.3).
+ *   new_key, new_value  [num_seqs, num_kv_heads, head_dim]: sequence s's new
+ *                token, same dtype as query
+ *   slot_mapping [num_seqs] int32: its cell (physical_block * block_size +
+ *                offset), which must be the cell of position
+ *                context_lens[s] - 1 of sequence s (the only cell of the
+ *                launch it then writes and reads); a negative slot, or one
+ *                outside the pool, writes nothing
+ *   key_cache, value_cache  updated in place
+ * Every other argument, check and status is paged_attn_decode's.
+ */
+PAGED_KV_API int paged_attn_decode_write(
+    const void *query, const void *new_key, const void *new_value, const int32_t *slot_mapping,
+    void *key_cache, void *value_cache, const int32_t *block_tables, const int32_t *context_lens,
+    float scale, void *out, int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
+    int block_size, int num_blocks, int max_blocks_per_seq, int max_context_len,
+    int partition_size, int dtype, void *workspace, size_t workspace_bytes, void *stream);
+
+/*
  * The context partition size paged_attn_decode uses for these arguments
  * (partition_size 0 = its automatic choice), or a negative paged_kv_status
  * code when the arguments are invalid.  A partition size >= max_context_len

@@ -23,6 +23,7 @@ _TORCH_DTYPES = {torch.float32: PAGED_KV_F32, torch.float16: PAGED_KV_F16,
 EXPORTED = (
     "paged_kv_status_string",
     "paged_attn_decode",
+    "paged_attn_decode_write",
     "paged_attn_decode_partition_size",
     "paged_attn_decode_workspace_bytes",
     "kv_cache_write",
@@ -47,6 +48,8 @@ def _load_library(path: str = LIBRARY) -> ctypes.CDLL:
     lib.paged_kv_status_string.argtypes = [ci]
     lib.paged_kv_status_string.restype = ctypes.c_char_p
     lib.paged_attn_decode.argtypes = [vp, vp, vp, vp, vp, cf, vp] + [ci] * 10 + [vp, sz, vp]
+    lib.paged_attn_decode_write.argtypes = [vp] * 8 + [cf, vp] + [ci] * 10 + [vp, sz, vp]
+    lib.paged_attn_decode_write.restype = ci
     lib.paged_attn_decode.restype = ci
     lib.paged_attn_decode_partition_size.argtypes = [ci] * 9
     lib.paged_attn_decode_partition_size.restype = ci
@@ -144,15 +147,7 @@ def paged_attn_decode_workspace_bytes(num_seqs, num_q_heads, num_kv_heads, head_
     return r
 
 
-def paged_attn_decode(query: torch.Tensor, key_cache: torch.Tensor, value_cache: torch.Tensor,
-                      block_tables: torch.Tensor, context_lens: torch.Tensor, scale: float,
-                      out: torch.Tensor, *, max_context_len: int = 0, partition_size: int = 0,
-                      workspace: torch.Tensor | None = None) -> torch.Tensor:
-    """Decode attention over a paged KV cache (see paged_attn_decode in
-    include/paged_kv.h).  query/out [S, Hq, D]; key_cache/value_cache
-    [num_blocks, block_size, Hkv, D]; block_tables [S, max_blocks] int32;
-    context_lens [S] int32.  A workspace of the required size is allocated
-    with torch when none is given."""
+def _decode_checks(query, key_cache, value_cache, block_tables, context_lens, out):
     S, Hq, D = query.shape
     nb, bs, Hkv, D2 = key_cache.shape
     if D2 != D or tuple(value_cache.shape) != tuple(key_cache.shape):
@@ -165,21 +160,75 @@ def paged_attn_decode(query: torch.Tensor, key_cache: torch.Tensor, value_cache:
         raise TypeError("block_tables and context_lens must be int32")
     if block_tables.dim() != 2 or block_tables.shape[0] != S or tuple(context_lens.shape) != (S,):
         raise ValueError("block_tables must be [S, max_blocks] and context_lens [S]")
-    dt = _dtype_code(query)
-    mb = block_tables.shape[1]
+    return S, Hq, D, nb, bs, Hkv
+
+
+def _workspace(query, S, Hq, Hkv, D, bs, mb, max_context_len, partition_size, dt, workspace):
     need = paged_attn_decode_workspace_bytes(S, Hq, Hkv, D, bs, mb, max_context_len,
                                              partition_size, dt)
-    ws_ptr, ws_bytes = None, 0
-    if need > 0:
-        if workspace is None:
-            workspace = torch.empty(need, dtype=torch.uint8, device=query.device)
-        ws_ptr, ws_bytes = _dev(workspace, "workspace"), workspace.numel() * workspace.element_size()
+    if need == 0:
+        return None, 0
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=query.device)
+    return _dev(workspace, "workspace"), workspace.numel() * workspace.element_size()
+
+
+def paged_attn_decode(query: torch.Tensor, key_cache: torch.Tensor, value_cache: torch.Tensor,
+                      block_tables: torch.Tensor, context_lens: torch.Tensor, scale: float,
+                      out: torch.Tensor, *, max_context_len: int = 0, partition_size: int = 0,
+                      workspace: torch.Tensor | None = None) -> torch.Tensor:
+    """Decode attention over a paged KV cache (see paged_attn_decode in
+    include/paged_kv.h).  query/out [S, Hq, D]; key_cache/value_cache
+    [num_blocks, block_size, Hkv, D]; block_tables [S, max_blocks] int32;
+    context_lens [S] int32.  A workspace of the required size is allocated
+    with torch when none is given."""
+    S, Hq, D, nb, bs, Hkv = _decode_checks(query, key_cache, value_cache, block_tables,
+                                           context_lens, out)
+    dt = _dtype_code(query)
+    mb = block_tables.shape[1]
+    ws_ptr, ws_bytes = _workspace(query, S, Hq, Hkv, D, bs, mb, max_context_len, partition_size,
+                                  dt, workspace)
     status = _lib.paged_attn_decode(
         _dev(query, "query"), _dev(key_cache, "key_cache"), _dev(value_cache, "value_cache"),
         _dev(block_tables, "block_tables"), _dev(context_lens, "context_lens"),
         ctypes.c_float(scale), _dev(out, "out"), S, Hq, Hkv, D, bs, nb, mb, max_context_len,
         partition_size, dt, ws_ptr, ws_bytes, _stream(query.device))
     _check("paged_attn_decode", status)
+    return out
+
+
+def paged_attn_decode_write(query: torch.Tensor, new_key: torch.Tensor,
+                            new_value: torch.Tensor, slot_mapping: torch.Tensor,
+                            key_cache: torch.Tensor, value_cache: torch.Tensor,
+                            block_tables: torch.Tensor, context_lens: torch.Tensor, scale: float,
+                            out: torch.Tensor, *, max_context_len: int = 0,
+                            partition_size: int = 0,
+                            workspace: torch.Tensor | None = None) -> torch.Tensor:
+    """One decode step in one launch: each sequence's new token's K/V
+    (new_key/new_value [S, Hkv, D]) is stored in pool cell slot_mapping[s]
+    (int32 [S], the cell of position context_lens[s] - 1), then the decode
+    attends over the context (see paged_attn_decode_write in
+    include/paged_kv.h).  Same result as kv_cache_write followed by
+    paged_attn_decode."""
+    S, Hq, D, nb, bs, Hkv = _decode_checks(query, key_cache, value_cache, block_tables,
+                                           context_lens, out)
+    if tuple(new_key.shape) != (S, Hkv, D) or tuple(new_value.shape) != (S, Hkv, D) or \
+            new_key.dtype != query.dtype or new_value.dtype != query.dtype:
+        raise ValueError("new_key / new_value must be [S, Hkv, D] in the query's dtype")
+    if slot_mapping.dtype != torch.int32 or tuple(slot_mapping.shape) != (S,):
+        raise ValueError("slot_mapping must be int32 [S]")
+    dt = _dtype_code(query)
+    mb = block_tables.shape[1]
+    ws_ptr, ws_bytes = _workspace(query, S, Hq, Hkv, D, bs, mb, max_context_len, partition_size,
+                                  dt, workspace)
+    status = _lib.paged_attn_decode_write(
+        _dev(query, "query"), _dev(new_key, "new_key"), _dev(new_value, "new_value"),
+        _dev(slot_mapping, "slot_mapping"), _dev(key_cache, "key_cache"),
+        _dev(value_cache, "value_cache"), _dev(block_tables, "block_tables"),
+        _dev(context_lens, "context_lens"), ctypes.c_float(scale), _dev(out, "out"), S, Hq, Hkv,
+        D, bs, nb, mb, max_context_len, partition_size, dt, ws_ptr, ws_bytes,
+        _stream(query.device))
+    _check("paged_attn_decode_write", status)
     return out
 
 

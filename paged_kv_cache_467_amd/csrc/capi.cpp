@@ -62,12 +62,17 @@ size_t paged_attn_decode_workspace_bytes(int num_seqs, int num_q_heads, int num_
     return pkv::decode_workspace_bytes(pl, num_seqs, num_q_heads, head_dim);
 }
 
-int paged_attn_decode(const void *query, const void *key_cache, const void *value_cache,
-                      const int32_t *block_tables, const int32_t *context_lens, float scale,
-                      void *out, int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
-                      int block_size, int num_blocks, int max_blocks_per_seq,
-                      int max_context_len, int partition_size, int dtype, void *workspace,
-                      size_t workspace_bytes, void *stream) {
+}  // extern "C"
+
+namespace {
+
+// The decode, with (new_key non-null) or without the fused KV write.
+int decode(const void *query, const void *new_key, const void *new_value,
+           const int32_t *slot_mapping, const void *key_cache, const void *value_cache,
+           const int32_t *block_tables, const int32_t *context_lens, float scale, void *out,
+           int num_seqs, int num_q_heads, int num_kv_heads, int head_dim, int block_size,
+           int num_blocks, int max_blocks_per_seq, int max_context_len, int partition_size,
+           int dtype, void *workspace, size_t workspace_bytes, void *stream) {
     const pkv::DecodePlan pl = pkv::plan_decode(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
                                 max_blocks_per_seq, max_context_len, partition_size, dtype);
     if (pl.status != PAGED_KV_OK) return pl.status;
@@ -77,6 +82,9 @@ int paged_attn_decode(const void *query, const void *key_cache, const void *valu
         return PAGED_KV_ERR_NULL_POINTER;
     if (!aligned16(query) || !aligned16(key_cache) || !aligned16(value_cache) ||
         !aligned16(out) || !aligned4(block_tables) || !aligned4(context_lens))
+        return PAGED_KV_ERR_BAD_SHAPE;
+    if (new_key && (!new_value || !slot_mapping)) return PAGED_KV_ERR_NULL_POINTER;
+    if (new_key && (!aligned16(new_key) || !aligned16(new_value) || !aligned4(slot_mapping)))
         return PAGED_KV_ERR_BAD_SHAPE;
     const size_t need = pkv::decode_workspace_bytes(pl, num_seqs, num_q_heads, head_dim);
     if (need > 0 && (!workspace || workspace_bytes < need || !aligned16(workspace)))
@@ -112,12 +120,47 @@ int paged_attn_decode(const void *query, const void *key_cache, const void *valu
     p.num_head_groups = num_kv_heads / pl.heads_per_group;
     p.row_stride_bytes = num_kv_heads * head_dim * e;
     p.block_stride_bytes = (int64_t)block_size * p.row_stride_bytes;
+    p.new_key = static_cast<const char *>(new_key);
+    p.new_value = static_cast<const char *>(new_value);
+    p.slot_mapping = slot_mapping;
+    p.num_slots = (int64_t)num_blocks * block_size;
 
     const int group = num_q_heads / num_kv_heads;
     const int kernel = pkv::decode_kernel_choice(dtype, head_dim, group);
     const hipError_t err = pkv::launch_decode(p, dtype, head_dim, group, kernel,
                                               static_cast<hipStream_t>(stream));
     return err == hipSuccess ? PAGED_KV_OK : PAGED_KV_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+int paged_attn_decode(const void *query, const void *key_cache, const void *value_cache,
+                      const int32_t *block_tables, const int32_t *context_lens, float scale,
+                      void *out, int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
+                      int block_size, int num_blocks, int max_blocks_per_seq,
+                      int max_context_len, int partition_size, int dtype, void *workspace,
+                      size_t workspace_bytes, void *stream) {
+    return decode(query, nullptr, nullptr, nullptr, key_cache, value_cache, block_tables,
+                  context_lens, scale, out, num_seqs, num_q_heads, num_kv_heads, head_dim,
+                  block_size, num_blocks, max_blocks_per_seq, max_context_len, partition_size,
+                  dtype, workspace, workspace_bytes, stream);
+}
+
+int paged_attn_decode_write(const void *query, const void *new_key, const void *new_value,
+                            const int32_t *slot_mapping, void *key_cache, void *value_cache,
+                            const int32_t *block_tables, const int32_t *context_lens,
+                            float scale, void *out, int num_seqs, int num_q_heads,
+                            int num_kv_heads, int head_dim, int block_size, int num_blocks,
+                            int max_blocks_per_seq, int max_context_len, int partition_size,
+                            int dtype, void *workspace, size_t workspace_bytes, void *stream) {
+    if (num_seqs > 0 && (!new_key || !new_value || !slot_mapping))
+        return PAGED_KV_ERR_NULL_POINTER;
+    return decode(query, new_key, new_value, slot_mapping, key_cache, value_cache, block_tables,
+                  context_lens, scale, out, num_seqs, num_q_heads, num_kv_heads, head_dim,
+                  block_size, num_blocks, max_blocks_per_seq, max_context_len, partition_size,
+                  dtype, workspace, workspace_bytes, stream);
 }
 
 int kv_cache_write(const void *key, const void *value, const int32_t *slot_mapping,

@@ -40,6 +40,13 @@ struct DecodeParams {
     int num_head_groups;        // num_kv_heads / heads_per_group
     int64_t block_stride_bytes; // bs * Hkv * D * elem bytes
     int row_stride_bytes;       // Hkv * D * elem bytes
+    // Fused KV write (null new_key: none): sequence s's new token's rows
+    // new_key/new_value [S, Hkv, D] go to pool cell slot_mapping[s] before
+    // the sequence's attention reads its history.
+    const char *new_key;
+    const char *new_value;
+    const int32_t *slot_mapping;
+    int64_t num_slots;          // num_blocks * block_size
 };
 
 // dtype codes match paged_kv_dtype; kernel = 0 VALU, 1 MFMA.

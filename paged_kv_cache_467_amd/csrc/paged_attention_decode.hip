@@ -140,6 +140,35 @@ __device__ void store_constant(const DecodeParams &p, const WorkItem &w, bool na
     }
 }
 
+// Fused KV write: the new token of sequence s (position L - 1) goes to its
+// pool cell before the sequence's attention reads it.  The workgroup whose
+// partition holds position L - 1 (partition 0 when L is 0 or invalid: then
+// nothing is read) writes the rows of its kv heads, each wave its own head's
+// row -- the row that wave alone reads back -- and fences it.  A slot outside
+// the pool writes nothing.
+template <class T, int D>
+__device__ inline void write_new_token(const DecodeParams &p, const WorkItem &w) {
+    if (p.new_key == nullptr) return;
+    const bool reads = !w.bad_len && w.context_len >= 1;
+    const int owner = reads ? (w.context_len - 1) / p.partition_size : 0;
+    if (w.part != owner) return;
+    const int slot = p.slot_mapping[w.s];
+    if (slot < 0 || slot >= p.num_slots) return;
+    constexpr int kRowBytes = D * T::kBytes;
+    const int lane = threadIdx.x % kWave;
+    const int64_t src = ((int64_t)w.s * p.num_kv_heads + w.kvh) * kRowBytes;
+    const int64_t dst = (int64_t)(slot >> p.block_shift) * p.block_stride_bytes +
+                        (int64_t)(slot & (p.block_size - 1)) * p.row_stride_bytes +
+                        (int64_t)w.kvh * kRowBytes;
+    char *kc = const_cast<char *>(p.key_cache);
+    char *vc = const_cast<char *>(p.value_cache);
+    for (int b = lane * 16; b < kRowBytes; b += kWave * 16) {
+        store16(kc + dst + b, load16(p.new_key + src + b));
+        store16(vc + dst + b, load16(p.new_value + src + b));
+    }
+    __threadfence_block();
+}
+
 // Common prologue.  Returns false when the workgroup has nothing to read (it
 // has then already written whatever it owes).
 template <class T, int D, int G>
@@ -235,6 +264,7 @@ __global__ __launch_bounds__(kMaxDecodeThreads) void decode_valu_kernel(DecodePa
     __shared__ int32_t bt_lds[kBtLds];
 
     const WorkItem w = work_item(p);
+    write_new_token<T, D>(p, w);
     if (!prologue<T, D, G>(p, w)) return;
     const bool bad = stage_block_table(p, w, bt_lds);
     const int b0 = w.tok_begin >> p.block_shift;
@@ -400,6 +430,7 @@ __global__ __launch_bounds__(kMaxDecodeThreads) void decode_mfma_kernel(DecodePa
     __shared__ float lex[kMaxDecodeWaves][G];  // final l
 
     const WorkItem w = work_item(p);
+    write_new_token<T, D>(p, w);
     if (!prologue<T, D, G>(p, w)) return;
     const bool bad = stage_block_table(p, w, bt_lds);
     const int b0 = w.tok_begin >> p.block_shift;

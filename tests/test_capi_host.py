@@ -40,6 +40,7 @@ def lib():
     lib.paged_attn_prefill.argtypes = [vp] * 6 + [cf, vp] + [ci] * 11 + [vp]
     for name in ("paged_kv_swap_out", "paged_kv_swap_in"):
         getattr(lib, name).argtypes = [vp] * 5 + [ci] * 7 + [vp]
+    lib.paged_attn_decode_write.argtypes = [vp] * 8 + [cf, vp] + [ci] * 10 + [vp, sz, vp]
     lib.paged_kv_prefix_hash.argtypes = [vp] * 3 + [ci] * 4 + [ctypes.c_uint64, vp, vp]
     lib.paged_kv_prefix_insert.argtypes = [vp, vp, ci, vp, vp, ci, vp, vp]
     lib.paged_kv_prefix_match.argtypes = [vp, vp, ci, ci, vp, vp, ci, vp, vp, vp]
@@ -51,7 +52,8 @@ def test_header_declares_the_entry_points():
         "paged_kv_status_string", "paged_attn_decode", "paged_attn_decode_partition_size",
         "paged_attn_decode_workspace_bytes", "kv_cache_write", "paged_kv_gather",
         "paged_kv_copy_blocks", "paged_attn_prefill", "paged_kv_swap_out", "paged_kv_swap_in",
-        "paged_kv_prefix_hash", "paged_kv_prefix_insert", "paged_kv_prefix_match"])
+        "paged_kv_prefix_hash", "paged_kv_prefix_insert", "paged_kv_prefix_match",
+        "paged_attn_decode_write"])
 
 
 def test_library_exports_only_the_entry_points():
@@ -259,3 +261,21 @@ def test_prefix_match_rejects(lib, kw, status):
              table_blocks=P, capacity_log2=10, matched_blocks=P, matched_len=P, stream=None)
     a.update(kw)
     assert lib.paged_kv_prefix_match(*a.values()) == status
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(new_key=None), NULLPTR), (dict(slot_mapping=None), NULLPTR),
+    (dict(new_value=P + 8), BAD_SHAPE), (dict(slot_mapping=P + 2), BAD_SHAPE),
+    (dict(q=None), NULLPTR), (dict(head_dim=96), UNSUPPORTED),
+    (dict(num_seqs=0, q=None, new_key=None, new_value=None, slot_mapping=None, kc=None, vc=None,
+          bt=None, cl=None, out=None), OK),
+])
+def test_decode_write_rejects(lib, kw, status):
+    a = dict(q=P, new_key=P, new_value=P, slot_mapping=P, kc=P, vc=P, bt=P, cl=P, scale=0.1,
+             out=P, **SHAPE)
+    a.update(kw)
+    assert lib.paged_attn_decode_write(
+        a["q"], a["new_key"], a["new_value"], a["slot_mapping"], a["kc"], a["vc"], a["bt"],
+        a["cl"], a["scale"], a["out"], a["num_seqs"], a["num_q_heads"], a["num_kv_heads"],
+        a["head_dim"], a["block_size"], a["num_blocks"], a["max_blocks_per_seq"],
+        a["max_context_len"], a["partition_size"], a["dtype"], None, 0, None) == status

@@ -333,3 +333,87 @@ def test_invalid_device_values_give_nan(B):
         got = tensors.widen(run_decode(B, bad, partition_size=P, max_context_len=64), "bf16")
         assert np.all(np.isnan(got[0])) and np.all(np.isnan(got[1])) and np.all(np.isnan(got[3]))
         check_close(got[2:3], ref[2:3], "bf16", f"valid neighbour P={P}")
+
+
+FUSED = [("bf16", 32, 8, 128, 16, 0), ("bf16", 32, 8, 128, 16, 64), ("f16", 8, 8, 128, 32, 0),
+         ("f32", 8, 2, 64, 16, 32), ("bf16", 16, 4, 256, 1, 0), ("f16", 16, 2, 64, 8, 48)]
+
+
+@pytest.mark.parametrize("dtype,Hq,Hkv,D,bs,psize", FUSED)
+def test_decode_write_equals_write_then_decode(B, dtype, Hq, Hkv, D, bs, psize):
+    """The fused step (write each sequence's new token, then decode) gives
+    the bits of kv_cache_write followed by paged_attn_decode: output and
+    pool, with and without a context split, on a poisoned pool; an empty
+    sequence and a skipped slot included."""
+    _say(f"paged_attn_decode_write {dtype} Hq={Hq} Hkv={Hkv} D={D} bs={bs} partition={psize}")
+    b = W.make_custom(700 + D + bs + psize, dtype=dtype, num_seqs=6, num_q_heads=Hq,
+                      num_kv_heads=Hkv, head_dim=D, block_size=bs,
+                      context_lens=(1, 37, 300, 0, 129, 64), extra_blocks=5, poison=True)
+    b.slot_mapping[5] = -1          # this sequence's new token is not stored
+    ref, got = tensors.device_batch(b, DEV), tensors.device_batch(b, DEV)
+    B.kv_cache_write(ref.new_key, ref.new_value, ref.slot_mapping, ref.key_cache,
+                     ref.value_cache)
+    B.paged_attn_decode(ref.query, ref.key_cache, ref.value_cache, ref.block_tables,
+                        ref.context_lens, b.scale, ref.out, partition_size=psize)
+    B.paged_attn_decode_write(got.query, got.new_key, got.new_value, got.slot_mapping,
+                              got.key_cache, got.value_cache, got.block_tables,
+                              got.context_lens, b.scale, got.out, partition_size=psize)
+    torch.cuda.synchronize()
+    for a, c in ((ref.out, got.out), (ref.key_cache, got.key_cache),
+                 (ref.value_cache, got.value_cache)):
+        assert np.array_equal(tensors.to_host_bits(a).view(np.uint8),
+                              tensors.to_host_bits(c).view(np.uint8))
+
+
+def test_decode_write_on_the_bench_batch(B):
+    """The Llama-3-8B-shaped batch: fused step equals the two calls, and the
+    pool after it equals the oracle's write."""
+    b = W.make_workload("llama3_8b_gqa_bf16", poison=True)
+    _say("paged_attn_decode_write on the Llama-3-8B batch")
+    ref, got = tensors.device_batch(b, DEV), tensors.device_batch(b, DEV)
+    B.kv_cache_write(ref.new_key, ref.new_value, ref.slot_mapping, ref.key_cache,
+                     ref.value_cache)
+    B.paged_attn_decode(ref.query, ref.key_cache, ref.value_cache, ref.block_tables,
+                        ref.context_lens, b.scale, ref.out)
+    B.paged_attn_decode_write(got.query, got.new_key, got.new_value, got.slot_mapping,
+                              got.key_cache, got.value_cache, got.block_tables,
+                              got.context_lens, b.scale, got.out)
+    torch.cuda.synchronize()
+    assert np.array_equal(tensors.to_host_bits(ref.out), tensors.to_host_bits(got.out))
+    kc, vc = b.key_cache.copy(), b.value_cache.copy()
+    oracle.kv_cache_write(b.new_key, b.new_value, b.slot_mapping, kc, vc, b.dtype)
+    assert np.array_equal(tensors.to_host_bits(got.key_cache), kc)
+    assert np.array_equal(tensors.to_host_bits(got.value_cache), vc)
+
+
+def test_decode_write_graph_replay(B):
+    """The fused step captured in a HIP graph: every replay, with eager work
+    and synchronisations between replays, gives the eager result's bits."""
+    _say("paged_attn_decode_write in a HIP graph")
+    b = W.make_custom(811, dtype="bf16", num_seqs=8, num_q_heads=32, num_kv_heads=8,
+                      head_dim=128, block_size=16, context_lens=(5, 40, 640, 333, 1, 17, 900, 64),
+                      extra_blocks=4, poison=True)
+    eager, g = tensors.device_batch(b, DEV), tensors.device_batch(b, DEV)
+    B.paged_attn_decode_write(eager.query, eager.new_key, eager.new_value, eager.slot_mapping,
+                              eager.key_cache, eager.value_cache, eager.block_tables,
+                              eager.context_lens, b.scale, eager.out, partition_size=128)
+    torch.cuda.synchronize()
+    want = tensors.to_host_bits(eager.out)
+    ws = torch.empty(1 << 22, dtype=torch.uint8, device=DEV)
+    graph = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(graph, stream=side):
+            B.paged_attn_decode_write(g.query, g.new_key, g.new_value, g.slot_mapping,
+                                      g.key_cache, g.value_cache, g.block_tables,
+                                      g.context_lens, b.scale, g.out, partition_size=128,
+                                      workspace=ws)
+    torch.cuda.current_stream().wait_stream(side)
+    for r in range(4):
+        g.out.fill_(0.0)                     # eager work between replays
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(tensors.to_host_bits(g.out), want), f"replay {r}"
+    assert np.array_equal(tensors.to_host_bits(g.key_cache), tensors.to_host_bits(eager.key_cache))
