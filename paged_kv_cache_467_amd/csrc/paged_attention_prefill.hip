@@ -15,18 +15,21 @@
 // head, block of rows), row r = (new token r / G, query head r % G); each
 // wave owns MB blocks of 16 rows (32 rows for head_dim <= 128, 16 for 256),
 // so that every K/V operand read from LDS serves MB blocks.  The workgroup
-// walks the positions its rows can see in 32-token tiles, staged in LDS as
-// they lie in the pool ([token][d]; K rows padded by 16 bytes and V rows
-// by 32, so that neither operand read meets a bank conflict),
-// double-buffered with one barrier per tile and shared by its 4 waves:
+// walks the positions its rows can see in tiles of 64 positions (32 for
+// head_dim 256), staged in LDS as they lie in the pool ([token][d]; K rows
+// padded by 16 bytes and V rows by 32, so that neither operand read meets a
+// bank conflict), double-buffered with one barrier per tile and shared by
+// its 4 waves:
 //  * Scores are computed transposed, S^T = K Q^T, with
-//    v_mfma_f32_16x16x32 per 16-token half: A = K (lane l: token l % 16, 8
-//    consecutive d of k-group l / 16), B = Q^T from registers (lane l: row
+//    v_mfma_f32_16x16x32 per 16-token quarter: A = K (lane l: token l % 16,
+//    8 consecutive d of k-group l / 16), B = Q^T from registers (lane l: row
 //    l % 16, same d).  Lane l then holds tokens 4 (l / 16) + 0..3 of each
-//    half for row l % 16, and owns that row's running max, sum and rescale.
-//  * The value product O^T = V^T P^T also uses v_mfma_f32_16x16x32, with
-//    k-group g of the 32 tokens being {4g .. 4g+3} of the first half and
-//    {16+4g .. 16+4g+3} of the second -- what each lane already holds of P^T
+//    quarter for row l % 16, and owns that row's running max, sum and
+//    rescale.
+//  * The value product O^T = V^T P^T also uses v_mfma_f32_16x16x32, once
+//    per 32 tokens (two quarters), with k-group g of the 32 tokens being
+//    {4g .. 4g+3} of the first quarter and {16+4g .. 16+4g+3} of the
+//    second -- what each lane already holds of P^T
 //    after the softmax, so the weights feed the MFMA from registers.  The
 //    matching V^T operand (lane l: d = l % 16 of a 16-wide block, the same 8
 //    tokens) comes from the row-major V tile through ds_read_b64_tr_b16:
