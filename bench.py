@@ -548,11 +548,13 @@ def main() -> int:
     cl = tensors.int32(b.context_lens, dev)
     sm = tensors.int32(b.slot_mapping, dev)
     max_ctx = b.max_context_len
+    # the split a scheduler holding the lengths on the host would ask for
+    psize = args.partition_size or binding.paged_attn_decode_partition_size_for_lengths(
+        b.context_lens, Hq, Hkv, D, bs, b.max_blocks_per_seq, b.dtype_code)
     P = binding.paged_attn_decode_partition_size(S, Hq, Hkv, D, bs, b.max_blocks_per_seq,
-                                                 max_ctx, args.partition_size, b.dtype_code)
+                                                 max_ctx, psize, b.dtype_code)
     ws_bytes = binding.paged_attn_decode_workspace_bytes(S, Hq, Hkv, D, bs, b.max_blocks_per_seq,
-                                                         max_ctx, args.partition_size,
-                                                         b.dtype_code)
+                                                         max_ctx, psize, b.dtype_code)
     workspace = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
 
     def step(i, ev=None):
@@ -564,11 +566,11 @@ def main() -> int:
         if not args.fused:
             binding.paged_attn_decode(query, kc, vc, bt, cl, b.scale, out,
                                       max_context_len=max_ctx,
-                                      partition_size=args.partition_size, workspace=workspace)
+                                      partition_size=psize, workspace=workspace)
         else:
             binding.paged_attn_decode_write(query, new_key, new_value, sm, kc, vc, bt, cl,
                                             b.scale, out, max_context_len=max_ctx,
-                                            partition_size=args.partition_size,
+                                            partition_size=psize,
                                             workspace=workspace)
         if ev is not None:
             ev[1].record()

@@ -146,6 +146,20 @@ PAGED_KV_API int paged_attn_decode_partition_size(
     int max_blocks_per_seq, int max_context_len, int partition_size, int dtype);
 
 /*
+ * A partition size to pass to paged_attn_decode when the caller holds the
+ * batch's context lengths on the host (as the scheduler that builds the
+ * batch does): host_context_lens [num_seqs] int32 in host memory, read here
+ * and not kept.  The automatic choice sizes partitions from the longest
+ * context; when the batch needs a split and its lengths are very uneven
+ * (the longest above 1.5 times the mean) this returns the finest split
+ * instead, so that the long contexts' workgroups do not finish far behind
+ * the rest.  A negative paged_kv_status code when the arguments are invalid.
+ */
+PAGED_KV_API int paged_attn_decode_partition_size_for_lengths(
+    const int32_t *host_context_lens, int num_seqs, int num_q_heads, int num_kv_heads,
+    int head_dim, int block_size, int max_blocks_per_seq, int dtype);
+
+/*
  * Bytes of workspace paged_attn_decode needs for these arguments (0 when the
  * context is not split); (size_t)-1 for invalid arguments.  The split-context
  * partials are fp32: per (sequence, query head, partition) a running max, a

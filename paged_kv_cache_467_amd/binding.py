@@ -25,6 +25,7 @@ EXPORTED = (
     "paged_attn_decode",
     "paged_attn_decode_write",
     "paged_attn_decode_partition_size",
+    "paged_attn_decode_partition_size_for_lengths",
     "paged_attn_decode_workspace_bytes",
     "kv_cache_write",
     "paged_kv_gather",
@@ -49,6 +50,7 @@ def _load_library(path: str = LIBRARY) -> ctypes.CDLL:
     lib.paged_kv_status_string.restype = ctypes.c_char_p
     lib.paged_attn_decode.argtypes = [vp, vp, vp, vp, vp, cf, vp] + [ci] * 10 + [vp, sz, vp]
     lib.paged_attn_decode_write.argtypes = [vp] * 8 + [cf, vp] + [ci] * 10 + [vp, sz, vp]
+    lib.paged_attn_decode_partition_size_for_lengths.argtypes = [vp] + [ci] * 7
     lib.paged_attn_decode_write.restype = ci
     lib.paged_attn_decode.restype = ci
     lib.paged_attn_decode_partition_size.argtypes = [ci] * 9
@@ -133,6 +135,21 @@ def paged_attn_decode_partition_size(num_seqs, num_q_heads, num_kv_heads, head_d
                                               partition_size, dtype)
     if r < 0:
         raise PagedKVError("paged_attn_decode_partition_size", -r)
+    return r
+
+
+def paged_attn_decode_partition_size_for_lengths(context_lens, num_q_heads, num_kv_heads,
+                                                 head_dim, block_size, max_blocks_per_seq,
+                                                 dtype=PAGED_KV_BF16) -> int:
+    """The partition size for a batch whose lengths are known on the host
+    (numpy array or CPU tensor of int32); see the header."""
+    import numpy as np
+    lens = np.ascontiguousarray(np.asarray(context_lens), dtype=np.int32)
+    r = _lib.paged_attn_decode_partition_size_for_lengths(
+        lens.ctypes.data_as(ctypes.c_void_p), lens.size, num_q_heads, num_kv_heads, head_dim,
+        block_size, max_blocks_per_seq, dtype)
+    if r < 0:
+        raise PagedKVError("paged_attn_decode_partition_size_for_lengths", -r)
     return r
 
 

@@ -53,6 +53,17 @@ int paged_attn_decode_partition_size(int num_seqs, int num_q_heads, int num_kv_h
     return pl.status == PAGED_KV_OK ? pl.partition_size : -pl.status;
 }
 
+int paged_attn_decode_partition_size_for_lengths(const int32_t *host_context_lens,
+                                                 int num_seqs, int num_q_heads,
+                                                 int num_kv_heads, int head_dim, int block_size,
+                                                 int max_blocks_per_seq, int dtype) {
+    if (num_seqs < 0) return -PAGED_KV_ERR_BAD_SHAPE;
+    if (num_seqs > 0 && !host_context_lens) return -PAGED_KV_ERR_NULL_POINTER;
+    return pkv::plan_partition_for_lengths(host_context_lens, num_seqs, num_q_heads,
+                                           num_kv_heads, head_dim, block_size,
+                                           max_blocks_per_seq, dtype);
+}
+
 size_t paged_attn_decode_workspace_bytes(int num_seqs, int num_q_heads, int num_kv_heads,
                                          int head_dim, int block_size, int max_blocks_per_seq,
                                          int max_context_len, int partition_size, int dtype) {

@@ -77,6 +77,9 @@ DecodePlan plan_decode(int num_seqs, int num_q_heads, int num_kv_heads, int head
                        int partition_size, int dtype);
 // Floats per partition in each split-scratch array (rounded for alignment),
 // and the workspace bytes the plan needs (0 without a split).
+int plan_partition_for_lengths(const int32_t *lens, int num_seqs, int num_q_heads,
+                               int num_kv_heads, int head_dim, int block_size,
+                               int max_blocks_per_seq, int dtype);
 size_t decode_partial_floats(int num_seqs, int num_q_heads);
 size_t decode_workspace_bytes(const DecodePlan &pl, int num_seqs, int num_q_heads, int head_dim);
 

@@ -41,6 +41,7 @@ def lib():
     for name in ("paged_kv_swap_out", "paged_kv_swap_in"):
         getattr(lib, name).argtypes = [vp] * 5 + [ci] * 7 + [vp]
     lib.paged_attn_decode_write.argtypes = [vp] * 8 + [cf, vp] + [ci] * 10 + [vp, sz, vp]
+    lib.paged_attn_decode_partition_size_for_lengths.argtypes = [vp] + [ci] * 7
     lib.paged_kv_prefix_hash.argtypes = [vp] * 3 + [ci] * 4 + [ctypes.c_uint64, vp, vp]
     lib.paged_kv_prefix_insert.argtypes = [vp, vp, ci, vp, vp, ci, vp, vp]
     lib.paged_kv_prefix_match.argtypes = [vp, vp, ci, ci, vp, vp, ci, vp, vp, vp]
@@ -53,7 +54,7 @@ def test_header_declares_the_entry_points():
         "paged_attn_decode_workspace_bytes", "kv_cache_write", "paged_kv_gather",
         "paged_kv_copy_blocks", "paged_attn_prefill", "paged_kv_swap_out", "paged_kv_swap_in",
         "paged_kv_prefix_hash", "paged_kv_prefix_insert", "paged_kv_prefix_match",
-        "paged_attn_decode_write"])
+        "paged_attn_decode_write", "paged_attn_decode_partition_size_for_lengths"])
 
 
 def test_library_exports_only_the_entry_points():
@@ -279,3 +280,26 @@ def test_decode_write_rejects(lib, kw, status):
         a["cl"], a["scale"], a["out"], a["num_seqs"], a["num_q_heads"], a["num_kv_heads"],
         a["head_dim"], a["block_size"], a["num_blocks"], a["max_blocks_per_seq"],
         a["max_context_len"], a["partition_size"], a["dtype"], None, 0, None) == status
+
+
+def test_partition_for_host_lengths(lib):
+    """Uneven lengths in a batch that needs a split get the finest split;
+    even lengths keep the automatic rule (sized by the longest context); a
+    batch with enough work units is not split."""
+    import numpy as np
+    f = lib.paged_attn_decode_partition_size_for_lengths
+
+    def plan(lens, *shape):
+        a = np.ascontiguousarray(lens, dtype=np.int32)
+        return f(a.ctypes.data_as(ctypes.c_void_p), a.size, *shape)
+    rng = np.random.default_rng(5)
+    uneven = rng.integers(1, 2049, size=50)                  # 50 sequences, 40 MHA heads
+    assert plan(uneven, 40, 40, 128, 16, 128, 1) == 256
+    even = rng.integers(24576, 32769, size=8)                # 8 long contexts, GQA
+    p = plan(even, 32, 8, 128, 32, 1024, 2)
+    assert p == lib.paged_attn_decode_partition_size(8, 32, 8, 128, 32, 1024, int(even.max()), 0, 2)
+    assert p >= 512
+    many = rng.integers(512, 641, size=256)                  # enough units: no split
+    assert plan(many, 32, 8, 128, 16, 40, 2) >= int(many.max())
+    assert plan(uneven, 40, 40, 96, 16, 128, 1) == -UNSUPPORTED
+    assert plan(np.array([5000]), 8, 8, 128, 16, 128, 2) == -BAD_SHAPE  # longer than the table
