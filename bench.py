@@ -560,6 +560,8 @@ def main() -> int:
     def step(i, ev=None):
         kc, vc = copies[i % len(copies)]
         if not args.fused:
+            if ev is not None:
+                ev[2].record()
             binding.kv_cache_write(new_key, new_value, sm, kc, vc)
         if ev is not None:
             ev[0].record()
@@ -598,13 +600,15 @@ def main() -> int:
     elapsed = time.perf_counter() - t0
     ms_per_step = elapsed * 1e3 / steps
 
-    # Each launch on its own, between HIP events on the stream it runs on.
-    events = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+    # Each launch on its own, between HIP events on the stream it runs on
+    # (the write between the third and the first event of its step).
+    events = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(3))
               for _ in range(args.steps)]
     for i in range(args.steps):
         step(args.warmup + i, events[i])
     torch.cuda.synchronize()
-    decode_ms = [a.elapsed_time(z) for a, z in events]
+    decode_ms = [e[0].elapsed_time(e[1]) for e in events]
+    write_ms = None if args.fused else [e[2].elapsed_time(e[0]) for e in events]
     decode_avg_ms = sum(decode_ms) / len(decode_ms)
     b_dec = b.decode_algorithmic_bytes()
     b_step = b_dec + b.write_algorithmic_bytes()
@@ -639,8 +643,12 @@ def main() -> int:
         },
         "seq_per_s_per_layer": round(S / (decode_avg_ms * 1e-3), 1),
         "decode_ms": round(decode_avg_ms, 5),
+        "decode_ms_median": round(float(np.median(decode_ms)), 5),
         "decode_ms_p10_p90": [round(float(np.percentile(decode_ms, 10)), 5),
                               round(float(np.percentile(decode_ms, 90)), 5)],
+        "write_ms": None if write_ms is None else round(sum(write_ms) / len(write_ms), 5),
+        "write_GBps": None if write_ms is None else
+        round(b.write_algorithmic_bytes() / (sum(write_ms) / len(write_ms) * 1e-3) / 1e9, 2),
         "algorithmic_bytes_per_step": b_step,
         "roofline": {
             "bound": "hbm",
@@ -649,6 +657,10 @@ def main() -> int:
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBPS, 4),
             "traffic": traffic,
+            # HBM bytes (counters) over the launch time: differs from achieved
+            # where the batch re-reads cached data (a shared prefix)
+            "traffic_GBps": None if traffic is None else
+            round(traffic / (decode_avg_ms * 1e-3) / 1e9, 2),
             "kernel": "paged_attn_decode" if not args.fused else "paged_attn_decode_write",
             "algorithmic_bytes_per_launch": b_launch,
         },
