@@ -5,7 +5,6 @@ Each mutant is the oracle's C source with one textual change, compiled to a
 temporary library.  A mutant that passes every pin would mean the pins do
 not pin that part of the oracle.
 """
-import json
 import os
 import subprocess
 import sys
