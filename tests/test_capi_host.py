@@ -134,6 +134,11 @@ def test_partition_choice(lib):
     assert ps(8, 32, 8, 128, 32, 1024, 32768, 512, 2) == 512
     # invalid -> negative status
     assert ps(8, 32, 8, 96, 32, 1024, 32768, 0, 2) == -UNSUPPORTED
+    # a workgroup keeps at most 1024 block ids of its partition
+    assert ps(4, 8, 2, 128, 16, 2000, 0, 16384, 2) == 16384
+    assert ps(4, 8, 2, 128, 16, 2000, 0, 16384 + 16, 2) == -BAD_SHAPE
+    assert ps(4, 8, 2, 128, 1, 3000, 0, 1024, 2) == 1024
+    assert ps(4, 8, 2, 128, 1, 3000, 0, 1024 + 16, 2) == -BAD_SHAPE
     assert lib.paged_attn_decode_workspace_bytes(256, 32, 8, 128, 16, 40, 640, 0, 2) == 0
 
 

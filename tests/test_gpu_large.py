@@ -1,0 +1,232 @@
+"""GPU parity at the largest sizes the entry points take.
+
+* A pool of more than 4 GiB per cache, with every block a batch uses placed
+  past the first 4.5 GiB, so that each kernel's block and slot offsets need
+  more than 32 bits: the result must carry the bits of the same call on a
+  pool that holds only those blocks (and agree with the oracle).
+* Decode partitions of the largest length a workgroup takes (1024 blocks),
+  over contexts that need several of them.
+
+Bars as in the other parity tests: bit-exact for copies and writes, max-abs
+2e-2 and normwise relative 1e-2 for f16/bf16 attention (2e-3 max-abs f32).
+"""
+import sys
+
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+pytestmark = pytest.mark.gpu
+
+import oracle  # noqa: E402
+from paged_kv_cache_467_amd import tensors, workloads as W  # noqa: E402
+
+DEV = "cuda:0"
+TOL = {"f32": (2e-3, None), "f16": (2e-2, 1e-2), "bf16": (2e-2, 1e-2)}
+FAR = 4.5 * 2**30          # bytes of pool in front of the first block in use
+MAX_PARTITION_BLOCKS = 1024
+
+
+def _say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def B():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from paged_kv_cache_467_amd import binding
+    return binding
+
+
+@pytest.fixture(autouse=True)
+def _release_pools():
+    yield
+    if torch.cuda.is_available():
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+
+
+def check_close(got, ref, dtype, what=""):
+    got = np.asarray(got, dtype=np.float64)
+    assert got.shape == ref.shape
+    assert np.all(np.isfinite(got)), f"{what}: non-finite output"
+    err = np.abs(got - ref).max() if got.size else 0.0
+    nrm = np.linalg.norm(ref)
+    rel = np.linalg.norm(got - ref) / nrm if nrm > 0 else 0.0
+    amax, rmax = TOL[dtype]
+    _say(f"  {what}: max|err| {err:.3e}  normwise rel {rel:.3e}")
+    assert err <= amax, f"{what}: max abs error {err}"
+    if rmax is not None:
+        assert rel <= rmax, f"{what}: normwise relative error {rel}"
+
+
+def bits(t):
+    return tensors.to_host_bits(t).view(np.uint8)
+
+
+class FarPool:
+    """The batch's pool copied to blocks base .. base + num_blocks - 1 of a
+    pool of base + num_blocks blocks (the blocks in front are never read),
+    with the block tables and slots renumbered to match."""
+
+    def __init__(self, b):
+        self.b = b
+        block_bytes = b.block_size * b.num_kv_heads * b.head_dim * b.elem_bytes
+        self.base = int(-(-FAR // block_bytes))
+        self.num_blocks = self.base + b.num_blocks
+        shape = (self.num_blocks, b.block_size, b.num_kv_heads, b.head_dim)
+        self.key_cache = torch.empty(shape, dtype=tensors.TORCH_DTYPE[b.dtype], device=DEV)
+        self.value_cache = torch.empty_like(self.key_cache)
+        self.restore()
+        bt = b.block_tables.copy()
+        bt[(bt >= 0) & (bt < b.num_blocks)] += self.base
+        sm = b.slot_mapping.copy()
+        sm[sm >= 0] += self.base * b.block_size
+        self.block_tables = tensors.int32(bt, DEV)
+        self.slot_mapping = tensors.int32(sm, DEV)
+        assert self.base * block_bytes >= 2**32
+
+    def restore(self):
+        """Put the batch's original pool contents back."""
+        self.key_cache[self.base:] = tensors.to_device(self.b.key_cache, self.b.dtype, DEV)
+        self.value_cache[self.base:] = tensors.to_device(self.b.value_cache, self.b.dtype, DEV)
+
+    def used(self, cache):
+        return cache[self.base:]
+
+
+# (dtype, Hq, Hkv, D): the matrix-core decode, the MHA and the f32 decode
+DECODE = [("bf16", 32, 8, 128), ("f16", 8, 8, 128), ("f32", 16, 4, 64)]
+
+
+@pytest.mark.parametrize("dtype,Hq,Hkv,D", DECODE)
+def test_far_pool_write_and_decode(B, dtype, Hq, Hkv, D):
+    """kv_cache_write, paged_attn_decode (with and without a split) and
+    paged_attn_decode_write on a pool whose blocks in use lie past 4.5 GiB."""
+    b = W.make_custom(4100 + D + Hq, dtype=dtype, num_seqs=6, num_q_heads=Hq, num_kv_heads=Hkv,
+                      head_dim=D, block_size=16, context_lens=(1, 17, 300, 1000, 2049, 640),
+                      extra_blocks=4, poison=True)
+    far = FarPool(b)
+    _say(f"far pool {dtype} Hq={Hq} Hkv={Hkv} D={D}: blocks from {far.base} "
+         f"({far.num_blocks} blocks per cache)")
+    near = tensors.device_batch(b, DEV)
+    B.kv_cache_write(near.new_key, near.new_value, near.slot_mapping, near.key_cache,
+                     near.value_cache)
+    B.kv_cache_write(near.new_key, near.new_value, far.slot_mapping, far.key_cache,
+                     far.value_cache)
+    torch.cuda.synchronize()
+    assert np.array_equal(bits(far.used(far.key_cache)), bits(near.key_cache))
+    assert np.array_equal(bits(far.used(far.value_cache)), bits(near.value_cache))
+    ref = b.copy()
+    oracle.write_batch(ref)
+    assert np.array_equal(bits(near.key_cache), ref.key_cache.view(np.uint8))
+    want = oracle.decode_batch(ref)
+
+    for P in (0, 256):
+        _say(f"  paged_attn_decode partition_size={P}")
+        out_far = torch.empty_like(near.query)
+        B.paged_attn_decode(near.query, near.key_cache, near.value_cache, near.block_tables,
+                            near.context_lens, b.scale, near.out, partition_size=P)
+        B.paged_attn_decode(near.query, far.key_cache, far.value_cache, far.block_tables,
+                            near.context_lens, b.scale, out_far, partition_size=P)
+        torch.cuda.synchronize()
+        assert np.array_equal(bits(out_far), bits(near.out))
+        check_close(tensors.widen(tensors.to_host_bits(out_far), dtype), want, dtype,
+                    f"far decode P={P}")
+
+    _say("  paged_attn_decode_write")
+    far.restore()
+    out_far = torch.empty_like(near.query)
+    B.paged_attn_decode_write(near.query, near.new_key, near.new_value, far.slot_mapping,
+                              far.key_cache, far.value_cache, far.block_tables,
+                              near.context_lens, b.scale, out_far, partition_size=256)
+    torch.cuda.synchronize()
+    assert np.array_equal(bits(out_far), bits(near.out))
+    assert np.array_equal(bits(far.used(far.key_cache)), bits(near.key_cache))
+    assert np.array_equal(bits(far.used(far.value_cache)), bits(near.value_cache))
+
+
+def test_far_pool_gather_and_copy(B):
+    """paged_kv_gather and paged_kv_copy_blocks past 4.5 GiB, the last block
+    of the pool included as a copy destination."""
+    b = W.make_custom(4200, dtype="bf16", num_seqs=4, num_q_heads=32, num_kv_heads=8,
+                      head_dim=128, block_size=16, context_lens=(33, 700, 1, 257),
+                      extra_blocks=12, poison=True)
+    far = FarPool(b)
+    _say(f"far pool gather / copy: blocks from {far.base} ({far.num_blocks} blocks per cache)")
+    near = tensors.device_batch(b, DEV)
+    L = b.max_context_len
+    shape = (b.num_seqs, L, b.num_kv_heads, b.head_dim)
+    # rows past a sequence's length are left untouched: start from zeros
+    outs = [torch.zeros(shape, dtype=torch.bfloat16, device=DEV) for _ in range(4)]
+    B.paged_kv_gather(near.key_cache, near.value_cache, near.block_tables, near.context_lens,
+                      outs[0], outs[1])
+    B.paged_kv_gather(far.key_cache, far.value_cache, far.block_tables, near.context_lens,
+                      outs[2], outs[3])
+    torch.cuda.synchronize()
+    assert np.array_equal(bits(outs[2]), bits(outs[0]))
+    assert np.array_equal(bits(outs[3]), bits(outs[1]))
+
+    rng = np.random.default_rng(4201)
+    perm = rng.permutation(b.num_blocks - 1)
+    # five copies among the blocks, then one into the pool's very last block
+    last = b.num_blocks - 1
+    pairs = np.concatenate([np.stack([perm[:5], perm[5:10]], axis=1),
+                            [[perm[10], last]]]).astype(np.int32)
+    B.paged_kv_copy_blocks(far.key_cache, far.value_cache, tensors.int32(pairs + far.base, DEV))
+    torch.cuda.synchronize()
+    rk, rv = b.key_cache.copy(), b.value_cache.copy()
+    oracle.copy_blocks(rk, rv, pairs, "bf16")
+    assert np.array_equal(rk[last], b.key_cache[perm[10]])
+    assert np.array_equal(bits(far.key_cache[far.base:]), rk.view(np.uint8))
+    assert np.array_equal(bits(far.value_cache[far.base:]), rv.view(np.uint8))
+
+
+def test_far_pool_prefill(B):
+    """paged_attn_prefill on a pool whose blocks in use lie past 4.5 GiB."""
+    pb = W.make_prefill(4300, dtype="bf16", num_q_heads=32, num_kv_heads=8, head_dim=128,
+                        block_size=16, context_lens=(700, 1500, 64), query_lens=(200, 130, 64),
+                        poison=True)
+    far = FarPool(pb.base)
+    _say(f"far pool prefill: blocks from {far.base} ({far.num_blocks} blocks per cache)")
+    near = tensors.device_batch(pb.base, DEV)
+    q = tensors.to_device(pb.query, "bf16", DEV)
+    qs = tensors.int32(pb.query_start, DEV)
+    out_near, out_far = torch.empty_like(q), torch.empty_like(q)
+    mq = int(pb.query_lens.max())
+    B.paged_attn_prefill(q, near.key_cache, near.value_cache, near.block_tables,
+                         near.context_lens, qs, pb.scale, out_near, max_query_len=mq)
+    B.paged_attn_prefill(q, far.key_cache, far.value_cache, far.block_tables, near.context_lens,
+                         qs, pb.scale, out_far, max_query_len=mq)
+    torch.cuda.synchronize()
+    assert np.array_equal(bits(out_far), bits(out_near))
+    want = oracle.paged_attention_prefill(pb.query, pb.key_cache, pb.value_cache,
+                                          pb.block_tables, pb.context_lens, pb.query_start,
+                                          pb.scale, pb.dtype)
+    check_close(tensors.widen(tensors.to_host_bits(out_far), "bf16"), want, "bf16", "far prefill")
+
+
+@pytest.mark.parametrize("dtype,G,bs,lens", [
+    ("bf16", 4, 16, (16384, 16385, 40000, 5)),
+    ("f16", 1, 16, (16384, 33000, 100)),
+    ("f32", 2, 1, (1024, 1025, 3000, 2))])
+def test_decode_largest_partition(B, dtype, G, bs, lens):
+    """The longest partition a decode workgroup takes (1024 blocks), forced,
+    over contexts of one, just over one and several such partitions."""
+    P = MAX_PARTITION_BLOCKS * bs
+    b = W.make_custom(4400 + G + bs, dtype=dtype, num_seqs=len(lens), num_q_heads=2 * G,
+                      num_kv_heads=2, head_dim=128, block_size=bs, context_lens=lens,
+                      extra_blocks=3, poison=True)
+    _say(f"decode {dtype} G={G} bs={bs} partition_size={P} lengths {lens}")
+    d = tensors.device_batch(b, DEV)
+    B.paged_attn_decode(d.query, d.key_cache, d.value_cache, d.block_tables, d.context_lens,
+                        b.scale, d.out, partition_size=P)
+    torch.cuda.synchronize()
+    check_close(tensors.widen(tensors.to_host_bits(d.out), dtype), oracle.decode_batch(b), dtype,
+                f"P={P}")
+    with pytest.raises(B.PagedKVError):
+        B.paged_attn_decode(d.query, d.key_cache, d.value_cache, d.block_tables,
+                            d.context_lens, b.scale, d.out, partition_size=P + bs * 16)
