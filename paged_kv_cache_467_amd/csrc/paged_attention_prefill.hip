@@ -140,17 +140,17 @@ __device__ inline uint64_t lds_read_tr16(const uint16_t *p) {
 // Units are dispatched longest sequence first, so that the launch ends on
 // short ones (4% less time on the chunked-prefill workload, whose lengths
 // range over a factor of two): the sequence at position r of that order,
-// by descending context length, ties by index.  Each lane ranks one
-// sequence against all of them (a strict total order, so the ranks are a
-// permutation of 0 .. S - 1); with more than kSortedDispatchMaxSeqs
-// sequences the batch order is kept.
-constexpr int kSortedDispatchMaxSeqs = 64;
+// by descending context length, ties by index.  Lane i holds sequence i's
+// length and ranks it against the others' (read across lanes; a strict
+// total order, so the ranks are a permutation of 0 .. S - 1); with more
+// than one wave's worth of sequences the batch order is kept.
+constexpr int kSortedDispatchMaxSeqs = kWave;
 __device__ inline int seq_by_length_rank(const int32_t *lens, int num_seqs, int r) {
     const int i = threadIdx.x % kWave;
     const int li = i < num_seqs ? lens[i] : 0;
     int rank = 0;
     for (int j = 0; j < num_seqs; ++j) {
-        const int lj = lens[j];
+        const int lj = __builtin_amdgcn_readlane(li, j);
         rank += (lj > li || (lj == li && j < i)) ? 1 : 0;
     }
     const uint64_t hit = __builtin_amdgcn_ballot_w64(i < num_seqs && rank == r);
