@@ -180,3 +180,47 @@ def test_prefill_scale_sign_and_range(B, scale):
                        block_size=16, context_lens=(70, 200, 33), query_lens=(70, 64, 1),
                        poison=True, scale=scale)
     check_close(tensors.widen(run_prefill(B, b), "bf16"), ref_prefill(b), f"scale={scale}")
+
+
+def _many(seed, S, tie_every=0):
+    """S short sequences of random lengths (every tie_every-th one repeats
+    its neighbour's length and query count)."""
+    rng = np.random.default_rng(seed)
+    lens = rng.integers(1, 161, size=S)
+    qlens = np.minimum(lens, rng.integers(1, 41, size=S))
+    if tie_every:
+        lens[1::tie_every] = lens[0::tie_every][:len(lens[1::tie_every])]
+        qlens[1::tie_every] = qlens[0::tie_every][:len(qlens[1::tie_every])]
+    return W.make_prefill(seed, dtype="bf16", num_q_heads=8, num_kv_heads=2, head_dim=64,
+                          block_size=16, context_lens=tuple(int(x) for x in lens),
+                          query_lens=tuple(int(x) for x in qlens), poison=True)
+
+
+def _reorder(b, order):
+    """The same sequences in another batch order."""
+    base = b.base.copy()
+    base.block_tables = np.ascontiguousarray(b.block_tables[order])
+    base.context_lens = np.ascontiguousarray(b.context_lens[order])
+    rows = [b.query[b.query_start[s]:b.query_start[s + 1]] for s in order]
+    qs = np.zeros(len(order) + 1, dtype=np.int32)
+    qs[1:] = np.cumsum([len(r) for r in rows])
+    return W.PrefillBatch(base, np.ascontiguousarray(np.concatenate(rows)), qs)
+
+
+@pytest.mark.parametrize("S,tie_every", [(64, 3), (65, 0), (100, 4)])
+def test_prefill_many_sequences(B, S, tie_every):
+    """Workgroups are dispatched longest sequence first for up to 64
+    sequences (ranked inside the kernel, ties by index) and in batch order
+    beyond: both against the oracle, and a sequence's rows carry the same
+    bits whatever its place in the batch."""
+    b = _many(3700 + S, S, tie_every)
+    _say(f"prefill with {S} sequences, {b.total_q} new tokens")
+    got = run_prefill(B, b)
+    check_close(tensors.widen(got, "bf16"), ref_prefill(b), f"S={S}")
+    order = np.random.default_rng(S).permutation(S)
+    moved = _reorder(b, order)
+    got2 = run_prefill(B, moved)
+    r = moved.query_start
+    for k, s in enumerate(order):
+        q0, q1 = b.query_start[s], b.query_start[s + 1]
+        assert np.array_equal(got2[r[k]:r[k + 1]], got[q0:q1]), f"sequence {s}"
