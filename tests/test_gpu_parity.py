@@ -200,6 +200,29 @@ def test_decode_workload(B, name):
     check_close(tensors.widen(got, b.dtype), oracle_out(name), b.dtype, name)
 
 
+@pytest.mark.parametrize("name", W.WORKLOADS)
+def test_decode_workload_bench_launch(B, name):
+    """The launch bench.py times: max_context_len from the batch, the split
+    a scheduler holding the lengths on the host asks for, and a workspace
+    the caller allocated."""
+    b = workload(name)
+    psize = B.paged_attn_decode_partition_size_for_lengths(
+        b.context_lens, b.num_q_heads, b.num_kv_heads, b.head_dim, b.block_size,
+        b.max_blocks_per_seq, b.dtype_code)
+    ws_bytes = B.paged_attn_decode_workspace_bytes(
+        b.num_seqs, b.num_q_heads, b.num_kv_heads, b.head_dim, b.block_size,
+        b.max_blocks_per_seq, b.max_context_len, psize, b.dtype_code)
+    _say(f"decode {name} as benchmarked: partition {psize}, workspace {ws_bytes} B")
+    d = tensors.device_batch(b, DEV)
+    ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=DEV)
+    B.paged_attn_decode(d.query, d.key_cache, d.value_cache, d.block_tables, d.context_lens,
+                        b.scale, d.out, max_context_len=b.max_context_len,
+                        partition_size=psize, workspace=ws)
+    torch.cuda.synchronize()
+    check_close(tensors.widen(tensors.to_host_bits(d.out), b.dtype), oracle_out(name), b.dtype,
+                f"{name} P={psize}")
+
+
 @pytest.mark.parametrize("name", ["llama13b_mha_f16", "shared_prefix_bf16", "llama3_8b_gqa_bf16"])
 def test_decode_step_write_then_attend(B, name):
     """One decode step: write each sequence's new token at position L-1,
