@@ -82,6 +82,18 @@ def test_prefill_shapes(B, dtype, D, G, bs):
     check_close(tensors.widen(got, dtype), ref_prefill(b), f"{dtype} D={D} G={G} bs={bs}")
 
 
+@pytest.mark.parametrize("bs", [2, 8, 64, 128, 256])
+def test_prefill_block_sizes(B, bs):
+    """Block sizes below 16 (a 16-token quarter of a tile spans blocks: ids
+    per token) and above 32 (a tile inside one block), with contexts that
+    end inside a block and span several."""
+    lens, qlens = (1, 300, 517, 64), (1, 300, 45, 20)
+    b = W.make_prefill(3150 + bs, dtype="bf16", num_q_heads=8, num_kv_heads=2, head_dim=128,
+                       block_size=bs, context_lens=lens, query_lens=qlens, extra_blocks=3,
+                       poison=True)
+    check_close(tensors.widen(run_prefill(B, b), "bf16"), ref_prefill(b), f"bs={bs}")
+
+
 @pytest.mark.parametrize("Hkv,G", [(8, 4), (3, 1), (1, 8), (40, 1)])
 def test_prefill_head_counts(B, Hkv, G):
     lens, qlens = (130, 64, 300), (130, 3, 70)
