@@ -272,6 +272,33 @@ def test_decode_shapes(B, dtype, D, G, bs):
         check_close(tensors.widen(got, dtype), ref, dtype, f"{dtype} D={D} G={G} bs={bs} P={P}")
 
 
+@pytest.mark.parametrize("dtype,G", [("bf16", 4), ("f16", 1), ("f32", 2)])
+@pytest.mark.parametrize("bs", [2, 64, 128, 256])
+def test_decode_block_sizes(B, dtype, G, bs):
+    """Block sizes outside the common 1..32, with and without a split, and
+    the one-launch step at the same shapes."""
+    lens = (1, 63, 64, 65, 700, 257)
+    b = W.make_custom(2500 + bs + G, dtype=dtype, num_seqs=len(lens), num_q_heads=2 * G,
+                      num_kv_heads=2, head_dim=128, block_size=bs, context_lens=lens,
+                      extra_blocks=3, poison=True)
+    ref = oracle.decode_batch(b)
+    for P in (0, 2 * max(bs, 16)):
+        got = run_decode(B, b, partition_size=P)
+        check_close(tensors.widen(got, dtype), ref, dtype, f"{dtype} G={G} bs={bs} P={P}")
+    d = tensors.device_batch(b, DEV)
+    B.paged_attn_decode_write(d.query, d.new_key, d.new_value, d.slot_mapping, d.key_cache,
+                              d.value_cache, d.block_tables, d.context_lens, b.scale, d.out)
+    torch.cuda.synchronize()
+    stepped = b.copy()
+    oracle.write_batch(stepped)
+    for dev_pool, ref_pool in ((d.key_cache, stepped.key_cache),
+                               (d.value_cache, stepped.value_cache)):
+        assert np.array_equal(tensors.to_host_bits(dev_pool).view(np.uint8),
+                              ref_pool.view(np.uint8))      # bits: the pool holds NaN poison
+    check_close(tensors.widen(tensors.to_host_bits(d.out), dtype), oracle.decode_batch(stepped),
+                dtype, f"{dtype} G={G} bs={bs} fused step")
+
+
 # kv-head counts that give 1, 2 or 4 kv heads per decode workgroup and one
 # or several workgroups per sequence
 HEAD_GROUPS = [("bf16", 1, 4), ("f16", 3, 1), ("bf16", 6, 2), ("f16", 8, 8), ("bf16", 12, 4),
