@@ -236,3 +236,33 @@ def test_prefill_many_sequences(B, S, tie_every):
     for k, s in enumerate(order):
         q0, q1 = b.query_start[s], b.query_start[s + 1]
         assert np.array_equal(got2[r[k]:r[k + 1]], got[q0:q1]), f"sequence {s}"
+
+
+def test_prefill_graph_replay(B):
+    """The prefill captured in a HIP graph: every replay, with eager work
+    and synchronisations between replays, gives the eager result's bits."""
+    b = W.make_prefill(3801, dtype="bf16", num_q_heads=32, num_kv_heads=8, head_dim=128,
+                       block_size=16, context_lens=(700, 90, 333), query_lens=(128, 90, 1),
+                       poison=True)
+    _say("paged_attn_prefill in a HIP graph")
+    want = run_prefill(B, b)
+    d = tensors.device_batch(b.base, DEV)
+    q = tensors.to_device(b.query, "bf16", DEV)
+    qs = tensors.int32(b.query_start, DEV)
+    out = torch.empty_like(q)
+    mq = int(b.query_lens.max())
+    graph = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(graph, stream=side):
+            B.paged_attn_prefill(q, d.key_cache, d.value_cache, d.block_tables, d.context_lens,
+                                 qs, b.scale, out, max_query_len=mq,
+                                 max_context_len=b.base.max_context_len)
+    torch.cuda.current_stream().wait_stream(side)
+    for r in range(4):
+        out.fill_(0.0)                       # eager work between replays
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(tensors.to_host_bits(out), want), f"replay {r}"
