@@ -389,7 +389,8 @@ def bench_swap(args) -> int:
     return 0
 
 
-MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "f16": 2500.0}
+# dense matrix-core peaks of the MI355X (fp32: the fp32 matrix instructions)
+MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "f16": 2500.0, "f32": 157.3}
 
 
 def bench_prefill(args) -> int:
@@ -406,7 +407,10 @@ def bench_prefill(args) -> int:
     name = "llama3_8b_chunked_prefill_bf16"
     dev = torch.device("cuda:0")
     b = W.make_prefill_workload(name, values=False)
-    dt = tensors.TORCH_DTYPE[b.dtype]
+    dtype = args.prefill_dtype or b.dtype      # the same shapes in another element type
+    if dtype != b.dtype:
+        name = name[:-len(b.dtype)] + dtype
+    dt = tensors.TORCH_DTYPE[dtype]
     pool_shape = (b.num_blocks, b.block_size, b.num_kv_heads, b.head_dim)
     copies = [(torch.randn(pool_shape, device=dev).to(dt), torch.randn(pool_shape, device=dev).to(dt))
               for _ in range(max(1, args.copies))]
@@ -438,12 +442,12 @@ def bench_prefill(args) -> int:
     avg = sum(ms) / len(ms)
     flops = b.flops()
     tflops = flops / (avg * 1e-3) / 1e12
-    peak = MFMA_PEAK_TFLOPS[b.dtype]
+    peak = MFMA_PEAK_TFLOPS[dtype]
     result = {
         "metric": "chunked-prefill paged attention: achieved TFLOP/s (% of MFMA peak)",
         "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(elapsed * 1e3 / args.steps, 5),
-        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": b.dtype,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": dtype,
         "data": "synthetic",
         "config": {"workload": name, "num_seqs": b.num_seqs, "new_tokens": b.total_q,
                    "context_len_range": [int(b.context_lens.min()), int(b.context_lens.max())],
@@ -451,7 +455,7 @@ def bench_prefill(args) -> int:
                    "head_dim": b.head_dim, "block_size": b.block_size, "pool_copies": len(copies)},
         "prefill_ms": round(avg, 5),
         "new_tokens_per_s": round(b.total_q / (avg * 1e-3), 1),
-        "algorithmic_bytes_per_launch": b.algorithmic_bytes(),
+        "algorithmic_bytes_per_launch": b.algorithmic_bytes(tensors.ELEM_BYTES[dtype]),
         "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": peak,
                      "unit": "TFLOP/s", "frac": round(tflops / peak, 4), "traffic": None,
                      "kernel": "paged_attn_prefill", "flops_per_launch": flops},
@@ -495,6 +499,9 @@ def main() -> int:
     ap.add_argument("--fused", action="store_true",
                     help="time the decode step as one paged_attn_decode_write launch instead "
                          "of kv_cache_write + paged_attn_decode")
+    ap.add_argument("--prefill-dtype", choices=("bf16", "f16", "f32"), default=None,
+                    help="--op prefill: element type of the pool and queries (default: the "
+                         "workload's, bf16)")
     ap.add_argument("--op", choices=("decode", "copy_blocks", "prefill", "swap_out", "swap_in",
                                      "prefix_cache"),
                     default="decode",

@@ -205,8 +205,9 @@ PAGED_KV_API int kv_cache_write(
  *   out[row, h, :] = sum_j softmax(x)_j * value_cache[block, offset, h / G, :],
  * with position j at block block_tables[s][j / block_size], offset
  * j % block_size ("大模型推理框架 vllm 源码解析 一", §三).  With q_len = 1
- * this is paged_attn_decode.  Accumulation is fp32 (the weights enter the
- * value product rounded to the element type); out is rounded to nearest
+ * this is paged_attn_decode.  Accumulation is fp32 (for f16 and bf16 the
+ * weights enter the value product rounded to the element type; f32 runs
+ * on the fp32 matrix instructions throughout); out is rounded to nearest
  * even.
  *
  * Arguments:
@@ -219,7 +220,7 @@ PAGED_KV_API int kv_cache_write(
  *   max_query_len  upper bound on every q_len (sizes the grid)
  *   max_context_len  upper bound on every L; 0 means
  *                  max_blocks_per_seq * block_size
- * Supported: dtype f16, bf16 (f32: PAGED_KV_ERR_UNSUPPORTED); head_dim 64,
+ * Supported: dtype f32, f16, bf16; head_dim 64,
  * 128, 256; num_q_heads / num_kv_heads in {1, 2, 4, 8}; block_size a power
  * of two in [1, 256].  No workspace; nothing is allocated.
  * Device-side values: a sequence with q_len > L or L > max_context_len gets

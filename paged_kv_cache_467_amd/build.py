@@ -6,7 +6,7 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIBRARY = os.path.join(HERE, "libpaged_kv.so")
-SOURCES = ["paged_attention_decode.hip", "paged_attention_prefill.hip", "kv_cache_ops.hip",
+SOURCES = ["paged_attention_decode.hip", "paged_attention_prefill.hip", "paged_attention_prefill_f32.hip", "kv_cache_ops.hip",
            "prefix_cache.hip", "decode_plan.cpp", "capi.cpp"]
 ARCH = os.environ.get("PAGED_KV_ARCH", "gfx950")
 

@@ -202,8 +202,8 @@ int paged_attn_prefill(const void *query, const void *key_cache, const void *val
                        int total_q, int num_q_heads, int num_kv_heads, int head_dim,
                        int block_size, int num_blocks, int max_blocks_per_seq,
                        int max_query_len, int max_context_len, int dtype, void *stream) {
-    if (dtype == PAGED_KV_F32) return PAGED_KV_ERR_UNSUPPORTED;
-    if (dtype != PAGED_KV_F16 && dtype != PAGED_KV_BF16) return PAGED_KV_ERR_UNSUPPORTED;
+    if (dtype != PAGED_KV_F32 && dtype != PAGED_KV_F16 && dtype != PAGED_KV_BF16)
+        return PAGED_KV_ERR_UNSUPPORTED;
     if (num_seqs < 0 || total_q < 0 || num_q_heads < 1 || num_kv_heads < 1 ||
         num_q_heads % num_kv_heads != 0 || num_blocks < 1 || max_blocks_per_seq < 1 ||
         max_query_len < 0 || max_context_len < 0)
@@ -219,7 +219,8 @@ int paged_attn_prefill(const void *query, const void *key_cache, const void *val
     if (max_ctx > table_tokens || !isfinite(scale)) return PAGED_KV_ERR_BAD_SHAPE;
     const int e = elem_bytes(dtype);
     if ((int64_t)block_size * num_kv_heads * head_dim * e > INT_MAX) return PAGED_KV_ERR_BAD_SHAPE;
-    const int rpb = pkv::prefill_rows_per_block(head_dim);
+    const int rpb = dtype == PAGED_KV_F32 ? pkv::prefill_f32_rows_per_block()
+                                          : pkv::prefill_rows_per_block(head_dim);
     const int64_t row_blocks = ((int64_t)max_query_len * group + rpb - 1) / rpb;
     if ((int64_t)num_seqs * num_kv_heads * row_blocks > INT_MAX) return PAGED_KV_ERR_BAD_SHAPE;
     if (num_seqs == 0 || total_q == 0 || max_query_len == 0) return PAGED_KV_OK;
@@ -257,7 +258,9 @@ int paged_attn_prefill(const void *query, const void *key_cache, const void *val
     p.row_stride_bytes = num_kv_heads * head_dim * e;
     p.block_stride_bytes = (int64_t)block_size * p.row_stride_bytes;
     const hipError_t err =
-        pkv::launch_prefill(p, dtype, head_dim, static_cast<hipStream_t>(stream));
+        dtype == PAGED_KV_F32
+            ? pkv::launch_prefill_f32(p, head_dim, static_cast<hipStream_t>(stream))
+            : pkv::launch_prefill(p, dtype, head_dim, static_cast<hipStream_t>(stream));
     return err == hipSuccess ? PAGED_KV_OK : PAGED_KV_ERR_HIP;
 }
 

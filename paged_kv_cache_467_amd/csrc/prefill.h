@@ -1,5 +1,5 @@
 // Internal interface between the C ABI (capi.cpp) and the multi-token
-// (chunked-prefill) attention kernel.
+// (chunked-prefill) attention kernels.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -35,7 +35,10 @@ struct PrefillParams {
 
 // Query rows (new token, query head) one prefill workgroup covers.
 int prefill_rows_per_block(int head_dim);
-// dtype codes match paged_kv_dtype (f16 and bf16 only).
+int prefill_f32_rows_per_block();
+// dtype codes match paged_kv_dtype: the 16-bit kernel (f16, bf16) ...
 hipError_t launch_prefill(const PrefillParams &p, int dtype, int head_dim, hipStream_t stream);
+// ... and the fp32 kernel.
+hipError_t launch_prefill_f32(const PrefillParams &p, int head_dim, hipStream_t stream);
 
 }  // namespace pkv

@@ -356,11 +356,12 @@ class PrefillBatch:
                 total += int(q * (L - q) + q * (q + 1) // 2)
         return total * self.base.num_q_heads * 4 * self.base.head_dim
 
-    def algorithmic_bytes(self) -> int:
+    def algorithmic_bytes(self, elem_bytes: int | None = None) -> int:
         """Each sequence's K/V rows once, the queries read, the outputs
-        written, block-table entries and the two length arrays."""
+        written, block-table entries and the two length arrays (elements of
+        elem_bytes bytes, default the batch's own)."""
         b = self.base
-        e = b.elem_bytes
+        e = b.elem_bytes if elem_bytes is None else elem_bytes
         L = b.context_lens.astype(np.int64)
         kv = int(L.sum()) * b.num_kv_heads * b.head_dim * e * 2
         qo = 2 * self.total_q * b.num_q_heads * b.head_dim * e

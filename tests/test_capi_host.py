@@ -209,9 +209,10 @@ def prefill(lib, **kw):
 
 
 @pytest.mark.parametrize("kw,status", [
-    (dict(dtype=0), UNSUPPORTED),                      # f32 has no prefill kernel
     (dict(dtype=9), UNSUPPORTED),
     (dict(head_dim=96), UNSUPPORTED),
+    (dict(dtype=0, head_dim=96), UNSUPPORTED),
+    (dict(dtype=0, query=None), NULLPTR),
     (dict(num_q_heads=6, num_kv_heads=4), BAD_SHAPE),
     (dict(num_q_heads=48, num_kv_heads=2), UNSUPPORTED),  # group 24
     (dict(block_size=12), UNSUPPORTED),

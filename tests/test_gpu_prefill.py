@@ -2,7 +2,7 @@
 called through the C ABI, against the CPU oracle on the same seeded inputs.
 
 Bar: max-abs 2e-2 and normwise relative 1e-2 (f16/bf16, fp32 accumulation),
-the same as the decode; bit-identical results where the inputs are
+max-abs 2e-3 (f32), the same as the decode; bit-identical results where the inputs are
 bit-identical (poisoned unreferenced cells, relabelled blocks, repeated runs).
 """
 import functools
@@ -34,16 +34,21 @@ def B():
     return binding
 
 
-def check_close(got, ref, what=""):
+TOL = {"f32": (2e-3, None), "f16": (2e-2, 1e-2), "bf16": (2e-2, 1e-2)}
+
+
+def check_close(got, ref, what="", dtype="bf16"):
     got = np.asarray(got, dtype=np.float64)
     assert got.shape == ref.shape
     assert np.all(np.isfinite(got)), f"{what}: non-finite output"
     err = np.abs(got - ref).max() if got.size else 0.0
     nrm = np.linalg.norm(ref)
     rel = np.linalg.norm(got - ref) / nrm if nrm > 0 else 0.0
+    amax, rmax = TOL[dtype]
     _say(f"  {what}: max|err| {err:.3e}  normwise rel {rel:.3e}")
-    assert err <= 2e-2, f"{what}: max abs error {err}"
-    assert rel <= 1e-2, f"{what}: normwise relative error {rel}"
+    assert err <= amax, f"{what}: max abs error {err}"
+    if rmax is not None:
+        assert rel <= rmax, f"{what}: normwise relative error {rel}"
 
 
 def run_prefill(B, b, d=None, max_query_len=None, out_fill=None):
@@ -65,8 +70,8 @@ def ref_prefill(b):
                                           b.context_lens, b.query_start, b.scale, b.dtype)
 
 
-SHAPES = [(dt, D, G, bs) for dt in ("bf16", "f16") for D in (64, 128, 256) for G in (1, 2, 4, 8)
-          for bs in (1, 16, 32) if not (bs == 1 and D == 256)]
+SHAPES = [(dt, D, G, bs) for dt in ("bf16", "f16", "f32") for D in (64, 128, 256)
+          for G in (1, 2, 4, 8) for bs in (1, 16, 32) if not (bs == 1 and D == 256)]
 
 
 @pytest.mark.parametrize("dtype,D,G,bs", SHAPES)
@@ -79,19 +84,21 @@ def test_prefill_shapes(B, dtype, D, G, bs):
                        head_dim=D, block_size=bs, context_lens=lens, query_lens=qlens,
                        extra_blocks=4, poison=True)
     got = run_prefill(B, b)
-    check_close(tensors.widen(got, dtype), ref_prefill(b), f"{dtype} D={D} G={G} bs={bs}")
+    check_close(tensors.widen(got, dtype), ref_prefill(b), f"{dtype} D={D} G={G} bs={bs}", dtype)
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
 @pytest.mark.parametrize("bs", [2, 8, 64, 128, 256])
-def test_prefill_block_sizes(B, bs):
+def test_prefill_block_sizes(B, bs, dtype):
     """Block sizes below 16 (a 16-token quarter of a tile spans blocks: ids
     per token) and above 32 (a tile inside one block), with contexts that
     end inside a block and span several."""
     lens, qlens = (1, 300, 517, 64), (1, 300, 45, 20)
-    b = W.make_prefill(3150 + bs, dtype="bf16", num_q_heads=8, num_kv_heads=2, head_dim=128,
+    b = W.make_prefill(3150 + bs, dtype=dtype, num_q_heads=8, num_kv_heads=2, head_dim=128,
                        block_size=bs, context_lens=lens, query_lens=qlens, extra_blocks=3,
                        poison=True)
-    check_close(tensors.widen(run_prefill(B, b), "bf16"), ref_prefill(b), f"bs={bs}")
+    check_close(tensors.widen(run_prefill(B, b), dtype), ref_prefill(b), f"{dtype} bs={bs}",
+                dtype)
 
 
 @pytest.mark.parametrize("Hkv,G", [(8, 4), (3, 1), (1, 8), (40, 1)])
@@ -141,34 +148,36 @@ def test_prefill_one_token_matches_decode_kernel(B):
     check_close(dec, ref, "decode")
 
 
-def test_prefill_poison_and_permutation_bit_identical(B):
-    kw = dict(dtype="f16", num_q_heads=8, num_kv_heads=2, head_dim=128, block_size=16,
+@pytest.mark.parametrize("dtype", ["f16", "f32"])
+def test_prefill_poison_and_permutation_bit_identical(B, dtype):
+    kw = dict(dtype=dtype, num_q_heads=8, num_kv_heads=2, head_dim=128, block_size=16,
               context_lens=(90, 31, 200), query_lens=(40, 31, 1), extra_blocks=7)
     clean = W.make_prefill(3301, poison=False, **kw)
     dirty = W.make_prefill(3301, poison=True, **kw)
-    a = run_prefill(B, clean)
-    c = run_prefill(B, dirty)
+    a = run_prefill(B, clean).view(np.uint8)
+    c = run_prefill(B, dirty).view(np.uint8)
     assert np.array_equal(a, c)
     perm = W.PrefillBatch(W.permute_blocks(dirty.base, 4), dirty.query, dirty.query_start)
-    assert np.array_equal(run_prefill(B, perm), c)
-    assert np.array_equal(run_prefill(B, dirty), c)        # deterministic
+    assert np.array_equal(run_prefill(B, perm).view(np.uint8), c)
+    assert np.array_equal(run_prefill(B, dirty).view(np.uint8), c)        # deterministic
 
 
-def test_prefill_invalid_device_values(B):
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_prefill_invalid_device_values(B, dtype):
     """A sequence with more new tokens than cached ones, or with a table
     entry outside the pool, gets NaN rows; the other sequences are exact."""
-    b = W.make_prefill(3401, dtype="bf16", num_q_heads=8, num_kv_heads=2, head_dim=64,
+    b = W.make_prefill(3401, dtype=dtype, num_q_heads=8, num_kv_heads=2, head_dim=64,
                        block_size=16, context_lens=(40, 50, 60), query_lens=(10, 20, 30),
                        poison=True)
     ref = ref_prefill(b)
     bad = b.copy()
     bad.base.context_lens[0] = 5               # q_len 10 > L 5
     bad.base.block_tables[2, 0] = b.num_blocks + 9
-    got = tensors.widen(run_prefill(B, bad), "bf16")
+    got = tensors.widen(run_prefill(B, bad), dtype)
     q = b.query_start
     assert np.all(np.isnan(got[q[0]:q[1]]))
     assert np.all(np.isnan(got[q[2]:q[3]]))
-    check_close(got[q[1]:q[2]], ref[q[1]:q[2]], "valid neighbour")
+    check_close(got[q[1]:q[2]], ref[q[1]:q[2]], "valid neighbour", dtype)
 
 
 def test_prefill_rows_past_max_query_len_untouched(B):
@@ -182,16 +191,18 @@ def test_prefill_rows_past_max_query_len_untouched(B):
     check_close(wide[20:], ref[20:], "second sequence")
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
 @pytest.mark.parametrize("scale", [0.0, -0.0884, 3.0, -3.0])
-def test_prefill_scale_sign_and_range(B, scale):
+def test_prefill_scale_sign_and_range(B, scale, dtype):
     """A zero scale (uniform weights), negative scales (the query's sign is
     flipped inside the kernel) and scales large enough that the weights span
     hundreds of binary orders of magnitude: a running max reduced over the
     wrong lanes would overflow here."""
-    b = W.make_prefill(3601, dtype="bf16", num_q_heads=8, num_kv_heads=2, head_dim=128,
+    b = W.make_prefill(3601, dtype=dtype, num_q_heads=8, num_kv_heads=2, head_dim=128,
                        block_size=16, context_lens=(70, 200, 33), query_lens=(70, 64, 1),
                        poison=True, scale=scale)
-    check_close(tensors.widen(run_prefill(B, b), "bf16"), ref_prefill(b), f"scale={scale}")
+    check_close(tensors.widen(run_prefill(B, b), dtype), ref_prefill(b),
+                f"{dtype} scale={scale}", dtype)
 
 
 def _many(seed, S, tie_every=0):
