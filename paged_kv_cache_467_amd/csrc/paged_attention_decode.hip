@@ -19,9 +19,8 @@
 // heads that share that kv head, so every K/V byte is read once for all G
 // heads.  The waves of a workgroup read the same token rows side by side (a
 // block of all kv heads is one contiguous stretch of the pool), and a wave's
-// result needs no merge with other waves.  K/V tiles are loaded DEPTH - 1
-// tiles ahead of the one being consumed (DEPTH per kernel below), with
-// non-temporal loads.
+// result needs no merge with other waves.  K/V tiles are loaded one tile
+// ahead of the one being consumed, with non-temporal loads.
 //
 // Addressing: tiles never cross a 16-token boundary, so with block_size >= 16
 // a tile lies in one block and its base address is wave-uniform (block id
@@ -31,11 +30,12 @@
 //
 // Two per-tile inner loops:
 //  * decode_mfma_kernel (f16/bf16, G >= 2): the scores of a 16-token tile for
-//    all G heads are one 16x16x32 MFMA chain; the K rows are loaded straight
-//    into the B operand (lane = token, 16 contiguous bytes per lane), the
-//    query rows (repeated 16/G times) form the A operand.  The softmax
-//    weights are passed through LDS to the lanes that hold the V rows and PV
-//    is accumulated with fp32 FMAs.
+//    all G heads are one 16x16x32 MFMA chain.  K and V rows are both loaded
+//    whole-row coalesced (consecutive lanes read consecutive 16-byte chunks
+//    of one row); K goes through a wave-private LDS slice to the B operand
+//    layout (lane = token), the query rows (repeated 16/G times) form the A
+//    operand.  The softmax weights are passed through LDS to the lanes that
+//    hold the V rows and PV is accumulated with fp32 FMAs.
 //  * decode_valu_kernel (all dtypes, any G): each row of head_dim elements is
 //    spread over head_dim * bytes / 16 lanes, 16 bytes each; scores are dot
 //    products (packed 16-bit dot instructions for f16/bf16, fp32 FMAs for
@@ -54,13 +54,10 @@
 namespace pkv {
 namespace {
 
-// K/V tiles held in registers per wave: one being consumed, the rest in
-// flight.  HBM reads on this part are fastest with about 32 KB in flight per
-// compute unit; with 8 waves per unit the MFMA kernel stays closest to that
-// loading each tile just before it is consumed (measured 2% faster than one
-// tile ahead), while the VALU kernel's longer per-tile work pays for one
-// tile of look-ahead.
-constexpr int kMfmaDepth = 1;
+// K/V tiles held in registers per wave by the VALU kernel: one being
+// consumed, the rest in flight (one tile of look-ahead pays for its longer
+// per-tile work).  The MFMA kernel keeps one tile in registers and one in
+// LDS instead.
 constexpr int kValuDepth = 2;
 
 struct WorkItem {
@@ -411,6 +408,24 @@ __device__ inline f32x4 mfma16x16x32<F16>(const u32x4 &a, const u32x4 &b, const 
 // lane l receives result rows 4 * (l / 16) + r, r = 0..3, of column l % 16.
 // Any pairing of k values works as long as A and B use the same one, so the
 // k-group of lane l in step ks is 16-byte chunk (l / 16) + 4 * ks of a row.
+//
+// K tiles: loading them straight in that B layout makes every load
+// instruction touch 16 rows, 64 bytes each; on this part the same bytes read
+// about 3% faster as whole rows (4 rows x 256 bytes per instruction at
+// D = 128, the V layout).  So K is loaded like V and each wave turns its tile
+// around in its own LDS slice: 16 rows of D * 2 bytes plus a 16-byte pad, so
+// that the 16 rows a B-layout read touches start in different banks.
+//
+// V tiles go through LDS too, in the lanes' own order: a wave's registers
+// are then free for the next tile's loads as soon as the current tile has
+// arrived.
+template <int D>
+constexpr int k_lds_row_bytes() { return D * 2 + 16; }
+template <int D>
+constexpr int v_lds_offset() { return 16 * k_lds_row_bytes<D>(); }
+template <int D>
+constexpr int kv_lds_wave_bytes() { return v_lds_offset<D>() + 16 * D * 2; }
+
 template <class T, int D, int G, bool BT>
 __global__ __launch_bounds__(kMaxDecodeThreads) void decode_mfma_kernel(DecodeParams p) {
     static_assert(T::kBytes == 2, "MFMA path is for 16-bit element types");
@@ -421,13 +436,17 @@ __global__ __launch_bounds__(kMaxDecodeThreads) void decode_mfma_kernel(DecodePa
     constexpr int NV = 16 / TPI;      // V loads per lane per tile
     constexpr int TILE = 16;
     constexpr int HW = G < 4 ? G : 4;  // heads among a lane's four result rows
-    constexpr int DEPTH = kMfmaDepth;
+    constexpr int KRS = k_lds_row_bytes<D>();
+    static_assert(NV == KS, "a K tile in row layout takes as many loads as MFMA steps");
 
     __shared__ int32_t bt_lds[kBtLds];
     // softmax weights of the tile (16-byte aligned: read and written as f32x4)
     __shared__ __attribute__((aligned(16))) float pex[kMaxDecodeWaves][TILE][G];
     __shared__ float aex[kMaxDecodeWaves][G];  // rescale factors, then final m
     __shared__ float lex[kMaxDecodeWaves][G];  // final l
+    // K tiles turned from row layout to the B layout, and V tiles: one slice
+    // per wave, kv_lds_wave_bytes<D>() each (dynamic, sized by the launch)
+    extern __shared__ __attribute__((aligned(16))) char k_lds[];
 
     const WorkItem w = work_item(p);
     write_new_token<T, D>(p, w);
@@ -444,10 +463,14 @@ __global__ __launch_bounds__(kMaxDecodeThreads) void decode_mfma_kernel(DecodePa
     const int vtg = lane / CPR;
     const int vc = lane % CPR;
     const int head_bytes = w.kvh * D * 2;
-    // offsets from the row of the tile's first token
-    const uint32_t k_off = (uint32_t)(kt * p.row_stride_bytes + head_bytes + 16 * rg);
+    // offset from the row of the tile's first token (K and V alike)
     const uint32_t v_off = (uint32_t)(vtg * p.row_stride_bytes + head_bytes + 16 * vc);
     const uint32_t v_step = (uint32_t)(TPI * p.row_stride_bytes);
+    // this wave's K slice (row-layout writes, B-layout reads) and V slice
+    char *k_slice = k_lds + wave * kv_lds_wave_bytes<D>();
+    char *k_wr = k_slice + vtg * KRS + 16 * vc;
+    const char *k_rd = k_slice + kt * KRS + 16 * rg;
+    char *v_slot = k_slice + v_lds_offset<D>() + lane * 16;
     // row group rg holds heads 4 * rg .. 4 * rg + HW - 1; groups with
     // 4 * rg >= G hold copies of those rows
     const bool owns_rows = 4 * rg < G;
@@ -476,119 +499,120 @@ __global__ __launch_bounds__(kMaxDecodeThreads) void decode_mfma_kernel(DecodePa
     const int span = w.tok_end - w.tok_begin;
     const int ntiles = bad ? 0 : (span + TILE - 1) / TILE;
     const int nfull = bad ? 0 : span / TILE;
-    u32x4 kbuf[DEPTH][KS], vbuf[DEPTH][NV];
+    // K and V of the tile in flight, in row layout
+    u32x4 kbuf[NV], vbuf[NV];
 
-    auto load = [&](int tile, int slot, bool full) {
+    auto load = [&](int tile, bool full) {
         const int t0 = w.tok_begin + tile * TILE;
+        if (BT && full) {
+            const int64_t base = uniform_row_offset(p, bt_lds, b0, t0);
+            const char *kb = p.key_cache + base;
+            const char *vb = p.value_cache + base;
 #pragma unroll
-        for (int j = 0; j < DEPTH; ++j) {
-            if (j != slot) continue;
-            if (BT && full) {
-                const int64_t base = uniform_row_offset(p, bt_lds, b0, t0);
-                const char *kb = p.key_cache + base;
-                const char *vb = p.value_cache + base;
+            for (int i = 0; i < NV; ++i) kbuf[i] = load16_stream(kb + (v_off + i * v_step));
 #pragma unroll
-                for (int ks = 0; ks < KS; ++ks)
-                    kbuf[j][ks] = load16_stream(kb + (k_off + 64 * ks));
-#pragma unroll
-                for (int i = 0; i < NV; ++i) vbuf[j][i] = load16_stream(vb + (v_off + i * v_step));
-            } else {
-                const int t = t0 + kt;
-                if (t < w.tok_end) {
-                    const char *row = p.key_cache + row_offset(p, bt_lds, b0, t, head_bytes);
-#pragma unroll
-                    for (int ks = 0; ks < KS; ++ks)
-                        kbuf[j][ks] = load16_stream(row + 16 * (rg + 4 * ks));
-                } else {
-#pragma unroll
-                    for (int ks = 0; ks < KS; ++ks) kbuf[j][ks] = u32x4{0, 0, 0, 0};
-                }
-#pragma unroll
-                for (int i = 0; i < NV; ++i) {
-                    const int tv = t0 + i * TPI + vtg;
-                    if (tv < w.tok_end)
-                        vbuf[j][i] = load16_stream(
-                            p.value_cache + row_offset(p, bt_lds, b0, tv, head_bytes) + 16 * vc);
-                    else
-                        vbuf[j][i] = u32x4{0, 0, 0, 0};
-                }
-            }
-        }
-    };
-
-    auto consume = [&](int tile, int slot, bool full) {
-#pragma unroll
-        for (int j = 0; j < DEPTH; ++j) {
-            if (j != slot) continue;
-            f32x4 s = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-            for (int ks = 0; ks < KS; ++ks) s = mfma16x16x32<T>(qa[ks], kbuf[j][ks], s);
-
-            const bool valid = full || w.tok_begin + tile * TILE + kt < w.tok_end;
-            float sc[4];
-            bool up = false;
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                sc[r] = valid ? s[r] * p.scale_log2 : -INFINITY;
-                up |= sc[r] > m[r];
-            }
-            // Every head is held by some lane, so "no lane's score exceeds its
-            // row's max" means no head's max moves in this tile.
-            const bool rescale = __builtin_amdgcn_ballot_w64(up) != 0;
-            if (rescale) {
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const float mn = vmax(m[r], group_max<16>(sc[r]));  // 16 tokens of the tile
-                    const float alpha = fast_exp2(m[r] - mn);          // 0 on the first tile
-                    m[r] = mn;
-                    l[r] *= alpha;
-                    if (r < HW && owns_rows && kt == 0) aex[wave][4 * rg + r] = alpha;
-                }
-            }
-            float pr[4];
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                pr[r] = fast_exp2(sc[r] - m[r]);
-                l[r] += pr[r];
-            }
-            if (owns_rows) {
-                if constexpr (HW == 4) {
-                    *reinterpret_cast<f32x4 *>(&pex[wave][kt][4 * rg]) =
-                        f32x4{pr[0], pr[1], pr[2], pr[3]};
-                } else {
-#pragma unroll
-                    for (int r = 0; r < HW; ++r) pex[wave][kt][4 * rg + r] = pr[r];
-                }
-            }
-            // The weights were written by this wave; LDS executes a wave's
-            // accesses in order, so only compiler ordering must be kept.
-            __builtin_amdgcn_wave_barrier();
-            if (rescale) {
-                float alpha[G];
-#pragma unroll
-                for (int g = 0; g < G; ++g) alpha[g] = aex[wave][g];
-#pragma unroll
-                for (int g = 0; g < G; ++g)
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) acc[g][e] *= alpha[g];
-            }
+            for (int i = 0; i < NV; ++i) vbuf[i] = load16_stream(vb + (v_off + i * v_step));
+        } else {
 #pragma unroll
             for (int i = 0; i < NV; ++i) {
-                float v[8];
-                T::widen(vbuf[j][i], v);
-                float pw[G];
-#pragma unroll
-                for (int g = 0; g < G; ++g) pw[g] = pex[wave][i * TPI + vtg][g];
-#pragma unroll
-                for (int g = 0; g < G; ++g)
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) acc[g][e] = fmaf(pw[g], v[e], acc[g][e]);
+                const int tv = t0 + i * TPI + vtg;
+                if (tv < w.tok_end) {
+                    const int64_t o = row_offset(p, bt_lds, b0, tv, head_bytes) + 16 * vc;
+                    kbuf[i] = load16_stream(p.key_cache + o);
+                    vbuf[i] = load16_stream(p.value_cache + o);
+                } else {
+                    kbuf[i] = u32x4{0, 0, 0, 0};
+                    vbuf[i] = u32x4{0, 0, 0, 0};
+                }
             }
-            __builtin_amdgcn_wave_barrier();
         }
     };
 
-    run_tiles<DEPTH>(ntiles, nfull, load, consume);
+    // Per tile: the tile's K and V go from registers to this wave's LDS
+    // slices as soon as they arrive, which frees the registers for the next
+    // tile's loads; those are issued before the tile's arithmetic, so every
+    // wave keeps one tile in flight while it computes.  LDS executes a
+    // wave's accesses in order, so only compiler ordering must be kept.
+    if (ntiles > 0) load(0, 0 < nfull);
+    for (int tile = 0; tile < ntiles; ++tile) {
+        const bool full = tile < nfull;
+#pragma unroll
+        for (int i = 0; i < NV; ++i) {
+            *reinterpret_cast<u32x4 *>(k_wr + i * TPI * KRS) = kbuf[i];
+            *reinterpret_cast<u32x4 *>(v_slot + i * (kWave * 16)) = vbuf[i];
+        }
+        if (tile + 1 < ntiles) load(tile + 1, tile + 1 < nfull);
+        __builtin_amdgcn_wave_barrier();
+        // scores: K in the B layout
+        u32x4 kb[KS];
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) kb[ks] = *reinterpret_cast<const u32x4 *>(k_rd + 64 * ks);
+        f32x4 s = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) s = mfma16x16x32<T>(qa[ks], kb[ks], s);
+
+        const bool valid = full || w.tok_begin + tile * TILE + kt < w.tok_end;
+        float sc[4];
+        bool up = false;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            sc[r] = valid ? s[r] * p.scale_log2 : -INFINITY;
+            up |= sc[r] > m[r];
+        }
+        // Every head is held by some lane, so "no lane's score exceeds its
+        // row's max" means no head's max moves in this tile.
+        const bool rescale = __builtin_amdgcn_ballot_w64(up) != 0;
+        if (rescale) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const float mn = vmax(m[r], group_max<16>(sc[r]));  // 16 tokens of the tile
+                const float alpha = fast_exp2(m[r] - mn);          // 0 on the first tile
+                m[r] = mn;
+                l[r] *= alpha;
+                if (r < HW && owns_rows && kt == 0) aex[wave][4 * rg + r] = alpha;
+            }
+        }
+        float pr[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            pr[r] = fast_exp2(sc[r] - m[r]);
+            l[r] += pr[r];
+        }
+        if (owns_rows) {
+            if constexpr (HW == 4) {
+                *reinterpret_cast<f32x4 *>(&pex[wave][kt][4 * rg]) =
+                    f32x4{pr[0], pr[1], pr[2], pr[3]};
+            } else {
+#pragma unroll
+                for (int r = 0; r < HW; ++r) pex[wave][kt][4 * rg + r] = pr[r];
+            }
+        }
+        // The weights were written by this wave; LDS executes a wave's
+        // accesses in order, so only compiler ordering must be kept.
+        __builtin_amdgcn_wave_barrier();
+        if (rescale) {
+            float alpha[G];
+#pragma unroll
+            for (int g = 0; g < G; ++g) alpha[g] = aex[wave][g];
+#pragma unroll
+            for (int g = 0; g < G; ++g)
+#pragma unroll
+                for (int e = 0; e < 8; ++e) acc[g][e] *= alpha[g];
+        }
+#pragma unroll
+        for (int i = 0; i < NV; ++i) {
+            float v[8];
+            T::widen(*reinterpret_cast<const u32x4 *>(v_slot + i * (kWave * 16)), v);
+            float pw[G];
+#pragma unroll
+            for (int g = 0; g < G; ++g) pw[g] = pex[wave][i * TPI + vtg][g];
+#pragma unroll
+            for (int g = 0; g < G; ++g)
+#pragma unroll
+                for (int e = 0; e < 8; ++e) acc[g][e] = fmaf(pw[g], v[e], acc[g][e]);
+        }
+        __builtin_amdgcn_wave_barrier();
+    }
 
     // l: sum over the 16 tokens of each row; acc: over the value token slots.
 #pragma unroll
@@ -682,7 +706,8 @@ int blocks_per_cu(int threads) {
     hipError_t e;
     if constexpr (T::kBytes == 2 && G >= 2)
         e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
-            &n, reinterpret_cast<const void *>(&decode_mfma_kernel<T, D, G, BT>), threads, 0);
+            &n, reinterpret_cast<const void *>(&decode_mfma_kernel<T, D, G, BT>), threads,
+            (threads / kWave) * kv_lds_wave_bytes<D>());
     else
         e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
             &n, reinterpret_cast<const void *>(&decode_valu_kernel<T, D, G, BT>), threads, 0);
@@ -719,8 +744,8 @@ hipError_t launch_main(const DecodeParams &p, int kernel, hipStream_t stream) {
     // the VALU kernel (decode_kernel_choice); only those pairs are built.
     if constexpr (T::kBytes == 2 && G >= 2) {
         if (kernel != 1) return hipErrorInvalidValue;
-        hipLaunchKernelGGL((decode_mfma_kernel<T, D, G, BT>), dim3(grid), dim3(threads), 0,
-                           stream, p);
+        hipLaunchKernelGGL((decode_mfma_kernel<T, D, G, BT>), dim3(grid), dim3(threads),
+                           p.heads_per_group * kv_lds_wave_bytes<D>(), stream, p);
     } else {
         if (kernel != 0) return hipErrorInvalidValue;
         hipLaunchKernelGGL((decode_valu_kernel<T, D, G, BT>), dim3(grid), dim3(threads), 0,
