@@ -272,6 +272,25 @@ def test_decode_shapes(B, dtype, D, G, bs):
         check_close(tensors.widen(got, dtype), ref, dtype, f"{dtype} D={D} G={G} bs={bs} P={P}")
 
 
+WIDE = [(dt, D, G, Hkv) for dt in ("f16", "bf16") for D in (64, 128, 256) for G in (2, 4, 8)
+        for Hkv in (4, 8)]
+
+
+@pytest.mark.parametrize("dtype,D,G,Hkv", WIDE)
+def test_decode_mfma_full_workgroups(B, dtype, D, G, Hkv):
+    """The matrix-core decode with four kv heads (four waves, each with its
+    own K/V tile slices in LDS) per workgroup, at every head size: the
+    largest LDS footprint the kernel takes, tiles whole and partial."""
+    lens = (1, 16, 17, 250, 513)
+    b = W.make_custom(3100 + D + 10 * G + Hkv, dtype=dtype, num_seqs=len(lens),
+                      num_q_heads=G * Hkv, num_kv_heads=Hkv, head_dim=D, block_size=16,
+                      context_lens=lens, extra_blocks=4, poison=True)
+    ref = oracle.decode_batch(b)
+    for P in (0, 64):
+        got = run_decode(B, b, partition_size=P)
+        check_close(tensors.widen(got, dtype), ref, dtype, f"{dtype} D={D} G={G} Hkv={Hkv} P={P}")
+
+
 @pytest.mark.parametrize("dtype,G", [("bf16", 4), ("f16", 1), ("f32", 2)])
 @pytest.mark.parametrize("bs", [2, 64, 128, 256])
 def test_decode_block_sizes(B, dtype, G, bs):
