@@ -451,7 +451,6 @@ __global__ __launch_bounds__(kMaxDecodeThreads) void decode_mfma_kernel(DecodePa
     const WorkItem w = work_item(p);
     write_new_token<T, D>(p, w);
     if (!prologue<T, D, G>(p, w)) return;
-    const bool bad = stage_block_table(p, w, bt_lds);
     const int b0 = w.tok_begin >> p.block_shift;
 
     const int wave = threadIdx.x / kWave;
@@ -497,21 +496,22 @@ __global__ __launch_bounds__(kMaxDecodeThreads) void decode_mfma_kernel(DecodePa
         for (int e = 0; e < 8; ++e) acc[g][e] = 0.0f;
 
     const int span = w.tok_end - w.tok_begin;
-    const int ntiles = bad ? 0 : (span + TILE - 1) / TILE;
-    const int nfull = bad ? 0 : span / TILE;
     // K and V of the tile in flight, in row layout
     u32x4 kbuf[NV], vbuf[NV];
 
+    // a whole tile at pool byte offset base (the row of its first token)
+    auto load_full = [&](int64_t base) {
+        const char *kb = p.key_cache + base;
+        const char *vb = p.value_cache + base;
+#pragma unroll
+        for (int i = 0; i < NV; ++i) kbuf[i] = load16_stream(kb + (v_off + i * v_step));
+#pragma unroll
+        for (int i = 0; i < NV; ++i) vbuf[i] = load16_stream(vb + (v_off + i * v_step));
+    };
     auto load = [&](int tile, bool full) {
         const int t0 = w.tok_begin + tile * TILE;
         if (BT && full) {
-            const int64_t base = uniform_row_offset(p, bt_lds, b0, t0);
-            const char *kb = p.key_cache + base;
-            const char *vb = p.value_cache + base;
-#pragma unroll
-            for (int i = 0; i < NV; ++i) kbuf[i] = load16_stream(kb + (v_off + i * v_step));
-#pragma unroll
-            for (int i = 0; i < NV; ++i) vbuf[i] = load16_stream(vb + (v_off + i * v_step));
+            load_full(uniform_row_offset(p, bt_lds, b0, t0));
         } else {
 #pragma unroll
             for (int i = 0; i < NV; ++i) {
@@ -528,12 +528,46 @@ __global__ __launch_bounds__(kMaxDecodeThreads) void decode_mfma_kernel(DecodePa
         }
     };
 
+    // When the first tile is whole and the partition's block ids fit one per
+    // thread, the tile goes out while the ids are staged: the ids' load is
+    // issued first and the tile's block id is read on its own (a scalar
+    // load), so the staging waits only for the ids (loads complete in
+    // order), and all of it is straight-line code, which lets the compiler
+    // count the tile's loads as still in flight.  An id outside the pool
+    // loads block 0 instead (in bounds, never used: the staging flags the
+    // partition).  Other partitions take the general staging first.
+    const int nb = ((w.tok_end - 1) >> p.block_shift) - b0 + 1;
+    const bool early = BT && span >= TILE && nb <= (int)blockDim.x;
+    bool bad;
+    if (early) {
+        const int32_t *row = p.block_tables + (int64_t)w.s * p.max_blocks_per_seq;
+        const int tid = threadIdx.x;
+        const int id = tid < nb ? row[b0 + tid] : 0;
+        // the table is never written by a decode: read as constant memory,
+        // this entry is a scalar load
+        typedef const __attribute__((address_space(4))) int32_t const_i32;
+        int blk = ((const_i32 *)row)[b0];
+        blk = blk >= 0 && blk < p.num_blocks ? blk : 0;
+        load_full((int64_t)blk * p.block_stride_bytes +
+                  (int64_t)(w.tok_begin & (p.block_size - 1)) * p.row_stride_bytes);
+        const bool ok = id >= 0 && id < p.num_blocks;
+        if (tid < nb) bt_lds[tid] = ok ? id : 0;
+        bad = __syncthreads_or(tid < nb && !ok) != 0;
+    } else {
+        bad = stage_block_table(p, w, bt_lds);
+    }
+    const int ntiles = bad ? 0 : (span + TILE - 1) / TILE;
+    const int nfull = bad ? 0 : span / TILE;
+    // a flagged partition never consumes the first tile: let its loads land
+    // before the wave moves on
+    if (bad && early) __builtin_amdgcn_s_waitcnt(0);
+
     // Per tile: the tile's K and V go from registers to this wave's LDS
     // slices as soon as they arrive, which frees the registers for the next
     // tile's loads; those are issued before the tile's arithmetic, so every
     // wave keeps one tile in flight while it computes.  LDS executes a
     // wave's accesses in order, so only compiler ordering must be kept.
-    if (ntiles > 0) load(0, 0 < nfull);
+    if (ntiles > 0 && !early) load(0, 0 < nfull);
     for (int tile = 0; tile < ntiles; ++tile) {
         const bool full = tile < nfull;
 #pragma unroll
