@@ -675,19 +675,38 @@ __global__ __launch_bounds__(kMaxDecodeThreads) void decode_mfma_kernel(DecodePa
 // Cross-partition reduce: out = sum_p 2^(m_p - M) o_p / sum_p 2^(m_p - M) l_p
 // with M = max_p m_p.  One wave per (sequence, query head): the lanes split
 // the partitions for M and the denominator, then each lane owns head_dim / 64
-// output elements and walks the partitions with several loads in flight.
+// output elements and walks the partitions, 16 loads in flight at a time.
 // ------------------------------------------------------------------------
 constexpr int kReduceThreads = 64;
 
 template <class T, int D>
 __global__ __launch_bounds__(kReduceThreads) void decode_reduce_kernel(DecodeParams p) {
     constexpr int EL = D / kReduceThreads;  // output elements per lane: 1, 2 or 4
-    constexpr int UNROLL = 8;
+    constexpr int R = 16;                   // partitions' outputs loaded per round
     const int sh = blockIdx.x;
     const int lane = threadIdx.x;
     const int s = sh / p.num_q_heads;
-    const int L = p.context_lens[s];
     const int64_t obase = (int64_t)sh * D + lane * EL;
+    const int64_t pbase = (int64_t)sh * p.num_partitions;
+    const float *pm = p.part_max + pbase;
+    const float *ps = p.part_sum + pbase;
+    const float *po = p.part_out + pbase * D + lane * EL;
+    const int np = p.num_partitions;
+
+    // Everything up to the first R partitions is loaded before the length is
+    // known (every index stays below num_partitions, inside the workspace;
+    // what lies past this sequence's partitions is masked below), so the
+    // loads take one round trip instead of a chain of them.
+    float mq = lane < np ? pm[lane] : -INFINITY;  // lane q holds partition q < 64
+    float lq = lane < np ? ps[lane] : 0.0f;
+    float v[R][EL];
+#pragma unroll
+    for (int u = 0; u < R; ++u) {
+        const int q = u < np ? u : 0;
+#pragma unroll
+        for (int e = 0; e < EL; ++e) v[u][e] = po[(int64_t)q * D + e];
+    }
+    const int L = p.context_lens[s];
     if (L < 0 || L > p.max_context_len) {
 #pragma unroll
         for (int e = 0; e < EL; ++e) T::store_nan(p.out, obase + e);
@@ -699,35 +718,54 @@ __global__ __launch_bounds__(kReduceThreads) void decode_reduce_kernel(DecodePar
         return;
     }
     const int nparts = (L + p.partition_size - 1) / p.partition_size;
-    const int64_t pbase = (int64_t)sh * p.num_partitions;
-    const float *pm = p.part_max + pbase;
-    const float *ps = p.part_sum + pbase;
-    float M = -INFINITY;
-    for (int q = lane; q < nparts; q += kReduceThreads) M = vmax(M, pm[q]);
+    if (lane >= nparts) {
+        mq = -INFINITY;
+        lq = 0.0f;
+    }
+    float M = mq;
+    for (int q = lane + kReduceThreads; q < nparts; q += kReduceThreads) M = vmax(M, pm[q]);
     M = group_max<kReduceThreads>(M);
-    float Ls = 0.0f;
-    for (int q = lane; q < nparts; q += kReduceThreads) Ls += ps[q] * fast_exp2(pm[q] - M);
+    float Ls = lane < nparts ? lq * fast_exp2(mq - M) : 0.0f;
+    for (int q = lane + kReduceThreads; q < nparts; q += kReduceThreads)
+        Ls += ps[q] * fast_exp2(pm[q] - M);
     Ls = group_sum<kReduceThreads>(Ls);
     const float inv = 1.0f / Ls;
 
-    const float *po = p.part_out + pbase * D + lane * EL;
+    // weight of partition q (q < 64 is held by lane q)
+    const float wl = lane < nparts ? fast_exp2(mq - M) : 0.0f;
+    auto weight = [&](int q) {
+        return q < kReduceThreads
+                   ? __builtin_bit_cast(float, __builtin_amdgcn_readlane(
+                                                   __builtin_bit_cast(int, wl), q))
+                   : fast_exp2(pm[q] - M);
+    };
     float o[EL];
 #pragma unroll
     for (int e = 0; e < EL; ++e) o[e] = 0.0f;
-    for (int q0 = 0; q0 < nparts; q0 += UNROLL) {
-        float v[UNROLL][EL], wq[UNROLL];
 #pragma unroll
-        for (int u = 0; u < UNROLL; ++u) {
-            // past the last partition: reread partition 0 (in bounds, finite) with weight 0
+    for (int u = 0; u < R; ++u) {
+        if (u < nparts) {
+            const float wq = weight(u);
+#pragma unroll
+            for (int e = 0; e < EL; ++e) o[e] = fmaf(wq, v[u][e], o[e]);
+        }
+    }
+    for (int q0 = R; q0 < nparts; q0 += R) {
+#pragma unroll
+        for (int u = 0; u < R; ++u) {
+            // past the last partition: reread partition 0 (in bounds, finite)
             const int q = q0 + u < nparts ? q0 + u : 0;
-            wq[u] = q0 + u < nparts ? fast_exp2(pm[q] - M) : 0.0f;
 #pragma unroll
             for (int e = 0; e < EL; ++e) v[u][e] = po[(int64_t)q * D + e];
         }
 #pragma unroll
-        for (int u = 0; u < UNROLL; ++u)
+        for (int u = 0; u < R; ++u) {
+            if (q0 + u < nparts) {
+                const float wq = weight(q0 + u);
 #pragma unroll
-            for (int e = 0; e < EL; ++e) o[e] = fmaf(wq[u], v[u][e], o[e]);
+                for (int e = 0; e < EL; ++e) o[e] = fmaf(wq, v[u][e], o[e]);
+            }
+        }
     }
 #pragma unroll
     for (int e = 0; e < EL; ++e) T::store(p.out, obase + e, o[e] * inv);
