@@ -104,6 +104,45 @@ __device__ inline bool stage_block_table(const DecodeParams &p, const WorkItem &
     return __syncthreads_or(bad) != 0;
 }
 
+// Stages the block table like stage_block_table, and when `early` also
+// issues the partition's first tile in the middle of it: the ids' load goes
+// out first, the tile's own block id is read on its own (a scalar load:
+// the table is never written by a decode, so it is read as constant
+// memory), issue_first(base) issues the tile, and only then does the
+// staging wait for the ids.  Memory loads complete in order, so that wait
+// does not cover the tile, and the code is straight-line, so the compiler
+// can count the tile's loads as still in flight.  `early` requires
+// block_size >= 16, a whole first tile and at most one id per thread.  An
+// id outside the pool gives base of block 0 (in bounds, never used: the
+// staging flags the partition, and the caller then waits for the loads).
+template <class IssueFirst>
+__device__ inline bool stage_block_table_early(const DecodeParams &p, const WorkItem &w,
+                                               int32_t *bt_lds, bool early,
+                                               IssueFirst &&issue_first) {
+    if (!early) return stage_block_table(p, w, bt_lds);
+    const int b0 = w.tok_begin >> p.block_shift;
+    const int nb = ((w.tok_end - 1) >> p.block_shift) - b0 + 1;
+    const int32_t *row = p.block_tables + (int64_t)w.s * p.max_blocks_per_seq;
+    const int tid = threadIdx.x;
+    const int id = tid < nb ? row[b0 + tid] : 0;
+    typedef const __attribute__((address_space(4))) int32_t const_i32;
+    int blk = ((const_i32 *)row)[b0];
+    blk = blk >= 0 && blk < p.num_blocks ? blk : 0;
+    issue_first((int64_t)blk * p.block_stride_bytes +
+                (int64_t)(w.tok_begin & (p.block_size - 1)) * p.row_stride_bytes);
+    const bool ok = id >= 0 && id < p.num_blocks;
+    if (tid < nb) bt_lds[tid] = ok ? id : 0;
+    return __syncthreads_or(tid < nb && !ok) != 0;
+}
+
+// Whether stage_block_table_early may issue the first tile of `tile` tokens.
+template <bool BT>
+__device__ inline bool first_tile_early(const DecodeParams &p, const WorkItem &w, int tile) {
+    const int b0 = w.tok_begin >> p.block_shift;
+    const int nb = ((w.tok_end - 1) >> p.block_shift) - b0 + 1;
+    return BT && w.tok_end - w.tok_begin >= tile && nb <= (int)blockDim.x;
+}
+
 // Byte offset of (token, kv head) in the pool; token must be in the staged
 // range.
 __device__ inline int64_t row_offset(const DecodeParams &p, const int32_t *bt_lds, int b0,
@@ -224,18 +263,21 @@ __device__ inline void write_result(const DecodeParams &p, const WorkItem &w, in
 // nfull are complete; load(t, slot, full) fills register slot `slot` with
 // tile t, consume(t, slot, full) folds it into the softmax state.  Slots are
 // compile-time indices after unrolling, so the buffers stay in registers.
+// With first_issued, tile 0 is already in flight in slot 0.
 template <int DEPTH, class Load, class Consume>
-__device__ inline void run_tiles(int ntiles, int nfull, Load &&load, Consume &&consume) {
+__device__ inline void run_tiles(int ntiles, int nfull, Load &&load, Consume &&consume,
+                                 bool first_issued = false) {
 #pragma unroll
     for (int j = 0; j < DEPTH - 1; ++j)
-        if (j < ntiles) load(j, j, j < nfull);
+        if (j < ntiles && !(first_issued && j == 0)) load(j, j, j < nfull);
     for (int t0 = 0; t0 < ntiles; t0 += DEPTH) {
 #pragma unroll
         for (int j = 0; j < DEPTH; ++j) {
             const int t = t0 + j;
             if (t < ntiles) {
                 const int ahead = t + DEPTH - 1;
-                if (ahead < ntiles) load(ahead, (j + DEPTH - 1) % DEPTH, ahead < nfull);
+                if (ahead < ntiles && !(first_issued && ahead == 0))
+                    load(ahead, (j + DEPTH - 1) % DEPTH, ahead < nfull);
                 consume(t, j, t < nfull);
             }
         }
@@ -263,7 +305,6 @@ __global__ __launch_bounds__(kMaxDecodeThreads) void decode_valu_kernel(DecodePa
     const WorkItem w = work_item(p);
     write_new_token<T, D>(p, w);
     if (!prologue<T, D, G>(p, w)) return;
-    const bool bad = stage_block_table(p, w, bt_lds);
     const int b0 = w.tok_begin >> p.block_shift;
 
     const int lane = threadIdx.x % kWave;
@@ -290,24 +331,25 @@ __global__ __launch_bounds__(kMaxDecodeThreads) void decode_valu_kernel(DecodePa
     }
 
     const int span = w.tok_end - w.tok_begin;
-    const int ntiles = bad ? 0 : (span + TILE - 1) / TILE;
-    const int nfull = bad ? 0 : span / TILE;
     u32x4 kbuf[DEPTH][NL], vbuf[DEPTH][NL];
 
+    // a whole tile at pool byte offset base (the row of its first token)
+    auto load_full = [&](int64_t base, int j) {
+        const char *kb = p.key_cache + base;
+        const char *vb = p.value_cache + base;
+#pragma unroll
+        for (int i = 0; i < NL; ++i) {
+            kbuf[j][i] = load16_stream(kb + (lane_off + i * step_off));
+            vbuf[j][i] = load16_stream(vb + (lane_off + i * step_off));
+        }
+    };
     auto load = [&](int tile, int slot, bool full) {
         const int t0 = w.tok_begin + tile * TILE;
 #pragma unroll
         for (int j = 0; j < DEPTH; ++j) {
             if (j != slot) continue;
             if (BT && full) {
-                const int64_t base = uniform_row_offset(p, bt_lds, b0, t0);
-                const char *kb = p.key_cache + base;
-                const char *vb = p.value_cache + base;
-#pragma unroll
-                for (int i = 0; i < NL; ++i) {
-                    kbuf[j][i] = load16_stream(kb + (lane_off + i * step_off));
-                    vbuf[j][i] = load16_stream(vb + (lane_off + i * step_off));
-                }
+                load_full(uniform_row_offset(p, bt_lds, b0, t0), j);
             } else {
 #pragma unroll
                 for (int i = 0; i < NL; ++i) {
@@ -371,7 +413,16 @@ __global__ __launch_bounds__(kMaxDecodeThreads) void decode_valu_kernel(DecodePa
         }
     };
 
-    run_tiles<DEPTH>(ntiles, nfull, load, consume);
+    // the first tile goes out while the block ids are staged
+    const bool early = first_tile_early<BT>(p, w, TILE);
+    const bool bad = stage_block_table_early(p, w, bt_lds, early,
+                                             [&](int64_t base) { load_full(base, 0); });
+    // a flagged partition never consumes the first tile: let its loads land
+    // before the wave moves on
+    if (bad && early) __builtin_amdgcn_s_waitcnt(0);
+    const int ntiles = bad ? 0 : (span + TILE - 1) / TILE;
+    const int nfull = bad ? 0 : span / TILE;
+    run_tiles<DEPTH>(ntiles, nfull, load, consume, early);
 
     // Combine the token groups of the wave: l and acc over the TPI groups.
 #pragma unroll
@@ -528,34 +579,9 @@ __global__ __launch_bounds__(kMaxDecodeThreads) void decode_mfma_kernel(DecodePa
         }
     };
 
-    // When the first tile is whole and the partition's block ids fit one per
-    // thread, the tile goes out while the ids are staged: the ids' load is
-    // issued first and the tile's block id is read on its own (a scalar
-    // load), so the staging waits only for the ids (loads complete in
-    // order), and all of it is straight-line code, which lets the compiler
-    // count the tile's loads as still in flight.  An id outside the pool
-    // loads block 0 instead (in bounds, never used: the staging flags the
-    // partition).  Other partitions take the general staging first.
-    const int nb = ((w.tok_end - 1) >> p.block_shift) - b0 + 1;
-    const bool early = BT && span >= TILE && nb <= (int)blockDim.x;
-    bool bad;
-    if (early) {
-        const int32_t *row = p.block_tables + (int64_t)w.s * p.max_blocks_per_seq;
-        const int tid = threadIdx.x;
-        const int id = tid < nb ? row[b0 + tid] : 0;
-        // the table is never written by a decode: read as constant memory,
-        // this entry is a scalar load
-        typedef const __attribute__((address_space(4))) int32_t const_i32;
-        int blk = ((const_i32 *)row)[b0];
-        blk = blk >= 0 && blk < p.num_blocks ? blk : 0;
-        load_full((int64_t)blk * p.block_stride_bytes +
-                  (int64_t)(w.tok_begin & (p.block_size - 1)) * p.row_stride_bytes);
-        const bool ok = id >= 0 && id < p.num_blocks;
-        if (tid < nb) bt_lds[tid] = ok ? id : 0;
-        bad = __syncthreads_or(tid < nb && !ok) != 0;
-    } else {
-        bad = stage_block_table(p, w, bt_lds);
-    }
+    // the first tile goes out while the block ids are staged
+    const bool early = first_tile_early<BT>(p, w, TILE);
+    const bool bad = stage_block_table_early(p, w, bt_lds, early, load_full);
     const int ntiles = bad ? 0 : (span + TILE - 1) / TILE;
     const int nfull = bad ? 0 : span / TILE;
     // a flagged partition never consumes the first tile: let its loads land
