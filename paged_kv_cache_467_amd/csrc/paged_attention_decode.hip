@@ -55,10 +55,14 @@ namespace pkv {
 namespace {
 
 // K/V tiles held in registers per wave by the VALU kernel: one being
-// consumed, the rest in flight (one tile of look-ahead pays for its longer
-// per-tile work).  The MFMA kernel keeps one tile in registers and one in
-// LDS instead.
-constexpr int kValuDepth = 2;
+// consumed, the rest in flight.  For 16-bit types (the multi-head decode)
+// three tiles of look-ahead measured best (on a 13B-shaped f16 batch: 0.9%
+// faster with two than with one, 0.4% more with three, five no better),
+// though it halves the waves a SIMD holds; f32 keeps one, which fits
+// without spilling at every group size.  The MFMA kernel keeps one tile in
+// registers and one in LDS instead.
+constexpr int kValuDepth16 = 4;
+constexpr int kValuDepth32 = 2;
 
 struct WorkItem {
     int s, kvh0, part;  // sequence, first kv head of the workgroup, partition
@@ -298,7 +302,8 @@ __global__ __launch_bounds__(kMaxDecodeThreads) void decode_valu_kernel(DecodePa
     static_assert(CPR >= 4 && CPR <= 64 && kWave % CPR == 0, "row layout");
     static_assert(16 % TILE == 0, "tiles must not cross a 16-token boundary");
     // wide rows or many fp32 accumulators: no room for a second tile
-    constexpr int DEPTH = (D >= 256 || G * EPC >= 32) ? 1 : kValuDepth;
+    constexpr int DEPTH =
+        (D >= 256 || G * EPC >= 32) ? 1 : T::kBytes == 2 ? kValuDepth16 : kValuDepth32;
 
     __shared__ int32_t bt_lds[kBtLds];
 
