@@ -404,6 +404,24 @@ def test_invalid_device_values_give_nan(B):
         check_close(got[2:3], ref[2:3], "bf16", f"valid neighbour P={P}")
 
 
+@pytest.mark.parametrize("dtype,G", [("bf16", 4), ("f16", 1)])
+@pytest.mark.parametrize("first", [-1, "past"])
+def test_invalid_first_block_id_gives_nan(B, dtype, G, first):
+    """An invalid id in the first table entry of a partition whose first tile
+    is whole (the tile the kernels issue before the ids are checked) makes
+    that sequence NaN, with and without a split; the others are unaffected."""
+    b = W.make_custom(131 + G, dtype=dtype, num_seqs=3, num_q_heads=4 * G, num_kv_heads=4,
+                      head_dim=128, block_size=16, context_lens=(48, 100, 37), poison=True)
+    ref = oracle.decode_batch(b)
+    bad = b.copy()
+    bad.block_tables[0, 0] = -1 if first == -1 else b.num_blocks
+    bad.block_tables[1, 2] = -7 if first == -1 else b.num_blocks + 5   # partition 1 at P=32
+    for P in (0, 32):
+        got = tensors.widen(run_decode(B, bad, partition_size=P), dtype)
+        assert np.all(np.isnan(got[0])) and np.all(np.isnan(got[1])), f"P={P}"
+        check_close(got[2:3], ref[2:3], dtype, f"valid neighbour P={P}")
+
+
 FUSED = [("bf16", 32, 8, 128, 16, 0), ("bf16", 32, 8, 128, 16, 64), ("f16", 8, 8, 128, 32, 0),
          ("f32", 8, 2, 64, 16, 32), ("bf16", 16, 4, 256, 1, 0), ("f16", 16, 2, 64, 8, 48)]
 
