@@ -452,6 +452,37 @@ def test_decode_write_equals_write_then_decode(B, dtype, Hq, Hkv, D, bs, psize):
                               tensors.to_host_bits(c).view(np.uint8))
 
 
+@pytest.mark.parametrize("dtype,Hq,Hkv", [("bf16", 16, 4), ("f16", 4, 4), ("f32", 8, 4)])
+def test_decode_write_new_token_in_the_first_tile(B, dtype, Hq, Hkv):
+    """The fused step when the new token sits in a partition's first whole
+    tile (the tile the kernels issue right after the new rows are stored):
+    lengths 16 and 32, 48 with 16-token partitions; same bits as the two
+    calls, and the oracle's result after the oracle's write."""
+    _say(f"paged_attn_decode_write, new token in the first tile: {dtype} Hq={Hq} Hkv={Hkv}")
+    b = W.make_custom(911 + Hq, dtype=dtype, num_seqs=4, num_q_heads=Hq, num_kv_heads=Hkv,
+                      head_dim=128, block_size=16, context_lens=(16, 32, 48, 17),
+                      extra_blocks=3, poison=True)
+    stepped = b.copy()
+    oracle.write_batch(stepped)
+    want = oracle.decode_batch(stepped)
+    for psize in (0, 16):
+        ref, got = tensors.device_batch(b, DEV), tensors.device_batch(b, DEV)
+        B.kv_cache_write(ref.new_key, ref.new_value, ref.slot_mapping, ref.key_cache,
+                         ref.value_cache)
+        B.paged_attn_decode(ref.query, ref.key_cache, ref.value_cache, ref.block_tables,
+                            ref.context_lens, b.scale, ref.out, partition_size=psize)
+        B.paged_attn_decode_write(got.query, got.new_key, got.new_value, got.slot_mapping,
+                                  got.key_cache, got.value_cache, got.block_tables,
+                                  got.context_lens, b.scale, got.out, partition_size=psize)
+        torch.cuda.synchronize()
+        for a, c in ((ref.out, got.out), (ref.key_cache, got.key_cache),
+                     (ref.value_cache, got.value_cache)):
+            assert np.array_equal(tensors.to_host_bits(a).view(np.uint8),
+                                  tensors.to_host_bits(c).view(np.uint8)), f"P={psize}"
+        check_close(tensors.widen(tensors.to_host_bits(got.out), dtype), want, dtype,
+                    f"{dtype} fused P={psize}")
+
+
 def test_decode_write_on_the_bench_batch(B):
     """The Llama-3-8B-shaped batch: fused step equals the two calls, and the
     pool after it equals the oracle's write."""
