@@ -64,6 +64,24 @@ def measured_traffic(workload: str):
     return float(tot.group(1))
 
 
+def time_back_to_back(fn, first: int, steps: int):
+    """Runs fn(first), ..., fn(first + steps - 1) back to back between one
+    pair of HIP events on the current stream (the stream the library's
+    calls run on).  Returns (wall-clock seconds, average ms per call): the
+    gaps between calls are included, and no event pair adds its own cost
+    to each call."""
+    import torch
+    a, z = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    a.record()
+    for i in range(steps):
+        fn(first + i)
+    z.record()
+    torch.cuda.synchronize()
+    return time.perf_counter() - t0, a.elapsed_time(z) / steps
+
+
 def cpu_baseline(workload: str, batch_values, budget_s: float = 10.0):
     """The fp64 CPU oracle on this host's cores, on the whole batch, repeated
     until about budget_s seconds have passed (at least three runs; median),
@@ -143,18 +161,7 @@ def bench_copy_blocks(args) -> int:
 
     for i in range(args.warmup):
         step(i)
-    torch.cuda.synchronize()
-    events = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-              for _ in range(args.steps)]
-    t0 = time.perf_counter()
-    for i, (a, z) in enumerate(events):
-        a.record()
-        step(args.warmup + i)
-        z.record()
-    torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t0
-    ms = [a.elapsed_time(z) for a, z in events]
-    avg = sum(ms) / len(ms)
+    elapsed, avg = time_back_to_back(step, args.warmup, args.steps)
     byt = 2 * 2 * npairs * block_bytes + 8 * npairs
     achieved = byt / (avg * 1e-3) / 1e9
     result = {
@@ -326,16 +333,7 @@ def bench_swap(args) -> int:
     def timed(fn, steps, warmup):
         for i in range(warmup):
             fn(i)
-        torch.cuda.synchronize()
-        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-              for _ in range(steps)]
-        t0 = time.perf_counter()
-        for i, (a, z) in enumerate(ev):
-            a.record()
-            fn(warmup + i)
-            z.record()
-        torch.cuda.synchronize()
-        return time.perf_counter() - t0, sum(a.elapsed_time(z) for a, z in ev) / steps
+        return time_back_to_back(fn, warmup, steps)
 
     elapsed, avg = timed(step, args.steps, args.warmup)
     byt = 2 * npairs * block_bytes
@@ -429,18 +427,7 @@ def bench_prefill(args) -> int:
 
     for i in range(args.warmup):
         step(i)
-    torch.cuda.synchronize()
-    events = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-              for _ in range(args.steps)]
-    t0 = time.perf_counter()
-    for i, (a, z) in enumerate(events):
-        a.record()
-        step(args.warmup + i)
-        z.record()
-    torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t0
-    ms = [a.elapsed_time(z) for a, z in events]
-    avg = sum(ms) / len(ms)
+    elapsed, avg = time_back_to_back(step, args.warmup, args.steps)
     flops = b.flops()
     tflops = flops / (avg * 1e-3) / 1e12
     peak = MFMA_PEAK_TFLOPS[dtype]

@@ -403,14 +403,17 @@ def make_prefill_workload(name: str, seed: int | None = None, poison: bool = Fal
                           values: bool = True) -> PrefillBatch:
     """Chunked prefill on the Llama-3-8B shape: 16 prompts of 1024..2048
     tokens whose last 512 tokens are processed as one chunk (the earlier ones
-    already cached), 32 query / 8 kv heads, head_dim 128, block_size 16,
-    bf16."""
-    if name != "llama3_8b_chunked_prefill_bf16":
+    already cached), 32 query / 8 kv heads, head_dim 128, block_size 16;
+    bf16 (llama3_8b_chunked_prefill_bf16), or the same draws in f16 or f32
+    (the name's suffix)."""
+    stem = "llama3_8b_chunked_prefill_"
+    dtype = name[len(stem):] if name.startswith(stem) else None
+    if dtype not in ("bf16", "f16", "f32"):
         raise ValueError(name)
     seed = 46710 if seed is None else seed
     rng = np.random.default_rng(seed)
     lens = rng.integers(1024, 2048, size=16, endpoint=True)
-    return make_prefill(seed, dtype="bf16", num_q_heads=32, num_kv_heads=8, head_dim=128,
+    return make_prefill(seed, dtype=dtype, num_q_heads=32, num_kv_heads=8, head_dim=128,
                         block_size=16, context_lens=lens, query_lens=np.full(16, 512),
                         pool_factor=1.5, poison=poison, values=values, name=name)
 
