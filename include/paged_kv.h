@@ -117,17 +117,14 @@ PAGED_KV_API int paged_attn_decode(
  * followed by paged_attn_decode, with the same results (pool bits and
  * output) as the two calls.  The worker writes each new token's K/V into its
  * pool cell and the kernel then reads the sequence's history, the new token
- * included ("大模型推理框架VLLM-0.7.3源码", §3.3); this launch takes the new
- * token's K/V from new_key / new_value and stores them in the cell.
+ * included ("大模型推理框架VLLM-0.7.3源码", §3.3).
  *   new_key, new_value  [num_seqs, num_kv_heads, head_dim]: sequence s's new
  *                token, same dtype as query
  *   slot_mapping [num_seqs] int32: its cell (physical_block * block_size +
  *                offset), which must be the cell of position
- *                context_lens[s] - 1 of sequence s, and a cell no other
- *                sequence of the launch reads (position L - 1 is then read
- *                as new_key / new_value); a negative slot, or one outside
- *                the pool, writes nothing, and position L - 1 is read from
- *                the pool
+ *                context_lens[s] - 1 of sequence s (the only cell of the
+ *                launch it then writes and reads); a negative slot, or one
+ *                outside the pool, writes nothing
  *   key_cache, value_cache  updated in place
  * Every other argument, check and status is paged_attn_decode's.
  */

@@ -41,9 +41,8 @@ struct DecodeParams {
     int64_t block_stride_bytes; // bs * Hkv * D * elem bytes
     int row_stride_bytes;       // Hkv * D * elem bytes
     // Fused KV write (null new_key: none): sequence s's new token's rows
-    // new_key/new_value [S, Hkv, D] go to pool cell slot_mapping[s], the
-    // cell of position L - 1, which the attention reads from new_key /
-    // new_value instead.
+    // new_key/new_value [S, Hkv, D] go to pool cell slot_mapping[s] before
+    // the sequence's attention reads its history.
     const char *new_key;
     const char *new_value;
     const int32_t *slot_mapping;

@@ -180,63 +180,33 @@ __device__ void store_constant(const DecodeParams &p, const WorkItem &w, bool na
     }
 }
 
-// Fused KV write.  Sequence s's new token (position L - 1) belongs in pool
-// cell slot_mapping[s], which the caller guarantees is that position's cell
-// (a slot outside the pool writes nothing).  The workgroup whose partition
-// holds position L - 1 (partition 0 when L is 0 or invalid: then nothing is
-// read) writes the rows of its kv heads, each wave its own head's row.  It
-// does not read that cell back: the lanes that load position L - 1 take the
-// row from new_key / new_value instead (subst_token below), so the pool
-// store needs no fence and goes out after the decode, from registers loaded
-// at the start (at most one 16-byte chunk of K and one of V per lane: a
-// row is at most 1 KB).
-struct NewToken {
-    u32x4 k, v;
-    int64_t dst;  // pool byte offset of this wave's row in the token's cell
-    bool write;   // this workgroup stores the token
-    int subst;    // position read from new_key / new_value (-1: none)
-};
-
-template <class T, int D, bool FUSED>
-__device__ inline NewToken fetch_new_token(const DecodeParams &p, const WorkItem &w) {
-    constexpr int kRowBytes = D * T::kBytes;
-    static_assert(kRowBytes <= kWave * 16, "one 16-byte chunk per lane");
-    NewToken nt;
-    nt.write = false;
-    nt.subst = -1;
-    if constexpr (!FUSED) return nt;
+// Fused KV write: the new token of sequence s (position L - 1) goes to its
+// pool cell before the sequence's attention reads it.  The workgroup whose
+// partition holds position L - 1 (partition 0 when L is 0 or invalid: then
+// nothing is read) writes the rows of its kv heads, each wave its own head's
+// row -- the row that wave alone reads back -- and fences it.  A slot outside
+// the pool writes nothing.
+template <class T, int D>
+__device__ inline void write_new_token(const DecodeParams &p, const WorkItem &w) {
+    if (p.new_key == nullptr) return;
     const bool reads = !w.bad_len && w.context_len >= 1;
     const int owner = reads ? (w.context_len - 1) / p.partition_size : 0;
-    if (w.part != owner) return nt;
+    if (w.part != owner) return;
     const int slot = p.slot_mapping[w.s];
-    if (slot < 0 || slot >= p.num_slots) return nt;
-    nt.write = true;
-    nt.subst = reads ? w.context_len - 1 : -1;
-    nt.dst = (int64_t)(slot >> p.block_shift) * p.block_stride_bytes +
-             (int64_t)(slot & (p.block_size - 1)) * p.row_stride_bytes +
-             (int64_t)w.kvh * kRowBytes;
-    const int b = (int)(threadIdx.x % kWave) * 16;
-    if (b < kRowBytes) {
-        const int64_t src = ((int64_t)w.s * p.num_kv_heads + w.kvh) * kRowBytes + b;
-        nt.k = load16(p.new_key + src);
-        nt.v = load16(p.new_value + src);
-    }
-    return nt;
-}
-
-template <class T, int D, bool FUSED>
-__device__ inline void store_new_token(const DecodeParams &p, const NewToken &nt) {
+    if (slot < 0 || slot >= p.num_slots) return;
     constexpr int kRowBytes = D * T::kBytes;
-    const int b = (int)(threadIdx.x % kWave) * 16;
-    if (!FUSED || !nt.write || b >= kRowBytes) return;
-    store16(const_cast<char *>(p.key_cache) + nt.dst + b, nt.k);
-    store16(const_cast<char *>(p.value_cache) + nt.dst + b, nt.v);
-}
-
-// Byte offset of sequence s's new row for kv head kvh in new_key / new_value.
-template <class T, int D>
-__device__ inline int64_t new_row_offset(const DecodeParams &p, const WorkItem &w) {
-    return ((int64_t)w.s * p.num_kv_heads + w.kvh) * (D * T::kBytes);
+    const int lane = threadIdx.x % kWave;
+    const int64_t src = ((int64_t)w.s * p.num_kv_heads + w.kvh) * kRowBytes;
+    const int64_t dst = (int64_t)(slot >> p.block_shift) * p.block_stride_bytes +
+                        (int64_t)(slot & (p.block_size - 1)) * p.row_stride_bytes +
+                        (int64_t)w.kvh * kRowBytes;
+    char *kc = const_cast<char *>(p.key_cache);
+    char *vc = const_cast<char *>(p.value_cache);
+    for (int b = lane * 16; b < kRowBytes; b += kWave * 16) {
+        store16(kc + dst + b, load16(p.new_key + src + b));
+        store16(vc + dst + b, load16(p.new_value + src + b));
+    }
+    __threadfence_block();
 }
 
 // Common prologue.  Returns false when the workgroup has nothing to read (it
@@ -321,7 +291,7 @@ __device__ inline void run_tiles(int ntiles, int nfull, Load &&load, Consume &&c
 // ------------------------------------------------------------------------
 // VALU kernel
 // ------------------------------------------------------------------------
-template <class T, int D, int G, bool BT, bool FUSED>
+template <class T, int D, int G, bool BT>
 __global__ __launch_bounds__(kMaxDecodeThreads) void decode_valu_kernel(DecodeParams p) {
     constexpr int EPC = T::kPerChunk;   // elements per 16-byte chunk
     constexpr int CPR = D / EPC;        // lanes holding one row
@@ -338,11 +308,8 @@ __global__ __launch_bounds__(kMaxDecodeThreads) void decode_valu_kernel(DecodePa
     __shared__ int32_t bt_lds[kBtLds];
 
     const WorkItem w = work_item(p);
-    const NewToken nt = fetch_new_token<T, D, FUSED>(p, w);
-    if (!prologue<T, D, G>(p, w)) {
-        store_new_token<T, D, FUSED>(p, nt);
-        return;
-    }
+    write_new_token<T, D>(p, w);
+    if (!prologue<T, D, G>(p, w)) return;
     const int b0 = w.tok_begin >> p.block_shift;
 
     const int lane = threadIdx.x % kWave;
@@ -381,32 +348,21 @@ __global__ __launch_bounds__(kMaxDecodeThreads) void decode_valu_kernel(DecodePa
             vbuf[j][i] = load16_stream(vb + (lane_off + i * step_off));
         }
     };
-    // the tile holding the position read from new_key / new_value
-    const int subst_tile = nt.subst >= 0 ? (nt.subst - w.tok_begin) / TILE : -1;
     auto load = [&](int tile, int slot, bool full) {
         const int t0 = w.tok_begin + tile * TILE;
 #pragma unroll
         for (int j = 0; j < DEPTH; ++j) {
             if (j != slot) continue;
-            if (BT && full && (!FUSED || tile != subst_tile)) {
+            if (BT && full) {
                 load_full(uniform_row_offset(p, bt_lds, b0, t0), j);
             } else {
 #pragma unroll
                 for (int i = 0; i < NL; ++i) {
                     const int t = t0 + i * TPI + tg;
                     if (t < w.tok_end) {
-                        const char *kp, *vp;
-                        if (FUSED && t == nt.subst) {
-                            const int64_t o = new_row_offset<T, D>(p, w) + c * 16;
-                            kp = p.new_key + o;
-                            vp = p.new_value + o;
-                        } else {
-                            const int64_t o = row_offset(p, bt_lds, b0, t, head_bytes);
-                            kp = p.key_cache + o;
-                            vp = p.value_cache + o;
-                        }
-                        kbuf[j][i] = load16_stream(kp);
-                        vbuf[j][i] = load16_stream(vp);
+                        const int64_t o = row_offset(p, bt_lds, b0, t, head_bytes);
+                        kbuf[j][i] = load16_stream(p.key_cache + o);
+                        vbuf[j][i] = load16_stream(p.value_cache + o);
                     } else {
                         kbuf[j][i] = u32x4{0, 0, 0, 0};
                         vbuf[j][i] = u32x4{0, 0, 0, 0};
@@ -463,7 +419,7 @@ __global__ __launch_bounds__(kMaxDecodeThreads) void decode_valu_kernel(DecodePa
     };
 
     // the first tile goes out while the block ids are staged
-    const bool early = first_tile_early<BT>(p, w, TILE) && (!FUSED || subst_tile != 0);
+    const bool early = first_tile_early<BT>(p, w, TILE);
     const bool bad = stage_block_table_early(p, w, bt_lds, early,
                                              [&](int64_t base) { load_full(base, 0); });
     // a flagged partition never consumes the first tile: let its loads land
@@ -485,7 +441,6 @@ __global__ __launch_bounds__(kMaxDecodeThreads) void decode_valu_kernel(DecodePa
         for (int g = 0; g < G; ++g)
             write_result<T, D>(p, w, w.kvh * G + g, c * EPC, acc[g], m[g], l[g], bad, c == 0);
     }
-    store_new_token<T, D, FUSED>(p, nt);
 }
 
 // ------------------------------------------------------------------------
@@ -527,7 +482,7 @@ constexpr int v_lds_offset() { return 16 * k_lds_row_bytes<D>(); }
 template <int D>
 constexpr int kv_lds_wave_bytes() { return v_lds_offset<D>() + 16 * D * 2; }
 
-template <class T, int D, int G, bool BT, bool FUSED>
+template <class T, int D, int G, bool BT>
 __global__ __launch_bounds__(kMaxDecodeThreads) void decode_mfma_kernel(DecodeParams p) {
     static_assert(T::kBytes == 2, "MFMA path is for 16-bit element types");
     static_assert(G == 2 || G == 4 || G == 8, "group size");
@@ -550,11 +505,8 @@ __global__ __launch_bounds__(kMaxDecodeThreads) void decode_mfma_kernel(DecodePa
     extern __shared__ __attribute__((aligned(16))) char k_lds[];
 
     const WorkItem w = work_item(p);
-    const NewToken nt = fetch_new_token<T, D, FUSED>(p, w);
-    if (!prologue<T, D, G>(p, w)) {
-        store_new_token<T, D, FUSED>(p, nt);
-        return;
-    }
+    write_new_token<T, D>(p, w);
+    if (!prologue<T, D, G>(p, w)) return;
     const int b0 = w.tok_begin >> p.block_shift;
 
     const int wave = threadIdx.x / kWave;
@@ -612,29 +564,18 @@ __global__ __launch_bounds__(kMaxDecodeThreads) void decode_mfma_kernel(DecodePa
 #pragma unroll
         for (int i = 0; i < NV; ++i) vbuf[i] = load16_stream(vb + (v_off + i * v_step));
     };
-    // the tile holding the position read from new_key / new_value
-    const int subst_tile = nt.subst >= 0 ? (nt.subst - w.tok_begin) / TILE : -1;
     auto load = [&](int tile, bool full) {
         const int t0 = w.tok_begin + tile * TILE;
-        if (BT && full && (!FUSED || tile != subst_tile)) {
+        if (BT && full) {
             load_full(uniform_row_offset(p, bt_lds, b0, t0));
         } else {
 #pragma unroll
             for (int i = 0; i < NV; ++i) {
                 const int tv = t0 + i * TPI + vtg;
                 if (tv < w.tok_end) {
-                    const char *kp, *vp;
-                    if (FUSED && tv == nt.subst) {
-                        const int64_t o = new_row_offset<T, D>(p, w) + 16 * vc;
-                        kp = p.new_key + o;
-                        vp = p.new_value + o;
-                    } else {
-                        const int64_t o = row_offset(p, bt_lds, b0, tv, head_bytes) + 16 * vc;
-                        kp = p.key_cache + o;
-                        vp = p.value_cache + o;
-                    }
-                    kbuf[i] = load16_stream(kp);
-                    vbuf[i] = load16_stream(vp);
+                    const int64_t o = row_offset(p, bt_lds, b0, tv, head_bytes) + 16 * vc;
+                    kbuf[i] = load16_stream(p.key_cache + o);
+                    vbuf[i] = load16_stream(p.value_cache + o);
                 } else {
                     kbuf[i] = u32x4{0, 0, 0, 0};
                     vbuf[i] = u32x4{0, 0, 0, 0};
@@ -644,7 +585,7 @@ __global__ __launch_bounds__(kMaxDecodeThreads) void decode_mfma_kernel(DecodePa
     };
 
     // the first tile goes out while the block ids are staged
-    const bool early = first_tile_early<BT>(p, w, TILE) && (!FUSED || subst_tile != 0);
+    const bool early = first_tile_early<BT>(p, w, TILE);
     const bool bad = stage_block_table_early(p, w, bt_lds, early, load_full);
     const int ntiles = bad ? 0 : (span + TILE - 1) / TILE;
     const int nfull = bad ? 0 : span / TILE;
@@ -759,7 +700,6 @@ __global__ __launch_bounds__(kMaxDecodeThreads) void decode_mfma_kernel(DecodePa
             write_result<T, D>(p, w, w.kvh * G + g, vc * 8, acc[g], aex[wave][g], lex[wave][g],
                                bad, vc == 0);
     }
-    store_new_token<T, D, FUSED>(p, nt);
 }
 
 // ------------------------------------------------------------------------
@@ -869,11 +809,11 @@ int blocks_per_cu(int threads) {
     hipError_t e;
     if constexpr (T::kBytes == 2 && G >= 2)
         e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
-            &n, reinterpret_cast<const void *>(&decode_mfma_kernel<T, D, G, BT, false>), threads,
+            &n, reinterpret_cast<const void *>(&decode_mfma_kernel<T, D, G, BT>), threads,
             (threads / kWave) * kv_lds_wave_bytes<D>());
     else
         e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
-            &n, reinterpret_cast<const void *>(&decode_valu_kernel<T, D, G, BT, false>), threads, 0);
+            &n, reinterpret_cast<const void *>(&decode_valu_kernel<T, D, G, BT>), threads, 0);
     return e == hipSuccess ? n : 0;
 }
 
@@ -907,21 +847,12 @@ hipError_t launch_main(const DecodeParams &p, int kernel, hipStream_t stream) {
     // the VALU kernel (decode_kernel_choice); only those pairs are built.
     if constexpr (T::kBytes == 2 && G >= 2) {
         if (kernel != 1) return hipErrorInvalidValue;
-        const size_t lds = p.heads_per_group * kv_lds_wave_bytes<D>();
-        if (p.new_key != nullptr)
-            hipLaunchKernelGGL((decode_mfma_kernel<T, D, G, BT, true>), dim3(grid),
-                               dim3(threads), lds, stream, p);
-        else
-            hipLaunchKernelGGL((decode_mfma_kernel<T, D, G, BT, false>), dim3(grid),
-                               dim3(threads), lds, stream, p);
+        hipLaunchKernelGGL((decode_mfma_kernel<T, D, G, BT>), dim3(grid), dim3(threads),
+                           p.heads_per_group * kv_lds_wave_bytes<D>(), stream, p);
     } else {
         if (kernel != 0) return hipErrorInvalidValue;
-        if (p.new_key != nullptr)
-            hipLaunchKernelGGL((decode_valu_kernel<T, D, G, BT, true>), dim3(grid),
-                               dim3(threads), 0, stream, p);
-        else
-            hipLaunchKernelGGL((decode_valu_kernel<T, D, G, BT, false>), dim3(grid),
-                               dim3(threads), 0, stream, p);
+        hipLaunchKernelGGL((decode_valu_kernel<T, D, G, BT>), dim3(grid), dim3(threads), 0,
+                           stream, p);
     }
     return hipGetLastError();
 }
