@@ -15,7 +15,8 @@
  *    row-major, 16-byte aligned.  The library never allocates memory and
  *    keeps no state between calls besides a cache of the device's compute
  *    unit count and of kernel occupancies, filled on first use; entry points
- *    are re-entrant.
+ *    are re-entrant.  (paged_attn_decode_noalloc also uses a fixed scratch
+ *    array that the library's code object holds on each GPU.)
  *  - Element data are one dtype per call (paged_kv_dtype); index arrays are
  *    int32.
  *  - Every call is asynchronous on `stream` (a hipStream_t; NULL means the
@@ -54,7 +55,8 @@ typedef enum {
     PAGED_KV_ERR_UNSUPPORTED = 3,  /* valid but not implemented (dtype, head_dim, ...) */
     PAGED_KV_ERR_WORKSPACE = 4,    /* workspace missing or smaller than required */
     PAGED_KV_ERR_HIP = 5,          /* the HIP runtime reported an error */
-    PAGED_KV_ERR_HOST_MEMORY = 6   /* a host buffer is not pinned, device-mapped memory */
+    PAGED_KV_ERR_HOST_MEMORY = 6,  /* a host buffer is not pinned, device-mapped memory */
+    PAGED_KV_ERR_SCRATCH_LIMIT = 7 /* needs more than the library's static scratch holds */
 } paged_kv_status;
 
 /* Human-readable name of a status code (static storage, never NULL). */
@@ -134,6 +136,34 @@ PAGED_KV_API int paged_attn_decode_write(
     float scale, void *out, int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
     int block_size, int num_blocks, int max_blocks_per_seq, int max_context_len,
     int partition_size, int dtype, void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * paged_attn_decode for callers that cannot allocate device memory: code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc.  Same arguments (minus the workspace), checks, kernels and
+ * results, bit for bit, as paged_attn_decode; the split-context partials go
+ * to a scratch buffer the library itself holds in device memory, one per
+ * GPU, PAGED_KV_NOALLOC_SCRATCH_BYTES bytes, kept until the process ends
+ * (its address is looked up on a device's first call, with that device
+ * current).  Nothing is allocated by the call, on the host or the device.
+ *   A call whose split needs more scratch than that
+ * (paged_attn_decode_workspace_bytes(...) > PAGED_KV_NOALLOC_SCRATCH_BYTES)
+ * returns PAGED_KV_ERR_SCRATCH_LIMIT and enqueues nothing; pass a larger
+ * partition_size, or use paged_attn_decode with a workspace.
+ *   The current device must be the one `stream` runs on.  Every call on one
+ * GPU shares that GPU's scratch: two calls that may run at the same time on
+ * one GPU (different streams, or different host threads without ordering)
+ * race on it and may return wrong results.  Calls ordered on one stream are
+ * safe.  The scratch needs no initialisation: every value the merge reads
+ * is written earlier in the same call.
+ */
+#define PAGED_KV_NOALLOC_SCRATCH_BYTES (32u << 20)
+PAGED_KV_API int paged_attn_decode_noalloc(
+    const void *query, const void *key_cache, const void *value_cache,
+    const int32_t *block_tables, const int32_t *context_lens, float scale, void *out,
+    int num_seqs, int num_q_heads, int num_kv_heads, int head_dim, int block_size,
+    int num_blocks, int max_blocks_per_seq, int max_context_len, int partition_size, int dtype,
+    void *stream);
 
 /*
  * The context partition size paged_attn_decode uses for these arguments

@@ -24,6 +24,7 @@ EXPORTED = (
     "paged_kv_status_string",
     "paged_attn_decode",
     "paged_attn_decode_write",
+    "paged_attn_decode_noalloc",
     "paged_attn_decode_partition_size",
     "paged_attn_decode_partition_size_for_lengths",
     "paged_attn_decode_workspace_bytes",
@@ -52,6 +53,8 @@ def _load_library(path: str = LIBRARY) -> ctypes.CDLL:
     lib.paged_attn_decode_write.argtypes = [vp] * 8 + [cf, vp] + [ci] * 10 + [vp, sz, vp]
     lib.paged_attn_decode_partition_size_for_lengths.argtypes = [vp] + [ci] * 7
     lib.paged_attn_decode_write.restype = ci
+    lib.paged_attn_decode_noalloc.argtypes = [vp, vp, vp, vp, vp, cf, vp] + [ci] * 10 + [vp]
+    lib.paged_attn_decode_noalloc.restype = ci
     lib.paged_attn_decode.restype = ci
     lib.paged_attn_decode_partition_size.argtypes = [ci] * 9
     lib.paged_attn_decode_partition_size.restype = ci
@@ -211,6 +214,30 @@ def paged_attn_decode(query: torch.Tensor, key_cache: torch.Tensor, value_cache:
         ctypes.c_float(scale), _dev(out, "out"), S, Hq, Hkv, D, bs, nb, mb, max_context_len,
         partition_size, dt, ws_ptr, ws_bytes, _stream(query.device))
     _check("paged_attn_decode", status)
+    return out
+
+
+# bytes of the library's own split scratch on each GPU (PAGED_KV_NOALLOC_SCRATCH_BYTES)
+NOALLOC_SCRATCH_BYTES = 32 << 20
+
+
+def paged_attn_decode_noalloc(query: torch.Tensor, key_cache: torch.Tensor,
+                              value_cache: torch.Tensor, block_tables: torch.Tensor,
+                              context_lens: torch.Tensor, scale: float, out: torch.Tensor, *,
+                              max_context_len: int = 0,
+                              partition_size: int = 0) -> torch.Tensor:
+    """paged_attn_decode without a workspace: the split's scratch is the
+    library's own static buffer on the GPU, so nothing is allocated (see
+    paged_attn_decode_noalloc in include/paged_kv.h; calls that may overlap
+    on one GPU race on that buffer)."""
+    S, Hq, D, nb, bs, Hkv = _decode_checks(query, key_cache, value_cache, block_tables,
+                                           context_lens, out)
+    status = _lib.paged_attn_decode_noalloc(
+        _dev(query, "query"), _dev(key_cache, "key_cache"), _dev(value_cache, "value_cache"),
+        _dev(block_tables, "block_tables"), _dev(context_lens, "context_lens"),
+        ctypes.c_float(scale), _dev(out, "out"), S, Hq, Hkv, D, bs, nb, block_tables.shape[1],
+        max_context_len, partition_size, _dtype_code(query), _stream(query.device))
+    _check("paged_attn_decode_noalloc", status)
     return out
 
 

@@ -7,7 +7,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIBRARY = os.path.join(HERE, "libpaged_kv.so")
 SOURCES = ["paged_attention_decode.hip", "paged_attention_prefill.hip", "paged_attention_prefill_f32.hip", "kv_cache_ops.hip",
-           "prefix_cache.hip", "decode_plan.cpp", "capi.cpp"]
+           "prefix_cache.hip", "decode_plan.cpp", "capi.cpp", "decode_noalloc.hip"]
 ARCH = os.environ.get("PAGED_KV_ARCH", "gfx950")
 
 FLAGS = [

@@ -41,6 +41,8 @@ const char *paged_kv_status_string(int status) {
         case PAGED_KV_ERR_WORKSPACE: return "workspace missing or too small";
         case PAGED_KV_ERR_HIP: return "HIP runtime error";
         case PAGED_KV_ERR_HOST_MEMORY: return "host buffer is not pinned, device-mapped memory";
+        case PAGED_KV_ERR_SCRATCH_LIMIT:
+            return "the split needs more scratch than the library's static buffer holds";
         default: return "unknown status";
     }
 }
@@ -75,15 +77,18 @@ size_t paged_attn_decode_workspace_bytes(int num_seqs, int num_q_heads, int num_
 
 }  // extern "C"
 
-namespace {
+namespace pkv {
 
-// The decode, with (new_key non-null) or without the fused KV write.
-int decode(const void *query, const void *new_key, const void *new_value,
-           const int32_t *slot_mapping, const void *key_cache, const void *value_cache,
-           const int32_t *block_tables, const int32_t *context_lens, float scale, void *out,
-           int num_seqs, int num_q_heads, int num_kv_heads, int head_dim, int block_size,
-           int num_blocks, int max_blocks_per_seq, int max_context_len, int partition_size,
-           int dtype, void *workspace, size_t workspace_bytes, void *stream) {
+// The decode, with (new_key non-null) or without the fused KV write; with
+// static_scratch the split's scratch is the library's own buffer
+// (decode_noalloc.hip) instead of the caller's workspace.
+int run_decode(const void *query, const void *new_key, const void *new_value,
+               const int32_t *slot_mapping, const void *key_cache, const void *value_cache,
+               const int32_t *block_tables, const int32_t *context_lens, float scale, void *out,
+               int num_seqs, int num_q_heads, int num_kv_heads, int head_dim, int block_size,
+               int num_blocks, int max_blocks_per_seq, int max_context_len, int partition_size,
+               int dtype, void *workspace, size_t workspace_bytes, void *stream,
+               bool static_scratch) {
     const pkv::DecodePlan pl = pkv::plan_decode(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
                                 max_blocks_per_seq, max_context_len, partition_size, dtype);
     if (pl.status != PAGED_KV_OK) return pl.status;
@@ -97,13 +102,23 @@ int decode(const void *query, const void *new_key, const void *new_value,
     if (new_key && (!new_value || !slot_mapping)) return PAGED_KV_ERR_NULL_POINTER;
     if (new_key && (!aligned16(new_key) || !aligned16(new_value) || !aligned4(slot_mapping)))
         return PAGED_KV_ERR_BAD_SHAPE;
-    const size_t need = pkv::decode_workspace_bytes(pl, num_seqs, num_q_heads, head_dim);
-    if (need > 0 && (!workspace || workspace_bytes < need || !aligned16(workspace)))
-        return PAGED_KV_ERR_WORKSPACE;
-
     const int e = elem_bytes(dtype);
     // The kernels address a block's rows with 32-bit offsets.
     if ((int64_t)block_size * num_kv_heads * head_dim * e > INT_MAX) return PAGED_KV_ERR_BAD_SHAPE;
+    const size_t need = pkv::decode_workspace_bytes(pl, num_seqs, num_q_heads, head_dim);
+    if (static_scratch) {
+        if (need > PAGED_KV_NOALLOC_SCRATCH_BYTES) return PAGED_KV_ERR_SCRATCH_LIMIT;
+        workspace = nullptr;
+        workspace_bytes = 0;
+        if (need > 0) {
+            workspace = noalloc_scratch();
+            if (!workspace) return PAGED_KV_ERR_HIP;
+            workspace_bytes = PAGED_KV_NOALLOC_SCRATCH_BYTES;
+        }
+    }
+    if (need > 0 && (!workspace || workspace_bytes < need || !aligned16(workspace)))
+        return PAGED_KV_ERR_WORKSPACE;
+
     pkv::DecodeParams p;
     p.query = query;
     p.key_cache = static_cast<const char *>(key_cache);
@@ -143,7 +158,7 @@ int decode(const void *query, const void *new_key, const void *new_value,
     return err == hipSuccess ? PAGED_KV_OK : PAGED_KV_ERR_HIP;
 }
 
-}  // namespace
+}  // namespace pkv
 
 extern "C" {
 
@@ -153,10 +168,11 @@ int paged_attn_decode(const void *query, const void *key_cache, const void *valu
                       int block_size, int num_blocks, int max_blocks_per_seq,
                       int max_context_len, int partition_size, int dtype, void *workspace,
                       size_t workspace_bytes, void *stream) {
-    return decode(query, nullptr, nullptr, nullptr, key_cache, value_cache, block_tables,
-                  context_lens, scale, out, num_seqs, num_q_heads, num_kv_heads, head_dim,
-                  block_size, num_blocks, max_blocks_per_seq, max_context_len, partition_size,
-                  dtype, workspace, workspace_bytes, stream);
+    return pkv::run_decode(query, nullptr, nullptr, nullptr, key_cache, value_cache,
+                           block_tables, context_lens, scale, out, num_seqs, num_q_heads,
+                           num_kv_heads, head_dim, block_size, num_blocks, max_blocks_per_seq,
+                           max_context_len, partition_size, dtype, workspace, workspace_bytes,
+                           stream, false);
 }
 
 int paged_attn_decode_write(const void *query, const void *new_key, const void *new_value,
@@ -168,10 +184,11 @@ int paged_attn_decode_write(const void *query, const void *new_key, const void *
                             int dtype, void *workspace, size_t workspace_bytes, void *stream) {
     if (num_seqs > 0 && (!new_key || !new_value || !slot_mapping))
         return PAGED_KV_ERR_NULL_POINTER;
-    return decode(query, new_key, new_value, slot_mapping, key_cache, value_cache, block_tables,
-                  context_lens, scale, out, num_seqs, num_q_heads, num_kv_heads, head_dim,
-                  block_size, num_blocks, max_blocks_per_seq, max_context_len, partition_size,
-                  dtype, workspace, workspace_bytes, stream);
+    return pkv::run_decode(query, new_key, new_value, slot_mapping, key_cache, value_cache,
+                           block_tables, context_lens, scale, out, num_seqs, num_q_heads,
+                           num_kv_heads, head_dim, block_size, num_blocks, max_blocks_per_seq,
+                           max_context_len, partition_size, dtype, workspace, workspace_bytes,
+                           stream, false);
 }
 
 int kv_cache_write(const void *key, const void *value, const int32_t *slot_mapping,

@@ -83,4 +83,21 @@ int plan_partition_for_lengths(const int32_t *lens, int num_seqs, int num_q_head
 size_t decode_partial_floats(int num_seqs, int num_q_heads);
 size_t decode_workspace_bytes(const DecodePlan &pl, int num_seqs, int num_q_heads, int head_dim);
 
+// The decode entry points' common path (capi.cpp): host checks, then the
+// launch; with new_key non-null the fused KV write runs first.  With
+// static_scratch the split's scratch is noalloc_scratch() (workspace and
+// workspace_bytes are ignored) and a split that needs more than it holds
+// returns PAGED_KV_ERR_SCRATCH_LIMIT.  Returns a paged_kv_status.
+int run_decode(const void *query, const void *new_key, const void *new_value,
+               const int32_t *slot_mapping, const void *key_cache, const void *value_cache,
+               const int32_t *block_tables, const int32_t *context_lens, float scale, void *out,
+               int num_seqs, int num_q_heads, int num_kv_heads, int head_dim, int block_size,
+               int num_blocks, int max_blocks_per_seq, int max_context_len, int partition_size,
+               int dtype, void *workspace, size_t workspace_bytes, void *stream,
+               bool static_scratch);
+// Device address of the current device's copy of the library's static
+// scratch (PAGED_KV_NOALLOC_SCRATCH_BYTES bytes, decode_noalloc.hip), looked
+// up on the first call on each device; nullptr if the runtime fails.
+void *noalloc_scratch();
+
 }  // namespace pkv
