@@ -200,8 +200,9 @@ def bench_prefix_cache(args) -> int:
     every full block of the 256 requests and looks up each request's
     longest cached prefix in a table that holds the blocks of 16 earlier
     requests and 400 000 other cached blocks (40% full).  value = tokens
-    handled per second; the roofline figure is the hash kernel's bytes
-    (tokens read, hashes written) over its own time."""
+    handled per second; the kernels move too few bytes (1.9 MB a batch) to
+    be bandwidth-bound, so the roofline object reports the latency of a
+    batch, hash + match, in microseconds."""
     import numpy as np
     import torch
 
@@ -262,9 +263,12 @@ def bench_prefix_cache(args) -> int:
                    "block_size": b.block_size, "full_blocks": nb,
                    "table_slots": 1 << cap_log2, "matched_blocks": matched},
         "hash_ms": round(hash_ms, 5), "match_ms": round(match_ms, 5),
-        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBPS,
-                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None,
-                     "kernel": "paged_kv_prefix_hash", "algorithmic_bytes_per_launch": hash_bytes},
+        # 1.9 MB of tokens and hashes per batch: far too little to load the
+        # memory system, so the figure of merit is the latency of a batch
+        "hash_GBps": round(achieved, 2), "hash_bytes_per_launch": hash_bytes,
+        "roofline": {"bound": "latency", "achieved": round((hash_ms + match_ms) * 1e3, 2),
+                     "peak": None, "unit": "us per batch (hash + match)", "frac": None,
+                     "traffic": None, "kernel": "paged_kv_prefix_hash + paged_kv_prefix_match"},
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:
@@ -475,15 +479,140 @@ def bench_prefill(args) -> int:
     return 0
 
 
+DEFAULT_WORKLOAD = "llama3_8b_gqa_bf16"
+
+
+class DecodeRig:
+    """One decode workload on the device: its pool held in several copies
+    that successive launches rotate through (so that a launch never finds
+    its pool in the 256 MB Infinity Cache from the launch before), the
+    query, output, new tokens, tables and lengths, and the split a
+    scheduler holding the lengths on the host would ask for.  Pool contents
+    are random: they do not change the timing."""
+
+    def __init__(self, workload, copies, partition_size, fused, dev):
+        import torch
+
+        from paged_kv_cache_467_amd import binding, tensors, workloads as W
+
+        self.binding, self.fused = binding, fused
+        b = self.b = W.make_workload(workload, values=False)
+        dt = tensors.TORCH_DTYPE[b.dtype]
+        S, Hq, Hkv, D, bs = b.num_seqs, b.num_q_heads, b.num_kv_heads, b.head_dim, b.block_size
+        pool_shape = (b.num_blocks, bs, Hkv, D)
+        self.copies = [(torch.randn(pool_shape, device=dev).to(dt),
+                        torch.randn(pool_shape, device=dev).to(dt))
+                       for _ in range(max(1, copies))]
+        self.query = torch.randn((S, Hq, D), device=dev).to(dt)
+        self.out = torch.empty_like(self.query)
+        self.new_key = torch.randn((S, Hkv, D), device=dev).to(dt)
+        self.new_value = torch.randn((S, Hkv, D), device=dev).to(dt)
+        self.bt = tensors.int32(b.block_tables, dev)
+        self.cl = tensors.int32(b.context_lens, dev)
+        self.sm = tensors.int32(b.slot_mapping, dev)
+        self.max_ctx = b.max_context_len
+        self.psize = partition_size or binding.paged_attn_decode_partition_size_for_lengths(
+            b.context_lens, Hq, Hkv, D, bs, b.max_blocks_per_seq, b.dtype_code)
+        self.partition_size = binding.paged_attn_decode_partition_size(
+            S, Hq, Hkv, D, bs, b.max_blocks_per_seq, self.max_ctx, self.psize, b.dtype_code)
+        ws_bytes = binding.paged_attn_decode_workspace_bytes(
+            S, Hq, Hkv, D, bs, b.max_blocks_per_seq, self.max_ctx, self.psize, b.dtype_code)
+        self.workspace = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
+        torch.cuda.synchronize()
+
+    def launch(self, i):
+        kc, vc = self.copies[i % len(self.copies)]
+        B = self.binding
+        if not self.fused:
+            B.paged_attn_decode(self.query, kc, vc, self.bt, self.cl, self.b.scale, self.out,
+                                max_context_len=self.max_ctx, partition_size=self.psize,
+                                workspace=self.workspace)
+        else:
+            B.paged_attn_decode_write(self.query, self.new_key, self.new_value, self.sm, kc, vc,
+                                      self.bt, self.cl, self.b.scale, self.out,
+                                      max_context_len=self.max_ctx, partition_size=self.psize,
+                                      workspace=self.workspace)
+
+    def write(self, i):
+        kc, vc = self.copies[i % len(self.copies)]
+        self.binding.kv_cache_write(self.new_key, self.new_value, self.sm, kc, vc)
+
+    def release(self):
+        self.copies = []
+
+
+def other_workload(workload: str, args, dev) -> dict:
+    """One of the other decode workloads, measured like the headline's
+    decode: --steps decode launches back to back between one event pair
+    (after --warmup), then as many kv_cache_write launches the same way.
+    The roofline fraction is taken on HBM bytes: the algorithmic bytes, or,
+    where sequences share cached blocks (the shared prefix), the rocprofv3
+    counter bytes of the committed profile (with the bytes of each distinct
+    pool cell counted once in their place while there is none); the
+    logical figure (every sequence's own context counted) is reported on
+    its own."""
+    import torch
+
+    rig = DecodeRig(workload, args.copies, 0, False, dev)
+    b = rig.b
+    for i in range(args.warmup):
+        rig.launch(i)
+    _, dec_ms = time_back_to_back(rig.launch, args.warmup, args.steps)
+    for i in range(args.warmup):
+        rig.write(i)
+    _, wr_ms = time_back_to_back(rig.write, args.warmup, args.steps)
+    psize = rig.partition_size
+    rig.release()
+    del rig
+    torch.cuda.empty_cache()
+    t = dec_ms * 1e-3
+    logical = b.decode_algorithmic_bytes()
+    unique = b.decode_unique_bytes()
+    traffic = measured_traffic(workload)
+    shared = unique < logical
+    hbm = (traffic if traffic is not None else unique) if shared else logical
+    r = {
+        "dtype": b.dtype,
+        "num_seqs": b.num_seqs, "num_q_heads": b.num_q_heads, "num_kv_heads": b.num_kv_heads,
+        "head_dim": b.head_dim, "block_size": b.block_size,
+        "context_tokens": int(b.context_lens.sum()),
+        "context_len_range": [int(b.context_lens.min()), int(b.context_lens.max())],
+        "partition_size": psize,
+        "decode_ms": round(dec_ms, 5),
+        "seq_per_s_per_layer": round(b.num_seqs / t, 1),
+        "algorithmic_bytes": logical,
+        "algorithmic_GBps": round(logical / t / 1e9, 2),
+        "roofline": {"bound": "hbm", "achieved": round(hbm / t / 1e9, 2),
+                     "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(hbm / t / 1e9 / HBM_PEAK_GBPS, 4),
+                     "bytes": "counter" if shared and traffic is not None else
+                              "unique cells" if shared else "algorithmic",
+                     "traffic": traffic,
+                     "traffic_GBps": None if traffic is None else round(traffic / t / 1e9, 2)},
+        "write_ms": round(wr_ms, 5),
+        "write_GBps": round(b.write_algorithmic_bytes() / (wr_ms * 1e-3) / 1e9, 2),
+    }
+    if shared:
+        r["unique_bytes"] = unique
+        r["logical_GBps"] = r.pop("algorithmic_GBps")
+    if logical < (1 << 20):
+        # a few hundred KB: the launch itself is the cost
+        r["roofline"]["bound"] = "launch latency"
+    return r
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default="llama3_8b_gqa_bf16")
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--copies", type=int, default=4, help="pool copies rotated across steps")
     ap.add_argument("--partition-size", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-workloads", action="store_true",
+                    help="skip the other four decode workloads that the default run measures "
+                         "after the headline one")
     ap.add_argument("--fused", action="store_true",
                     help="time the decode step as one paged_attn_decode_write launch instead "
                          "of kv_cache_write + paged_attn_decode")
@@ -512,7 +641,7 @@ def main() -> int:
     import numpy as np
     import torch
 
-    from paged_kv_cache_467_amd import binding, tensors, workloads as W
+    from paged_kv_cache_467_amd import workloads as W
 
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
@@ -527,51 +656,18 @@ def main() -> int:
         return bench_copy_blocks(args)
     if args.op == "prefill":
         return bench_prefill(args)
-    b = W.make_workload(args.workload, values=False)
-    dt = tensors.TORCH_DTYPE[b.dtype]
+    rig = DecodeRig(args.workload, args.copies, args.partition_size, args.fused, dev)
+    b = rig.b
     S, Hq, Hkv, D, bs = b.num_seqs, b.num_q_heads, b.num_kv_heads, b.head_dim, b.block_size
-    pool_shape = (b.num_blocks, bs, Hkv, D)
-    copies = []
-    for _ in range(max(1, args.copies)):
-        copies.append((torch.randn(pool_shape, device=dev).to(dt),
-                       torch.randn(pool_shape, device=dev).to(dt)))
-    query = torch.randn((S, Hq, D), device=dev).to(dt)
-    out = torch.empty_like(query)
-    new_key = torch.randn((S, Hkv, D), device=dev).to(dt)
-    new_value = torch.randn((S, Hkv, D), device=dev).to(dt)
-    bt = tensors.int32(b.block_tables, dev)
-    cl = tensors.int32(b.context_lens, dev)
-    sm = tensors.int32(b.slot_mapping, dev)
-    max_ctx = b.max_context_len
-    # the split a scheduler holding the lengths on the host would ask for
-    psize = args.partition_size or binding.paged_attn_decode_partition_size_for_lengths(
-        b.context_lens, Hq, Hkv, D, bs, b.max_blocks_per_seq, b.dtype_code)
-    P = binding.paged_attn_decode_partition_size(S, Hq, Hkv, D, bs, b.max_blocks_per_seq,
-                                                 max_ctx, psize, b.dtype_code)
-    ws_bytes = binding.paged_attn_decode_workspace_bytes(S, Hq, Hkv, D, bs, b.max_blocks_per_seq,
-                                                         max_ctx, psize, b.dtype_code)
-    workspace = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
-
-    def launch(kc, vc):
-        if not args.fused:
-            binding.paged_attn_decode(query, kc, vc, bt, cl, b.scale, out,
-                                      max_context_len=max_ctx,
-                                      partition_size=psize, workspace=workspace)
-        else:
-            binding.paged_attn_decode_write(query, new_key, new_value, sm, kc, vc, bt, cl,
-                                            b.scale, out, max_context_len=max_ctx,
-                                            partition_size=psize,
-                                            workspace=workspace)
 
     def step(i, ev=None):
-        kc, vc = copies[i % len(copies)]
         if not args.fused:
             if ev is not None:
                 ev[2].record()
-            binding.kv_cache_write(new_key, new_value, sm, kc, vc)
+            rig.write(i)
         if ev is not None:
             ev[0].record()
-        launch(kc, vc)
+        rig.launch(i)
         if ev is not None:
             ev[1].record()
 
@@ -613,13 +709,7 @@ def main() -> int:
     # average duration, the gaps between launches included, without the
     # cost an event pair adds to each launch it brackets (about 4 us here).
     # The roofline uses this figure.
-    ev_a, ev_b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    ev_a.record()
-    for i in range(steps):
-        launch(*copies[(args.warmup + i) % len(copies)])
-    ev_b.record()
-    torch.cuda.synchronize()
-    decode_avg_ms = ev_a.elapsed_time(ev_b) / steps
+    _, decode_avg_ms = time_back_to_back(rig.launch, args.warmup, steps)
     b_dec = b.decode_algorithmic_bytes()
     b_step = b_dec + b.write_algorithmic_bytes()
     b_launch = b_dec if not args.fused else b_step  # the timed launch's own bytes
@@ -645,7 +735,7 @@ def main() -> int:
             "block_size": bs, "num_blocks": b.num_blocks,
             "context_tokens": int(b.context_lens.sum()),
             "context_len_range": [int(b.context_lens.min()), int(b.context_lens.max())],
-            "partition_size": P, "pool_copies": len(copies),
+            "partition_size": rig.partition_size, "pool_copies": len(rig.copies),
             "step": ("kv_cache_write of one token per sequence + paged_attn_decode"
                      if not args.fused else
                      "paged_attn_decode_write: one new token per sequence stored in the pool "
@@ -678,9 +768,13 @@ def main() -> int:
         },
         "cpu_baseline": None,
     }
+    rig.release()
+    del rig
+    torch.cuda.empty_cache()
+    if not args.no_workloads and args.workload == DEFAULT_WORKLOAD and not args.fused:
+        result["workloads"] = {wl: other_workload(wl, args, dev) for wl in W.WORKLOADS
+                               if wl != args.workload}
     if not args.no_cpu_baseline:
-        del copies
-        torch.cuda.empty_cache()
         host = W.make_workload(args.workload)
         result["cpu_baseline"] = cpu_baseline(args.workload, host)
     print(json.dumps(result), flush=True)

@@ -25,22 +25,28 @@ namespace {
 
 constexpr int kCopyThreads = 256;
 
-// One workgroup per token.  Slots outside [0, num_slots) write nothing.
+// One lane per 16-byte chunk of a token's row (K and V): the chunks of all
+// tokens are numbered in one range, so a workgroup covers whole rows of
+// several tokens when rows are short and part of one when they are long,
+// and no lane idles but in the last workgroup.  Each lane issues its slot
+// read and its two row loads together (the rows do not depend on the
+// slot), so the write waits for one memory round trip before its stores.
+// Slots outside [0, num_slots) write nothing.
 __global__ __launch_bounds__(kCopyThreads) void kv_cache_write_kernel(
     const char *__restrict__ key, const char *__restrict__ value,
     const int32_t *__restrict__ slot_mapping, char *__restrict__ key_cache,
-    char *__restrict__ value_cache, int row_bytes, int64_t num_slots) {
-    const int t = blockIdx.x;
+    char *__restrict__ value_cache, int row_chunks, int64_t num_chunks, int64_t num_slots) {
+    const int64_t g = (int64_t)blockIdx.x * kCopyThreads + threadIdx.x;
+    if (g >= num_chunks) return;
+    const int t = (int)(g / row_chunks);
+    const int c = (int)(g - (int64_t)t * row_chunks);
     const int slot = slot_mapping[t];
+    const u32x4 k = load16(key + g * 16);
+    const u32x4 v = load16(value + g * 16);
     if (slot < 0 || (int64_t)slot >= num_slots) return;
-    const int64_t src = (int64_t)t * row_bytes;
-    const int64_t dst = (int64_t)slot * row_bytes;
-    for (int b = threadIdx.x * 16; b < row_bytes; b += kCopyThreads * 16) {
-        const u32x4 k = load16(key + src + b);
-        const u32x4 v = load16(value + src + b);
-        store16(key_cache + dst + b, k);
-        store16(value_cache + dst + b, v);
-    }
+    const int64_t dst = ((int64_t)slot * row_chunks + c) * 16;
+    store16(key_cache + dst, k);
+    store16(value_cache + dst, v);
 }
 
 // One workgroup per (sequence, logical block).  A block of the pool holds
@@ -135,10 +141,14 @@ hipError_t launch_kv_cache_write(const void *key, const void *value, const int32
                                  void *key_cache, void *value_cache, int num_tokens,
                                  int row_bytes, int64_t num_slots, hipStream_t stream) {
     if (num_tokens == 0) return hipSuccess;
-    hipLaunchKernelGGL(kv_cache_write_kernel, dim3(num_tokens), dim3(kCopyThreads), 0, stream,
-                       static_cast<const char *>(key), static_cast<const char *>(value),
+    const int row_chunks = row_bytes / 16;  // row_bytes is a multiple of 16
+    const int64_t chunks = (int64_t)num_tokens * row_chunks;
+    const int64_t groups = (chunks + kCopyThreads - 1) / kCopyThreads;
+    if (groups > 0x7FFFFFFF) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(kv_cache_write_kernel, dim3((unsigned)groups), dim3(kCopyThreads), 0,
+                       stream, static_cast<const char *>(key), static_cast<const char *>(value),
                        slot_mapping, static_cast<char *>(key_cache),
-                       static_cast<char *>(value_cache), row_bytes, num_slots);
+                       static_cast<char *>(value_cache), row_chunks, chunks, num_slots);
     return hipGetLastError();
 }
 

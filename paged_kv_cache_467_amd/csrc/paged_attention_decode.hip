@@ -724,20 +724,15 @@ __global__ __launch_bounds__(kReduceThreads) void decode_reduce_kernel(DecodePar
     const float *po = p.part_out + pbase * D + lane * EL;
     const int np = p.num_partitions;
 
-    // Everything up to the first R partitions is loaded before the length is
-    // known (every index stays below num_partitions, inside the workspace;
-    // what lies past this sequence's partitions is masked below), so the
-    // loads take one round trip instead of a chain of them.
+    // The maxima and sums of the first 64 partitions are loaded with the
+    // length (every index stays below num_partitions, inside the workspace;
+    // what lies past this sequence's own partitions is masked below, and
+    // shares cache lines with the partitions that are used).  The partial
+    // outputs, 4 * head_dim bytes a partition, are loaded only for the
+    // sequence's own partitions, once its length is known.
+    const int L = p.context_lens[s];
     float mq = lane < np ? pm[lane] : -INFINITY;  // lane q holds partition q < 64
     float lq = lane < np ? ps[lane] : 0.0f;
-    float v[R][EL];
-#pragma unroll
-    for (int u = 0; u < R; ++u) {
-        const int q = u < np ? u : 0;
-#pragma unroll
-        for (int e = 0; e < EL; ++e) v[u][e] = po[(int64_t)q * D + e];
-    }
-    const int L = p.context_lens[s];
     if (L < 0 || L > p.max_context_len) {
 #pragma unroll
         for (int e = 0; e < EL; ++e) T::store_nan(p.out, obase + e);
@@ -749,6 +744,14 @@ __global__ __launch_bounds__(kReduceThreads) void decode_reduce_kernel(DecodePar
         return;
     }
     const int nparts = (L + p.partition_size - 1) / p.partition_size;
+    float v[R][EL];
+#pragma unroll
+    for (int u = 0; u < R; ++u) {
+        // past the last partition: reread partition 0 (in bounds, finite, cached)
+        const int q = u < nparts ? u : 0;
+#pragma unroll
+        for (int e = 0; e < EL; ++e) v[u][e] = po[(int64_t)q * D + e];
+    }
     if (lane >= nparts) {
         mq = -INFINITY;
         lq = 0.0f;
@@ -784,7 +787,6 @@ __global__ __launch_bounds__(kReduceThreads) void decode_reduce_kernel(DecodePar
     for (int q0 = R; q0 < nparts; q0 += R) {
 #pragma unroll
         for (int u = 0; u < R; ++u) {
-            // past the last partition: reread partition 0 (in bounds, finite)
             const int q = q0 + u < nparts ? q0 + u : 0;
 #pragma unroll
             for (int e = 0; e < EL; ++e) v[u][e] = po[(int64_t)q * D + e];

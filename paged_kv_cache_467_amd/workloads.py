@@ -128,6 +128,24 @@ class DecodeBatch:
         bt = int(np.sum((L + self.block_size - 1) // self.block_size)) * 4
         return kv + qo + bt + 4 * self.num_seqs
 
+    def decode_unique_bytes(self) -> int:
+        """decode_algorithmic_bytes with each distinct pool cell counted once:
+        the least HBM traffic a decode of this batch can have when cells that
+        several sequences share (a common prefix) are fetched once."""
+        bs = self.block_size
+        cells = set()
+        for s in range(self.num_seqs):
+            L = int(self.context_lens[s])
+            for i in range((L + bs - 1) // bs):
+                blk = int(self.block_tables[s, i])
+                for off in range(min(bs, L - i * bs)):
+                    cells.add(blk * bs + off)
+        e = self.elem_bytes
+        kv = len(cells) * self.num_kv_heads * self.head_dim * e * 2
+        return self.decode_algorithmic_bytes() - \
+            int(self.context_lens.astype(np.int64).sum()) * self.num_kv_heads * self.head_dim * e * 2 \
+            + kv
+
     def write_algorithmic_bytes(self) -> int:
         t = len(self.slot_mapping)
         row = self.num_kv_heads * self.head_dim * self.elem_bytes
