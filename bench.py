@@ -82,6 +82,33 @@ def time_back_to_back(fn, first: int, steps: int):
     return time.perf_counter() - t0, a.elapsed_time(z) / steps
 
 
+def time_graph(fn, first: int, nodes: int = 20, replays: int = 10):
+    """Captures fn(first), ..., fn(first + nodes - 1) in one HIP graph and
+    replays it `replays` times between one pair of HIP events: the average
+    ms per call with the host out of the loop (the gaps between the graph's
+    kernels included).  For kernels of a few microseconds, whose launches
+    from Python come slower than the GPU runs them."""
+    import torch
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(g, stream=side):
+            for i in range(nodes):
+                fn(first + i)
+    torch.cuda.current_stream().wait_stream(side)
+    g.replay()
+    torch.cuda.synchronize()
+    a, z = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(replays):
+        g.replay()
+    z.record()
+    torch.cuda.synchronize()
+    del g
+    return a.elapsed_time(z) / (replays * nodes)
+
+
 def cpu_baseline(workload: str, batch_values, budget_s: float = 10.0):
     """The fp64 CPU oracle on this host's cores, on the whole batch, repeated
     until about budget_s seconds have passed (at least three runs; median),
@@ -541,30 +568,34 @@ class DecodeRig:
         self.copies = []
 
 
-def other_workload(workload: str, args, dev) -> dict:
+def other_workload(rig: "DecodeRig", args) -> dict:
     """One of the other decode workloads, measured like the headline's
     decode: --steps decode launches back to back between one event pair
-    (after --warmup), then as many kv_cache_write launches the same way.
+    (after as many untimed ones as the headline's decode has run by then),
+    then the kv_cache_write (and, for a batch of under 1 MB, the decode
+    again) from a HIP graph.
     The roofline fraction is taken on HBM bytes: the algorithmic bytes, or,
     where sequences share cached blocks (the shared prefix), the rocprofv3
     counter bytes of the committed profile (with the bytes of each distinct
     pool cell counted once in their place while there is none); the
     logical figure (every sequence's own context counted) is reported on
     its own."""
-    import torch
-
-    rig = DecodeRig(workload, args.copies, 0, False, dev)
     b = rig.b
-    for i in range(args.warmup):
+    workload = b.name
+    # as many untimed launches as the headline's decode sees before its
+    # back-to-back pass (warm-up, timed steps, event-pair steps)
+    warm = args.warmup + 2 * args.steps
+    for i in range(warm):
         rig.launch(i)
-    _, dec_ms = time_back_to_back(rig.launch, args.warmup, args.steps)
+    _, dec_ms = time_back_to_back(rig.launch, warm, args.steps)
+    # the write moves a few MB at most: its launches from Python come slower
+    # than the kernel runs, so it is timed from a HIP graph of 20 launches
     for i in range(args.warmup):
         rig.write(i)
-    _, wr_ms = time_back_to_back(rig.write, args.warmup, args.steps)
+    wr_ms = time_graph(rig.write, args.warmup)
+    small = b.decode_algorithmic_bytes() < (1 << 20)
+    dec_graph_ms = time_graph(rig.launch, warm) if small else None
     psize = rig.partition_size
-    rig.release()
-    del rig
-    torch.cuda.empty_cache()
     t = dec_ms * 1e-3
     logical = b.decode_algorithmic_bytes()
     unique = b.decode_unique_bytes()
@@ -591,11 +622,15 @@ def other_workload(workload: str, args, dev) -> dict:
                      "traffic_GBps": None if traffic is None else round(traffic / t / 1e9, 2)},
         "write_ms": round(wr_ms, 5),
         "write_GBps": round(b.write_algorithmic_bytes() / (wr_ms * 1e-3) / 1e9, 2),
+        "write_timing": "HIP graph of 20 launches",
     }
+    if dec_graph_ms is not None:
+        # launch-bound: decode_ms above is the host's launch rate
+        r["decode_graph_ms"] = round(dec_graph_ms, 5)
     if shared:
         r["unique_bytes"] = unique
         r["logical_GBps"] = r.pop("algorithmic_GBps")
-    if logical < (1 << 20):
+    if small:
         # a few hundred KB: the launch itself is the cost
         r["roofline"]["bound"] = "launch latency"
     return r
@@ -656,6 +691,14 @@ def main() -> int:
         return bench_copy_blocks(args)
     if args.op == "prefill":
         return bench_prefill(args)
+    # Every workload's device inputs are allocated up front, before anything
+    # is freed: pools allocated after others were freed measured 3-5% slower
+    # for the same launches (the first workload allocated in a process was
+    # the fast one, whichever it was).
+    others = []
+    if not args.no_workloads and args.workload == DEFAULT_WORKLOAD and not args.fused:
+        others = [DecodeRig(wl, args.copies, 0, False, dev) for wl in W.WORKLOADS
+                  if wl != args.workload]
     rig = DecodeRig(args.workload, args.copies, args.partition_size, args.fused, dev)
     b = rig.b
     S, Hq, Hkv, D, bs = b.num_seqs, b.num_q_heads, b.num_kv_heads, b.head_dim, b.block_size
@@ -710,6 +753,7 @@ def main() -> int:
     # cost an event pair adds to each launch it brackets (about 4 us here).
     # The roofline uses this figure.
     _, decode_avg_ms = time_back_to_back(rig.launch, args.warmup, steps)
+    write_graph_ms = None if args.fused else time_graph(rig.write, args.warmup)
     b_dec = b.decode_algorithmic_bytes()
     b_step = b_dec + b.write_algorithmic_bytes()
     b_launch = b_dec if not args.fused else b_step  # the timed launch's own bytes
@@ -751,6 +795,8 @@ def main() -> int:
         "write_ms": None if write_ms is None else round(sum(write_ms) / len(write_ms), 5),
         "write_GBps": None if write_ms is None else
         round(b.write_algorithmic_bytes() / (sum(write_ms) / len(write_ms) * 1e-3) / 1e9, 2),
+        # the write alone, from a HIP graph of 20 launches (no host in the loop)
+        "write_graph_ms": None if write_graph_ms is None else round(write_graph_ms, 5),
         "algorithmic_bytes_per_step": b_step,
         "roofline": {
             "bound": "hbm",
@@ -768,12 +814,13 @@ def main() -> int:
         },
         "cpu_baseline": None,
     }
+    if others:
+        result["workloads"] = {o.b.name: other_workload(o, args) for o in others}
     rig.release()
-    del rig
+    for o in others:
+        o.release()
+    del rig, others
     torch.cuda.empty_cache()
-    if not args.no_workloads and args.workload == DEFAULT_WORKLOAD and not args.fused:
-        result["workloads"] = {wl: other_workload(wl, args, dev) for wl in W.WORKLOADS
-                               if wl != args.workload}
     if not args.no_cpu_baseline:
         host = W.make_workload(args.workload)
         result["cpu_baseline"] = cpu_baseline(args.workload, host)
