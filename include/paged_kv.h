@@ -92,6 +92,16 @@ PAGED_KV_API const char *paged_kv_status_string(int status);
  *                workspace size on the device that will run the decode.  An
  *                explicit value must be a positive multiple of 16 and of
  *                block_size with partition_size / block_size <= 1024.
+ *                PAGED_KV_BALANCED_SPLIT asks for the balanced split instead
+ *                of partitions per sequence: the positions of all sequences,
+ *                each rounded up to a multiple of 16, are laid end to end
+ *                and cut into equal chunks, one workgroup each (per group of
+ *                kv heads), so that contexts of very different lengths still
+ *                give every workgroup the same work; a sequence that lies
+ *                in one chunk is finished there, the others are merged
+ *                across chunks.  It takes num_seqs <= 1024 and num_seqs *
+ *                (max_context_len rounded up to 16) < 2^31 (else
+ *                PAGED_KV_ERR_UNSUPPORTED).
  *   workspace, workspace_bytes  device scratch of at least
  *                paged_attn_decode_workspace_bytes(...) bytes for the same
  *                arguments; may be NULL when that size is 0.  Its contents
@@ -107,6 +117,7 @@ PAGED_KV_API const char *paged_kv_status_string(int status);
  * 2^31 elements (64-bit addressing); one block, block_size * num_kv_heads *
  * head_dim elements, must fit in 2^31 - 1 bytes (else PAGED_KV_ERR_BAD_SHAPE).
  */
+#define PAGED_KV_BALANCED_SPLIT 1
 PAGED_KV_API int paged_attn_decode(
     const void *query, const void *key_cache, const void *value_cache,
     const int32_t *block_tables, const int32_t *context_lens, float scale, void *out,
@@ -128,7 +139,9 @@ PAGED_KV_API int paged_attn_decode(
  *                launch it then writes and reads); a negative slot, or one
  *                outside the pool, writes nothing
  *   key_cache, value_cache  updated in place
- * Every other argument, check and status is paged_attn_decode's.
+ * Every other argument, check and status is paged_attn_decode's, except
+ * that partition_size PAGED_KV_BALANCED_SPLIT returns
+ * PAGED_KV_ERR_UNSUPPORTED.
  */
 PAGED_KV_API int paged_attn_decode_write(
     const void *query, const void *new_key, const void *new_value, const int32_t *slot_mapping,
@@ -169,7 +182,8 @@ PAGED_KV_API int paged_attn_decode_noalloc(
  * The context partition size paged_attn_decode uses for these arguments
  * (partition_size 0 = its automatic choice), or a negative paged_kv_status
  * code when the arguments are invalid.  A partition size >= max_context_len
- * means no split: one pass writes out directly.
+ * means no split: one pass writes out directly; PAGED_KV_BALANCED_SPLIT
+ * (when asked for) means the balanced split.
  */
 PAGED_KV_API int paged_attn_decode_partition_size(
     int num_seqs, int num_q_heads, int num_kv_heads, int head_dim, int block_size,
@@ -181,9 +195,11 @@ PAGED_KV_API int paged_attn_decode_partition_size(
  * batch does): host_context_lens [num_seqs] int32 in host memory, read here
  * and not kept.  The automatic choice sizes partitions from the longest
  * context; when the batch needs a split and its lengths are very uneven
- * (the longest above 1.5 times the mean) this returns the finest split
- * instead, so that the long contexts' workgroups do not finish far behind
- * the rest.  A negative paged_kv_status code when the arguments are invalid.
+ * (the longest above 1.5 times the mean) this returns
+ * PAGED_KV_BALANCED_SPLIT instead (or, where that split does not apply, the
+ * finest split), so that the long contexts' workgroups do not finish far
+ * behind the rest.  A negative paged_kv_status code when the arguments are
+ * invalid.
  */
 PAGED_KV_API int paged_attn_decode_partition_size_for_lengths(
     const int32_t *host_context_lens, int num_seqs, int num_q_heads, int num_kv_heads,
@@ -192,7 +208,8 @@ PAGED_KV_API int paged_attn_decode_partition_size_for_lengths(
 /*
  * Bytes of workspace paged_attn_decode needs for these arguments (0 when the
  * context is not split); (size_t)-1 for invalid arguments.  The split-context
- * partials are fp32: per (sequence, query head, partition) a running max, a
+ * partials are fp32: per (sequence, query head, partition) -- or, with the
+ * balanced split, per (chunk, 2 slots, query head) -- a running max, a
  * running sum and head_dim unnormalised output values.
  */
 PAGED_KV_API size_t paged_attn_decode_workspace_bytes(

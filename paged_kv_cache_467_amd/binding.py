@@ -17,6 +17,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIBRARY = os.path.join(HERE, "libpaged_kv.so")
 
 PAGED_KV_F32, PAGED_KV_F16, PAGED_KV_BF16 = 0, 1, 2
+# partition_size asking for the balanced split (PAGED_KV_BALANCED_SPLIT)
+BALANCED_SPLIT = 1
 _TORCH_DTYPES = {torch.float32: PAGED_KV_F32, torch.float16: PAGED_KV_F16,
                  torch.bfloat16: PAGED_KV_BF16}
 

@@ -100,6 +100,7 @@ int run_decode(const void *query, const void *new_key, const void *new_value,
         !aligned16(out) || !aligned4(block_tables) || !aligned4(context_lens))
         return PAGED_KV_ERR_BAD_SHAPE;
     if (new_key && (!new_value || !slot_mapping)) return PAGED_KV_ERR_NULL_POINTER;
+    if (new_key && pl.num_chunks > 0) return PAGED_KV_ERR_UNSUPPORTED;
     if (new_key && (!aligned16(new_key) || !aligned16(new_value) || !aligned4(slot_mapping)))
         return PAGED_KV_ERR_BAD_SHAPE;
     const int e = elem_bytes(dtype);
@@ -126,7 +127,7 @@ int run_decode(const void *query, const void *new_key, const void *new_value,
     p.block_tables = block_tables;
     p.context_lens = context_lens;
     p.out = out;
-    const size_t nph = pkv::decode_partial_floats(num_seqs, num_q_heads) * pl.num_partitions;
+    const size_t nph = pkv::decode_partial_slots(pl, num_seqs, num_q_heads);
     float *ws = static_cast<float *>(workspace);
     p.part_max = need ? ws : nullptr;
     p.part_sum = need ? ws + nph : nullptr;
@@ -142,6 +143,7 @@ int run_decode(const void *query, const void *new_key, const void *new_value,
     p.max_context_len = pl.max_context_len;
     p.partition_size = pl.partition_size;
     p.num_partitions = pl.num_partitions;
+    p.num_chunks = pl.num_chunks;
     p.heads_per_group = pl.heads_per_group;
     p.num_head_groups = num_kv_heads / pl.heads_per_group;
     p.row_stride_bytes = num_kv_heads * head_dim * e;

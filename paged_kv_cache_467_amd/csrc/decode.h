@@ -14,6 +14,9 @@ constexpr int kBtLds = 1024;
 // most this many.
 constexpr int kMaxDecodeWaves = 8;
 constexpr int kMaxDecodeThreads = kMaxDecodeWaves * 64;
+// Balanced split: every workgroup keeps the padded start of every sequence
+// in LDS, so a batch may hold at most this many sequences.
+constexpr int kBalancedMaxSeqs = 1024;
 
 struct DecodeParams {
     const void *query;          // [S, Hq, D]
@@ -36,6 +39,11 @@ struct DecodeParams {
     int max_context_len;        // every valid context_len is <= this
     int partition_size;         // tokens per partition
     int num_partitions;         // P_max = ceil(max_context_len / partition_size)
+    // Balanced split (num_chunks > 0): the positions of all sequences, each
+    // padded to a multiple of 16, end to end, cut into num_chunks chunks of
+    // equal size; partition_size and num_partitions are then unused, and
+    // the partials are indexed by chunk (two slots per chunk).
+    int num_chunks;
     int heads_per_group;        // kv heads (= waves) per workgroup
     int num_head_groups;        // num_kv_heads / heads_per_group
     int64_t block_stride_bytes; // bs * Hkv * D * elem bytes
@@ -71,6 +79,7 @@ struct DecodePlan {
     int partition_size;
     int num_partitions;
     int heads_per_group;  // kv heads per decode workgroup (one wave each)
+    int num_chunks;       // > 0: balanced split into this many chunks
 };
 DecodePlan plan_decode(int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
                        int block_size, int max_blocks_per_seq, int max_context_len,
@@ -81,6 +90,9 @@ int plan_partition_for_lengths(const int32_t *lens, int num_seqs, int num_q_head
                                int num_kv_heads, int head_dim, int block_size,
                                int max_blocks_per_seq, int dtype);
 size_t decode_partial_floats(int num_seqs, int num_q_heads);
+// Entries of each split-scratch array (running max, running sum; the
+// output array holds head_dim times as many).
+size_t decode_partial_slots(const DecodePlan &pl, int num_seqs, int num_q_heads);
 size_t decode_workspace_bytes(const DecodePlan &pl, int num_seqs, int num_q_heads, int head_dim);
 
 // The decode entry points' common path (capi.cpp): host checks, then the

@@ -42,12 +42,40 @@ int heads_per_group_for(int num_kv_heads) {
     return 1;
 }
 
+// Workgroups of hpg kv heads the device should have running at once.
+int64_t target_workgroups(int dtype, int head_dim, int group, int block_size, int hpg) {
+    const DeviceOccupancy occ = decode_occupancy(dtype, head_dim, group, block_size, hpg);
+    int64_t per_cu = kTargetWavesPerCu / hpg;
+    if (occ.workgroups_per_cu > 0 && per_cu > occ.workgroups_per_cu)
+        per_cu = occ.workgroups_per_cu;
+    if (per_cu < 1) per_cu = 1;
+    return (occ.compute_units > 0 ? occ.compute_units : kFallbackComputeUnits) * per_cu;
+}
+
+// Balanced split: chunks per group of kv heads.  Two chunks per workgroup
+// slot the device holds at once (on a 13B-shaped MHA batch of 50 contexts of
+// 7..1965 tokens: 154.6 us against 165.4 us for one chunk per slot, 158.9 us
+// for four and 161.2 us for six), and enough chunks that one chunk's blocks
+// fit in a workgroup's block-id staging (a chunk of C tokens spans at most
+// C / block_size + 2 blocks).
+#ifndef PKV_BALANCED_ROUNDS
+#define PKV_BALANCED_ROUNDS 2
+#endif
+int64_t balanced_chunks(int64_t padded_positions, int num_head_groups, int64_t target,
+                        int block_size) {
+    int64_t w = (target * PKV_BALANCED_ROUNDS + num_head_groups - 1) / num_head_groups;
+    const int64_t per_chunk = (int64_t)(kBtLds - 2) * block_size - 16;
+    const int64_t w_min = (padded_positions + per_chunk - 1) / per_chunk;
+    if (w < w_min) w = w_min;
+    return w < 1 ? 1 : w;
+}
+
 }  // namespace
 
 // Shape checks shared by the decode entry points, and the partition choice.
 DecodePlan plan_decode(int num_seqs, int num_q_heads, int num_kv_heads, int head_dim, int block_size,
                  int max_blocks_per_seq, int max_context_len, int partition_size, int dtype) {
-    DecodePlan pl{PAGED_KV_OK, 0, 0, 1, 1};
+    DecodePlan pl{PAGED_KV_OK, 0, 0, 1, 1, 0};
     if (dtype != PAGED_KV_F32 && dtype != PAGED_KV_F16 && dtype != PAGED_KV_BF16) {
         pl.status = PAGED_KV_ERR_UNSUPPORTED;
         return pl;
@@ -76,6 +104,28 @@ DecodePlan plan_decode(int num_seqs, int num_q_heads, int num_kv_heads, int head
     }
     const int align = block_size > 16 ? block_size : 16;
     const int64_t max_part = (int64_t)kBtLds * block_size;
+    const int hpg = heads_per_group_for(num_kv_heads);
+    if (partition_size == PAGED_KV_BALANCED_SPLIT) {
+        const int64_t padded = (int64_t)num_seqs * round_up(max_ctx, 16);
+        if (num_seqs > kBalancedMaxSeqs || padded > INT_MAX - 16) {
+            pl.status = PAGED_KV_ERR_UNSUPPORTED;
+            return pl;
+        }
+        const int64_t w = balanced_chunks(padded, num_kv_heads / hpg,
+                                          target_workgroups(dtype, head_dim, group, block_size,
+                                                            hpg),
+                                          block_size);
+        if (w * (num_kv_heads / hpg) > INT_MAX || 2 * w * (int64_t)num_q_heads > INT_MAX) {
+            pl.status = PAGED_KV_ERR_BAD_SHAPE;
+            return pl;
+        }
+        pl.max_context_len = max_ctx;
+        pl.partition_size = PAGED_KV_BALANCED_SPLIT;
+        pl.num_partitions = 1;
+        pl.heads_per_group = hpg;
+        pl.num_chunks = (int)w;
+        return pl;
+    }
     int64_t P;
     if (partition_size > 0) {
         if (partition_size % 16 != 0 || partition_size % block_size != 0 ||
@@ -85,16 +135,8 @@ DecodePlan plan_decode(int num_seqs, int num_q_heads, int num_kv_heads, int head
         }
         P = partition_size;
     } else {
-        const int hpg = heads_per_group_for(num_kv_heads);
         const int64_t units = (int64_t)num_seqs * (num_kv_heads / hpg);
-        const DeviceOccupancy occ =
-            decode_occupancy(dtype, head_dim, group, block_size, hpg);
-        int64_t per_cu = kTargetWavesPerCu / hpg;
-        if (occ.workgroups_per_cu > 0 && per_cu > occ.workgroups_per_cu)
-            per_cu = occ.workgroups_per_cu;
-        if (per_cu < 1) per_cu = 1;
-        const int64_t target =
-            (occ.compute_units > 0 ? occ.compute_units : kFallbackComputeUnits) * per_cu;
+        const int64_t target = target_workgroups(dtype, head_dim, group, block_size, hpg);
         if (units >= target || max_ctx <= kMinSplitTokens) {
             P = max_ctx;  // enough units already, or nothing worth splitting
         } else {
@@ -116,7 +158,7 @@ DecodePlan plan_decode(int num_seqs, int num_q_heads, int num_kv_heads, int head
     pl.max_context_len = max_ctx;
     pl.partition_size = (int)P;
     pl.num_partitions = (int)nparts;
-    pl.heads_per_group = heads_per_group_for(num_kv_heads);
+    pl.heads_per_group = hpg;
     return pl;
 }
 
@@ -124,19 +166,25 @@ size_t decode_partial_floats(int num_seqs, int num_q_heads) {
     return round_up((int64_t)num_seqs * num_q_heads, 4);  // keeps the o array 16-byte aligned
 }
 
-size_t decode_workspace_bytes(const DecodePlan &pl, int num_seqs, int num_q_heads, int head_dim) {
+size_t decode_partial_slots(const DecodePlan &pl, int num_seqs, int num_q_heads) {
+    if (pl.num_chunks > 0) return round_up(2 * (int64_t)pl.num_chunks * num_q_heads, 4);
     if (pl.num_partitions <= 1) return 0;
-    const size_t n = decode_partial_floats(num_seqs, num_q_heads) * pl.num_partitions;
-    return n * (2 + (size_t)head_dim) * sizeof(float);
+    return decode_partial_floats(num_seqs, num_q_heads) * pl.num_partitions;
+}
+
+size_t decode_workspace_bytes(const DecodePlan &pl, int num_seqs, int num_q_heads, int head_dim) {
+    return decode_partial_slots(pl, num_seqs, num_q_heads) * (2 + (size_t)head_dim) *
+           sizeof(float);
 }
 
 // The partition for a batch whose lengths the caller holds on the host.  A
 // split sized by the longest context suits contexts of similar length; with
 // very uneven lengths (the longest more than 1.5 times the mean) the
 // workgroups of the long contexts would finish far behind the rest, so the
-// split is the finest one, kMinSplitTokens (256-token partitions measured
-// 169 us against 192 us for 1024 on a batch of 50 contexts of 1..2048
-// tokens; 1024 stays best for contexts of 24K..32K tokens).
+// split is the balanced one, or where that does not apply the finest
+// partition, kMinSplitTokens (256-token partitions measured 169 us against
+// 192 us for 1024 on a batch of 50 contexts of 1..2048 tokens; 1024 stays
+// best for contexts of 24K..32K tokens).
 int plan_partition_for_lengths(const int32_t *lens, int num_seqs, int num_q_heads,
                                int num_kv_heads, int head_dim, int block_size,
                                int max_blocks_per_seq, int dtype) {
@@ -153,6 +201,10 @@ int plan_partition_for_lengths(const int32_t *lens, int num_seqs, int num_q_head
                                       max_blocks_per_seq, longest > 0 ? longest : 1, 0, dtype);
     if (pl.status != PAGED_KV_OK) return -pl.status;
     if (pl.num_partitions > 1 && 2 * (int64_t)longest * num_seqs > 3 * sum) {
+        const DecodePlan bal = plan_decode(num_seqs, num_q_heads, num_kv_heads, head_dim,
+                                           block_size, max_blocks_per_seq, longest,
+                                           PAGED_KV_BALANCED_SPLIT, dtype);
+        if (bal.status == PAGED_KV_OK) return PAGED_KV_BALANCED_SPLIT;
         const int align = block_size > 16 ? block_size : 16;
         return (int)round_up(kMinSplitTokens, align);
     }

@@ -11,7 +11,11 @@
 // ("23.1 vLLM：高吞吐推理框架原理与部署", §二.2 step 3).
 //
 // Work decomposition: one workgroup per (sequence, group of kv heads,
-// context partition), one wave per kv head of the group.  The workgroup
+// context partition), one wave per kv head of the group -- or, with the
+// balanced split (for batches whose context lengths are very uneven), one
+// workgroup per (chunk, group of kv heads), a chunk being an equal share of
+// all the batch's positions laid end to end, which it walks sequence piece
+// by sequence piece.  The workgroup
 // stages the partition's block ids in LDS once (checking each against the
 // pool size); then every wave walks the whole partition for its kv head, one
 // tile of at most 16 tokens at a time, keeping the online-softmax state
@@ -70,6 +74,7 @@ struct WorkItem {
     int context_len;
     int tok_begin, tok_end;  // this partition's token range [begin, end)
     bool bad_len;            // context_len < 0 or > max_context_len
+    bool final;              // the range is the whole context: write the output
 };
 
 __device__ inline WorkItem work_item(const DecodeParams &p) {
@@ -86,7 +91,117 @@ __device__ inline WorkItem work_item(const DecodeParams &p) {
     w.tok_begin = w.part * p.partition_size;
     const int end = w.tok_begin + p.partition_size;
     w.tok_end = end < w.context_len ? end : w.context_len;
+    w.final = p.num_partitions == 1;
     return w;
+}
+
+// ------------------------------------------------------------------------
+// Balanced split.  The positions of all sequences, each padded to a
+// multiple of 16 (a length outside [0, max_context_len] counts 0), are laid
+// end to end and cut into num_chunks chunks of C positions, C a multiple of
+// 16; workgroup (chunk w, kv-head group) computes every piece of a sequence
+// that falls in chunk w (a segment).  A sequence whose positions lie in one
+// chunk is finished there.  The others leave one partial result per chunk
+// they touch, in slot 2 w + 1 of the chunk they start in and in slot 2 w of
+// every later one (a chunk holds at most one sequence that continues from
+// the chunk before and one that continues into the next), and the reduce
+// merges them.
+// ------------------------------------------------------------------------
+__device__ inline int padded_len(const DecodeParams &p, int L) {
+    return (L > 0 && L <= p.max_context_len) ? (L + 15) & ~15 : 0;
+}
+
+__device__ inline int chunk_size(int total, int num_chunks) {
+    const int64_t c = ((int64_t)total + num_chunks - 1) / num_chunks;
+    const int r = (int)((c + 15) & ~(int64_t)15);
+    return r < 16 ? 16 : r;
+}
+
+__device__ inline int scan_inclusive_wave(int x) {
+    const int lane = threadIdx.x % kWave;
+#pragma unroll
+    for (int d = 1; d < kWave; d <<= 1) {
+        const int y = __shfl_up(x, d);
+        if (lane >= d) x += y;
+    }
+    return x;
+}
+
+// start[s] for s = 0 .. num_seqs: exclusive prefix sums of the padded
+// lengths, written to LDS by the whole workgroup (start[num_seqs] = total).
+__device__ inline void padded_starts(const DecodeParams &p, int32_t *start, int32_t *wave_tot) {
+    const int S = p.num_seqs;
+    const int nt = blockDim.x;
+    const int t = threadIdx.x;
+    const int k = (S + nt - 1) / nt;  // consecutive sequences per thread
+    const int s0 = t * k;
+    int local = 0;
+    for (int i = 0; i < k; ++i)
+        if (s0 + i < S) local += padded_len(p, p.context_lens[s0 + i]);
+    const int incl = scan_inclusive_wave(local);
+    const int wave = t / kWave;
+    if (t % kWave == kWave - 1) wave_tot[wave] = incl;
+    __syncthreads();
+    int before = 0;
+    for (int v = 0; v < wave; ++v) before += wave_tot[v];
+    int run = before + incl - local;
+    for (int i = 0; i < k; ++i) {
+        if (s0 + i < S) {
+            start[s0 + i] = run;
+            run += padded_len(p, p.context_lens[s0 + i]);
+        }
+    }
+    if (t == nt - 1) start[S] = before + incl;
+    __syncthreads();
+}
+
+// Runs body(work item) for each segment of this workgroup's chunk, with a
+// workgroup barrier after each (the segments reuse the block-id staging).
+template <class Body>
+__device__ inline void for_each_segment(const DecodeParams &p, int32_t *start,
+                                        int32_t *wave_tot, Body &&body) {
+    padded_starts(p, start, wave_tot);
+    const int S = p.num_seqs;
+    const int total = start[S];
+    const int C = chunk_size(total, p.num_chunks);
+    const int chunk = blockIdx.x / p.num_head_groups;
+    const int hg = blockIdx.x % p.num_head_groups;
+    const int lo = (int)((int64_t)chunk * C < total ? (int64_t)chunk * C : total);
+    if (lo >= total) return;
+    const int hi = total - lo < C ? total : lo + C;
+    // the last sequence starting at or before lo: the one holding position lo
+    int a = 0, b = S - 1;
+    while (a < b) {
+        const int mid = (a + b + 1) / 2;
+        if (start[mid] <= lo) a = mid; else b = mid - 1;
+    }
+    for (int s = a; s < S && start[s] < hi; ++s) {
+        if (start[s + 1] == start[s]) continue;  // empty or invalid length
+        const int L = p.context_lens[s];
+        const int begin = (lo > start[s] ? lo : start[s]) - start[s];
+        const int e0 = (hi < start[s + 1] ? hi : start[s + 1]) - start[s];
+        const int end = e0 < L ? e0 : L;
+        if (begin >= end) continue;               // only padding of s in this chunk
+        const int first = start[s] / C, last = (start[s] + L - 1) / C;
+        WorkItem w;
+        w.s = s;
+        w.kvh0 = hg * p.heads_per_group;
+        w.kvh = w.kvh0 + (int)(threadIdx.x / kWave);
+        w.part = chunk == first ? 2 * chunk + 1 : 2 * chunk;  // partial slot
+        w.context_len = L;
+        w.tok_begin = begin;
+        w.tok_end = end;
+        w.bad_len = false;
+        w.final = first == last;
+        body(w);
+        __syncthreads();
+    }
+}
+
+// Index of the partial result of query head h for work item w.
+__device__ inline int64_t partial_index(const DecodeParams &p, const WorkItem &w, int h) {
+    if (p.num_chunks > 0) return (int64_t)w.part * p.num_q_heads + h;
+    return ((int64_t)w.s * p.num_q_heads + h) * p.num_partitions + w.part;
 }
 
 // Copies the block ids covering tokens [begin, end) into LDS.  Returns true
@@ -96,8 +211,8 @@ __device__ inline bool stage_block_table(const DecodeParams &p, const WorkItem &
     const int b0 = w.tok_begin >> p.block_shift;
     const int b1 = (w.tok_end - 1) >> p.block_shift;
     const int32_t *row = p.block_tables + (int64_t)w.s * p.max_blocks_per_seq;
-    int bad = 0;
-    for (int i = threadIdx.x; i <= b1 - b0; i += blockDim.x) {
+    int bad = b1 - b0 + 1 > kBtLds;  // never with the host's split (kept in bounds regardless)
+    for (int i = threadIdx.x; i <= b1 - b0 && i < kBtLds; i += blockDim.x) {
         int id = row[b0 + i];
         if (id < 0 || id >= p.num_blocks) {
             bad = 1;
@@ -232,7 +347,7 @@ __device__ inline void write_result(const DecodeParams &p, const WorkItem &w, in
                                     const float *acc, float m, float l, bool bad,
                                     bool write_ml) {
     constexpr int EPC = T::kPerChunk;
-    if (p.num_partitions == 1) {
+    if (w.final) {
         const int64_t o = ((int64_t)w.s * p.num_q_heads + h) * D + d0;
         u32x4 c;
         if (bad) {
@@ -246,7 +361,7 @@ __device__ inline void write_result(const DecodeParams &p, const WorkItem &w, in
         }
         store16(static_cast<char *>(p.out) + o * T::kBytes, c);
     } else {
-        const int64_t ph = ((int64_t)w.s * p.num_q_heads + h) * p.num_partitions + w.part;
+        const int64_t ph = partial_index(p, w, h);
         float *po = p.part_out + ph * D + d0;
 #pragma unroll
         for (int e = 0; e < EPC; e += 4) {
@@ -291,7 +406,7 @@ __device__ inline void run_tiles(int ntiles, int nfull, Load &&load, Consume &&c
 // ------------------------------------------------------------------------
 // VALU kernel
 // ------------------------------------------------------------------------
-template <class T, int D, int G, bool BT>
+template <class T, int D, int G, bool BT, bool BAL>
 __global__ __launch_bounds__(kMaxDecodeThreads) void decode_valu_kernel(DecodeParams p) {
     constexpr int EPC = T::kPerChunk;   // elements per 16-byte chunk
     constexpr int CPR = D / EPC;        // lanes holding one row
@@ -307,9 +422,8 @@ __global__ __launch_bounds__(kMaxDecodeThreads) void decode_valu_kernel(DecodePa
 
     __shared__ int32_t bt_lds[kBtLds];
 
-    const WorkItem w = work_item(p);
-    write_new_token<T, D>(p, w);
-    if (!prologue<T, D, G>(p, w)) return;
+    // one partition (or, with the balanced split, one segment) of a sequence
+    auto segment = [&](const WorkItem &w) {
     const int b0 = w.tok_begin >> p.block_shift;
 
     const int lane = threadIdx.x % kWave;
@@ -441,6 +555,18 @@ __global__ __launch_bounds__(kMaxDecodeThreads) void decode_valu_kernel(DecodePa
         for (int g = 0; g < G; ++g)
             write_result<T, D>(p, w, w.kvh * G + g, c * EPC, acc[g], m[g], l[g], bad, c == 0);
     }
+    };
+
+    if constexpr (BAL) {
+        __shared__ int32_t seq_start[kBalancedMaxSeqs + 1];
+        __shared__ int32_t wave_tot[kMaxDecodeWaves];
+        for_each_segment(p, seq_start, wave_tot, segment);
+    } else {
+        const WorkItem w = work_item(p);
+        write_new_token<T, D>(p, w);
+        if (!prologue<T, D, G>(p, w)) return;
+        segment(w);
+    }
 }
 
 // ------------------------------------------------------------------------
@@ -482,7 +608,7 @@ constexpr int v_lds_offset() { return 16 * k_lds_row_bytes<D>(); }
 template <int D>
 constexpr int kv_lds_wave_bytes() { return v_lds_offset<D>() + 16 * D * 2; }
 
-template <class T, int D, int G, bool BT>
+template <class T, int D, int G, bool BT, bool BAL>
 __global__ __launch_bounds__(kMaxDecodeThreads) void decode_mfma_kernel(DecodeParams p) {
     static_assert(T::kBytes == 2, "MFMA path is for 16-bit element types");
     static_assert(G == 2 || G == 4 || G == 8, "group size");
@@ -504,9 +630,8 @@ __global__ __launch_bounds__(kMaxDecodeThreads) void decode_mfma_kernel(DecodePa
     // per wave, kv_lds_wave_bytes<D>() each (dynamic, sized by the launch)
     extern __shared__ __attribute__((aligned(16))) char k_lds[];
 
-    const WorkItem w = work_item(p);
-    write_new_token<T, D>(p, w);
-    if (!prologue<T, D, G>(p, w)) return;
+    // one partition (or, with the balanced split, one segment) of a sequence
+    auto segment = [&](const WorkItem &w) {
     const int b0 = w.tok_begin >> p.block_shift;
 
     const int wave = threadIdx.x / kWave;
@@ -700,6 +825,18 @@ __global__ __launch_bounds__(kMaxDecodeThreads) void decode_mfma_kernel(DecodePa
             write_result<T, D>(p, w, w.kvh * G + g, vc * 8, acc[g], aex[wave][g], lex[wave][g],
                                bad, vc == 0);
     }
+    };
+
+    if constexpr (BAL) {
+        __shared__ int32_t seq_start[kBalancedMaxSeqs + 1];
+        __shared__ int32_t wave_tot[kMaxDecodeWaves];
+        for_each_segment(p, seq_start, wave_tot, segment);
+    } else {
+        const WorkItem w = work_item(p);
+        write_new_token<T, D>(p, w);
+        if (!prologue<T, D, G>(p, w)) return;
+        segment(w);
+    }
 }
 
 // ------------------------------------------------------------------------
@@ -804,6 +941,110 @@ __global__ __launch_bounds__(kReduceThreads) void decode_reduce_kernel(DecodePar
     for (int e = 0; e < EL; ++e) T::store(p.out, obase + e, o[e] * inv);
 }
 
+// The reduce of the balanced split, one wave per (sequence, query head):
+// the same merge over the sequence's partial results, which sit in slot
+// 2 f + 1 (its first chunk f) and slots 2 c of its later chunks c.  A
+// sequence that lies in one chunk was finished by the partition kernel.
+__device__ inline int wave_sum_int(int x) {
+#pragma unroll
+    for (int d = 1; d < kWave; d <<= 1) x += __shfl_xor(x, d);
+    return x;
+}
+
+template <class T, int D>
+__global__ __launch_bounds__(kReduceThreads) void decode_reduce_balanced_kernel(DecodeParams p) {
+    constexpr int EL = D / kReduceThreads;
+    constexpr int R = 16;
+    const int sh = blockIdx.x;
+    const int lane = threadIdx.x;
+    const int s = sh / p.num_q_heads;
+    const int h = sh % p.num_q_heads;
+    const int64_t obase = (int64_t)sh * D + lane * EL;
+    const int L = p.context_lens[s];
+    if (L < 0 || L > p.max_context_len) {
+#pragma unroll
+        for (int e = 0; e < EL; ++e) T::store_nan(p.out, obase + e);
+        return;
+    }
+    if (L == 0) {
+#pragma unroll
+        for (int e = 0; e < EL; ++e) T::store(p.out, obase + e, 0.0f);
+        return;
+    }
+    // this sequence's padded start and the padded total, as the partition
+    // kernel lays them out
+    int before = 0, total = 0;
+    for (int i = lane; i < p.num_seqs; i += kReduceThreads) {
+        const int pi = padded_len(p, p.context_lens[i]);
+        total += pi;
+        if (i < s) before += pi;
+    }
+    before = wave_sum_int(before);
+    total = wave_sum_int(total);
+    const int C = chunk_size(total, p.num_chunks);
+    const int first = before / C;
+    const int n = (before + L - 1) / C - first + 1;  // partial results
+    if (n == 1) return;
+    auto index = [&](int q) -> int64_t {
+        const int slot = q == 0 ? 2 * first + 1 : 2 * (first + q);
+        return (int64_t)slot * p.num_q_heads + h;
+    };
+    const float mq = lane < n ? p.part_max[index(lane)] : -INFINITY;  // lane q: partial q < 64
+    const float lq = lane < n ? p.part_sum[index(lane)] : 0.0f;
+    float v[R][EL];
+#pragma unroll
+    for (int u = 0; u < R; ++u) {
+        const int64_t o = index(u < n ? u : 0) * D + lane * EL;
+#pragma unroll
+        for (int e = 0; e < EL; ++e) v[u][e] = p.part_out[o + e];
+    }
+    float M = mq;
+    for (int q = lane + kReduceThreads; q < n; q += kReduceThreads)
+        M = vmax(M, p.part_max[index(q)]);
+    M = group_max<kReduceThreads>(M);
+    float Ls = lane < n ? lq * fast_exp2(mq - M) : 0.0f;
+    for (int q = lane + kReduceThreads; q < n; q += kReduceThreads)
+        Ls += p.part_sum[index(q)] * fast_exp2(p.part_max[index(q)] - M);
+    Ls = group_sum<kReduceThreads>(Ls);
+    const float inv = 1.0f / Ls;
+    const float wl = lane < n ? fast_exp2(mq - M) : 0.0f;
+    auto weight = [&](int q) {
+        return q < kReduceThreads
+                   ? __builtin_bit_cast(float, __builtin_amdgcn_readlane(
+                                                   __builtin_bit_cast(int, wl), q))
+                   : fast_exp2(p.part_max[index(q)] - M);
+    };
+    float o[EL];
+#pragma unroll
+    for (int e = 0; e < EL; ++e) o[e] = 0.0f;
+#pragma unroll
+    for (int u = 0; u < R; ++u) {
+        if (u < n) {
+            const float wq = weight(u);
+#pragma unroll
+            for (int e = 0; e < EL; ++e) o[e] = fmaf(wq, v[u][e], o[e]);
+        }
+    }
+    for (int q0 = R; q0 < n; q0 += R) {
+#pragma unroll
+        for (int u = 0; u < R; ++u) {
+            const int64_t oo = index(q0 + u < n ? q0 + u : 0) * D + lane * EL;
+#pragma unroll
+            for (int e = 0; e < EL; ++e) v[u][e] = p.part_out[oo + e];
+        }
+#pragma unroll
+        for (int u = 0; u < R; ++u) {
+            if (q0 + u < n) {
+                const float wq = weight(q0 + u);
+#pragma unroll
+                for (int e = 0; e < EL; ++e) o[e] = fmaf(wq, v[u][e], o[e]);
+            }
+        }
+    }
+#pragma unroll
+    for (int e = 0; e < EL; ++e) T::store(p.out, obase + e, o[e] * inv);
+}
+
 // Workgroups of this kernel instance one compute unit holds at once.
 template <class T, int D, int G, bool BT>
 int blocks_per_cu(int threads) {
@@ -811,11 +1052,11 @@ int blocks_per_cu(int threads) {
     hipError_t e;
     if constexpr (T::kBytes == 2 && G >= 2)
         e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
-            &n, reinterpret_cast<const void *>(&decode_mfma_kernel<T, D, G, BT>), threads,
+            &n, reinterpret_cast<const void *>(&decode_mfma_kernel<T, D, G, BT, false>), threads,
             (threads / kWave) * kv_lds_wave_bytes<D>());
     else
         e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
-            &n, reinterpret_cast<const void *>(&decode_valu_kernel<T, D, G, BT>), threads, 0);
+            &n, reinterpret_cast<const void *>(&decode_valu_kernel<T, D, G, BT, false>), threads, 0);
     return e == hipSuccess ? n : 0;
 }
 
@@ -843,18 +1084,29 @@ int blocks_per_cu_t(int head_dim, int group, bool bt, int threads) {
 template <class T, int D, int G, bool BT>
 hipError_t launch_main(const DecodeParams &p, int kernel, hipStream_t stream) {
     const unsigned grid =
-        (unsigned)((int64_t)p.num_seqs * p.num_head_groups * p.num_partitions);
+        p.num_chunks > 0
+            ? (unsigned)((int64_t)p.num_chunks * p.num_head_groups)
+            : (unsigned)((int64_t)p.num_seqs * p.num_head_groups * p.num_partitions);
     const unsigned threads = (unsigned)(p.heads_per_group * kWave);
     // 16-bit types with grouped queries take the MFMA kernel, everything else
     // the VALU kernel (decode_kernel_choice); only those pairs are built.
     if constexpr (T::kBytes == 2 && G >= 2) {
         if (kernel != 1) return hipErrorInvalidValue;
-        hipLaunchKernelGGL((decode_mfma_kernel<T, D, G, BT>), dim3(grid), dim3(threads),
-                           p.heads_per_group * kv_lds_wave_bytes<D>(), stream, p);
+        const size_t lds = p.heads_per_group * kv_lds_wave_bytes<D>();
+        if (p.num_chunks > 0)
+            hipLaunchKernelGGL((decode_mfma_kernel<T, D, G, BT, true>), dim3(grid),
+                               dim3(threads), lds, stream, p);
+        else
+            hipLaunchKernelGGL((decode_mfma_kernel<T, D, G, BT, false>), dim3(grid),
+                               dim3(threads), lds, stream, p);
     } else {
         if (kernel != 0) return hipErrorInvalidValue;
-        hipLaunchKernelGGL((decode_valu_kernel<T, D, G, BT>), dim3(grid), dim3(threads), 0,
-                           stream, p);
+        if (p.num_chunks > 0)
+            hipLaunchKernelGGL((decode_valu_kernel<T, D, G, BT, true>), dim3(grid),
+                               dim3(threads), 0, stream, p);
+        else
+            hipLaunchKernelGGL((decode_valu_kernel<T, D, G, BT, false>), dim3(grid),
+                               dim3(threads), 0, stream, p);
     }
     return hipGetLastError();
 }
@@ -864,7 +1116,11 @@ hipError_t launch_typed(const DecodeParams &p, int kernel, hipStream_t stream) {
     hipError_t e = p.block_size >= 16 ? launch_main<T, D, G, true>(p, kernel, stream)
                                       : launch_main<T, D, G, false>(p, kernel, stream);
     if (e != hipSuccess) return e;
-    if (p.num_partitions > 1) {
+    if (p.num_chunks > 0) {
+        hipLaunchKernelGGL((decode_reduce_balanced_kernel<T, D>),
+                           dim3(p.num_seqs * p.num_q_heads), dim3(kReduceThreads), 0, stream, p);
+        e = hipGetLastError();
+    } else if (p.num_partitions > 1) {
         hipLaunchKernelGGL((decode_reduce_kernel<T, D>), dim3(p.num_seqs * p.num_q_heads),
                            dim3(kReduceThreads), 0, stream, p);
         e = hipGetLastError();

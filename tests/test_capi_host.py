@@ -338,6 +338,29 @@ def test_decode_write_rejects(lib, kw, status):
         a["max_context_len"], a["partition_size"], a["dtype"], None, 0, None) == status
 
 
+BALANCED = 1   # PAGED_KV_BALANCED_SPLIT
+
+
+def test_balanced_split_plan(lib):
+    """The balanced split is kept when asked for, sizes its own workspace
+    (two fp32 partial slots per chunk and query head), and is refused past
+    1024 sequences, past 2^31 padded positions and for the fused step."""
+    ps = lib.paged_attn_decode_partition_size
+    ws = lib.paged_attn_decode_workspace_bytes
+    assert ps(50, 40, 40, 128, 16, 128, 2048, BALANCED, 1) == BALANCED
+    need = ws(50, 40, 40, 128, 16, 128, 2048, BALANCED, 1)
+    assert need > 0 and need % ((128 + 2) * 4) == 0
+    assert need // ((128 + 2) * 4) % (2 * 40) in (0, 40)      # 2 slots x 40 heads per chunk
+    assert ps(1024, 8, 2, 128, 16, 64, 1024, BALANCED, 2) == BALANCED
+    assert ps(1025, 8, 2, 128, 16, 64, 1024, BALANCED, 2) == -UNSUPPORTED
+    assert ps(1024, 8, 2, 128, 16, 200000, 0, BALANCED, 2) == -UNSUPPORTED   # > 2^31 positions
+    # the fused step does not take it (host check before anything is enqueued)
+    lib.paged_attn_decode_write.restype = ctypes.c_int
+    st = lib.paged_attn_decode_write(P, P, P, P, P, P, P, P, 0.1, P, 4, 8, 2, 128, 16, 64, 8, 0,
+                                     BALANCED, 2, P, 1 << 30, None)
+    assert st == UNSUPPORTED
+
+
 def test_partition_for_host_lengths(lib):
     """Uneven lengths in a batch that needs a split get the finest split;
     even lengths keep the automatic rule (sized by the longest context); a
@@ -350,7 +373,11 @@ def test_partition_for_host_lengths(lib):
         return f(a.ctypes.data_as(ctypes.c_void_p), a.size, *shape)
     rng = np.random.default_rng(5)
     uneven = rng.integers(1, 2049, size=50)                  # 50 sequences, 40 MHA heads
-    assert plan(uneven, 40, 40, 128, 16, 128, 1) == 256
+    assert plan(uneven, 40, 40, 128, 16, 128, 1) == BALANCED
+    # past the balanced split's 1024 sequences: the finest partition instead
+    # (with 4 MHA heads 1100 sequences are still too few units for the device)
+    many_uneven = rng.integers(1, 8193, size=1100)
+    assert plan(many_uneven, 1, 1, 128, 16, 512, 1) == 256
     even = rng.integers(24576, 32769, size=8)                # 8 long contexts, GQA
     p = plan(even, 32, 8, 128, 32, 1024, 2)
     assert p == lib.paged_attn_decode_partition_size(8, 32, 8, 128, 32, 1024, int(even.max()), 0, 2)

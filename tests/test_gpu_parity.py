@@ -537,3 +537,101 @@ def test_decode_score_extremes(B, dtype, G, case):
     for P in (0, 32):
         got = run_decode(B, b, partition_size=P)
         check_close(tensors.widen(got, dtype), ref, dtype, f"{case} {dtype} G={G} P={P}")
+
+
+# ------------------------------------------------------- balanced split
+BALANCED = 1   # PAGED_KV_BALANCED_SPLIT
+
+
+@pytest.mark.parametrize("name", W.WORKLOADS)
+def test_decode_workload_balanced(B, name):
+    """Every workload with the balanced split (all positions end to end, cut
+    into equal chunks; sequences that span chunks merged by the reduce)."""
+    _say(f"decode {name}, balanced split")
+    b = workload(name)
+    assert B.paged_attn_decode_partition_size(
+        b.num_seqs, b.num_q_heads, b.num_kv_heads, b.head_dim, b.block_size,
+        b.max_blocks_per_seq, b.max_context_len, BALANCED, b.dtype_code) == BALANCED
+    got = run_decode(B, b, partition_size=BALANCED)
+    check_close(tensors.widen(got, b.dtype), oracle_out(name), b.dtype, f"{name} balanced")
+
+
+BALANCED_SHAPES = [(dt, D, G, bs) for dt in ("f32", "f16", "bf16") for D in (64, 128, 256)
+                   for G in (1, 4, 8) for bs in (1, 16, 32)]
+
+
+@pytest.mark.parametrize("dtype,D,G,bs", BALANCED_SHAPES)
+def test_decode_balanced_shapes(B, dtype, D, G, bs):
+    """Both kernels with the balanced split: empty, one-token and tile-edge
+    contexts beside long ones, so that chunks hold several whole sequences,
+    pieces of two, or a piece of one long context."""
+    lens = (0, 1, 15, 16, 17, 77, 300, 2500, 3, 1000)
+    b = W.make_custom(5600 + D + 10 * G + bs, dtype=dtype, num_seqs=len(lens),
+                      num_q_heads=G * 2, num_kv_heads=2, head_dim=D, block_size=bs,
+                      context_lens=lens, extra_blocks=5, poison=True)
+    got = run_decode(B, b, partition_size=BALANCED)
+    check_close(tensors.widen(got, dtype), oracle.decode_batch(b), dtype,
+                f"{dtype} D={D} G={G} bs={bs} balanced")
+
+
+@pytest.mark.parametrize("dtype,G,Hkv", [("bf16", 4, 8), ("f16", 1, 40), ("f32", 2, 4)])
+def test_decode_balanced_long_and_short(B, dtype, G, Hkv):
+    """One context far longer than the rest: it spans many chunks (more than
+    64 with 8 kv heads: the reduce walks its partials in rounds)."""
+    lens = (40000, 5, 33, 0, 700, 1)
+    b = W.make_custom(5700 + G + Hkv, dtype=dtype, num_seqs=len(lens), num_q_heads=G * Hkv,
+                      num_kv_heads=Hkv, head_dim=128, block_size=16, context_lens=lens,
+                      extra_blocks=3, poison=True)
+    got = run_decode(B, b, partition_size=BALANCED)
+    check_close(tensors.widen(got, dtype), oracle.decode_batch(b), dtype,
+                f"{dtype} G={G} Hkv={Hkv} long+short balanced")
+
+
+def test_decode_balanced_many_sequences(B):
+    """1024 sequences (the most the balanced split takes), lengths 0..400."""
+    rng = np.random.default_rng(5800)
+    lens = tuple(int(x) for x in rng.integers(0, 401, size=1024))
+    b = W.make_custom(5800, dtype="bf16", num_seqs=1024, num_q_heads=8, num_kv_heads=2,
+                      head_dim=128, block_size=16, context_lens=lens, extra_blocks=3,
+                      poison=True)
+    got = run_decode(B, b, partition_size=BALANCED)
+    check_close(tensors.widen(got, "bf16"), oracle.decode_batch(b), "bf16", "1024 seqs balanced")
+
+
+def test_decode_balanced_permutation_and_poison(B):
+    """Bit-identical results under a relabelling of the physical blocks, and
+    repeated runs agree bit for bit."""
+    b = medium()
+    p = W.permute_blocks(b, 9)
+    first = run_decode(B, b, partition_size=BALANCED)
+    assert np.array_equal(first.view(np.uint16), run_decode(B, p, partition_size=BALANCED).view(np.uint16))
+    assert np.array_equal(first.view(np.uint16), run_decode(B, b, partition_size=BALANCED).view(np.uint16))
+
+
+def test_decode_balanced_invalid_values(B):
+    """Invalid lengths and block ids with the balanced split: NaN for those
+    sequences, the others unaffected."""
+    b = W.make_custom(5900, dtype="bf16", num_seqs=5, num_q_heads=8, num_kv_heads=2,
+                      head_dim=128, block_size=16, context_lens=(20, 900, 60, 33, 2000),
+                      max_blocks_per_seq=130, poison=True)
+    ref = oracle.decode_batch(b)
+    bad = b.copy()
+    bad.context_lens[0] = 3000         # above max_context_len = 2080
+    bad.block_tables[1, 40] = b.num_blocks + 3
+    bad.context_lens[3] = -5
+    bad.block_tables[4, 100] = -2
+    got = tensors.widen(run_decode(B, bad, partition_size=BALANCED, max_context_len=2080), "bf16")
+    for s in (0, 1, 3, 4):
+        assert np.all(np.isnan(got[s])), s
+    check_close(got[2:3], ref[2:3], "bf16", "valid neighbour balanced")
+
+
+def test_decode_balanced_extremes(B):
+    """Score extremes (scale, staircases, dominant tiles) with the balanced
+    split on the matrix-core and vector kernels."""
+    for dtype, G in (("bf16", 4), ("f16", 1), ("f32", 4)):
+        for case in EXTREME_CASES:
+            b = with_scores(extreme_batch(dtype, G), case)
+            got = run_decode(B, b, partition_size=BALANCED)
+            check_close(tensors.widen(got, dtype), oracle.decode_batch(b), dtype,
+                        f"{case} {dtype} G={G} balanced")
