@@ -635,3 +635,73 @@ def test_decode_balanced_extremes(B):
             got = run_decode(B, b, partition_size=BALANCED)
             check_close(tensors.widen(got, dtype), oracle.decode_batch(b), dtype,
                         f"{case} {dtype} G={G} balanced")
+
+
+def test_decode_balanced_empty_and_invalid_batches(B):
+    """All contexts empty (nothing to walk: the reduce writes the zeros), and
+    all invalid (NaN everywhere), with the balanced split."""
+    b = W.make_custom(5950, dtype="bf16", num_seqs=4, num_q_heads=8, num_kv_heads=2,
+                      head_dim=128, block_size=16, context_lens=(0, 0, 0, 0),
+                      max_blocks_per_seq=4, poison=True)
+    got = tensors.widen(run_decode(B, b, partition_size=BALANCED, max_context_len=64), "bf16")
+    assert np.all(got == 0)
+    bad = b.copy()
+    bad.context_lens[:] = (-1, 65, 100, -3)
+    got = tensors.widen(run_decode(B, bad, partition_size=BALANCED, max_context_len=64), "bf16")
+    assert np.all(np.isnan(got))
+
+
+def test_decode_balanced_graph_replay(B):
+    """The balanced-split decode captured in a HIP graph: every replay, with
+    eager work and synchronisations between replays, gives the eager bits."""
+    _say("balanced decode in a HIP graph")
+    b = W.make_custom(5960, dtype="bf16", num_seqs=6, num_q_heads=32, num_kv_heads=8,
+                      head_dim=128, block_size=16, context_lens=(3000, 5, 640, 0, 17, 1200),
+                      extra_blocks=4, poison=True)
+    eager, g = tensors.device_batch(b, DEV), tensors.device_batch(b, DEV)
+    ws_bytes = B.paged_attn_decode_workspace_bytes(
+        b.num_seqs, b.num_q_heads, b.num_kv_heads, b.head_dim, b.block_size,
+        b.max_blocks_per_seq, b.max_context_len, BALANCED, b.dtype_code)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=DEV)
+    B.paged_attn_decode(eager.query, eager.key_cache, eager.value_cache, eager.block_tables,
+                        eager.context_lens, b.scale, eager.out, max_context_len=b.max_context_len,
+                        partition_size=BALANCED, workspace=ws)
+    torch.cuda.synchronize()
+    want = tensors.to_host_bits(eager.out)
+    check_close(tensors.widen(want, "bf16"), oracle.decode_batch(b), "bf16", "balanced eager")
+    graph = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(graph, stream=side):
+            B.paged_attn_decode(g.query, g.key_cache, g.value_cache, g.block_tables,
+                                g.context_lens, b.scale, g.out, max_context_len=b.max_context_len,
+                                partition_size=BALANCED, workspace=ws)
+    torch.cuda.current_stream().wait_stream(side)
+    for r in range(4):
+        g.out.fill_(0.0)                     # eager work between replays
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(tensors.to_host_bits(g.out), want), f"replay {r}"
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_decode_balanced_random_batches(B, seed):
+    """Seeded random batches for the balanced split: dtype, head size, group
+    size, block size, kv heads, 1..40 sequences and lengths 0..3000 drawn."""
+    rng = np.random.default_rng(6000 + seed)
+    dtype = ("f32", "f16", "bf16")[rng.integers(3)]
+    D = int(rng.choice([64, 128, 256]))
+    G = int(rng.choice([1, 2, 4, 8]))
+    Hkv = int(rng.choice([1, 2, 4, 8]))
+    bs = int(rng.choice([1, 8, 16, 32, 64]))
+    S = int(rng.integers(1, 41))
+    lens = tuple(int(x) for x in rng.integers(0, 3001, size=S))
+    _say(f"balanced random {seed}: {dtype} D={D} G={G} Hkv={Hkv} bs={bs} S={S}")
+    b = W.make_custom(6000 + seed, dtype=dtype, num_seqs=S, num_q_heads=G * Hkv,
+                      num_kv_heads=Hkv, head_dim=D, block_size=bs, context_lens=lens,
+                      extra_blocks=3, poison=True)
+    got = run_decode(B, b, partition_size=BALANCED)
+    check_close(tensors.widen(got, dtype), oracle.decode_batch(b), dtype,
+                f"random {seed} balanced")

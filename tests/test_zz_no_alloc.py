@@ -82,6 +82,20 @@ def test_noalloc_decode_matches_workspace_decode(B, first, p1, second, p2):
                     f"noalloc {name} P={P}")
 
 
+def test_noalloc_decode_balanced_split(B):
+    """The balanced split through the static scratch: the same bits as the
+    decode with a workspace, twice in a row (the second batch smaller), and
+    the oracle's result."""
+    for seed, lens in ((74, (1965, 7, 300, 0, 1200, 45, 16, 800)), (75, (33, 500, 2))):
+        b = W.make_custom(seed, dtype="f16", num_seqs=len(lens), num_q_heads=8, num_kv_heads=8,
+                          head_dim=128, block_size=16, context_lens=lens, extra_blocks=4,
+                          poison=True)
+        got, want, need = _both(B, b, B.BALANCED_SPLIT)
+        _say(f"paged_attn_decode_noalloc balanced, {len(lens)} sequences: {need} B of scratch")
+        assert np.array_equal(got.view(np.uint8), want.view(np.uint8))
+        check_close(tensors.widen(got, "f16"), oracle.decode_batch(b), "f16", "noalloc balanced")
+
+
 def test_noalloc_decode_without_a_split(B):
     """No split: the static scratch is not touched; same bits as the decode."""
     b = W.make_workload("tiny_f32", poison=True)
