@@ -514,6 +514,15 @@ DEFAULT_WORKLOAD = "llama3_8b_gqa_bf16"
 SETTLE_LAUNCHES = 400
 
 
+BALANCED_SPLIT = 1   # PAGED_KV_BALANCED_SPLIT
+
+
+def split_name(partition_size: int):
+    """The decode's split as the JSON line reports it: tokens per partition,
+    or the balanced split (all positions cut into equal chunks)."""
+    return "balanced" if partition_size == BALANCED_SPLIT else partition_size
+
+
 class DecodeRig:
     """One decode workload on the device: its pool held in several copies
     that successive launches rotate through (so that a launch never finds
@@ -613,7 +622,7 @@ def other_workload(rig: "DecodeRig", args) -> dict:
         "head_dim": b.head_dim, "block_size": b.block_size,
         "context_tokens": int(b.context_lens.sum()),
         "context_len_range": [int(b.context_lens.min()), int(b.context_lens.max())],
-        "partition_size": psize,
+        "partition_size": split_name(psize),
         "decode_ms": round(dec_ms, 5),
         "seq_per_s_per_layer": round(b.num_seqs / t, 1),
         "algorithmic_bytes": logical,
@@ -786,7 +795,7 @@ def main() -> int:
             "block_size": bs, "num_blocks": b.num_blocks,
             "context_tokens": int(b.context_lens.sum()),
             "context_len_range": [int(b.context_lens.min()), int(b.context_lens.max())],
-            "partition_size": rig.partition_size, "pool_copies": len(rig.copies),
+            "partition_size": split_name(rig.partition_size), "pool_copies": len(rig.copies),
             "step": ("kv_cache_write of one token per sequence + paged_attn_decode"
                      if not args.fused else
                      "paged_attn_decode_write: one new token per sequence stored in the pool "
