@@ -559,6 +559,14 @@ class DecodeRig:
         ws_bytes = binding.paged_attn_decode_workspace_bytes(
             S, Hq, Hkv, D, bs, b.max_blocks_per_seq, self.max_ctx, self.psize, b.dtype_code)
         self.workspace = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
+        # a batch whose sequences share a prefix (which its caller knows) is
+        # also decoded with paged_attn_decode_shared_prefix
+        self.prefix_len = b.meta.get("prefix_blocks", 0) * bs
+        if self.prefix_len:
+            sp_bytes = binding.paged_attn_decode_shared_prefix_workspace_bytes(
+                S, Hq, Hkv, D, bs, b.max_blocks_per_seq, self.max_ctx, self.prefix_len, 0, 0,
+                b.dtype_code)
+            self.sp_workspace = torch.empty(sp_bytes, dtype=torch.uint8, device=dev)
         torch.cuda.synchronize()
 
     def launch(self, i):
@@ -574,12 +582,47 @@ class DecodeRig:
                                       max_context_len=self.max_ctx, partition_size=self.psize,
                                       workspace=self.workspace)
 
+    def launch_shared(self, i):
+        kc, vc = self.copies[i % len(self.copies)]
+        self.binding.paged_attn_decode_shared_prefix(
+            self.query, kc, vc, self.bt, self.cl, self.b.scale, self.out,
+            prefix_len=self.prefix_len, max_context_len=self.max_ctx,
+            workspace=self.sp_workspace)
+
     def write(self, i):
         kc, vc = self.copies[i % len(self.copies)]
         self.binding.kv_cache_write(self.new_key, self.new_value, self.sm, kc, vc)
 
     def release(self):
         self.copies = []
+
+
+def shared_prefix_timing(rig: "DecodeRig", args, decode_ms: float) -> dict:
+    """The same batch through paged_attn_decode_shared_prefix (the prefix
+    pass on the matrix cores, the suffixes, the merge: three launches per
+    call): back to back from Python, and from a HIP graph of 20 calls, which
+    takes the host out of the loop.  The faster of the two is the call's
+    time; the batch is far too small to be bound by HBM (it moves about
+    26 MB of distinct K/V), so the bound named is latency."""
+    b = rig.b
+    for i in range(SETTLE_LAUNCHES):
+        rig.launch_shared(i)
+    _, sp_ms = time_back_to_back(rig.launch_shared, SETTLE_LAUNCHES, args.steps)
+    sp_graph_ms = time_graph(rig.launch_shared, SETTLE_LAUNCHES)
+    t_ms = min(sp_ms, sp_graph_ms)
+    t = t_ms * 1e-3
+    flops = (rig.prefix_len * b.num_seqs * b.num_q_heads * b.head_dim * 4)
+    return {
+        "entry": "paged_attn_decode_shared_prefix",
+        "prefix_len": rig.prefix_len,
+        "decode_ms": round(sp_ms, 5),
+        "decode_graph_ms": round(sp_graph_ms, 5),
+        "seq_per_s_per_layer": round(b.num_seqs / t, 1),
+        "logical_GBps": round(b.decode_algorithmic_bytes() / t / 1e9, 2),
+        "prefix_TFLOPs": round(flops / t / 1e12, 2),
+        "speedup_vs_paged_attn_decode": round(decode_ms / t_ms, 3),
+        "roofline": {"bound": "latency"},
+    }
 
 
 def other_workload(rig: "DecodeRig", args) -> dict:
@@ -647,6 +690,8 @@ def other_workload(rig: "DecodeRig", args) -> dict:
     if small:
         # a few hundred KB: the launch itself is the cost
         r["roofline"]["bound"] = "launch latency"
+    if rig.prefix_len:
+        r["shared_prefix"] = shared_prefix_timing(rig, args, dec_ms)
     return r
 
 
@@ -830,6 +875,8 @@ def main() -> int:
         },
         "cpu_baseline": None,
     }
+    if rig.prefix_len and not args.fused:
+        result["shared_prefix"] = shared_prefix_timing(rig, args, decode_avg_ms)
     if others:
         result["workloads"] = {o.b.name: other_workload(o, args) for o in others}
     rig.release()

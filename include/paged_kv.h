@@ -179,6 +179,66 @@ PAGED_KV_API int paged_attn_decode_noalloc(
     void *stream);
 
 /*
+ * paged_attn_decode for a batch whose sequences all begin with the same
+ * prefix_len positions held in the same physical blocks: a common prompt,
+ * parallel samples or beams of one prompt, whose blocks the sequences share
+ * ("23.1 vLLM：高吞吐推理框架原理与部署", §二.3).  Same result as
+ * paged_attn_decode up to rounding, computed in three launches on the
+ * caller's stream:
+ *   1. the prefix pass: for each kv head, every sequence's query rows at
+ *      once against the shared positions, read once, as two matrix products
+ *      on the matrix cores (the prefill kernel's tiles), in partitions of
+ *      prefix_partition_size positions;
+ *   2. the decode kernels over each sequence's positions [prefix_len, L), in
+ *      partitions of partition_size;
+ *   3. the merge of the two passes' partial results per (sequence, head).
+ *   prefix_len   positions every sequence shares: a multiple of 16 and of
+ *                block_size, at most max_context_len.  The caller promises
+ *                that every sequence's first prefix_len / block_size table
+ *                entries equal the first row's and that every context_len
+ *                is at least prefix_len.  0 runs paged_attn_decode.
+ *   prefix_partition_size  positions per partition of the prefix pass; 0
+ *                picks one (about one workgroup per compute unit), else a
+ *                positive multiple of 64.
+ *   partition_size  positions per partition after the prefix; 0 picks one
+ *                (enough workgroups to fill the device once), else as for
+ *                paged_attn_decode; PAGED_KV_BALANCED_SPLIT is
+ *                PAGED_KV_ERR_UNSUPPORTED.
+ *   workspace, workspace_bytes  device scratch of at least
+ *                paged_attn_decode_shared_prefix_workspace_bytes(...) bytes
+ *                (never 0 with a prefix), 16-byte aligned; no
+ *                initialisation needed, garbage afterwards.
+ * Every other argument is paged_attn_decode's.  Supported: f16 and bf16
+ * (f32: PAGED_KV_ERR_UNSUPPORTED when prefix_len > 0), head_dim 64, 128,
+ * 256, num_q_heads / num_kv_heads in {1, 2, 4, 8}, block_size a power of two
+ * in [1, 256].
+ * Device-side values: a sequence whose context_len is below prefix_len
+ * (0 included), negative or above max_context_len, or whose first
+ * prefix_len / block_size table entries differ from the first row's, gets
+ * NaN in every output element; a table entry outside [0, num_blocks) among
+ * the shared ones makes every sequence's output NaN, one after the prefix
+ * only its own sequence's.  Nothing out of range is read.
+ */
+PAGED_KV_API int paged_attn_decode_shared_prefix(
+    const void *query, const void *key_cache, const void *value_cache,
+    const int32_t *block_tables, const int32_t *context_lens, float scale, void *out,
+    int num_seqs, int num_q_heads, int num_kv_heads, int head_dim, int block_size,
+    int num_blocks, int max_blocks_per_seq, int max_context_len, int prefix_len,
+    int prefix_partition_size, int partition_size, int dtype, void *workspace,
+    size_t workspace_bytes, void *stream);
+
+/*
+ * Bytes of workspace paged_attn_decode_shared_prefix needs for these
+ * arguments ((size_t)-1 for invalid ones): fp32 partial results (running
+ * max, running sum, head_dim output values) per (sequence, query head) and
+ * partition of either pass.
+ */
+PAGED_KV_API size_t paged_attn_decode_shared_prefix_workspace_bytes(
+    int num_seqs, int num_q_heads, int num_kv_heads, int head_dim, int block_size,
+    int max_blocks_per_seq, int max_context_len, int prefix_len, int prefix_partition_size,
+    int partition_size, int dtype);
+
+/*
  * The context partition size paged_attn_decode uses for these arguments
  * (partition_size 0 = its automatic choice), or a negative paged_kv_status
  * code when the arguments are invalid.  A partition size >= max_context_len

@@ -27,6 +27,8 @@ EXPORTED = (
     "paged_attn_decode",
     "paged_attn_decode_write",
     "paged_attn_decode_noalloc",
+    "paged_attn_decode_shared_prefix",
+    "paged_attn_decode_shared_prefix_workspace_bytes",
     "paged_attn_decode_partition_size",
     "paged_attn_decode_partition_size_for_lengths",
     "paged_attn_decode_workspace_bytes",
@@ -56,6 +58,10 @@ def _load_library(path: str = LIBRARY) -> ctypes.CDLL:
     lib.paged_attn_decode_partition_size_for_lengths.argtypes = [vp] + [ci] * 7
     lib.paged_attn_decode_write.restype = ci
     lib.paged_attn_decode_noalloc.argtypes = [vp, vp, vp, vp, vp, cf, vp] + [ci] * 10 + [vp]
+    lib.paged_attn_decode_shared_prefix.argtypes = ([vp, vp, vp, vp, vp, cf, vp] + [ci] * 12 +
+                                                    [vp, sz, vp])
+    lib.paged_attn_decode_shared_prefix_workspace_bytes.argtypes = [ci] * 11
+    lib.paged_attn_decode_shared_prefix_workspace_bytes.restype = sz
     lib.paged_attn_decode_noalloc.restype = ci
     lib.paged_attn_decode.restype = ci
     lib.paged_attn_decode_partition_size.argtypes = [ci] * 9
@@ -216,6 +222,51 @@ def paged_attn_decode(query: torch.Tensor, key_cache: torch.Tensor, value_cache:
         ctypes.c_float(scale), _dev(out, "out"), S, Hq, Hkv, D, bs, nb, mb, max_context_len,
         partition_size, dt, ws_ptr, ws_bytes, _stream(query.device))
     _check("paged_attn_decode", status)
+    return out
+
+
+def paged_attn_decode_shared_prefix_workspace_bytes(num_seqs, num_q_heads, num_kv_heads,
+                                                    head_dim, block_size, max_blocks_per_seq,
+                                                    max_context_len=0, prefix_len=0,
+                                                    prefix_partition_size=0, partition_size=0,
+                                                    dtype=PAGED_KV_BF16) -> int:
+    r = _lib.paged_attn_decode_shared_prefix_workspace_bytes(
+        num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq,
+        max_context_len, prefix_len, prefix_partition_size, partition_size, dtype)
+    if r == ctypes.c_size_t(-1).value:
+        raise PagedKVError("paged_attn_decode_shared_prefix_workspace_bytes", 2)
+    return r
+
+
+def paged_attn_decode_shared_prefix(query: torch.Tensor, key_cache: torch.Tensor,
+                                    value_cache: torch.Tensor, block_tables: torch.Tensor,
+                                    context_lens: torch.Tensor, scale: float, out: torch.Tensor,
+                                    *, prefix_len: int, max_context_len: int = 0,
+                                    prefix_partition_size: int = 0, partition_size: int = 0,
+                                    workspace: torch.Tensor | None = None) -> torch.Tensor:
+    """paged_attn_decode for a batch whose sequences share their first
+    prefix_len positions in the same physical blocks (see
+    paged_attn_decode_shared_prefix in include/paged_kv.h).  A workspace of
+    the required size is allocated with torch when none is given."""
+    S, Hq, D, nb, bs, Hkv = _decode_checks(query, key_cache, value_cache, block_tables,
+                                           context_lens, out)
+    dt = _dtype_code(query)
+    mb = block_tables.shape[1]
+    need = paged_attn_decode_shared_prefix_workspace_bytes(
+        S, Hq, Hkv, D, bs, mb, max_context_len, prefix_len, prefix_partition_size,
+        partition_size, dt)
+    ws_ptr, ws_bytes = None, 0
+    if need > 0:
+        if workspace is None:
+            workspace = torch.empty(need, dtype=torch.uint8, device=query.device)
+        ws_ptr, ws_bytes = _dev(workspace, "workspace"), workspace.numel() * workspace.element_size()
+    status = _lib.paged_attn_decode_shared_prefix(
+        _dev(query, "query"), _dev(key_cache, "key_cache"), _dev(value_cache, "value_cache"),
+        _dev(block_tables, "block_tables"), _dev(context_lens, "context_lens"),
+        ctypes.c_float(scale), _dev(out, "out"), S, Hq, Hkv, D, bs, nb, mb, max_context_len,
+        prefix_len, prefix_partition_size, partition_size, dt, ws_ptr, ws_bytes,
+        _stream(query.device))
+    _check("paged_attn_decode_shared_prefix", status)
     return out
 
 

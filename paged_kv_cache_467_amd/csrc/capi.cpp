@@ -78,6 +78,65 @@ size_t paged_attn_decode_workspace_bytes(int num_seqs, int num_q_heads, int num_
 }  // extern "C"
 
 namespace pkv {
+namespace {
+
+// Pointer and value checks common to the decode entry points.
+int check_decode_args(const void *query, const void *key_cache, const void *value_cache,
+                      const int32_t *block_tables, const int32_t *context_lens, float scale,
+                      const void *out, int num_blocks) {
+    if (num_blocks < 1 || !isfinite(scale)) return PAGED_KV_ERR_BAD_SHAPE;
+    if (!query || !key_cache || !value_cache || !block_tables || !context_lens || !out)
+        return PAGED_KV_ERR_NULL_POINTER;
+    if (!aligned16(query) || !aligned16(key_cache) || !aligned16(value_cache) ||
+        !aligned16(out) || !aligned4(block_tables) || !aligned4(context_lens))
+        return PAGED_KV_ERR_BAD_SHAPE;
+    return PAGED_KV_OK;
+}
+
+// The decode kernels' parameters for plan pl (no fused write, no shared
+// prefix); ws holds nph entries per partial array.
+DecodeParams decode_params(const void *query, const void *key_cache, const void *value_cache,
+                           const int32_t *block_tables, const int32_t *context_lens, float scale,
+                           void *out, int num_seqs, int num_q_heads, int num_kv_heads,
+                           int head_dim, int block_size, int num_blocks, int max_blocks_per_seq,
+                           const DecodePlan &pl, float *ws, size_t nph, int dtype) {
+    const int e = elem_bytes(dtype);
+    DecodeParams p;
+    p.query = query;
+    p.key_cache = static_cast<const char *>(key_cache);
+    p.value_cache = static_cast<const char *>(value_cache);
+    p.block_tables = block_tables;
+    p.context_lens = context_lens;
+    p.out = out;
+    p.part_max = ws;
+    p.part_sum = ws ? ws + nph : nullptr;
+    p.part_out = ws ? ws + 2 * nph : nullptr;
+    p.scale_log2 = (float)((double)scale * 1.4426950408889634);  // scale * log2(e)
+    p.num_seqs = num_seqs;
+    p.num_q_heads = num_q_heads;
+    p.num_kv_heads = num_kv_heads;
+    p.block_size = block_size;
+    p.block_shift = log2i(block_size);
+    p.num_blocks = num_blocks;
+    p.max_blocks_per_seq = max_blocks_per_seq;
+    p.max_context_len = pl.max_context_len;
+    p.partition_size = pl.partition_size;
+    p.num_partitions = pl.num_partitions;
+    p.num_chunks = pl.num_chunks;
+    p.prefix_len = 0;
+    p.prefix_parts = 0;
+    p.heads_per_group = pl.heads_per_group;
+    p.num_head_groups = num_kv_heads / pl.heads_per_group;
+    p.row_stride_bytes = num_kv_heads * head_dim * e;
+    p.block_stride_bytes = (int64_t)block_size * p.row_stride_bytes;
+    p.new_key = nullptr;
+    p.new_value = nullptr;
+    p.slot_mapping = nullptr;
+    p.num_slots = (int64_t)num_blocks * block_size;
+    return p;
+}
+
+}  // namespace
 
 // The decode, with (new_key non-null) or without the fused KV write; with
 // static_scratch the split's scratch is the library's own buffer
@@ -94,11 +153,9 @@ int run_decode(const void *query, const void *new_key, const void *new_value,
     if (pl.status != PAGED_KV_OK) return pl.status;
     if (num_blocks < 1 || !isfinite(scale)) return PAGED_KV_ERR_BAD_SHAPE;
     if (num_seqs == 0) return PAGED_KV_OK;
-    if (!query || !key_cache || !value_cache || !block_tables || !context_lens || !out)
-        return PAGED_KV_ERR_NULL_POINTER;
-    if (!aligned16(query) || !aligned16(key_cache) || !aligned16(value_cache) ||
-        !aligned16(out) || !aligned4(block_tables) || !aligned4(context_lens))
-        return PAGED_KV_ERR_BAD_SHAPE;
+    const int chk = check_decode_args(query, key_cache, value_cache, block_tables, context_lens,
+                                      scale, out, num_blocks);
+    if (chk != PAGED_KV_OK) return chk;
     if (new_key && (!new_value || !slot_mapping)) return PAGED_KV_ERR_NULL_POINTER;
     if (new_key && pl.num_chunks > 0) return PAGED_KV_ERR_UNSUPPORTED;
     if (new_key && (!aligned16(new_key) || !aligned16(new_value) || !aligned4(slot_mapping)))
@@ -120,38 +177,14 @@ int run_decode(const void *query, const void *new_key, const void *new_value,
     if (need > 0 && (!workspace || workspace_bytes < need || !aligned16(workspace)))
         return PAGED_KV_ERR_WORKSPACE;
 
-    pkv::DecodeParams p;
-    p.query = query;
-    p.key_cache = static_cast<const char *>(key_cache);
-    p.value_cache = static_cast<const char *>(value_cache);
-    p.block_tables = block_tables;
-    p.context_lens = context_lens;
-    p.out = out;
     const size_t nph = pkv::decode_partial_slots(pl, num_seqs, num_q_heads);
-    float *ws = static_cast<float *>(workspace);
-    p.part_max = need ? ws : nullptr;
-    p.part_sum = need ? ws + nph : nullptr;
-    p.part_out = need ? ws + 2 * nph : nullptr;
-    p.scale_log2 = (float)((double)scale * 1.4426950408889634);  // scale * log2(e)
-    p.num_seqs = num_seqs;
-    p.num_q_heads = num_q_heads;
-    p.num_kv_heads = num_kv_heads;
-    p.block_size = block_size;
-    p.block_shift = log2i(block_size);
-    p.num_blocks = num_blocks;
-    p.max_blocks_per_seq = max_blocks_per_seq;
-    p.max_context_len = pl.max_context_len;
-    p.partition_size = pl.partition_size;
-    p.num_partitions = pl.num_partitions;
-    p.num_chunks = pl.num_chunks;
-    p.heads_per_group = pl.heads_per_group;
-    p.num_head_groups = num_kv_heads / pl.heads_per_group;
-    p.row_stride_bytes = num_kv_heads * head_dim * e;
-    p.block_stride_bytes = (int64_t)block_size * p.row_stride_bytes;
+    pkv::DecodeParams p = decode_params(
+        query, key_cache, value_cache, block_tables, context_lens, scale, out, num_seqs,
+        num_q_heads, num_kv_heads, head_dim, block_size, num_blocks, max_blocks_per_seq, pl,
+        need ? static_cast<float *>(workspace) : nullptr, nph, dtype);
     p.new_key = static_cast<const char *>(new_key);
     p.new_value = static_cast<const char *>(new_value);
     p.slot_mapping = slot_mapping;
-    p.num_slots = (int64_t)num_blocks * block_size;
 
     const int group = num_q_heads / num_kv_heads;
     const int kernel = pkv::decode_kernel_choice(dtype, head_dim, group);
@@ -160,9 +193,108 @@ int run_decode(const void *query, const void *new_key, const void *new_value,
     return err == hipSuccess ? PAGED_KV_OK : PAGED_KV_ERR_HIP;
 }
 
+// The shared-prefix decode: the prefix pass (the prefill kernel over the
+// shared blocks, all sequences' query rows at once), then the decode
+// kernels over each sequence's positions after the prefix, then the merge.
+int run_shared_prefix_decode(const void *query, const void *key_cache, const void *value_cache,
+                             const int32_t *block_tables, const int32_t *context_lens,
+                             float scale, void *out, int num_seqs, int num_q_heads,
+                             int num_kv_heads, int head_dim, int block_size, int num_blocks,
+                             int max_blocks_per_seq, int max_context_len, int prefix_len,
+                             int prefix_partition_size, int partition_size, int dtype,
+                             void *workspace, size_t workspace_bytes, void *stream) {
+    const SharedPrefixPlan sp = plan_shared_prefix(
+        num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq,
+        max_context_len, prefix_len, prefix_partition_size, partition_size, dtype);
+    if (sp.status != PAGED_KV_OK) return sp.status;
+    if (sp.prefix_parts == 0)
+        return run_decode(query, nullptr, nullptr, nullptr, key_cache, value_cache, block_tables,
+                          context_lens, scale, out, num_seqs, num_q_heads, num_kv_heads,
+                          head_dim, block_size, num_blocks, max_blocks_per_seq, max_context_len,
+                          partition_size, dtype, workspace, workspace_bytes, stream, false);
+    if (num_blocks < 1 || !isfinite(scale)) return PAGED_KV_ERR_BAD_SHAPE;
+    if (num_seqs == 0) return PAGED_KV_OK;
+    const int chk = check_decode_args(query, key_cache, value_cache, block_tables, context_lens,
+                                      scale, out, num_blocks);
+    if (chk != PAGED_KV_OK) return chk;
+    const int e = elem_bytes(dtype);
+    if ((int64_t)block_size * num_kv_heads * head_dim * e > INT_MAX) return PAGED_KV_ERR_BAD_SHAPE;
+    if (!workspace || workspace_bytes < sp.workspace_bytes || !aligned16(workspace))
+        return PAGED_KV_ERR_WORKSPACE;
+
+    const size_t nph = decode_partial_floats(num_seqs, num_q_heads) * sp.suffix.num_partitions;
+    float *ws = static_cast<float *>(workspace);
+    DecodeParams p = decode_params(query, key_cache, value_cache, block_tables, context_lens,
+                                   scale, out, num_seqs, num_q_heads, num_kv_heads, head_dim,
+                                   block_size, num_blocks, max_blocks_per_seq, sp.suffix, ws,
+                                   nph, dtype);
+    p.prefix_len = sp.prefix_len;
+    p.prefix_parts = sp.prefix_parts;
+
+    PrefillParams q{};
+    q.query = query;
+    q.key_cache = p.key_cache;
+    q.value_cache = p.value_cache;
+    q.block_tables = block_tables;
+    q.context_lens = context_lens;
+    q.score_scale = (float)(fabs((double)scale) * 1.4426950408889634);
+    q.negate_query = scale < 0.0f;
+    q.num_seqs = num_seqs;
+    q.num_q_heads = num_q_heads;
+    q.num_kv_heads = num_kv_heads;
+    q.group = num_q_heads / num_kv_heads;
+    q.block_size = block_size;
+    q.block_shift = p.block_shift;
+    q.num_blocks = num_blocks;
+    q.max_blocks_per_seq = max_blocks_per_seq;
+    q.max_context_len = sp.suffix.max_context_len;
+    q.row_blocks = sp.row_blocks;
+    q.block_stride_bytes = p.block_stride_bytes;
+    q.row_stride_bytes = p.row_stride_bytes;
+    q.prefix_len = sp.prefix_len;
+    q.prefix_part = sp.prefix_part;
+    q.prefix_parts = sp.prefix_parts;
+    q.num_slots = sp.suffix.num_partitions;
+    q.part_max = p.part_max;
+    q.part_sum = p.part_sum;
+    q.part_out = p.part_out;
+
+    const hipStream_t st = static_cast<hipStream_t>(stream);
+    hipError_t err = launch_shared_prefix(q, dtype, head_dim, st);
+    if (err != hipSuccess) return PAGED_KV_ERR_HIP;
+    const int group = num_q_heads / num_kv_heads;
+    err = launch_decode(p, dtype, head_dim, group, decode_kernel_choice(dtype, head_dim, group), st);
+    return err == hipSuccess ? PAGED_KV_OK : PAGED_KV_ERR_HIP;
+}
+
 }  // namespace pkv
 
 extern "C" {
+
+int paged_attn_decode_shared_prefix(const void *query, const void *key_cache,
+                                    const void *value_cache, const int32_t *block_tables,
+                                    const int32_t *context_lens, float scale, void *out,
+                                    int num_seqs, int num_q_heads, int num_kv_heads,
+                                    int head_dim, int block_size, int num_blocks,
+                                    int max_blocks_per_seq, int max_context_len, int prefix_len,
+                                    int prefix_partition_size, int partition_size, int dtype,
+                                    void *workspace, size_t workspace_bytes, void *stream) {
+    return pkv::run_shared_prefix_decode(
+        query, key_cache, value_cache, block_tables, context_lens, scale, out, num_seqs,
+        num_q_heads, num_kv_heads, head_dim, block_size, num_blocks, max_blocks_per_seq,
+        max_context_len, prefix_len, prefix_partition_size, partition_size, dtype, workspace,
+        workspace_bytes, stream);
+}
+
+size_t paged_attn_decode_shared_prefix_workspace_bytes(
+    int num_seqs, int num_q_heads, int num_kv_heads, int head_dim, int block_size,
+    int max_blocks_per_seq, int max_context_len, int prefix_len, int prefix_partition_size,
+    int partition_size, int dtype) {
+    const pkv::SharedPrefixPlan sp = pkv::plan_shared_prefix(
+        num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq,
+        max_context_len, prefix_len, prefix_partition_size, partition_size, dtype);
+    return sp.status == PAGED_KV_OK ? sp.workspace_bytes : (size_t)-1;
+}
 
 int paged_attn_decode(const void *query, const void *key_cache, const void *value_cache,
                       const int32_t *block_tables, const int32_t *context_lens, float scale,

@@ -44,6 +44,12 @@ struct DecodeParams {
     // equal size; partition_size and num_partitions are then unused, and
     // the partials are indexed by chunk (two slots per chunk).
     int num_chunks;
+    // Shared-prefix decode (0 and 0 otherwise): every sequence's positions
+    // [0, prefix_len) were computed by the shared-prefix pass into partial
+    // slots [0, prefix_parts); this launch covers [prefix_len, L) in
+    // partitions of partition_size, partition q in slot prefix_parts + q.
+    int prefix_len;
+    int prefix_parts;
     int heads_per_group;        // kv heads (= waves) per workgroup
     int num_head_groups;        // num_kv_heads / heads_per_group
     int64_t block_stride_bytes; // bs * Hkv * D * elem bytes
@@ -84,6 +90,23 @@ struct DecodePlan {
 DecodePlan plan_decode(int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
                        int block_size, int max_blocks_per_seq, int max_context_len,
                        int partition_size, int dtype);
+// Host-side plan of the shared-prefix decode (decode_plan.cpp).  With
+// prefix_len 0 it is paged_attn_decode's plan (suffix, prefix_parts 0).
+struct SharedPrefixPlan {
+    int status;
+    DecodePlan suffix;  // the per-sequence pass over [prefix_len, L): its
+                        // partition size and heads per group; num_partitions
+                        // counts every partial slot (prefix and suffix)
+    int prefix_len;
+    int prefix_part;    // positions per prefix partition
+    int prefix_parts;   // prefix partitions (0: plain decode)
+    int row_blocks;     // workgroups of (sequence, query head) rows per kv head
+    size_t workspace_bytes;
+};
+SharedPrefixPlan plan_shared_prefix(int num_seqs, int num_q_heads, int num_kv_heads,
+                                    int head_dim, int block_size, int max_blocks_per_seq,
+                                    int max_context_len, int prefix_len,
+                                    int prefix_partition_size, int partition_size, int dtype);
 // Floats per partition in each split-scratch array (rounded for alignment),
 // and the workspace bytes the plan needs (0 without a split).
 int plan_partition_for_lengths(const int32_t *lens, int num_seqs, int num_q_heads,

@@ -7,6 +7,7 @@
 #include <stdint.h>
 
 #include "decode.h"
+#include "prefill.h"
 
 namespace pkv {
 namespace {
@@ -160,6 +161,112 @@ DecodePlan plan_decode(int num_seqs, int num_q_heads, int num_kv_heads, int head
     pl.num_partitions = (int)nparts;
     pl.heads_per_group = hpg;
     return pl;
+}
+
+// The shared-prefix decode.  The prefix pass gets about one workgroup per
+// two compute units, the prefix cut into partitions of whole 64-position
+// tiles: every partition leaves a partial result per (sequence, query
+// head), which the pass writes and the merge reads, so finer partitions
+// cost more than the parallelism they add (on the 64-sequence batch with a
+// 2000-token prefix, 16 x 128 rows x 8 kv heads: 33.3 us per call with
+// 256-position partitions, 35.1 with 128, 38.3 with 512, 40.2 with 64).  The suffix pass (positions after
+// the prefix: a few hundred at most in the workloads this is for) is split
+// for latency rather than bandwidth: its partitions are sized so that its
+// workgroups fill the device once, with no 256-token minimum.
+SharedPrefixPlan plan_shared_prefix(int num_seqs, int num_q_heads, int num_kv_heads,
+                                    int head_dim, int block_size, int max_blocks_per_seq,
+                                    int max_context_len, int prefix_len,
+                                    int prefix_partition_size, int partition_size, int dtype) {
+    SharedPrefixPlan sp{};
+    const DecodePlan base = plan_decode(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
+                                        max_blocks_per_seq, max_context_len, 0, dtype);
+    if (base.status != PAGED_KV_OK) {
+        sp.status = base.status;
+        return sp;
+    }
+    if (partition_size == PAGED_KV_BALANCED_SPLIT) {
+        sp.status = PAGED_KV_ERR_UNSUPPORTED;
+        return sp;
+    }
+    const int max_ctx = base.max_context_len;
+    if (partition_size < 0 || prefix_partition_size < 0 || prefix_len < 0 ||
+        prefix_len % 16 != 0 || prefix_len % block_size != 0 || prefix_len > max_ctx ||
+        prefix_partition_size % 64 != 0) {
+        sp.status = PAGED_KV_ERR_BAD_SHAPE;
+        return sp;
+    }
+    sp.prefix_len = prefix_len;
+    if (prefix_len == 0) {  // nothing shared: the plain decode
+        sp.suffix = plan_decode(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
+                                max_blocks_per_seq, max_context_len, partition_size, dtype);
+        sp.status = sp.suffix.status;
+        if (sp.status == PAGED_KV_OK)
+            sp.workspace_bytes = decode_workspace_bytes(sp.suffix, num_seqs, num_q_heads, head_dim);
+        return sp;
+    }
+    if (dtype == PAGED_KV_F32) {
+        sp.status = PAGED_KV_ERR_UNSUPPORTED;
+        return sp;
+    }
+    const int group = num_q_heads / num_kv_heads;
+    const int hpg = base.heads_per_group;
+    const int64_t rows = (int64_t)num_seqs * group;
+    const int64_t rpb = prefill_rows_per_block(head_dim);
+    const int64_t row_blocks = (rows + rpb - 1) / rpb;
+    const DeviceOccupancy occ = decode_occupancy(dtype, head_dim, group, block_size, hpg);
+    const int64_t cus = occ.compute_units > 0 ? occ.compute_units : kFallbackComputeUnits;
+    int64_t pp;
+    if (prefix_partition_size > 0) {
+        pp = prefix_partition_size;
+    } else {
+        const int64_t units = row_blocks * num_kv_heads;
+        int64_t parts = units > 0 ? cus / (2 * units) : 1;
+        if (parts < 1) parts = 1;
+        pp = round_up((prefix_len + parts - 1) / parts, 64);
+    }
+    const int64_t prefix_parts = (prefix_len + pp - 1) / pp;
+
+    // the suffix pass
+    const int suffix_max = max_ctx - prefix_len;
+    int64_t P = 16, suffix_parts = 0;
+    if (suffix_max > 0) {
+        const int align = block_size > 16 ? block_size : 16;
+        const int64_t max_part = (int64_t)kBtLds * block_size;
+        if (partition_size > 0) {
+            if (partition_size % 16 != 0 || partition_size % block_size != 0 ||
+                partition_size > max_part) {
+                sp.status = PAGED_KV_ERR_BAD_SHAPE;
+                return sp;
+            }
+            P = partition_size;
+        } else {
+            const int64_t units = (int64_t)num_seqs * (num_kv_heads / hpg);
+            const int64_t target = target_workgroups(dtype, head_dim, group, block_size, hpg);
+            int64_t parts = units > 0 ? target / units : 1;
+            if (parts < 1) parts = 1;
+            P = round_up((suffix_max + parts - 1) / parts, align);
+            if (P > kMaxAutoTokens) P = round_up(kMaxAutoTokens, align);
+            if (P > max_part) P = max_part;
+        }
+        suffix_parts = (suffix_max + P - 1) / P;
+    }
+    const int64_t slots = prefix_parts + suffix_parts;
+    if (row_blocks * num_kv_heads * prefix_parts > INT_MAX ||
+        (int64_t)num_seqs * num_kv_heads * suffix_parts > INT_MAX || slots > INT_MAX ||
+        (int64_t)num_seqs * num_q_heads > INT_MAX) {
+        sp.status = PAGED_KV_ERR_BAD_SHAPE;
+        return sp;
+    }
+    sp.status = PAGED_KV_OK;
+    sp.suffix = base;
+    sp.suffix.partition_size = (int)P;
+    sp.suffix.num_partitions = (int)slots;
+    sp.prefix_part = (int)pp;
+    sp.prefix_parts = (int)prefix_parts;
+    sp.row_blocks = (int)row_blocks;
+    sp.workspace_bytes = decode_partial_floats(num_seqs, num_q_heads) * (size_t)slots *
+                         (2 + (size_t)head_dim) * sizeof(float);
+    return sp;
 }
 
 size_t decode_partial_floats(int num_seqs, int num_q_heads) {

@@ -82,13 +82,15 @@ __device__ inline WorkItem work_item(const DecodeParams &p) {
     const int id = blockIdx.x;
     const int hg = id % p.num_head_groups;
     const int rest = id / p.num_head_groups;
-    w.part = rest % p.num_partitions;
-    w.s = rest / p.num_partitions;
+    const int parts = p.num_partitions - p.prefix_parts;  // partitions in the grid
+    const int q = rest % parts;
+    w.part = p.prefix_parts + q;
+    w.s = rest / parts;
     w.kvh0 = hg * p.heads_per_group;
     w.kvh = w.kvh0 + (int)(threadIdx.x / kWave);
     w.context_len = p.context_lens[w.s];
     w.bad_len = w.context_len < 0 || w.context_len > p.max_context_len;
-    w.tok_begin = w.part * p.partition_size;
+    w.tok_begin = p.prefix_len + q * p.partition_size;
     const int end = w.tok_begin + p.partition_size;
     w.tok_end = end < w.context_len ? end : w.context_len;
     w.final = p.num_partitions == 1;
@@ -870,7 +872,9 @@ __global__ __launch_bounds__(kReduceThreads) void decode_reduce_kernel(DecodePar
     const int L = p.context_lens[s];
     float mq = lane < np ? pm[lane] : -INFINITY;  // lane q holds partition q < 64
     float lq = lane < np ? ps[lane] : 0.0f;
-    if (L < 0 || L > p.max_context_len) {
+    // (a context shorter than the shared prefix breaks the shared-prefix
+    // decode's contract)
+    if (L < 0 || L > p.max_context_len || L < p.prefix_len) {
 #pragma unroll
         for (int e = 0; e < EL; ++e) T::store_nan(p.out, obase + e);
         return;
@@ -880,7 +884,8 @@ __global__ __launch_bounds__(kReduceThreads) void decode_reduce_kernel(DecodePar
         for (int e = 0; e < EL; ++e) T::store(p.out, obase + e, 0.0f);
         return;
     }
-    const int nparts = (L + p.partition_size - 1) / p.partition_size;
+    const int nparts =
+        p.prefix_parts + (L - p.prefix_len + p.partition_size - 1) / p.partition_size;
     float v[R][EL];
 #pragma unroll
     for (int u = 0; u < R; ++u) {
@@ -1086,7 +1091,9 @@ hipError_t launch_main(const DecodeParams &p, int kernel, hipStream_t stream) {
     const unsigned grid =
         p.num_chunks > 0
             ? (unsigned)((int64_t)p.num_chunks * p.num_head_groups)
-            : (unsigned)((int64_t)p.num_seqs * p.num_head_groups * p.num_partitions);
+            : (unsigned)((int64_t)p.num_seqs * p.num_head_groups *
+                         (p.num_partitions - p.prefix_parts));
+    if (grid == 0) return hipSuccess;  // a shared prefix that is the whole context
     const unsigned threads = (unsigned)(p.heads_per_group * kWave);
     // 16-bit types with grouped queries take the MFMA kernel, everything else
     // the VALU kernel (decode_kernel_choice); only those pairs are built.
@@ -1120,7 +1127,7 @@ hipError_t launch_typed(const DecodeParams &p, int kernel, hipStream_t stream) {
         hipLaunchKernelGGL((decode_reduce_balanced_kernel<T, D>),
                            dim3(p.num_seqs * p.num_q_heads), dim3(kReduceThreads), 0, stream, p);
         e = hipGetLastError();
-    } else if (p.num_partitions > 1) {
+    } else if (p.num_partitions > 1 || p.prefix_parts > 0) {
         hipLaunchKernelGGL((decode_reduce_kernel<T, D>), dim3(p.num_seqs * p.num_q_heads),
                            dim3(kReduceThreads), 0, stream, p);
         e = hipGetLastError();

@@ -107,7 +107,9 @@ __device__ inline uint64_t lds_read_tr16(const uint16_t *p) {
     return __builtin_bit_cast(uint64_t, v);
 }
 
-template <class T, int D, bool BT>
+// SHARED: the shared-prefix pass of the shared-prefix decode (see
+// launch_shared_prefix) instead of the prefill.
+template <class T, int D, bool BT, bool SHARED>
 __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(PrefillParams p) {
     static_assert(T::kBytes == 2, "MFMA path is for 16-bit element types");
     constexpr int MB = blocks_per_wave(D);
@@ -133,56 +135,112 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(PrefillParams 
     __shared__ __attribute__((aligned(16))) uint16_t v_lds[2][TT * VSTR];
 
     // ---- work item
-    const PrefillWork wk = prefill_work(p, blockIdx.x);
-    const int s = wk.s, kvh = wk.kvh, rb = wk.rb;
     const int G = p.group;
-    const int qs0 = p.query_start[s];
-    const int qs1 = p.query_start[s + 1];
-    const int L = p.context_lens[s];
-    if (qs0 < 0 || qs1 > p.total_q || qs1 < qs0) return;  // rows not identifiable: nothing written
-    const int q_len = qs1 - qs0;
-    const int nrows = (q_len < p.max_query_len ? q_len : p.max_query_len) * G;
-    const int row0 = rb * RPB;
-    if (row0 >= nrows) return;
-    const bool bad_len = L < q_len || L > p.max_context_len;
-
     const int wave = threadIdx.x / kWave;
     const int lane = threadIdx.x % kWave;
     const int lrow = lane & 15;   // this lane's row within each 16-row block
     const int kg = lane >> 4;     // k-group / token group
-    const int w_first = row0 + wave * 16 * MB;
+    int kvh, row0, nrows;
+    int tb = 0;     // the workgroup reads positions tb .. pmax (tb a multiple of 16)
+    int pmax;
+    int wave_pmax;  // the last position any row of this wave sees
+    int wave_pmin;  // tiles ending at or below this position need no mask
+    int part = 0;   // SHARED: the prefix partition
+    const int32_t *bt_row;
     bool row_ok[MB];
-    int pos[MB];        // the row's position; -1 for a row past the end (sees nothing)
+    int pos[MB];        // the row's last visible position; -1 for a row past the end
     int64_t obase[MB];  // element offset of the row's output / query
+    if constexpr (SHARED) {
+        // rows (sequence r / G, query head kvh * G + r % G) of the decode
+        // batch, all seeing the partition's positions of the shared prefix
+        const SharedPrefixWork sw = shared_prefix_work(p, blockIdx.x);
+        kvh = sw.kvh;
+        part = sw.part;
+        nrows = p.num_seqs * G;
+        row0 = sw.rb * RPB;
+        if (row0 >= nrows) return;
+        tb = part * p.prefix_part;
+        pmax = (tb + p.prefix_part < p.prefix_len ? tb + p.prefix_part : p.prefix_len) - 1;
+        bt_row = p.block_tables;  // the first sequence's blocks: the shared ones
+        const int w_first = row0 + wave * 16 * MB;
 #pragma unroll
-    for (int mb = 0; mb < MB; ++mb) {
-        const int row = w_first + 16 * mb + lrow;
-        row_ok[mb] = row < nrows;
-        const int tok = row / G;
-        pos[mb] = row_ok[mb] ? L - q_len + tok : -1;
-        obase[mb] = (((int64_t)qs0 + tok) * p.num_q_heads + kvh * G + row % G) * D;
-    }
-
-    if (bad_len) {
+        for (int mb = 0; mb < MB; ++mb) {
+            const int row = w_first + 16 * mb + lrow;
+            row_ok[mb] = row < nrows;
+            pos[mb] = row_ok[mb] ? pmax : -1;
+            obase[mb] = ((int64_t)(row / G) * p.num_q_heads + kvh * G + row % G) * D;
+        }
+        wave_pmax = pmax;
+        wave_pmin = w_first + 16 * MB <= nrows ? pmax : -1;
+    } else {
+        const PrefillWork wk = prefill_work(p, blockIdx.x);
+        const int s = wk.s;
+        kvh = wk.kvh;
+        const int qs0 = p.query_start[s];
+        const int qs1 = p.query_start[s + 1];
+        const int L = p.context_lens[s];
+        if (qs0 < 0 || qs1 > p.total_q || qs1 < qs0) return;  // rows not identifiable: nothing written
+        const int q_len = qs1 - qs0;
+        nrows = (q_len < p.max_query_len ? q_len : p.max_query_len) * G;
+        row0 = wk.rb * RPB;
+        if (row0 >= nrows) return;
+        const bool bad_len = L < q_len || L > p.max_context_len;
+        const int w_first = row0 + wave * 16 * MB;
 #pragma unroll
-        for (int mb = 0; mb < MB; ++mb)
-            if (row_ok[mb])
-                for (int d = kg * 4; d < D; d += 16)
-                    *reinterpret_cast<uint64_t *>(static_cast<char *>(p.out) +
-                                                  (obase[mb] + d) * 2) =
-                        ((uint64_t)T::kNanPair << 32) | T::kNanPair;
-        return;
-    }
+        for (int mb = 0; mb < MB; ++mb) {
+            const int row = w_first + 16 * mb + lrow;
+            row_ok[mb] = row < nrows;
+            const int tok = row / G;
+            pos[mb] = row_ok[mb] ? L - q_len + tok : -1;
+            obase[mb] = (((int64_t)qs0 + tok) * p.num_q_heads + kvh * G + row % G) * D;
+        }
 
-    // positions the workgroup's rows can see: 0 .. pmax (the last valid row's)
-    const int last_row = (row0 + RPB < nrows ? row0 + RPB : nrows) - 1;
-    const int pmax = L - q_len + last_row / G;
-    const int ntiles = pmax / TT + 1;
-    const int w_last = (w_first + 16 * MB < nrows ? w_first + 16 * MB : nrows) - 1;
+        if (bad_len) {
+#pragma unroll
+            for (int mb = 0; mb < MB; ++mb)
+                if (row_ok[mb])
+                    for (int d = kg * 4; d < D; d += 16)
+                        *reinterpret_cast<uint64_t *>(static_cast<char *>(p.out) +
+                                                      (obase[mb] + d) * 2) =
+                            ((uint64_t)T::kNanPair << 32) | T::kNanPair;
+            return;
+        }
+
+        // positions the workgroup's rows can see: 0 .. pmax (the last valid row's)
+        const int last_row = (row0 + RPB < nrows ? row0 + RPB : nrows) - 1;
+        pmax = L - q_len + last_row / G;
+        const int w_last = (w_first + 16 * MB < nrows ? w_first + 16 * MB : nrows) - 1;
+        wave_pmax = L - q_len + w_last / G;
+        wave_pmin = w_first + 16 * MB <= nrows ? L - q_len + w_first / G : -1;
+        bt_row = p.block_tables + (int64_t)s * p.max_blocks_per_seq;
+    }
+    const int w_first = row0 + wave * 16 * MB;
     const bool wave_active = w_first < nrows;
-    const int wave_pmax = L - q_len + w_last / G;
-    // tiles ending at or below this position need no causal mask
-    const int wave_pmin = w_first + 16 * MB <= nrows ? L - q_len + w_first / G : -1;
+    const int ntiles = (pmax - tb) / TT + 1;
+
+    // Shared prefix: a sequence whose table does not hold the first row's
+    // blocks over this partition (the caller's promise broken) gets NaN
+    // partial results.  The flags are cleared here; the table entries of
+    // the first kCheckAhead pairs (sequence, block) of each thread are
+    // loaded with the first tile's, compared once the first barrier has
+    // passed, and read back after the tile loop's barriers.
+    __shared__ int seq_bad[SHARED ? RPB : 1];
+    constexpr int kCheckAhead = SHARED ? 4 : 0;
+    int s_first = 0, npairs = 0, nb = 1, b_first = 0;
+    int chk_mine[kCheckAhead > 0 ? kCheckAhead : 1], chk_ref[kCheckAhead > 0 ? kCheckAhead : 1];
+    if constexpr (SHARED) {
+        s_first = row0 / G;
+        const int ns = ((row0 + RPB < nrows ? row0 + RPB : nrows) - 1) / G - s_first + 1;
+        b_first = tb >> p.block_shift;
+        nb = (pmax >> p.block_shift) - b_first + 1;
+        npairs = ns * nb;
+        for (int i = threadIdx.x; i < ns; i += kPrefillThreads) seq_bad[i] = 0;
+    }
+    auto check_pair = [&](int i) {  // the pair's entry and the first row's
+        const int si = i / nb, b = b_first + i % nb;
+        return int2{p.block_tables[(int64_t)(s_first + si) * p.max_blocks_per_seq + b],
+                    p.block_tables[b]};
+    };
 
     // B operand of the score MFMA: Q^T, lane = row, 16-byte chunk kg + 4 * ks
     u32x4 qb[MB][KS];
@@ -204,7 +262,6 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(PrefillParams 
     // With block_size >= 16 each 16-token quarter of a tile lies in one
     // block: its id is uniform (a scalar register) and each thread adds a
     // fixed offset; the quarter a chunk falls in is the same for a whole wave.
-    const int32_t *bt_row = p.block_tables + (int64_t)s * p.max_blocks_per_seq;
     const int64_t head_off = (int64_t)kvh * D * 2;
     int bad = 0;
     u32x4 kreg[CPT], vreg[CPT];
@@ -235,13 +292,13 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(PrefillParams 
     auto fetch_ids = [&](int tile) {
 #pragma unroll
         for (int h = 0; h < NQ; ++h) {
-            const int th = min(tile * TT + 16 * h, pmax);
+            const int th = min(tb + tile * TT + 16 * h, pmax);
             next_id[h] = __builtin_amdgcn_raw_buffer_load_b32(bt_rsrc, (th >> p.block_shift) * 4,
                                                               0, 0);
         }
     };
     auto load_tile = [&](int tile) {
-        const int t0 = tile * TT;
+        const int t0 = tb + tile * TT;
         int64_t half_base[NQ] = {};
         if constexpr (BT) {
 #pragma unroll
@@ -284,7 +341,7 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(PrefillParams 
         if constexpr (BT) fetch_ids(tile + 1);  // past the last tile: pmax's block again
     };
     auto store_tile = [&](int buf, int tile) {
-        const int t0 = tile * TT;
+        const int t0 = tb + tile * TT;
 #pragma unroll
         for (int c = 0; c < CPT; ++c) {
             const int idx = threadIdx.x + c * kPrefillThreads;
@@ -317,12 +374,35 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(PrefillParams 
     const int vt_elem = (4 * kg + lrow / 4) * VSTR + 4 * (lrow % 4);
 
     if constexpr (BT) fetch_ids(0);
+    if constexpr (SHARED) {
+#pragma unroll
+        for (int k = 0; k < kCheckAhead; ++k) {
+            const int i = threadIdx.x + k * kPrefillThreads;
+            if (i < npairs) {
+                const int2 e = check_pair(i);
+                chk_mine[k] = e.x;
+                chk_ref[k] = e.y;
+            }
+        }
+    }
     load_tile(0);
     store_tile(0, 0);
     __syncthreads();
+    if constexpr (SHARED) {  // the flags were cleared before the barrier
+#pragma unroll
+        for (int k = 0; k < kCheckAhead; ++k) {
+            const int i = threadIdx.x + k * kPrefillThreads;
+            if (i < npairs && chk_mine[k] != chk_ref[k]) seq_bad[i / nb] = 1;
+        }
+        for (int i = threadIdx.x + kCheckAhead * kPrefillThreads; i < npairs;
+             i += kPrefillThreads) {
+            const int2 e = check_pair(i);
+            if (e.x != e.y) seq_bad[i / nb] = 1;
+        }
+    }
     for (int tile = 0; tile < ntiles; ++tile) {
         const int buf = tile & 1;
-        const int t0 = tile * TT;
+        const int t0 = tb + tile * TT;
         bool prefetched = false;
         if (wave_active && t0 <= wave_pmax) {
             const uint16_t *kt = k_lds[buf];
@@ -452,6 +532,39 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(PrefillParams 
     for (int mb = 0; mb < MB; ++mb) {
         lsum[mb] = row_reduce4<false>(lsum[mb]);
     }
+    if constexpr (SHARED) {
+        // the partition's partial result per row: running max (log2
+        // domain), sum and unnormalised output, fp32; NaN sum and output
+        // for a row that read an invalid block id or broke the sharing.
+        // (Non-temporal stores: 4% faster here, where the partials of 16
+        // or more partitions per row are written at once at the end.)
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) {
+            if (!row_ok[mb]) continue;
+            const bool nan =
+                bad || seq_bad[(w_first + 16 * mb + lrow) / G - s_first] != 0;
+            const int64_t slot = (obase[mb] / D) * p.num_slots + part;
+            float *po = p.part_out + slot * D;
+#pragma unroll
+            for (int b = 0; b < DB; ++b) {
+                // (through scalars: clang reads element 0 for a bit cast of
+                // an indexed vector element)
+                const float o0 = acc[mb][b][0], o1 = acc[mb][b][1], o2 = acc[mb][b][2],
+                            o3 = acc[mb][b][3];
+                const u32x4 c = nan ? u32x4{0x7FC00000u, 0x7FC00000u, 0x7FC00000u, 0x7FC00000u}
+                                    : u32x4{__builtin_bit_cast(uint32_t, o0),
+                                            __builtin_bit_cast(uint32_t, o1),
+                                            __builtin_bit_cast(uint32_t, o2),
+                                            __builtin_bit_cast(uint32_t, o3)};
+                store16_stream(po + b * 16 + 4 * kg, c);
+            }
+            if (kg == 0) {
+                __builtin_nontemporal_store(nan ? 0.0f : m[mb], p.part_max + slot);
+                __builtin_nontemporal_store(nan ? NAN : lsum[mb], p.part_sum + slot);
+            }
+        }
+        return;
+    }
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) {
         if (!row_ok[mb]) continue;
@@ -477,11 +590,33 @@ template <class T, int D>
 void launch_d(const PrefillParams &p, hipStream_t stream) {
     const unsigned grid = (unsigned)((int64_t)p.num_seqs * p.num_kv_heads * p.row_blocks);
     if (p.block_size >= 16)
-        hipLaunchKernelGGL((prefill_kernel<T, D, true>), dim3(grid), dim3(kPrefillThreads), 0,
-                           stream, p);
+        hipLaunchKernelGGL((prefill_kernel<T, D, true, false>), dim3(grid),
+                           dim3(kPrefillThreads), 0, stream, p);
     else
-        hipLaunchKernelGGL((prefill_kernel<T, D, false>), dim3(grid), dim3(kPrefillThreads), 0,
-                           stream, p);
+        hipLaunchKernelGGL((prefill_kernel<T, D, false, false>), dim3(grid),
+                           dim3(kPrefillThreads), 0, stream, p);
+}
+
+template <class T, int D>
+void launch_shared_d(const PrefillParams &p, hipStream_t stream) {
+    const unsigned grid = (unsigned)((int64_t)p.num_kv_heads * p.row_blocks * p.prefix_parts);
+    if (p.block_size >= 16)
+        hipLaunchKernelGGL((prefill_kernel<T, D, true, true>), dim3(grid),
+                           dim3(kPrefillThreads), 0, stream, p);
+    else
+        hipLaunchKernelGGL((prefill_kernel<T, D, false, true>), dim3(grid),
+                           dim3(kPrefillThreads), 0, stream, p);
+}
+
+template <class T>
+hipError_t launch_shared_t(const PrefillParams &p, int head_dim, hipStream_t stream) {
+    switch (head_dim) {
+        case 64: launch_shared_d<T, 64>(p, stream); break;
+        case 128: launch_shared_d<T, 128>(p, stream); break;
+        case 256: launch_shared_d<T, 256>(p, stream); break;
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
 }
 
 template <class T>
@@ -503,6 +638,15 @@ hipError_t launch_prefill(const PrefillParams &p, int dtype, int head_dim, hipSt
     switch (dtype) {
         case 1: return launch_t<F16>(p, head_dim, stream);
         case 2: return launch_t<BF16>(p, head_dim, stream);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+hipError_t launch_shared_prefix(const PrefillParams &p, int dtype, int head_dim,
+                                hipStream_t stream) {
+    switch (dtype) {
+        case 1: return launch_shared_t<F16>(p, head_dim, stream);
+        case 2: return launch_shared_t<BF16>(p, head_dim, stream);
         default: return hipErrorInvalidValue;
     }
 }

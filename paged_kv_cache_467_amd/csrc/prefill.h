@@ -31,6 +31,19 @@ struct PrefillParams {
     int row_blocks;               // ceil(max_query_len * group / rows per workgroup)
     int64_t block_stride_bytes;   // bs * Hkv * D * elem bytes
     int row_stride_bytes;         // Hkv * D * elem bytes
+    // Shared-prefix pass only (launch_shared_prefix): the rows are the
+    // decode batch's (sequence, query head) pairs, query [num_seqs, Hq, D];
+    // positions [0, prefix_len) are read through block_tables' first row,
+    // in prefix_parts partitions of prefix_part positions; partition q of
+    // row (s, h) leaves its running max, sum and unnormalised output in slot
+    // (s * Hq + h) * num_slots + q of the decode's split scratch.
+    int prefix_len;
+    int prefix_part;
+    int prefix_parts;
+    int num_slots;
+    float *part_max;
+    float *part_sum;
+    float *part_out;
 };
 
 // Query rows (new token, query head) one prefill workgroup covers.
@@ -40,5 +53,9 @@ int prefill_f32_rows_per_block();
 hipError_t launch_prefill(const PrefillParams &p, int dtype, int head_dim, hipStream_t stream);
 // ... and the fp32 kernel.
 hipError_t launch_prefill_f32(const PrefillParams &p, int head_dim, hipStream_t stream);
+// The shared-prefix pass of the shared-prefix decode (16-bit types), on the
+// prefill kernel: grid num_kv_heads * row_blocks * prefix_parts.
+hipError_t launch_shared_prefix(const PrefillParams &p, int dtype, int head_dim,
+                                hipStream_t stream);
 
 }  // namespace pkv

@@ -64,6 +64,25 @@ struct PrefillWork {
     int s, kvh, rb;  // sequence, kv head, block of query rows
 };
 
+// Workgroup id -> (unit, row block) for n_units units of nrb row blocks
+// each: the row blocks of one unit read the same K/V, so they get ids 8
+// apart -- the same XCD, dispatched together, sharing that XCD's L2 --
+// while consecutive units go to consecutive XCDs (the units left over
+// after the last whole round of 8 are numbered plainly).  rb counts from
+// 0 in dispatch order.
+__device__ inline void xcd_grouped(int id, int n_units, int nrb, int &unit, int &rb) {
+    const int full = n_units / kXcds * kXcds;  // units placed XCD by XCD
+    if (id < full * nrb) {
+        const int k = id / kXcds;
+        rb = k % nrb;
+        unit = (k / nrb) * kXcds + id % kXcds;
+    } else {
+        const int r = id - full * nrb;
+        unit = full + r / nrb;
+        rb = r % nrb;
+    }
+}
+
 // Workgroups go to the 8 XCDs round-robin.  All row blocks of one
 // (sequence, kv head) unit read the same K/V, so they get ids 8 apart: the
 // same XCD, dispatched together, sharing that XCD's L2.  A unit's last row
@@ -73,23 +92,30 @@ struct PrefillWork {
 // first (seq_by_length_rank).
 __device__ inline PrefillWork prefill_work(const PrefillParams &p, int id) {
     const int nrb = p.row_blocks;
-    const int n_units = p.num_seqs * p.num_kv_heads;
-    const int full = n_units / kXcds * kXcds;  // units placed XCD by XCD
-    int unit, rb;
-    if (id < full * nrb) {
-        const int k = id / kXcds;
-        rb = nrb - 1 - k % nrb;
-        unit = (k / nrb) * kXcds + id % kXcds;
-    } else {
-        const int r = id - full * nrb;
-        unit = full + r / nrb;
-        rb = nrb - 1 - r % nrb;
-    }
+    int unit, k;
+    xcd_grouped(id, p.num_seqs * p.num_kv_heads, nrb, unit, k);
     PrefillWork w;
     w.kvh = unit % p.num_kv_heads;
     w.s = p.num_seqs <= kSortedDispatchMaxSeqs
               ? seq_by_length_rank(p.context_lens, p.num_seqs, unit / p.num_kv_heads)
               : unit / p.num_kv_heads;
+    w.rb = nrb - 1 - k;
+    return w;
+}
+
+// The shared-prefix pass: a unit is (prefix partition, kv head), its row
+// blocks are blocks of (sequence, query head) rows; every workgroup has the
+// same work, so they go in plain order within the XCD grouping (with 8 kv
+// heads, XCD x serves kv head x of every partition).
+struct SharedPrefixWork {
+    int kvh, rb, part;  // kv head, block of rows, prefix partition
+};
+__device__ inline SharedPrefixWork shared_prefix_work(const PrefillParams &p, int id) {
+    int unit, rb;
+    xcd_grouped(id, p.prefix_parts * p.num_kv_heads, p.row_blocks, unit, rb);
+    SharedPrefixWork w;
+    w.kvh = unit % p.num_kv_heads;
+    w.part = unit / p.num_kv_heads;
     w.rb = rb;
     return w;
 }

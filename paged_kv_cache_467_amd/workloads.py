@@ -332,6 +332,42 @@ def make_custom(seed: int, *, dtype="f32", num_seqs=2, num_q_heads=2, num_kv_hea
                      poison=poison, seed=seed, keys_identical=keys_identical)
 
 
+def make_shared_prefix(seed: int, *, dtype="bf16", num_q_heads=8, num_kv_heads=2,
+                       head_dim=128, block_size=16, prefix_len=64, suffix_lens=(0, 5),
+                       max_blocks_per_seq=None, poison=False, scale=None) -> DecodeBatch:
+    """A batch whose sequences all begin with the same prefix_len positions
+    in the same physical blocks (the first prefix_len / block_size of a
+    random permutation of the pool), each followed by suffix_lens[s]
+    positions in blocks of its own; like the shared-prefix workload, at any
+    shape."""
+    assert prefix_len % block_size == 0
+    rng = np.random.default_rng(seed)
+    S = len(suffix_lens)
+    bs = block_size
+    suffix = np.asarray(suffix_lens, dtype=np.int64)
+    pb = prefix_len // bs
+    priv = (suffix + bs - 1) // bs
+    need = pb + int(priv.max()) if S else pb
+    mb = max_blocks_per_seq if max_blocks_per_seq is not None else max(1, need)
+    assert mb >= need
+    total = pb + int(priv.sum())
+    pool = total + 3
+    perm = rng.permutation(pool)
+    free_block = int(perm[total])
+    tables = np.full((S, mb), free_block, dtype=np.int32)
+    k = pb
+    for s in range(S):
+        tables[s, :pb] = perm[:pb]
+        tables[s, pb:pb + priv[s]] = perm[k:k + priv[s]]
+        k += int(priv[s])
+    if scale is None:
+        scale = 1.0 / math.sqrt(head_dim)
+    return _assemble(f"shared{seed}", dtype, rng, S=S, Hq=num_q_heads, Hkv=num_kv_heads,
+                     D=head_dim, bs=bs, lens=prefix_len + suffix, tables=tables,
+                     num_blocks=pool, max_blocks=mb, scale=scale, poison=poison, seed=seed,
+                     meta={"prefix_blocks": pb})
+
+
 @dataclass
 class PrefillBatch:
     """Multi-token (chunked-prefill) inputs: a paged pool whose sequences

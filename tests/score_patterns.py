@@ -59,6 +59,9 @@ def with_scores(b, case):
     # about offset * head_dim * scale (natural-log units)
     per_tile = {"rise": 14.0, "steep": 40.0}.get(case)  # score step per 16-token tile
     kc = W.bits_to_f32(b.key_cache, dt)
+    # a pool cell that several sequences share (a common prefix, at the same
+    # position in each) takes its offset once, from the first of them
+    done = np.zeros(kc.shape[:2], dtype=bool)
     for s in range(b.num_seqs):
         L = int(b.context_lens[s])
         j = np.arange(L)
@@ -72,7 +75,9 @@ def with_scores(b, case):
             off = np.where(j >= first_of_last, 80.0 / (D * b.scale), 0.0)
         blk = b.block_tables[s, j // b.block_size]
         slot = j % b.block_size
-        kc[blk, slot] += off[:, None, None].astype(np.float32)
+        new = ~done[blk, slot]
+        kc[blk[new], slot[new]] += off[new][:, None, None].astype(np.float32)
+        done[blk, slot] = True
     b.key_cache = W.f32_to_bits(kc, dt)
     return b
 

@@ -43,6 +43,10 @@ def lib():
     lib.paged_attn_decode_write.argtypes = [vp] * 8 + [cf, vp] + [ci] * 10 + [vp, sz, vp]
     lib.paged_attn_decode_partition_size_for_lengths.argtypes = [vp] + [ci] * 7
     lib.paged_attn_decode_noalloc.argtypes = [vp, vp, vp, vp, vp, cf, vp] + [ci] * 10 + [vp]
+    lib.paged_attn_decode_shared_prefix.argtypes = ([vp, vp, vp, vp, vp, cf, vp] + [ci] * 12 +
+                                                    [vp, sz, vp])
+    lib.paged_attn_decode_shared_prefix_workspace_bytes.argtypes = [ci] * 11
+    lib.paged_attn_decode_shared_prefix_workspace_bytes.restype = sz
     lib.paged_kv_prefix_hash.argtypes = [vp] * 3 + [ci] * 4 + [ctypes.c_uint64, vp, vp]
     lib.paged_kv_prefix_insert.argtypes = [vp, vp, ci, vp, vp, ci, vp, vp]
     lib.paged_kv_prefix_match.argtypes = [vp, vp, ci, ci, vp, vp, ci, vp, vp, vp]
@@ -56,7 +60,8 @@ def test_header_declares_the_entry_points():
         "paged_kv_copy_blocks", "paged_attn_prefill", "paged_kv_swap_out", "paged_kv_swap_in",
         "paged_kv_prefix_hash", "paged_kv_prefix_insert", "paged_kv_prefix_match",
         "paged_attn_decode_write", "paged_attn_decode_partition_size_for_lengths",
-        "paged_attn_decode_noalloc"])
+        "paged_attn_decode_noalloc", "paged_attn_decode_shared_prefix",
+        "paged_attn_decode_shared_prefix_workspace_bytes"])
 
 
 def test_library_exports_only_the_entry_points():
@@ -160,6 +165,60 @@ def test_decode_noalloc_scratch_limit_is_the_header_size(lib):
 def test_decode_noalloc_zero_sequences_is_a_noop(lib):
     assert decode_noalloc(lib, q=None, kc=None, vc=None, bt=None, cl=None, out=None,
                           num_seqs=0) == OK
+
+
+def shared(lib, q=P, kc=P, vc=P, bt=P, cl=P, out=P, scale=0.1, ws=None, ws_bytes=0,
+           prefix_len=64, prefix_partition_size=0, **kw):
+    a = dict(SHAPE, **kw)
+    return lib.paged_attn_decode_shared_prefix(
+        q, kc, vc, bt, cl, scale, out, a["num_seqs"], a["num_q_heads"], a["num_kv_heads"],
+        a["head_dim"], a["block_size"], a["num_blocks"], a["max_blocks_per_seq"],
+        a["max_context_len"], prefix_len, prefix_partition_size, a["partition_size"],
+        a["dtype"], ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), NULLPTR), (dict(out=None), NULLPTR), (dict(cl=None), NULLPTR),
+    (dict(prefix_len=8), BAD_SHAPE), (dict(prefix_len=24), BAD_SHAPE),
+    (dict(prefix_len=-16), BAD_SHAPE), (dict(prefix_len=144), BAD_SHAPE),   # > 8 blocks * 16
+    (dict(block_size=32, prefix_len=48), BAD_SHAPE),         # not whole blocks
+    (dict(prefix_partition_size=32), BAD_SHAPE), (dict(prefix_partition_size=-64), BAD_SHAPE),
+    (dict(partition_size=24), BAD_SHAPE), (dict(partition_size=1), UNSUPPORTED),  # balanced
+    (dict(dtype=0), UNSUPPORTED),                            # f32 with a prefix
+    (dict(head_dim=96), UNSUPPORTED), (dict(num_q_heads=6, num_kv_heads=4), BAD_SHAPE),
+    (dict(num_blocks=0), BAD_SHAPE), (dict(scale=float("nan")), BAD_SHAPE),
+    (dict(q=P + 8), BAD_SHAPE), (dict(bt=P + 2), BAD_SHAPE),
+    (dict(), WORKSPACE),                                     # a prefix always needs one
+    (dict(ws=P + 4, ws_bytes=1 << 20), WORKSPACE),           # misaligned
+    (dict(prefix_len=0, partition_size=16), WORKSPACE),      # 0: paged_attn_decode's checks
+])
+def test_shared_prefix_rejects(lib, kw, status):
+    """Host checks of the shared-prefix decode, before any device call."""
+    assert shared(lib, **kw) == status
+
+
+def test_shared_prefix_zero_sequences_is_a_noop(lib):
+    assert shared(lib, q=None, kc=None, vc=None, bt=None, cl=None, out=None, num_seqs=0) == OK
+
+
+def test_shared_prefix_workspace(lib):
+    """Partial slots per (sequence, query head): the prefix partitions plus
+    the partitions after the prefix; prefix 0 is paged_attn_decode's size."""
+    wb = lib.paged_attn_decode_shared_prefix_workspace_bytes
+    per = 130 * 4                     # (head_dim + 2) floats per slot
+    # a 2000-token prefix in 4 partitions of 512; up to 189 more in 3 of 64
+    assert wb(64, 32, 8, 128, 16, 141, 2189, 2000, 512, 64, 2) == 64 * 32 * 7 * per
+    # the prefix is the whole context: its 2 partitions only
+    assert wb(4, 8, 2, 128, 16, 8, 128, 128, 64, 0, 2) == 4 * 8 * 2 * per
+    assert wb(64, 32, 8, 128, 16, 141, 2189, 0, 0, 0, 2) == \
+        lib.paged_attn_decode_workspace_bytes(64, 32, 8, 128, 16, 141, 2189, 0, 2)
+    # the automatic prefix partitions are whole 64-position tiles
+    auto = wb(64, 32, 8, 128, 16, 141, 2189, 2000, 0, 64, 2) // (64 * 32 * per) - 3
+    assert 1 <= auto <= 2000 // 64 + 1
+    bad = ctypes.c_size_t(-1).value
+    assert wb(64, 32, 8, 128, 16, 141, 2189, 2008, 0, 0, 2) == bad      # not a multiple of 16
+    assert wb(64, 32, 8, 128, 16, 141, 2189, 2000, 0, 0, 0) == bad      # f32
+    assert wb(64, 32, 8, 128, 16, 141, 1999, 2000, 0, 0, 2) == bad      # beyond the context
 
 
 def test_decode_zero_sequences_is_a_noop(lib):
