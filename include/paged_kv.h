@@ -208,8 +208,8 @@ PAGED_KV_API int paged_attn_decode_noalloc(
  *                paged_attn_decode_shared_prefix_workspace_bytes(...) bytes
  *                (never 0 with a prefix), 16-byte aligned; no
  *                initialisation needed, garbage afterwards.
- * Every other argument is paged_attn_decode's.  Supported: f16 and bf16
- * (f32: PAGED_KV_ERR_UNSUPPORTED when prefix_len > 0), head_dim 64, 128,
+ * Every other argument is paged_attn_decode's.  Supported: f32, f16, bf16
+ * (the prefix pass on fp32 matrix instructions for f32), head_dim 64, 128,
  * 256, num_q_heads / num_kv_heads in {1, 2, 4, 8}, block_size a power of two
  * in [1, 256].
  * Device-side values: a sequence whose context_len is below prefix_len

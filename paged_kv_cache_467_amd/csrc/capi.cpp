@@ -260,7 +260,8 @@ int run_shared_prefix_decode(const void *query, const void *key_cache, const voi
     q.part_out = p.part_out;
 
     const hipStream_t st = static_cast<hipStream_t>(stream);
-    hipError_t err = launch_shared_prefix(q, dtype, head_dim, st);
+    hipError_t err = dtype == PAGED_KV_F32 ? launch_shared_prefix_f32(q, head_dim, st)
+                                           : launch_shared_prefix(q, dtype, head_dim, st);
     if (err != hipSuccess) return PAGED_KV_ERR_HIP;
     const int group = num_q_heads / num_kv_heads;
     err = launch_decode(p, dtype, head_dim, group, decode_kernel_choice(dtype, head_dim, group), st);

@@ -204,14 +204,11 @@ SharedPrefixPlan plan_shared_prefix(int num_seqs, int num_q_heads, int num_kv_he
             sp.workspace_bytes = decode_workspace_bytes(sp.suffix, num_seqs, num_q_heads, head_dim);
         return sp;
     }
-    if (dtype == PAGED_KV_F32) {
-        sp.status = PAGED_KV_ERR_UNSUPPORTED;
-        return sp;
-    }
     const int group = num_q_heads / num_kv_heads;
     const int hpg = base.heads_per_group;
     const int64_t rows = (int64_t)num_seqs * group;
-    const int64_t rpb = prefill_rows_per_block(head_dim);
+    const int64_t rpb = dtype == PAGED_KV_F32 ? prefill_f32_rows_per_block()
+                                              : prefill_rows_per_block(head_dim);
     const int64_t row_blocks = (rows + rpb - 1) / rpb;
     const DeviceOccupancy occ = decode_occupancy(dtype, head_dim, group, block_size, hpg);
     const int64_t cus = occ.compute_units > 0 ? occ.compute_units : kFallbackComputeUnits;

@@ -47,7 +47,9 @@ __device__ inline f32x4 mfma_k4(float a, float b, const f32x4 &c) {
     return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
 
-template <int D, bool BT>
+// SHARED: the shared-prefix pass of the shared-prefix decode (see
+// launch_shared_prefix_f32) instead of the prefill.
+template <int D, bool BT, bool SHARED>
 __global__ __launch_bounds__(kF32Threads) void prefill_f32_kernel(PrefillParams p) {
     constexpr int TT = f32_tile_tokens(D);  // positions per tile
     constexpr int NQ = TT / 16;             // 16-token quarters of a tile
@@ -64,46 +66,98 @@ __global__ __launch_bounds__(kF32Threads) void prefill_f32_kernel(PrefillParams 
     __shared__ __attribute__((aligned(16))) float v_lds[2][TT * STR];
 
     // ---- work item
-    const PrefillWork wk = prefill_work(p, blockIdx.x);
-    const int s = wk.s, kvh = wk.kvh;
     const int G = p.group;
-    const int qs0 = p.query_start[s];
-    const int qs1 = p.query_start[s + 1];
-    const int L = p.context_lens[s];
-    if (qs0 < 0 || qs1 > p.total_q || qs1 < qs0) return;  // rows not identifiable: nothing written
-    const int q_len = qs1 - qs0;
-    const int nrows = (q_len < p.max_query_len ? q_len : p.max_query_len) * G;
-    const int row0 = wk.rb * kF32Rows;
-    if (row0 >= nrows) return;
-    const bool bad_len = L < q_len || L > p.max_context_len;
-
     const int wave = threadIdx.x / kWave;
     const int lane = threadIdx.x % kWave;
     const int lrow = lane & 15;  // this lane's row within the wave's 16-row block
     const int g = lane >> 4;     // lane group: d span of the scores, token group of a quarter
+    int kvh, row0, nrows;
+    int tb = 0;     // the workgroup reads positions tb .. pmax (tb a multiple of 16)
+    int pmax, wave_pmax, wave_pmin, pos;
+    int part = 0;   // SHARED: the prefix partition
+    int64_t obase;  // element offset of the row's output / query
+    const int32_t *bt_row;
+    if constexpr (SHARED) {
+        // rows (sequence r / G, query head kvh * G + r % G) of the decode
+        // batch, all seeing the partition's positions of the shared prefix
+        const SharedPrefixWork sw = shared_prefix_work(p, blockIdx.x);
+        kvh = sw.kvh;
+        part = sw.part;
+        nrows = p.num_seqs * G;
+        row0 = sw.rb * kF32Rows;
+        if (row0 >= nrows) return;
+        tb = part * p.prefix_part;
+        pmax = (tb + p.prefix_part < p.prefix_len ? tb + p.prefix_part : p.prefix_len) - 1;
+        bt_row = p.block_tables;  // the first sequence's blocks: the shared ones
+        const int row = row0 + wave * 16 + lrow;
+        pos = row < nrows ? pmax : -1;
+        obase = ((int64_t)(row / G) * p.num_q_heads + kvh * G + row % G) * D;
+        wave_pmax = pmax;
+        wave_pmin = row0 + wave * 16 + 16 <= nrows ? pmax : -1;
+    } else {
+        const PrefillWork wk = prefill_work(p, blockIdx.x);
+        const int s = wk.s;
+        kvh = wk.kvh;
+        const int qs0 = p.query_start[s];
+        const int qs1 = p.query_start[s + 1];
+        const int L = p.context_lens[s];
+        if (qs0 < 0 || qs1 > p.total_q || qs1 < qs0) return;  // rows not identifiable: nothing written
+        const int q_len = qs1 - qs0;
+        nrows = (q_len < p.max_query_len ? q_len : p.max_query_len) * G;
+        row0 = wk.rb * kF32Rows;
+        if (row0 >= nrows) return;
+        const bool bad_len = L < q_len || L > p.max_context_len;
+        const int w_first = row0 + wave * 16;
+        const int row = w_first + lrow;
+        pos = row < nrows ? L - q_len + row / G : -1;  // -1: a row past the end sees nothing
+        obase = (((int64_t)qs0 + row / G) * p.num_q_heads + kvh * G + row % G) * D;
+
+        if (bad_len) {
+            if (row < nrows)
+                for (int d = g * 4; d < D; d += 16)
+                    *reinterpret_cast<u32x4 *>(static_cast<char *>(p.out) + (obase + d) * 4) =
+                        u32x4{F32::kNanPair, F32::kNanPair, F32::kNanPair, F32::kNanPair};
+            return;
+        }
+
+        // positions the workgroup's rows can see: 0 .. pmax (the last valid row's)
+        const int last_row = (row0 + kF32Rows < nrows ? row0 + kF32Rows : nrows) - 1;
+        pmax = L - q_len + last_row / G;
+        const int w_last = (w_first + 16 < nrows ? w_first + 16 : nrows) - 1;
+        wave_pmax = L - q_len + w_last / G;
+        // tiles ending at or below this position need no causal mask
+        wave_pmin = w_first + 16 <= nrows ? L - q_len + w_first / G : -1;
+        bt_row = p.block_tables + (int64_t)s * p.max_blocks_per_seq;
+    }
     const int w_first = row0 + wave * 16;
     const int row = w_first + lrow;
     const bool row_ok = row < nrows;
-    const int pos = row_ok ? L - q_len + row / G : -1;  // -1: a row past the end sees nothing
-    const int64_t obase = (((int64_t)qs0 + row / G) * p.num_q_heads + kvh * G + row % G) * D;
-
-    if (bad_len) {
-        if (row_ok)
-            for (int d = g * 4; d < D; d += 16)
-                *reinterpret_cast<u32x4 *>(static_cast<char *>(p.out) + (obase + d) * 4) =
-                    u32x4{F32::kNanPair, F32::kNanPair, F32::kNanPair, F32::kNanPair};
-        return;
-    }
-
-    // positions the workgroup's rows can see: 0 .. pmax (the last valid row's)
-    const int last_row = (row0 + kF32Rows < nrows ? row0 + kF32Rows : nrows) - 1;
-    const int pmax = L - q_len + last_row / G;
-    const int ntiles = pmax / TT + 1;
-    const int w_last = (w_first + 16 < nrows ? w_first + 16 : nrows) - 1;
     const bool wave_active = w_first < nrows;
-    const int wave_pmax = L - q_len + w_last / G;
-    // tiles ending at or below this position need no causal mask
-    const int wave_pmin = w_first + 16 <= nrows ? L - q_len + w_first / G : -1;
+    const int ntiles = (pmax - tb) / TT + 1;
+
+    // Shared prefix: a sequence whose table does not hold the first row's
+    // blocks over this partition (the caller's promise broken) gets NaN
+    // partial results.  The flags are cleared here, the first kCheckAhead
+    // pairs (sequence, block) of each thread loaded with the first tile,
+    // compared once the first barrier has passed and read back after the
+    // tile loop's barriers.
+    __shared__ int seq_bad[SHARED ? kF32Rows : 1];
+    constexpr int kCheckAhead = SHARED ? 4 : 0;
+    int s_first = 0, npairs = 0, nb = 1, b_first = 0;
+    int chk_mine[kCheckAhead > 0 ? kCheckAhead : 1], chk_ref[kCheckAhead > 0 ? kCheckAhead : 1];
+    if constexpr (SHARED) {
+        s_first = row0 / G;
+        const int ns = ((row0 + kF32Rows < nrows ? row0 + kF32Rows : nrows) - 1) / G - s_first + 1;
+        b_first = tb >> p.block_shift;
+        nb = (pmax >> p.block_shift) - b_first + 1;
+        npairs = ns * nb;
+        for (int i = threadIdx.x; i < ns; i += kF32Threads) seq_bad[i] = 0;
+    }
+    auto check_pair = [&](int i) {  // the pair's entry and the first row's
+        const int si = i / nb, b = b_first + i % nb;
+        return int2{p.block_tables[(int64_t)(s_first + si) * p.max_blocks_per_seq + b],
+                    p.block_tables[b]};
+    };
 
     // B operand of the score product: Q^T, this lane's row, d = g KJ + j
     float qv[KJ];
@@ -123,7 +177,6 @@ __global__ __launch_bounds__(kF32Threads) void prefill_f32_kernel(PrefillParams 
     // cooperative tile loader: thread -> (token of the tile, 16-byte chunk);
     // with block_size >= 16 the quarter of chunk c is the same for every
     // thread and lies in one block (a scalar block id per quarter)
-    const int32_t *bt_row = p.block_tables + (int64_t)s * p.max_blocks_per_seq;
     const int64_t head_off = (int64_t)kvh * D * 4;
     int bad = 0;
     u32x4 kreg[CPT], vreg[CPT];
@@ -140,7 +193,7 @@ __global__ __launch_bounds__(kF32Threads) void prefill_f32_kernel(PrefillParams 
     auto fetch_ids = [&](int tile) {  // one tile ahead; past pmax: pmax's block
 #pragma unroll
         for (int h = 0; h < NQ; ++h) {
-            const int th = min(tile * TT + 16 * h, pmax);
+            const int th = min(tb + tile * TT + 16 * h, pmax);
             next_id[h] = __builtin_amdgcn_raw_buffer_load_b32(bt_rsrc, (th >> p.block_shift) * 4,
                                                               0, 0);
         }
@@ -148,7 +201,7 @@ __global__ __launch_bounds__(kF32Threads) void prefill_f32_kernel(PrefillParams 
     // every chunk is loaded from an in-bounds cell; tokens past pmax are
     // zeroed when the last tile is stored
     auto load_tile = [&](int tile) {
-        const int t0 = tile * TT;
+        const int t0 = tb + tile * TT;
         int64_t quarter_base[NQ] = {};
         if constexpr (BT) {
 #pragma unroll
@@ -186,7 +239,7 @@ __global__ __launch_bounds__(kF32Threads) void prefill_f32_kernel(PrefillParams 
         if constexpr (BT) fetch_ids(tile + 1);
     };
     auto store_tile = [&](int buf, int tile) {
-        const int t0 = tile * TT;
+        const int t0 = tb + tile * TT;
         const bool last = t0 + TT - 1 > pmax;
 #pragma unroll
         for (int c = 0; c < CPT; ++c) {
@@ -206,12 +259,34 @@ __global__ __launch_bounds__(kF32Threads) void prefill_f32_kernel(PrefillParams 
     for (int b = 0; b < DB; ++b) acc[b] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 
     if constexpr (BT) fetch_ids(0);
+    if constexpr (SHARED) {
+#pragma unroll
+        for (int k = 0; k < kCheckAhead; ++k) {
+            const int i = threadIdx.x + k * kF32Threads;
+            if (i < npairs) {
+                const int2 e = check_pair(i);
+                chk_mine[k] = e.x;
+                chk_ref[k] = e.y;
+            }
+        }
+    }
     load_tile(0);
     store_tile(0, 0);
     __syncthreads();
+    if constexpr (SHARED) {  // the flags were cleared before the barrier
+#pragma unroll
+        for (int k = 0; k < kCheckAhead; ++k) {
+            const int i = threadIdx.x + k * kF32Threads;
+            if (i < npairs && chk_mine[k] != chk_ref[k]) seq_bad[i / nb] = 1;
+        }
+        for (int i = threadIdx.x + kCheckAhead * kF32Threads; i < npairs; i += kF32Threads) {
+            const int2 e = check_pair(i);
+            if (e.x != e.y) seq_bad[i / nb] = 1;
+        }
+    }
     for (int tile = 0; tile < ntiles; ++tile) {
         const int buf = tile & 1;
-        const int t0 = tile * TT;
+        const int t0 = tb + tile * TT;
         if (tile + 1 < ntiles) load_tile(tile + 1);
         if (wave_active && t0 <= wave_pmax) {
             const float *kt = k_lds[buf];
@@ -284,6 +359,31 @@ __global__ __launch_bounds__(kF32Threads) void prefill_f32_kernel(PrefillParams 
     // the accumulator holds d = 16 b + 4 g + r of row lrow
     lsum = row_reduce4<false>(lsum);
     if (!row_ok) return;
+    if constexpr (SHARED) {
+        // the partition's partial result for this row: running max (log2
+        // domain), sum and unnormalised output, fp32 (NaN sum and output for
+        // an invalid block id or a sequence that broke the sharing)
+        const bool nan = bad || seq_bad[row / G - s_first] != 0;
+        const int64_t slot = (obase / D) * p.num_slots + part;
+        float *po = p.part_out + slot * D;
+#pragma unroll
+        for (int b = 0; b < DB; ++b) {
+            // (through scalars: clang reads element 0 for a bit cast of an
+            // indexed vector element)
+            const float o0 = acc[b][0], o1 = acc[b][1], o2 = acc[b][2], o3 = acc[b][3];
+            const u32x4 c = nan ? u32x4{0x7FC00000u, 0x7FC00000u, 0x7FC00000u, 0x7FC00000u}
+                                : u32x4{__builtin_bit_cast(uint32_t, o0),
+                                        __builtin_bit_cast(uint32_t, o1),
+                                        __builtin_bit_cast(uint32_t, o2),
+                                        __builtin_bit_cast(uint32_t, o3)};
+            store16_stream(po + b * 16 + 4 * g, c);
+        }
+        if (g == 0) {
+            __builtin_nontemporal_store(nan ? 0.0f : m, p.part_max + slot);
+            __builtin_nontemporal_store(nan ? NAN : lsum, p.part_sum + slot);
+        }
+        return;
+    }
     const float inv = lsum > 0.0f ? 1.0f / lsum : 0.0f;
     char *op = static_cast<char *>(p.out) + obase * 4;
 #pragma unroll
@@ -303,11 +403,22 @@ template <int D>
 void launch_d(const PrefillParams &p, hipStream_t stream) {
     const unsigned grid = (unsigned)((int64_t)p.num_seqs * p.num_kv_heads * p.row_blocks);
     if (p.block_size >= 16)
-        hipLaunchKernelGGL((prefill_f32_kernel<D, true>), dim3(grid), dim3(kF32Threads), 0,
+        hipLaunchKernelGGL((prefill_f32_kernel<D, true, false>), dim3(grid), dim3(kF32Threads),
+                           0, stream, p);
+    else
+        hipLaunchKernelGGL((prefill_f32_kernel<D, false, false>), dim3(grid), dim3(kF32Threads),
+                           0, stream, p);
+}
+
+template <int D>
+void launch_shared_d(const PrefillParams &p, hipStream_t stream) {
+    const unsigned grid = (unsigned)((int64_t)p.num_kv_heads * p.row_blocks * p.prefix_parts);
+    if (p.block_size >= 16)
+        hipLaunchKernelGGL((prefill_f32_kernel<D, true, true>), dim3(grid), dim3(kF32Threads), 0,
                            stream, p);
     else
-        hipLaunchKernelGGL((prefill_f32_kernel<D, false>), dim3(grid), dim3(kF32Threads), 0,
-                           stream, p);
+        hipLaunchKernelGGL((prefill_f32_kernel<D, false, true>), dim3(grid), dim3(kF32Threads),
+                           0, stream, p);
 }
 
 }  // namespace
@@ -319,6 +430,16 @@ hipError_t launch_prefill_f32(const PrefillParams &p, int head_dim, hipStream_t 
         case 64: launch_d<64>(p, stream); break;
         case 128: launch_d<128>(p, stream); break;
         case 256: launch_d<256>(p, stream); break;
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_shared_prefix_f32(const PrefillParams &p, int head_dim, hipStream_t stream) {
+    switch (head_dim) {
+        case 64: launch_shared_d<64>(p, stream); break;
+        case 128: launch_shared_d<128>(p, stream); break;
+        case 256: launch_shared_d<256>(p, stream); break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();

@@ -53,9 +53,11 @@ int prefill_f32_rows_per_block();
 hipError_t launch_prefill(const PrefillParams &p, int dtype, int head_dim, hipStream_t stream);
 // ... and the fp32 kernel.
 hipError_t launch_prefill_f32(const PrefillParams &p, int head_dim, hipStream_t stream);
-// The shared-prefix pass of the shared-prefix decode (16-bit types), on the
-// prefill kernel: grid num_kv_heads * row_blocks * prefix_parts.
+// The shared-prefix pass of the shared-prefix decode on the prefill
+// kernels: grid num_kv_heads * row_blocks * prefix_parts (rows per block:
+// prefill_rows_per_block, for fp32 prefill_f32_rows_per_block).
 hipError_t launch_shared_prefix(const PrefillParams &p, int dtype, int head_dim,
                                 hipStream_t stream);
+hipError_t launch_shared_prefix_f32(const PrefillParams &p, int head_dim, hipStream_t stream);
 
 }  // namespace pkv

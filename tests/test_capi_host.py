@@ -184,7 +184,7 @@ def shared(lib, q=P, kc=P, vc=P, bt=P, cl=P, out=P, scale=0.1, ws=None, ws_bytes
     (dict(block_size=32, prefix_len=48), BAD_SHAPE),         # not whole blocks
     (dict(prefix_partition_size=32), BAD_SHAPE), (dict(prefix_partition_size=-64), BAD_SHAPE),
     (dict(partition_size=24), BAD_SHAPE), (dict(partition_size=1), UNSUPPORTED),  # balanced
-    (dict(dtype=0), UNSUPPORTED),                            # f32 with a prefix
+    (dict(dtype=5), UNSUPPORTED),
     (dict(head_dim=96), UNSUPPORTED), (dict(num_q_heads=6, num_kv_heads=4), BAD_SHAPE),
     (dict(num_blocks=0), BAD_SHAPE), (dict(scale=float("nan")), BAD_SHAPE),
     (dict(q=P + 8), BAD_SHAPE), (dict(bt=P + 2), BAD_SHAPE),
@@ -217,7 +217,7 @@ def test_shared_prefix_workspace(lib):
     assert 1 <= auto <= 2000 // 64 + 1
     bad = ctypes.c_size_t(-1).value
     assert wb(64, 32, 8, 128, 16, 141, 2189, 2008, 0, 0, 2) == bad      # not a multiple of 16
-    assert wb(64, 32, 8, 128, 16, 141, 2189, 2000, 0, 0, 0) == bad      # f32
+    assert wb(64, 32, 8, 128, 16, 141, 2189, 2000, 512, 64, 0) == 64 * 32 * 7 * per  # f32
     assert wb(64, 32, 8, 128, 16, 141, 1999, 2000, 0, 0, 2) == bad      # beyond the context
 
 

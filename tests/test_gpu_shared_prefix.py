@@ -6,7 +6,7 @@ give paged_attn_decode's result, within its tolerance (tests/parity.py).
 The batches share their first prefix_len positions in the same physical
 blocks, as parallel samples of one prompt do ("23.1 vLLM：高吞吐推理框架原理
 与部署", §二.3).  Covered: the shared-prefix workload, every head size,
-group size and 16-bit dtype over block sizes 1..256, several row blocks
+group size and dtype over block sizes 1..256, several row blocks
 and prefix partitions with ragged ends, a prefix that is the whole context,
 the caller's promises broken (NaN for exactly the sequences concerned),
 extreme scores, block relabelling and poisoned memory (bit-identical), and
@@ -96,7 +96,7 @@ def test_shared_prefix_zero_is_plain_decode(B):
 
 
 # ----------------------------------------------------------------- shapes
-SHAPES = [(dt, G, D, bs) for dt in ("f16", "bf16") for G in (1, 2, 4, 8)
+SHAPES = [(dt, G, D, bs) for dt in ("f32", "f16", "bf16") for G in (1, 2, 4, 8)
           for D in (64, 128, 256) for bs in (8, 16, 32)]
 
 
@@ -105,9 +105,9 @@ def test_shared_prefix_shapes(B, dtype, G, D, bs):
     """Five sequences after a 96-position prefix, suffixes of 0, 1, 15, 17
     and 40 positions, poisoned memory; automatic partitions, then prefix
     partitions of 64 (two, the second ragged) with suffix partitions of the
-    block size."""
+    block size.  fp32 runs the prefix pass on the fp32 prefill kernel."""
     Hkv = 2
-    b = W.make_shared_prefix(7000 + 100 * G + D + bs + (0 if dtype == "f16" else 7),
+    b = W.make_shared_prefix(7000 + 100 * G + D + bs + {"f16": 0, "bf16": 7, "f32": 13}[dtype],
                              dtype=dtype, num_q_heads=G * Hkv, num_kv_heads=Hkv, head_dim=D,
                              block_size=bs, prefix_len=96, suffix_lens=(0, 1, 15, 17, 40),
                              poison=True)
@@ -127,6 +127,10 @@ def test_shared_prefix_shapes(B, dtype, G, D, bs):
     ("f16", 4, 256, 16, 64, tuple(range(3, 36))),     # 132 rows of 64 per workgroup
     ("bf16", 2, 128, 16, 4096, (0, 7, 900)),          # a long prefix, many partitions
     ("f16", 1, 128, 32, 1024, (1,) * 12),             # MHA, many sequences of one row each
+    ("f32", 4, 128, 1, 48, (0, 3, 20)),
+    ("f32", 8, 64, 16, 160, tuple(range(0, 40))),     # 320 rows of 64 per workgroup
+    ("f32", 2, 256, 128, 256, (0, 1, 300)),
+    ("f32", 1, 128, 16, 2048, (0, 7, 900)),
 ])
 def test_shared_prefix_edge_shapes(B, dtype, G, D, bs, prefix, suffixes):
     Hkv = 2
@@ -187,7 +191,8 @@ def test_shared_prefix_invalid_shared_block(B):
 
 # ------------------------------------------------------------ extremes
 @pytest.mark.parametrize("case", EXTREME_CASES)
-@pytest.mark.parametrize("dtype,G", [("bf16", 4), ("f16", 1), ("f16", 8)])
+@pytest.mark.parametrize("dtype,G", [("bf16", 4), ("f16", 1), ("f16", 8), ("f32", 1),
+                                     ("f32", 4)])
 def test_shared_prefix_extremes(B, case, dtype, G):
     """Scales 0, negative and +-3; scores rising on every tile (by more than
     2^8, or 2^40); the first or the last tile dominating by over 2^100 --
@@ -262,7 +267,7 @@ def test_shared_prefix_random_batches(B, seed):
     size, 1..24 sequences, a prefix of 16..1200 positions and suffixes of
     0..400."""
     rng = np.random.default_rng(8200 + seed)
-    dtype = ("f16", "bf16")[rng.integers(2)]
+    dtype = ("f32", "f16", "bf16")[rng.integers(3)]
     D = int(rng.choice([64, 128, 256]))
     G = int(rng.choice([1, 2, 4, 8]))
     Hkv = int(rng.choice([1, 2, 4, 8]))
