@@ -203,7 +203,7 @@ PAGED_KV_API int paged_attn_decode_noalloc(
  *   partition_size  positions per partition after the prefix; 0 picks one
  *                (enough workgroups to fill the device once), else as for
  *                paged_attn_decode; PAGED_KV_BALANCED_SPLIT is
- *                PAGED_KV_ERR_UNSUPPORTED.
+ *                PAGED_KV_ERR_UNSUPPORTED when prefix_len > 0.
  *   workspace, workspace_bytes  device scratch of at least
  *                paged_attn_decode_shared_prefix_workspace_bytes(...) bytes
  *                (never 0 with a prefix), 16-byte aligned; no

@@ -184,10 +184,6 @@ SharedPrefixPlan plan_shared_prefix(int num_seqs, int num_q_heads, int num_kv_he
         sp.status = base.status;
         return sp;
     }
-    if (partition_size == PAGED_KV_BALANCED_SPLIT) {
-        sp.status = PAGED_KV_ERR_UNSUPPORTED;
-        return sp;
-    }
     const int max_ctx = base.max_context_len;
     if (partition_size < 0 || prefix_partition_size < 0 || prefix_len < 0 ||
         prefix_len % 16 != 0 || prefix_len % block_size != 0 || prefix_len > max_ctx ||
@@ -195,8 +191,12 @@ SharedPrefixPlan plan_shared_prefix(int num_seqs, int num_q_heads, int num_kv_he
         sp.status = PAGED_KV_ERR_BAD_SHAPE;
         return sp;
     }
+    if (partition_size == PAGED_KV_BALANCED_SPLIT && prefix_len > 0) {
+        sp.status = PAGED_KV_ERR_UNSUPPORTED;
+        return sp;
+    }
     sp.prefix_len = prefix_len;
-    if (prefix_len == 0) {  // nothing shared: the plain decode
+    if (prefix_len == 0) {  // nothing shared: the plain decode, balanced split included
         sp.suffix = plan_decode(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
                                 max_blocks_per_seq, max_context_len, partition_size, dtype);
         sp.status = sp.suffix.status;

@@ -191,6 +191,7 @@ def shared(lib, q=P, kc=P, vc=P, bt=P, cl=P, out=P, scale=0.1, ws=None, ws_bytes
     (dict(), WORKSPACE),                                     # a prefix always needs one
     (dict(ws=P + 4, ws_bytes=1 << 20), WORKSPACE),           # misaligned
     (dict(prefix_len=0, partition_size=16), WORKSPACE),      # 0: paged_attn_decode's checks
+    (dict(prefix_len=0, partition_size=1), WORKSPACE),       # ... its balanced split included
 ])
 def test_shared_prefix_rejects(lib, kw, status):
     """Host checks of the shared-prefix decode, before any device call."""
@@ -212,6 +213,8 @@ def test_shared_prefix_workspace(lib):
     assert wb(4, 8, 2, 128, 16, 8, 128, 128, 64, 0, 2) == 4 * 8 * 2 * per
     assert wb(64, 32, 8, 128, 16, 141, 2189, 0, 0, 0, 2) == \
         lib.paged_attn_decode_workspace_bytes(64, 32, 8, 128, 16, 141, 2189, 0, 2)
+    assert wb(64, 32, 8, 128, 16, 141, 2189, 0, 0, 1, 2) == \
+        lib.paged_attn_decode_workspace_bytes(64, 32, 8, 128, 16, 141, 2189, 1, 2) > 0
     # the automatic prefix partitions are whole 64-position tiles
     auto = wb(64, 32, 8, 128, 16, 141, 2189, 2000, 0, 64, 2) // (64 * 32 * per) - 3
     assert 1 <= auto <= 2000 // 64 + 1

@@ -83,14 +83,16 @@ def test_shared_prefix_workload(B, pps, ps):
     check(b, got, f"shared_prefix_bf16 pps={pps} ps={ps}", workload_ref())
 
 
-def test_shared_prefix_zero_is_plain_decode(B):
-    """prefix_len 0 runs paged_attn_decode: the same bits."""
+@pytest.mark.parametrize("ps", [0, 1])
+def test_shared_prefix_zero_is_plain_decode(B, ps):
+    """prefix_len 0 runs paged_attn_decode, its balanced split (1) included:
+    the same bits."""
     b = workload()
-    _say("shared prefix 0 == paged_attn_decode")
-    got = run_shared(B, b, 0)
+    _say(f"shared prefix 0 == paged_attn_decode, partition_size {ps}")
+    got = run_shared(B, b, 0, partition_size=ps)
     d = tensors.device_batch(b, DEV)
     B.paged_attn_decode(d.query, d.key_cache, d.value_cache, d.block_tables, d.context_lens,
-                        b.scale, d.out, max_context_len=b.max_context_len)
+                        b.scale, d.out, max_context_len=b.max_context_len, partition_size=ps)
     torch.cuda.synchronize()
     assert np.array_equal(got, tensors.to_host_bits(d.out))
 
