@@ -582,6 +582,13 @@ class DecodeRig:
                                       max_context_len=self.max_ctx, partition_size=self.psize,
                                       workspace=self.workspace)
 
+    def launch_fused(self, i):
+        kc, vc = self.copies[i % len(self.copies)]
+        self.binding.paged_attn_decode_write(
+            self.query, self.new_key, self.new_value, self.sm, kc, vc, self.bt, self.cl,
+            self.b.scale, self.out, max_context_len=self.max_ctx, partition_size=self.psize,
+            workspace=self.workspace)
+
     def launch_shared(self, i):
         kc, vc = self.copies[i % len(self.copies)]
         self.binding.paged_attn_decode_shared_prefix(
@@ -808,6 +815,23 @@ def main() -> int:
     decode_ms = [e[0].elapsed_time(e[1]) for e in events]
     write_ms = None if args.fused else [e[2].elapsed_time(e[0]) for e in events]
 
+    # The same step as one paged_attn_decode_write launch (same work, same
+    # bits), timed the same way.
+    fused_step = None
+    if not args.fused:
+        for i in range(args.warmup):
+            rig.launch_fused(i)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(steps):
+            rig.launch_fused(args.warmup + i)
+        torch.cuda.synchronize()
+        fused_ms = (time.perf_counter() - t0) * 1e3 / steps
+        fused_step = {"entry": "paged_attn_decode_write", "ms_per_step": round(fused_ms, 5),
+                      "GBps": round((b.decode_algorithmic_bytes() + b.write_algorithmic_bytes())
+                                    / (fused_ms * 1e-3) / 1e9, 2),
+                      "speedup_vs_two_launches": round(ms_per_step / fused_ms, 4)}
+
     # The decode launches alone, back to back between one event pair on the
     # stream they run on (rotating the pool copies as the steps do): their
     # average duration, the gaps between launches included, without the
@@ -875,6 +899,8 @@ def main() -> int:
         },
         "cpu_baseline": None,
     }
+    if fused_step is not None:
+        result["fused_step"] = fused_step
     if rig.prefix_len and not args.fused:
         result["shared_prefix"] = shared_prefix_timing(rig, args, decode_avg_ms)
     if others:

@@ -55,8 +55,10 @@ struct DecodeParams {
     int64_t block_stride_bytes; // bs * Hkv * D * elem bytes
     int row_stride_bytes;       // Hkv * D * elem bytes
     // Fused KV write (null new_key: none): sequence s's new token's rows
-    // new_key/new_value [S, Hkv, D] go to pool cell slot_mapping[s] before
-    // the sequence's attention reads its history.
+    // new_key/new_value [S, Hkv, D] go to pool cell slot_mapping[s], and the
+    // sequence's attention sees them at position L - 1 (the VALU kernel
+    // stores them before reading its history; the MFMA kernel's fused
+    // instance reads them from new_key/new_value and stores them after).
     const char *new_key;
     const char *new_value;
     const int32_t *slot_mapping;

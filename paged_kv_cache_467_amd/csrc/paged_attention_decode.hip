@@ -301,12 +301,14 @@ __device__ void store_constant(const DecodeParams &p, const WorkItem &w, bool na
     }
 }
 
-// Fused KV write: the new token of sequence s (position L - 1) goes to its
-// pool cell before the sequence's attention reads it.  The workgroup whose
-// partition holds position L - 1 (partition 0 when L is 0 or invalid: then
-// nothing is read) writes the rows of its kv heads, each wave its own head's
-// row -- the row that wave alone reads back -- and fences it.  A slot outside
-// the pool writes nothing.
+// Fused KV write, store first (the VALU kernel; the MFMA kernel's fused
+// instance only for a context that reads nothing; the plain instances are
+// launched with new_key null): the new token of sequence s (position L - 1)
+// goes to its pool cell before the sequence's attention reads it.  The
+// workgroup whose partition holds position L - 1 (partition 0 when L is 0 or
+// invalid: then nothing is read) writes the rows of its kv heads, each wave
+// its own head's row -- the row that wave alone reads back -- and fences it.
+// A slot outside the pool writes nothing.
 template <class T, int D>
 __device__ inline void write_new_token(const DecodeParams &p, const WorkItem &w) {
     if (p.new_key == nullptr) return;
@@ -712,9 +714,10 @@ __device__ inline void write_result4(const DecodeParams &p, const WorkItem &w, i
     }
 }
 
-template <class T, int D, int G, bool BT, bool BAL>
+template <class T, int D, int G, bool BT, bool BAL, bool FW = false>
 __global__ __launch_bounds__(kMaxDecodeThreads) void decode_mfma_kernel(DecodeParams p) {
     static_assert(T::kBytes == 2, "MFMA path is for 16-bit element types");
+    static_assert(!(FW && BAL), "the fused write takes the plain split");
     static_assert(G == 2 || G == 4 || G == 8, "group size");
     constexpr int KS = D / 32;        // MFMA k-steps per tile
     constexpr int CPR = D / 8;        // 16-byte chunks per row
@@ -842,6 +845,30 @@ __global__ __launch_bounds__(kMaxDecodeThreads) void decode_mfma_kernel(DecodePa
     // before the wave moves on
     if (bad && early) __builtin_amdgcn_s_waitcnt(0);
 
+    // Fused write (FW): the partition that ends at the context's end holds
+    // the new token, position L - 1, whose pool cell is slot_mapping[s] by
+    // the entry point's contract.  Its rows are read from new_key /
+    // new_value (each lane its chunk vc), put in place of the pool's rows in
+    // the LDS copy of the tile that holds the position, and stored in the
+    // cell after the loop; nothing else in the launch reads that cell.
+    int nt_tile = -1, nt_row = 0;
+    int64_t nt_dst = 0;
+    u32x4 nk = {0, 0, 0, 0}, nv = {0, 0, 0, 0};
+    if constexpr (FW) {
+        const int slot = p.slot_mapping[w.s];
+        if (w.tok_end == w.context_len && slot >= 0 && slot < p.num_slots) {
+            const int rel = w.context_len - 1 - w.tok_begin;
+            nt_tile = rel / TILE;
+            nt_row = rel % TILE;
+            const int64_t src = ((int64_t)w.s * p.num_kv_heads + w.kvh) * (D * 2) + 16 * vc;
+            nk = load16(p.new_key + src);
+            nv = load16(p.new_value + src);
+            nt_dst = (int64_t)(slot >> p.block_shift) * p.block_stride_bytes +
+                     (int64_t)(slot & (p.block_size - 1)) * p.row_stride_bytes + head_bytes +
+                     16 * vc;
+        }
+    }
+
     // Per tile: the tile's K and V go from registers to this wave's LDS
     // slices as soon as they arrive, which frees the registers for the next
     // tile's loads; those are issued before the tile's arithmetic, so every
@@ -854,6 +881,15 @@ __global__ __launch_bounds__(kMaxDecodeThreads) void decode_mfma_kernel(DecodePa
         for (int i = 0; i < NV; ++i) {
             *reinterpret_cast<u32x4 *>(k_wr + i * TPI * KRS) = kbuf[i];
             *reinterpret_cast<u32x4 *>(v_slot + i * v_wr_step) = vbuf[i];
+        }
+        if constexpr (FW) {
+            // the new token's rows over the pool's (LDS keeps a wave's
+            // writes in order)
+            if (tile == nt_tile && vtg == nt_row % TPI) {
+                const int i = nt_row / TPI;
+                *reinterpret_cast<u32x4 *>(k_wr + i * TPI * KRS) = nk;
+                *reinterpret_cast<u32x4 *>(v_slot + i * v_wr_step) = nv;
+            }
         }
         if (tile + 1 < ntiles) load(tile + 1, tile + 1 < nfull);
         __builtin_amdgcn_wave_barrier();
@@ -947,6 +983,14 @@ __global__ __launch_bounds__(kMaxDecodeThreads) void decode_mfma_kernel(DecodePa
         __builtin_amdgcn_wave_barrier();
     }
 
+    if constexpr (FW) {
+        // every read of the cell (the last tile's loads) has landed
+        if (nt_tile >= 0 && vtg == 0) {
+            store16(const_cast<char *>(p.key_cache) + nt_dst, nk);
+            store16(const_cast<char *>(p.value_cache) + nt_dst, nv);
+        }
+    }
+
     // l: sum over the 16 tokens of each row; acc: over the value token
     // slots (the value MFMA sums over the tokens itself).
 #pragma unroll
@@ -988,7 +1032,12 @@ __global__ __launch_bounds__(kMaxDecodeThreads) void decode_mfma_kernel(DecodePa
         for_each_segment(p, seq_start, wave_tot, segment);
     } else {
         const WorkItem w = work_item(p);
-        write_new_token<T, D>(p, w);
+        if constexpr (FW) {
+            // a context that reads nothing: the row goes straight to its cell
+            if (w.bad_len || w.context_len < 1) write_new_token<T, D>(p, w);
+        } else {
+            write_new_token<T, D>(p, w);
+        }
         if (!prologue<T, D, G>(p, w)) return;
         segment(w);
     }
@@ -1255,6 +1304,9 @@ hipError_t launch_main(const DecodeParams &p, int kernel, hipStream_t stream) {
         const size_t lds = p.heads_per_group * kv_lds_wave_bytes<D, G>();
         if (p.num_chunks > 0)
             hipLaunchKernelGGL((decode_mfma_kernel<T, D, G, BT, true>), dim3(grid),
+                               dim3(threads), lds, stream, p);
+        else if (p.new_key != nullptr)
+            hipLaunchKernelGGL((decode_mfma_kernel<T, D, G, BT, false, true>), dim3(grid),
                                dim3(threads), lds, stream, p);
         else
             hipLaunchKernelGGL((decode_mfma_kernel<T, D, G, BT, false>), dim3(grid),
