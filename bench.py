@@ -816,9 +816,10 @@ def main() -> int:
     write_ms = None if args.fused else [e[2].elapsed_time(e[0]) for e in events]
 
     # The same step as one paged_attn_decode_write launch (same work, same
-    # bits), timed the same way.
+    # bits), timed the same way (not with the balanced split, which that
+    # entry point does not take).
     fused_step = None
-    if not args.fused:
+    if not args.fused and rig.psize != BALANCED_SPLIT:
         for i in range(args.warmup):
             rig.launch_fused(i)
         torch.cuda.synchronize()
