@@ -1,20 +1,24 @@
 #!/usr/bin/env python3
 """Paged decode-attention bench on one MI355X.
 
-A step is one decode step of the whole path over one batch: kv_cache_write of
-each sequence's new token (slot_mapping scatter), then paged_attn_decode over
-every sequence's full context (block-table addressing, K/V tiles, online
-softmax, split-context partitions and their reduce when the context is
-split).  Inputs are resident in HBM before timing starts; the K/V pool is
-held in several copies that the steps rotate through, so that a step never
-finds its pool in the 256 MB Infinity Cache from the previous step.
+A step is one decode step of the whole path over one batch: each sequence's
+new token stored in its pool cell (the slot_mapping scatter of
+kv_cache_write), and the decode over every sequence's full context
+(block-table addressing, K/V tiles, online softmax, split-context partitions
+and their reduce when the context is split).  By default the step is one
+paged_attn_decode_write launch; with --two-launch, or for a batch that takes
+the balanced split, it is kv_cache_write then paged_attn_decode (same bits
+either way; the line reports the other form's step time too).  Inputs are
+resident in HBM before timing starts; the K/V pool is held in several copies
+that the steps rotate through, so that a step never finds its pool in the
+256 MB Infinity Cache from the previous step.
 
 Prints one JSON line.  `value` is algorithmic bytes per step (K/V rows of
 every context token, query, output, block-table entries and lengths, plus
-the write's bytes) divided by the step time.  `roofline` covers the decode
-kernel alone: its launches run back to back between two HIP events on the
-stream they run on, and the average launch duration divides its bytes.
-`cpu_baseline` times the fp64 CPU oracle on this host.
+the write's bytes) divided by the step time.  `roofline` covers the step's
+decode launch alone: its launches run back to back between two HIP events
+on the stream they run on, and the average launch duration divides its
+bytes.  `cpu_baseline` times the fp64 CPU oracle on this host.
 """
 from __future__ import annotations
 
@@ -49,16 +53,18 @@ def decode_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def measured_traffic(workload: str):
-    """HBM bytes per decode launch from the committed rocprofv3 counter
-    summary, or None when there is none or the decode kernel source has
-    changed since it was taken."""
+def measured_traffic(workload: str, one_launch: bool = False):
+    """HBM bytes per decode launch (paged_attn_decode's kernels, or with
+    one_launch paged_attn_decode_write's) from the committed rocprofv3
+    counter summary, or None when there is none or the decode kernel source
+    has changed since it was taken."""
     path = os.path.join(PROFILES, f"decode_{workload}_traffic.md")
     if not os.path.exists(path):
         return None
     text = open(path).read()
     src = re.search(r"decode_source_sha256:\s*(\w+)", text)
-    tot = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    key = "one_launch_hbm_bytes_per_launch" if one_launch else "hbm_bytes_per_launch"
+    tot = re.search(r"^" + key + r":\s*([0-9.eE+]+)", text, re.M)
     if not src or not tot or src.group(1) != decode_source_hash():
         return None
     return float(tot.group(1))
@@ -531,12 +537,12 @@ class DecodeRig:
     scheduler holding the lengths on the host would ask for.  Pool contents
     are random: they do not change the timing."""
 
-    def __init__(self, workload, copies, partition_size, fused, dev):
+    def __init__(self, workload, copies, partition_size, dev):
         import torch
 
         from paged_kv_cache_467_amd import binding, tensors, workloads as W
 
-        self.binding, self.fused = binding, fused
+        self.binding = binding
         b = self.b = W.make_workload(workload, values=False)
         dt = tensors.TORCH_DTYPE[b.dtype]
         S, Hq, Hkv, D, bs = b.num_seqs, b.num_q_heads, b.num_kv_heads, b.head_dim, b.block_size
@@ -571,16 +577,9 @@ class DecodeRig:
 
     def launch(self, i):
         kc, vc = self.copies[i % len(self.copies)]
-        B = self.binding
-        if not self.fused:
-            B.paged_attn_decode(self.query, kc, vc, self.bt, self.cl, self.b.scale, self.out,
-                                max_context_len=self.max_ctx, partition_size=self.psize,
-                                workspace=self.workspace)
-        else:
-            B.paged_attn_decode_write(self.query, self.new_key, self.new_value, self.sm, kc, vc,
-                                      self.bt, self.cl, self.b.scale, self.out,
-                                      max_context_len=self.max_ctx, partition_size=self.psize,
-                                      workspace=self.workspace)
+        self.binding.paged_attn_decode(self.query, kc, vc, self.bt, self.cl, self.b.scale,
+                                       self.out, max_context_len=self.max_ctx,
+                                       partition_size=self.psize, workspace=self.workspace)
 
     def launch_fused(self, i):
         kc, vc = self.copies[i % len(self.copies)]
@@ -714,9 +713,9 @@ def main() -> int:
     ap.add_argument("--no-workloads", action="store_true",
                     help="skip the other four decode workloads that the default run measures "
                          "after the headline one")
-    ap.add_argument("--fused", action="store_true",
-                    help="time the decode step as one paged_attn_decode_write launch instead "
-                         "of kv_cache_write + paged_attn_decode")
+    ap.add_argument("--two-launch", action="store_true",
+                    help="time the decode step as kv_cache_write + paged_attn_decode instead of "
+                         "one paged_attn_decode_write launch (a balanced split always takes two)")
     ap.add_argument("--prefill-dtype", choices=("bf16", "f16", "f32"), default=None,
                     help="--op prefill: element type of the pool and queries (default: the "
                          "workload's, bf16)")
@@ -762,23 +761,37 @@ def main() -> int:
     # for the same launches (the first workload allocated in a process was
     # the fast one, whichever it was).
     others = []
-    if not args.no_workloads and args.workload == DEFAULT_WORKLOAD and not args.fused:
-        others = [DecodeRig(wl, args.copies, 0, False, dev) for wl in W.WORKLOADS
+    if not args.no_workloads and args.workload == DEFAULT_WORKLOAD:
+        others = [DecodeRig(wl, args.copies, 0, dev) for wl in W.WORKLOADS
                   if wl != args.workload]
-    rig = DecodeRig(args.workload, args.copies, args.partition_size, args.fused, dev)
+    rig = DecodeRig(args.workload, args.copies, args.partition_size, dev)
     b = rig.b
     S, Hq, Hkv, D, bs = b.num_seqs, b.num_q_heads, b.num_kv_heads, b.head_dim, b.block_size
+    # The step: one paged_attn_decode_write launch (the new tokens stored and
+    # the decode, same bits as the two calls), or with --two-launch, or a
+    # balanced split (which that entry point does not take), kv_cache_write
+    # then paged_attn_decode.
+    one_launch_ok = rig.psize != BALANCED_SPLIT
+    fused = one_launch_ok and not args.two_launch
+    step_launch = rig.launch_fused if fused else rig.launch  # the step's decode launch
 
     def step(i, ev=None):
-        if not args.fused:
+        if not fused:
             if ev is not None:
                 ev[2].record()
             rig.write(i)
         if ev is not None:
             ev[0].record()
-        rig.launch(i)
+        step_launch(i)
         if ev is not None:
             ev[1].record()
+
+    def other_step(i):  # the step taken the other way
+        if fused:
+            rig.write(i)
+            rig.launch(i)
+        else:
+            rig.launch_fused(i)
 
     if args.calibrate_copy_mib:
         n = args.calibrate_copy_mib * (1 << 20)
@@ -789,7 +802,7 @@ def main() -> int:
         del src, dst
 
     for i in range(SETTLE_LAUNCHES):
-        rig.launch(i)
+        step_launch(i)
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
@@ -806,45 +819,51 @@ def main() -> int:
     ms_per_step = elapsed * 1e3 / steps
 
     # Each launch on its own, between HIP events on the stream it runs on
-    # (the write between the third and the first event of its step).
+    # (the write, in the two-launch step, between the third and the first
+    # event of its step).
     events = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(3))
               for _ in range(args.steps)]
     for i in range(args.steps):
         step(args.warmup + i, events[i])
     torch.cuda.synchronize()
-    decode_ms = [e[0].elapsed_time(e[1]) for e in events]
-    write_ms = None if args.fused else [e[2].elapsed_time(e[0]) for e in events]
+    decode_ev_ms = [e[0].elapsed_time(e[1]) for e in events]
+    write_ms = None if fused else [e[2].elapsed_time(e[0]) for e in events]
 
-    # The same step as one paged_attn_decode_write launch (same work, same
-    # bits), timed the same way (not with the balanced split, which that
-    # entry point does not take).
-    fused_step = None
-    if not args.fused and rig.psize != BALANCED_SPLIT:
+    # The same step taken the other way (same work, same bits), timed the
+    # same way.
+    b_dec = b.decode_algorithmic_bytes()
+    b_step = b_dec + b.write_algorithmic_bytes()
+    other = None
+    if one_launch_ok:
         for i in range(args.warmup):
-            rig.launch_fused(i)
+            other_step(i)
         torch.cuda.synchronize()
         t0 = time.perf_counter()
         for i in range(steps):
-            rig.launch_fused(args.warmup + i)
+            other_step(args.warmup + i)
         torch.cuda.synchronize()
-        fused_ms = (time.perf_counter() - t0) * 1e3 / steps
-        fused_step = {"entry": "paged_attn_decode_write", "ms_per_step": round(fused_ms, 5),
-                      "GBps": round((b.decode_algorithmic_bytes() + b.write_algorithmic_bytes())
-                                    / (fused_ms * 1e-3) / 1e9, 2),
-                      "speedup_vs_two_launches": round(ms_per_step / fused_ms, 4)}
+        other_ms = (time.perf_counter() - t0) * 1e3 / steps
+        other = {"entry": ("kv_cache_write + paged_attn_decode" if fused
+                           else "paged_attn_decode_write"),
+                 "ms_per_step": round(other_ms, 5),
+                 "GBps": round(b_step / (other_ms * 1e-3) / 1e9, 2),
+                 "step_speedup": round(other_ms / ms_per_step, 4)}
 
-    # The decode launches alone, back to back between one event pair on the
-    # stream they run on (rotating the pool copies as the steps do): their
+    # The step's decode launch alone, back to back between one event pair on
+    # the stream it runs on (rotating the pool copies as the steps do): its
     # average duration, the gaps between launches included, without the
     # cost an event pair adds to each launch it brackets (about 4 us here).
-    # The roofline uses this figure.
-    _, decode_avg_ms = time_back_to_back(rig.launch, args.warmup, steps)
-    write_graph_ms = None if args.fused else time_graph(rig.write, args.warmup)
-    b_dec = b.decode_algorithmic_bytes()
-    b_step = b_dec + b.write_algorithmic_bytes()
-    b_launch = b_dec if not args.fused else b_step  # the timed launch's own bytes
-    achieved = b_launch / (decode_avg_ms * 1e-3) / 1e9
-    traffic = None if args.fused else measured_traffic(args.workload)
+    # The roofline uses this figure.  With the one-launch step,
+    # paged_attn_decode is also timed alone.
+    _, launch_avg_ms = time_back_to_back(step_launch, args.warmup, steps)
+    decode_avg_ms = launch_avg_ms
+    if fused:
+        _, decode_avg_ms = time_back_to_back(rig.launch, args.warmup, steps)
+    write_graph_ms = time_graph(rig.write, args.warmup)
+    b_launch = b_step if fused else b_dec  # the timed launch's own bytes
+    achieved = b_launch / (launch_avg_ms * 1e-3) / 1e9
+    traffic = measured_traffic(args.workload, one_launch=fused)
+    entry = "paged_attn_decode_write" if fused else "paged_attn_decode"
 
     result = {
         "metric": METRIC,
@@ -866,23 +885,32 @@ def main() -> int:
             "context_tokens": int(b.context_lens.sum()),
             "context_len_range": [int(b.context_lens.min()), int(b.context_lens.max())],
             "partition_size": split_name(rig.partition_size), "pool_copies": len(rig.copies),
-            "step": ("kv_cache_write of one token per sequence + paged_attn_decode"
-                     if not args.fused else
-                     "paged_attn_decode_write: one new token per sequence stored in the pool "
-                     "and the decode, in one launch"),
+            "step": ("paged_attn_decode_write: one new token per sequence stored in the pool "
+                     "and the decode, in one launch" if fused else
+                     "kv_cache_write of one token per sequence + paged_attn_decode"),
         },
-        "seq_per_s_per_layer": round(S / (decode_avg_ms * 1e-3), 1),
-        "decode_ms": round(decode_avg_ms, 5),
+        # the step's decode launch: paged_attn_decode_write's kernel, or
+        # paged_attn_decode's (kernels; + reduce where the context is split)
+        "decode_entry": entry,
+        "decode_ms": round(launch_avg_ms, 5),
+        "seq_per_s_per_layer": round(S / (launch_avg_ms * 1e-3), 1),
         # each launch between its own event pair (the pair's cost included)
-        "decode_event_ms": {"mean": round(sum(decode_ms) / len(decode_ms), 5),
-                            "median": round(float(np.median(decode_ms)), 5),
-                            "p10": round(float(np.percentile(decode_ms, 10)), 5),
-                            "p90": round(float(np.percentile(decode_ms, 90)), 5)},
+        "decode_event_ms": {"mean": round(sum(decode_ev_ms) / len(decode_ev_ms), 5),
+                            "median": round(float(np.median(decode_ev_ms)), 5),
+                            "p10": round(float(np.percentile(decode_ev_ms, 10)), 5),
+                            "p90": round(float(np.percentile(decode_ev_ms, 90)), 5)},
+        # paged_attn_decode alone (the step's launch with --two-launch)
+        "paged_attn_decode": {
+            "decode_ms": round(decode_avg_ms, 5),
+            "achieved": round(b_dec / (decode_avg_ms * 1e-3) / 1e9, 2),
+            "frac": round(b_dec / (decode_avg_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+            "traffic": measured_traffic(args.workload),
+        },
         "write_ms": None if write_ms is None else round(sum(write_ms) / len(write_ms), 5),
         "write_GBps": None if write_ms is None else
         round(b.write_algorithmic_bytes() / (sum(write_ms) / len(write_ms) * 1e-3) / 1e9, 2),
         # the write alone, from a HIP graph of 20 launches (no host in the loop)
-        "write_graph_ms": None if write_graph_ms is None else round(write_graph_ms, 5),
+        "write_graph_ms": round(write_graph_ms, 5),
         "algorithmic_bytes_per_step": b_step,
         "roofline": {
             "bound": "hbm",
@@ -894,15 +922,15 @@ def main() -> int:
             # HBM bytes (counters) over the launch time: differs from achieved
             # where the batch re-reads cached data (a shared prefix)
             "traffic_GBps": None if traffic is None else
-            round(traffic / (decode_avg_ms * 1e-3) / 1e9, 2),
-            "kernel": "paged_attn_decode" if not args.fused else "paged_attn_decode_write",
+            round(traffic / (launch_avg_ms * 1e-3) / 1e9, 2),
+            "kernel": entry,
             "algorithmic_bytes_per_launch": b_launch,
         },
         "cpu_baseline": None,
     }
-    if fused_step is not None:
-        result["fused_step"] = fused_step
-    if rig.prefix_len and not args.fused:
+    if other is not None:
+        result["two_launch_step" if fused else "one_launch_step"] = other
+    if rig.prefix_len:
         result["shared_prefix"] = shared_prefix_timing(rig, args, decode_avg_ms)
     if others:
         result["workloads"] = {o.b.name: other_workload(o, args) for o in others}
