@@ -518,6 +518,11 @@ DEFAULT_WORKLOAD = "llama3_8b_gqa_bf16"
 # reach its steady clocks; with 5 warm-up steps the same launches measured
 # 1.5% slower on the Llama-3-8B batch and up to 16% slower on the others.
 SETTLE_LAUNCHES = 400
+# Launches in each back-to-back pass that times a decode launch on its own
+# (the roofline's figure): at least this many, whatever --steps is, since
+# the pass's fixed start and end (about 20-30 us) would otherwise add a
+# microsecond or more to each of a few launches.
+MIN_LAUNCH_PASS = 200
 
 
 BALANCED_SPLIT = 1   # PAGED_KV_BALANCED_SPLIT
@@ -613,7 +618,8 @@ def shared_prefix_timing(rig: "DecodeRig", args, decode_ms: float) -> dict:
     b = rig.b
     for i in range(SETTLE_LAUNCHES):
         rig.launch_shared(i)
-    _, sp_ms = time_back_to_back(rig.launch_shared, SETTLE_LAUNCHES, args.steps)
+    _, sp_ms = time_back_to_back(rig.launch_shared, SETTLE_LAUNCHES,
+                                 max(args.steps, MIN_LAUNCH_PASS))
     sp_graph_ms = time_graph(rig.launch_shared, SETTLE_LAUNCHES)
     t_ms = min(sp_ms, sp_graph_ms)
     t = t_ms * 1e-3
@@ -650,7 +656,7 @@ def other_workload(rig: "DecodeRig", args) -> dict:
     warm = SETTLE_LAUNCHES + args.warmup + 2 * args.steps
     for i in range(warm):
         rig.launch(i)
-    _, dec_ms = time_back_to_back(rig.launch, warm, args.steps)
+    _, dec_ms = time_back_to_back(rig.launch, warm, max(args.steps, MIN_LAUNCH_PASS))
     # the write moves a few MB at most: its launches from Python come slower
     # than the kernel runs, so it is timed from a HIP graph of 20 launches
     for i in range(args.warmup):
@@ -849,16 +855,17 @@ def main() -> int:
                  "GBps": round(b_step / (other_ms * 1e-3) / 1e9, 2),
                  "step_speedup": round(other_ms / ms_per_step, 4)}
 
-    # The step's decode launch alone, back to back between one event pair on
-    # the stream it runs on (rotating the pool copies as the steps do): its
-    # average duration, the gaps between launches included, without the
-    # cost an event pair adds to each launch it brackets (about 4 us here).
-    # The roofline uses this figure.  With the one-launch step,
-    # paged_attn_decode is also timed alone.
-    _, launch_avg_ms = time_back_to_back(step_launch, args.warmup, steps)
+    # The step's decode launch alone, max(K, MIN_LAUNCH_PASS) times back to
+    # back between one event pair on the stream it runs on (rotating the
+    # pool copies as the steps do): its average duration, the gaps between
+    # launches included, without the cost an event pair adds to each launch
+    # it brackets (about 4 us here).  The roofline uses this figure.  With
+    # the one-launch step, paged_attn_decode is also timed alone.
+    n_pass = max(steps, MIN_LAUNCH_PASS)
+    _, launch_avg_ms = time_back_to_back(step_launch, args.warmup, n_pass)
     decode_avg_ms = launch_avg_ms
     if fused:
-        _, decode_avg_ms = time_back_to_back(rig.launch, args.warmup, steps)
+        _, decode_avg_ms = time_back_to_back(rig.launch, args.warmup, n_pass)
     write_graph_ms = time_graph(rig.write, args.warmup)
     b_launch = b_step if fused else b_dec  # the timed launch's own bytes
     achieved = b_launch / (launch_avg_ms * 1e-3) / 1e9

@@ -836,6 +836,28 @@ __global__ __launch_bounds__(kMaxDecodeThreads) void decode_mfma_kernel(DecodePa
         }
     };
 
+    // Fused write (FW): the partition that ends at the context's end holds
+    // the new token, position L - 1, whose pool cell is slot_mapping[s] by
+    // the entry point's contract.  Its rows are read from new_key /
+    // new_value (each lane its chunk vc), put in place of the pool's rows in
+    // the LDS copy of the tile that holds the position, and stored in the
+    // cell after the loop; nothing else in the launch reads that cell.  The
+    // slot and the rows are loaded before the first tile, so that waiting
+    // for them overlaps the tile's loads.
+    int nt_tile = -1, nt_row = 0;
+    int64_t nt_dst = 0;
+    u32x4 nk = {0, 0, 0, 0}, nv = {0, 0, 0, 0};
+    const bool nt_part = FW && w.tok_end == w.context_len;
+    int slot = -1;
+    if constexpr (FW) {
+        slot = p.slot_mapping[w.s];
+        if (nt_part) {
+            const int64_t src = ((int64_t)w.s * p.num_kv_heads + w.kvh) * (D * 2) + 16 * vc;
+            nk = load16(p.new_key + src);
+            nv = load16(p.new_value + src);
+        }
+    }
+
     // the first tile goes out while the block ids are staged
     const bool early = first_tile_early<BT>(p, w, TILE);
     const bool bad = stage_block_table_early(p, w, bt_lds, early, load_full);
@@ -845,24 +867,11 @@ __global__ __launch_bounds__(kMaxDecodeThreads) void decode_mfma_kernel(DecodePa
     // before the wave moves on
     if (bad && early) __builtin_amdgcn_s_waitcnt(0);
 
-    // Fused write (FW): the partition that ends at the context's end holds
-    // the new token, position L - 1, whose pool cell is slot_mapping[s] by
-    // the entry point's contract.  Its rows are read from new_key /
-    // new_value (each lane its chunk vc), put in place of the pool's rows in
-    // the LDS copy of the tile that holds the position, and stored in the
-    // cell after the loop; nothing else in the launch reads that cell.
-    int nt_tile = -1, nt_row = 0;
-    int64_t nt_dst = 0;
-    u32x4 nk = {0, 0, 0, 0}, nv = {0, 0, 0, 0};
     if constexpr (FW) {
-        const int slot = p.slot_mapping[w.s];
-        if (w.tok_end == w.context_len && slot >= 0 && slot < p.num_slots) {
+        if (nt_part && slot >= 0 && slot < p.num_slots) {
             const int rel = w.context_len - 1 - w.tok_begin;
             nt_tile = rel / TILE;
             nt_row = rel % TILE;
-            const int64_t src = ((int64_t)w.s * p.num_kv_heads + w.kvh) * (D * 2) + 16 * vc;
-            nk = load16(p.new_key + src);
-            nv = load16(p.new_value + src);
             nt_dst = (int64_t)(slot >> p.block_shift) * p.block_stride_bytes +
                      (int64_t)(slot & (p.block_size - 1)) * p.row_stride_bytes + head_bytes +
                      16 * vc;
