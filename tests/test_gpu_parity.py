@@ -408,8 +408,13 @@ def test_invalid_first_block_id_gives_nan(B, dtype, G, first):
         check_close(got[2:3], ref[2:3], dtype, f"valid neighbour P={P}")
 
 
+# (dtype, Hq, Hkv, D, bs, partition): the matrix-core kernel's fused instance
+# at G = 2 (value product on FMAs), 4 and 8, block sizes below and above 16,
+# every head_dim; the vector kernel's store-first path at G = 1 and f32
 FUSED = [("bf16", 32, 8, 128, 16, 0), ("bf16", 32, 8, 128, 16, 64), ("f16", 8, 8, 128, 32, 0),
-         ("f32", 8, 2, 64, 16, 32), ("bf16", 16, 4, 256, 1, 0), ("f16", 16, 2, 64, 8, 48)]
+         ("f32", 8, 2, 64, 16, 32), ("bf16", 16, 4, 256, 1, 0), ("f16", 16, 2, 64, 8, 48),
+         ("bf16", 8, 4, 128, 16, 0), ("f16", 16, 8, 64, 32, 32), ("bf16", 16, 2, 256, 16, 64),
+         ("f16", 8, 4, 256, 4, 0)]
 
 
 @pytest.mark.parametrize("dtype,Hq,Hkv,D,bs,psize", FUSED)
