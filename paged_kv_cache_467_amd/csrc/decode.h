@@ -121,7 +121,8 @@ size_t decode_partial_slots(const DecodePlan &pl, int num_seqs, int num_q_heads)
 size_t decode_workspace_bytes(const DecodePlan &pl, int num_seqs, int num_q_heads, int head_dim);
 
 // The decode entry points' common path (capi.cpp): host checks, then the
-// launch; with new_key non-null the fused KV write runs first.  With
+// launch; with new_key non-null the launch also stores the new tokens (the
+// fused KV write, in the same kernels).  With
 // static_scratch the split's scratch is noalloc_scratch() (workspace and
 // workspace_bytes are ignored) and a split that needs more than it holds
 // returns PAGED_KV_ERR_SCRATCH_LIMIT.  Returns a paged_kv_status.

@@ -51,6 +51,13 @@
 // Online softmax: the running max only moves when some score of the tile
 // exceeds it; each lane checks its own scores, and the cross-lane max
 // reduction and the rescale of l and the accumulator run only when one did.
+//
+// Fused KV write (paged_attn_decode_write: each sequence's new token goes to
+// its pool cell, position L - 1, in the same launch): the VALU kernel stores
+// the new rows before it reads the context; the MFMA kernel has an instance
+// of its own (FW) that takes the rows from the new-token input, uses them in
+// place of the pool's in the tile that holds position L - 1, and stores them
+// in the cell after its loop.
 
 #include "decode.h"
 #include "device_utils.h"
