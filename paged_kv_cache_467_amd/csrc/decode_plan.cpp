@@ -160,6 +160,24 @@ DecodePlan plan_decode(int num_seqs, int num_q_heads, int num_kv_heads, int head
     pl.partition_size = (int)P;
     pl.num_partitions = (int)nparts;
     pl.heads_per_group = hpg;
+    // A batch that needs no split and whose workgroups are all resident at
+    // once (one round) ends when the most loaded compute unit does; with 2
+    // kv heads per workgroup instead of 4 each unit holds twice as many,
+    // smaller workgroups and the units' loads come out more even (the same
+    // waves per unit).  Only where the 2 heads' share of a token row stays
+    // at least 512 contiguous bytes.  Measured with 256 contexts of ~580
+    // tokens, 8 kv heads, bf16, head_dim 128: -2.0% (G = 4), -1.9% (G = 8),
+    // -1.1% (G = 2), -1.7% (f16, G = 1), and -1.9% with 384 contexts of ~390
+    // (three workgroups of 4 heads per unit); batches of more than one round
+    // gained nothing or lost up to 1.8%, and head_dim 64 (256-byte
+    // pieces) lost 2.7%.
+    if (nparts == 1 && hpg == 4 && (int64_t)head_dim * (dtype == PAGED_KV_F32 ? 4 : 2) >= 256) {
+        const DeviceOccupancy occ = decode_occupancy(dtype, head_dim, group, block_size, hpg);
+        const int64_t cus = occ.compute_units > 0 ? occ.compute_units : kFallbackComputeUnits;
+        const int64_t units = (int64_t)num_seqs * (num_kv_heads / hpg);
+        if (occ.workgroups_per_cu > 0 && units <= cus * occ.workgroups_per_cu)
+            pl.heads_per_group = 2;
+    }
     return pl;
 }
 
