@@ -475,8 +475,10 @@ def test_decode_write_new_token_in_the_first_tile(B, dtype, Hq, Hkv):
 
 
 def test_decode_write_on_the_bench_batch(B):
-    """The Llama-3-8B-shaped batch: fused step equals the two calls, and the
-    pool after it equals the oracle's write."""
+    """The Llama-3-8B-shaped batch in the bench's own step (one
+    paged_attn_decode_write launch, automatic split): the fused step equals
+    the two calls bit for bit, the pool after it equals the oracle's write,
+    and its output the oracle's decode of the written batch."""
     b = W.make_workload("llama3_8b_gqa_bf16", poison=True)
     _say("paged_attn_decode_write on the Llama-3-8B batch")
     ref, got = tensors.device_batch(b, DEV), tensors.device_batch(b, DEV)
@@ -489,10 +491,12 @@ def test_decode_write_on_the_bench_batch(B):
                               got.context_lens, b.scale, got.out)
     torch.cuda.synchronize()
     assert np.array_equal(tensors.to_host_bits(ref.out), tensors.to_host_bits(got.out))
-    kc, vc = b.key_cache.copy(), b.value_cache.copy()
-    oracle.kv_cache_write(b.new_key, b.new_value, b.slot_mapping, kc, vc, b.dtype)
-    assert np.array_equal(tensors.to_host_bits(got.key_cache), kc)
-    assert np.array_equal(tensors.to_host_bits(got.value_cache), vc)
+    stepped = b.copy()
+    oracle.write_batch(stepped)
+    assert np.array_equal(tensors.to_host_bits(got.key_cache), stepped.key_cache)
+    assert np.array_equal(tensors.to_host_bits(got.value_cache), stepped.value_cache)
+    check_close(tensors.widen(tensors.to_host_bits(got.out), b.dtype),
+                oracle.decode_batch(stepped), b.dtype, "fused step, Llama-3-8B batch")
 
 
 def test_decode_write_graph_replay(B):
