@@ -19,7 +19,10 @@
 // head_dim 256), staged in LDS as they lie in the pool ([token][d]; K rows
 // padded by 16 bytes and V rows by 32, so that neither operand read meets a
 // bank conflict), double-buffered with one barrier per tile and shared by
-// its 4 waves:
+// its 4 waves.  At head_dim 128 with blocks of 16 tokens or more the tiles
+// go from memory straight into LDS (global_load_lds, one 16-token quarter
+// per wave, issued at the start of the tile before) with the chunks of each
+// row placed by an XOR swizzle instead of padding:
 //  * Scores are computed transposed, S^T = K Q^T, with
 //    v_mfma_f32_16x16x32 per 16-token quarter: A = K (lane l: token l % 16,
 //    8 consecutive d of k-group l / 16), B = Q^T from registers (lane l: row
@@ -45,6 +48,8 @@
 #include "prefill_common.h"
 
 #include <math.h>
+
+#include <type_traits>
 
 namespace pkv {
 namespace {
@@ -92,6 +97,18 @@ __device__ inline uint32_t narrow_pair<F16>(float a, float b) {
     return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a, b}, f16x2));
 }
 
+// Staging of the K/V tiles straight from memory into LDS at head_dim 128
+// (see the kernel); 0 keeps the register staging everywhere.
+#ifndef PKV_PREFILL_DMA
+#define PKV_PREFILL_DMA 1
+#endif
+// s_waitcnt operand: vector memory count 0, the other counters untouched
+constexpr int kWaitVmcnt0 = 0x0F70;
+// Cache policy of those loads: the default.  The row blocks of a (sequence,
+// kv head) unit read the same K/V tiles through L2, and the non-temporal
+// hint measured 5% slower on the chunked-prefill workload.
+constexpr int kDmaAux = 0;
+
 // K operands of the score products in flight ahead of their use (4 LDS
 // reads cover their latency; measured 2-3% faster than 1 on the chunked-
 // prefill workload, no faster at 2..8).
@@ -130,9 +147,40 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(PrefillParams 
     constexpr int CPT = (CHUNKS + kPrefillThreads - 1) / kPrefillThreads;  // per thread
     constexpr int CPRW = D / 8;           // chunks per token row
     static_assert(CHUNKS % kPrefillThreads == 0, "every thread loads whole chunks");
+    // At head_dim 128 with whole 16-token quarters per block, the tiles go
+    // from memory straight into LDS (global_load_lds): each wave loads one
+    // quarter of each tile, 1 KB (4 rows) per instruction, with no register
+    // staging and no padding.  The 16-byte chunks are placed with an XOR
+    // swizzle instead -- chunk c of tile row r at position c ^ (r mod 16) in
+    // K and c ^ 2 (r mod 8) in V -- so that the score operand reads (16 rows,
+    // one chunk each) and the transposing value reads (4 rows x 32 bytes)
+    // still meet no bank conflict.
+    constexpr bool DMA = PKV_PREFILL_DMA && D == 128 && BT && NQ == kPrefillWaves;
+    constexpr int KROW = DMA ? D : KSTR;  // element stride of the LDS tile rows
+    constexpr int VROW = DMA ? D : VSTR;
 
-    __shared__ __attribute__((aligned(16))) uint16_t k_lds[2][TT * KSTR];
-    __shared__ __attribute__((aligned(16))) uint16_t v_lds[2][TT * VSTR];
+    // The two tile buffers.  With the loads straight to LDS each buffer is a
+    // variable of its own (the compiler then knows that loads into one do
+    // not touch reads of the other); otherwise one array of two.
+    constexpr int NKB = DMA ? 1 : 2;
+    __shared__ __attribute__((aligned(16))) uint16_t k_lds[NKB][DMA ? 8 : TT * KROW];
+    __shared__ __attribute__((aligned(16))) uint16_t v_lds[NKB][DMA ? 8 : TT * VROW];
+    __shared__ __attribute__((aligned(16))) uint16_t k_lds0[DMA ? TT * KROW : 8];
+    __shared__ __attribute__((aligned(16))) uint16_t k_lds1[DMA ? TT * KROW : 8];
+    __shared__ __attribute__((aligned(16))) uint16_t v_lds0[DMA ? TT * VROW : 8];
+    __shared__ __attribute__((aligned(16))) uint16_t v_lds1[DMA ? TT * VROW : 8];
+    auto kbuf = [&](int b) -> uint16_t * {
+        if constexpr (DMA)
+            return b ? k_lds1 : k_lds0;
+        else
+            return k_lds[b];
+    };
+    auto vbuf = [&](int b) -> uint16_t * {
+        if constexpr (DMA)
+            return b ? v_lds1 : v_lds0;
+        else
+            return v_lds[b];
+    };
 
     // ---- work item
     const int G = p.group;
@@ -290,11 +338,71 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(PrefillParams 
         const_cast<int32_t *>(bt_row), 0, p.max_blocks_per_seq * 4, kBufferConfig);
     int next_id[NQ];
     auto fetch_ids = [&](int tile) {
-#pragma unroll
-        for (int h = 0; h < NQ; ++h) {
-            const int th = min(tb + tile * TT + 16 * h, pmax);
-            next_id[h] = __builtin_amdgcn_raw_buffer_load_b32(bt_rsrc, (th >> p.block_shift) * 4,
+        if constexpr (DMA) {  // this wave's quarter only
+            const int th = min(tb + tile * TT + 16 * wave_s, pmax);
+            next_id[0] = __builtin_amdgcn_raw_buffer_load_b32(bt_rsrc, (th >> p.block_shift) * 4,
                                                               0, 0);
+        } else {
+#pragma unroll
+            for (int h = 0; h < NQ; ++h) {
+                const int th = min(tb + tile * TT + 16 * h, pmax);
+                next_id[h] = __builtin_amdgcn_raw_buffer_load_b32(
+                    bt_rsrc, (th >> p.block_shift) * 4, 0, 0);
+            }
+        }
+    };
+    // DMA: this lane's byte offset from its quarter's first row for each of
+    // the 4 instructions per tensor: tile row r = 4 j + lane / 16 of the
+    // quarter, LDS position lane % 16, holding the chunk the swizzle puts there
+    uint32_t dma_k[4], dma_v[4];
+    if constexpr (DMA) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int r = 4 * j + lane / 16, pos16 = lane % 16;
+            const uint32_t row = (uint32_t)(r * p.row_stride_bytes + head_off);
+            dma_k[j] = row + 16 * (pos16 ^ r);
+            dma_v[j] = row + 16 * (pos16 ^ (2 * (r & 7)));
+        }
+    }
+    // DMA: issues this wave's quarter of tile `tile` into LDS buffer buf
+    // (block id from fetch_ids, then the next tile's id is fetched)
+    auto dma_tile = [&](int buf, int tile) {
+        const int th = tb + tile * TT + 16 * wave_s;
+        int blk = __builtin_amdgcn_readfirstlane(next_id[0]);
+        if (blk < 0 || blk >= p.num_blocks) {
+            bad = 1;
+            blk = 0;
+        }
+        const int64_t qb = (int64_t)blk * p.block_stride_bytes +
+                           (int64_t)(th & (p.block_size - 1)) * p.row_stride_bytes;
+        const char *kq = p.key_cache + qb;
+        const char *vq = p.value_cache + qb;
+        typedef __attribute__((address_space(3))) void lds_void;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int row0 = 16 * wave_s + 4 * j;  // the instruction's first tile row
+            __builtin_amdgcn_global_load_lds(kq + dma_k[j], (lds_void *)&kbuf(buf)[row0 * KROW],
+                                             16, 0, kDmaAux);
+            __builtin_amdgcn_global_load_lds(vq + dma_v[j], (lds_void *)&vbuf(buf)[row0 * VROW],
+                                             16, 0, kDmaAux);
+        }
+        fetch_ids(tile + 1);  // past the last tile: pmax's block again
+    };
+    // DMA: once this wave's loads of tile `tile` have landed, zero the rows
+    // of its quarter past pmax (last tile only)
+    auto dma_finish = [&](int buf, int tile) {
+        __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+        const int t0 = tb + tile * TT;
+        if (t0 + TT - 1 > pmax) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int r = 16 * wave_s + 4 * j + lane / 16;
+                if (t0 + r <= pmax) continue;
+                *reinterpret_cast<u32x4 *>(&kbuf(buf)[r * KROW + 8 * (lane % 16)]) =
+                    u32x4{0, 0, 0, 0};
+                *reinterpret_cast<u32x4 *>(&vbuf(buf)[r * VROW + 8 * (lane % 16)]) =
+                    u32x4{0, 0, 0, 0};
+            }
         }
     };
     auto load_tile = [&](int tile) {
@@ -346,8 +454,8 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(PrefillParams 
         for (int c = 0; c < CPT; ++c) {
             const int idx = threadIdx.x + c * kPrefillThreads;
             const int row = idx / CPRW, col = (idx % CPRW) * 8;
-            *reinterpret_cast<u32x4 *>(&k_lds[buf][row * KSTR + col]) = kreg[c];
-            *reinterpret_cast<u32x4 *>(&v_lds[buf][row * VSTR + col]) = vreg[c];
+            *reinterpret_cast<u32x4 *>(&kbuf(buf)[row * KROW + col]) = kreg[c];
+            *reinterpret_cast<u32x4 *>(&vbuf(buf)[row * VROW + col]) = vreg[c];
         }
         if (t0 + TT - 1 > pmax) {  // the last tile: overwrite tokens past pmax
 #pragma unroll
@@ -355,8 +463,8 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(PrefillParams 
                 const int idx = threadIdx.x + c * kPrefillThreads;
                 if (t0 + idx / CPRW <= pmax) continue;
                 const int row = idx / CPRW, col = (idx % CPRW) * 8;
-                *reinterpret_cast<u32x4 *>(&k_lds[buf][row * KSTR + col]) = u32x4{0, 0, 0, 0};
-                *reinterpret_cast<u32x4 *>(&v_lds[buf][row * VSTR + col]) = u32x4{0, 0, 0, 0};
+                *reinterpret_cast<u32x4 *>(&kbuf(buf)[row * KROW + col]) = u32x4{0, 0, 0, 0};
+                *reinterpret_cast<u32x4 *>(&vbuf(buf)[row * VROW + col]) = u32x4{0, 0, 0, 0};
             }
         }
     };
@@ -371,7 +479,11 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(PrefillParams 
         for (int b = 0; b < DB; ++b) acc[mb][b] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
     }
     // this lane's V^T addresses inside a tile (quarter 0); quarter q is 16 q rows down
-    const int vt_elem = (4 * kg + lrow / 4) * VSTR + 4 * (lrow % 4);
+    // (DMA: d block b of the lane's row sits at swizzled chunk pair b ^ vt_swz)
+    const int vt_elem = DMA ? (4 * kg + lrow / 4) * VROW + 8 * ((lrow >> 1) & 1) +
+                                  4 * (lrow & 1)
+                            : (4 * kg + lrow / 4) * VSTR + 4 * (lrow % 4);
+    const int vt_swz = (4 * kg + lrow / 4) & 7;
 
     if constexpr (BT) fetch_ids(0);
     if constexpr (SHARED) {
@@ -385,8 +497,13 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(PrefillParams 
             }
         }
     }
-    load_tile(0);
-    store_tile(0, 0);
+    if constexpr (DMA) {
+        dma_tile(0, 0);
+        dma_finish(0, 0);
+    } else {
+        load_tile(0);
+        store_tile(0, 0);
+    }
     __syncthreads();
     if constexpr (SHARED) {  // the flags were cleared before the barrier
 #pragma unroll
@@ -400,13 +517,23 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(PrefillParams 
             if (e.x != e.y) seq_bad[i / nb] = 1;
         }
     }
-    for (int tile = 0; tile < ntiles; ++tile) {
-        const int buf = tile & 1;
+    // One tile: its scores, softmax and value product, with the next tile's
+    // loads in flight.  The LDS buffer is bufc: a compile-time constant when
+    // the loads go straight to LDS, so that the compiler can tell the next
+    // tile's loads (the other buffer) from this tile's reads and does not
+    // wait for them.
+    auto tile_step = [&](int tile, auto bufc) {
+        const int buf = bufc;
         const int t0 = tb + tile * TT;
         bool prefetched = false;
+        // DMA: the next tile goes out at once, into the buffer every wave
+        // finished reading before the last barrier
+        if constexpr (DMA) {
+            if (tile + 1 < ntiles) dma_tile(buf ^ 1, tile + 1);
+        }
         if (wave_active && t0 <= wave_pmax) {
-            const uint16_t *kt = k_lds[buf];
-            const uint16_t *vt = v_lds[buf];
+            const uint16_t *kt = kbuf(buf);
+            const uint16_t *vt = vbuf(buf);
             // S^T for every quarter and row block.  The K operands are read
             // kScoreReadAhead products ahead of their use (the schedule is
             // pinned below: left to itself the compiler reads each operand
@@ -421,8 +548,8 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(PrefillParams 
             u32x4 ka[NS];
             auto kread = [&](int step) {
                 const int u = step / KS, ks = step % KS;
-                ka[step] = *reinterpret_cast<const u32x4 *>(
-                    &kt[(16 * u + lrow) * KSTR + (kg + 4 * ks) * 8]);
+                const int chunk = DMA ? (kg + 4 * ks) ^ lrow : kg + 4 * ks;
+                ka[step] = *reinterpret_cast<const u32x4 *>(&kt[(16 * u + lrow) * KROW + chunk * 8]);
             };
 #pragma unroll
             for (int step = 0; step < PD; ++step) kread(step);
@@ -442,7 +569,9 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(PrefillParams 
                 __builtin_amdgcn_sched_group_barrier(kSchedMfma, MB, 0);
             }
             // the next tile's loads, issued once this tile's K operands are in registers
-            if (tile + 1 < ntiles) load_tile(tile + 1);
+            if constexpr (!DMA) {
+                if (tile + 1 < ntiles) load_tile(tile + 1);
+            }
             prefetched = true;
             const bool need_mask = t0 + TT - 1 > wave_pmin;  // wave-uniform
             const int first = t0 + 4 * kg;  // this lane's first token of quarter 0
@@ -510,9 +639,10 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(PrefillParams 
             for (int g = 0; g < NG; ++g) {
 #pragma unroll
                 for (int b = 0; b < DB; ++b) {
-                    const uint16_t *vg = vt + vt_elem + 32 * g * VSTR + 16 * b;
+                    const uint16_t *vg = vt + vt_elem + 32 * g * VROW +
+                                         (DMA ? 16 * (b ^ vt_swz) : 16 * b);
                     const uint64_t lo = lds_read_tr16(vg);
-                    const uint64_t hi = lds_read_tr16(vg + 16 * VSTR);
+                    const uint64_t hi = lds_read_tr16(vg + 16 * VROW);
                     const u32x4 a = u32x4{(uint32_t)lo, (uint32_t)(lo >> 32), (uint32_t)hi,
                                           (uint32_t)(hi >> 32)};
 #pragma unroll
@@ -521,9 +651,21 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(PrefillParams 
                 }
             }
         }
-        if (!prefetched && tile + 1 < ntiles) load_tile(tile + 1);
-        if (tile + 1 < ntiles) store_tile(buf ^ 1, tile + 1);
+        if constexpr (DMA) {
+            if (tile + 1 < ntiles) dma_finish(buf ^ 1, tile + 1);
+        } else {
+            if (!prefetched && tile + 1 < ntiles) load_tile(tile + 1);
+            if (tile + 1 < ntiles) store_tile(buf ^ 1, tile + 1);
+        }
         __syncthreads();
+    };
+    if constexpr (DMA) {
+        for (int tile = 0; tile < ntiles; tile += 2) {
+            tile_step(tile, std::integral_constant<int, 0>{});
+            if (tile + 1 < ntiles) tile_step(tile + 1, std::integral_constant<int, 1>{});
+        }
+    } else {
+        for (int tile = 0; tile < ntiles; ++tile) tile_step(tile, tile & 1);
     }
     bad = __syncthreads_or(bad);
 
