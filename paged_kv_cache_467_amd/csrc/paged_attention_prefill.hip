@@ -104,10 +104,6 @@ __device__ inline uint32_t narrow_pair<F16>(float a, float b) {
 #endif
 // s_waitcnt operand: vector memory count 0, the other counters untouched
 constexpr int kWaitVmcnt0 = 0x0F70;
-// Cache policy of those loads: the default.  The row blocks of a (sequence,
-// kv head) unit read the same K/V tiles through L2, and the non-temporal
-// hint measured 5% slower on the chunked-prefill workload.
-constexpr int kDmaAux = 0;
 
 // K operands of the score products in flight ahead of their use (4 LDS
 // reads cover their latency; measured 2-3% faster than 1 on the chunked-
@@ -116,6 +112,28 @@ constexpr int kScoreReadAhead = 4;
 // Instruction classes of __builtin_amdgcn_sched_group_barrier's mask.
 constexpr int kSchedMfma = 0x008;
 constexpr int kSchedLdsRead = 0x100;
+
+// One load straight into LDS: 64 lanes x 16 bytes, lane l's at LDS byte
+// address lds + 16 l (M0 holds lds; one wait state after writing M0).
+// Written out in assembly: through the builtin, the compiler cannot order
+// the LDS write against the LDS reads in flight and waits for all of them
+// (lgkmcnt(0)) wherever it needs one (2-3% slower on the chunked-prefill
+// workload).  The caller waits for the load (vmcnt) itself before its
+// barrier.  Default cache policy: the row blocks of a (sequence, kv head)
+// unit read the same K/V tiles through L2, and the non-temporal hint
+// measured 5% slower.  M0 is a reserved register that the compiler does
+// not preserve around the statement; none of the code generated for these
+// kernels uses it otherwise.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ inline void load_to_lds16(const char *g, uint32_t lds) {
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+                 :: "v"(g), "s"(lds) : "memory", "m0");
+}
+#pragma clang diagnostic pop
+__device__ inline uint32_t lds_address(const uint16_t *p) {
+    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) uint16_t *)p;
+}
 
 // Transposing 8-byte LDS read (see the layout note at the top of the file).
 __device__ inline uint64_t lds_read_tr16(const uint16_t *p) {
@@ -377,14 +395,11 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(PrefillParams 
                            (int64_t)(th & (p.block_size - 1)) * p.row_stride_bytes;
         const char *kq = p.key_cache + qb;
         const char *vq = p.value_cache + qb;
-        typedef __attribute__((address_space(3))) void lds_void;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const int row0 = 16 * wave_s + 4 * j;  // the instruction's first tile row
-            __builtin_amdgcn_global_load_lds(kq + dma_k[j], (lds_void *)&kbuf(buf)[row0 * KROW],
-                                             16, 0, kDmaAux);
-            __builtin_amdgcn_global_load_lds(vq + dma_v[j], (lds_void *)&vbuf(buf)[row0 * VROW],
-                                             16, 0, kDmaAux);
+            load_to_lds16(kq + dma_k[j], lds_address(&kbuf(buf)[row0 * KROW]));
+            load_to_lds16(vq + dma_v[j], lds_address(&vbuf(buf)[row0 * VROW]));
         }
         fetch_ids(tile + 1);  // past the last tile: pmax's block again
     };
@@ -581,6 +596,7 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(PrefillParams 
             for (int mb = 0; mb < MB; ++mb) {
                 // raw scores; the scale (>= 0) enters with the exponent
                 float sc[NQ][4];
+                const int lim = pos[mb] - first;  // tokens 16 u + r past it are masked
 #pragma unroll
                 for (int u = 0; u < NQ; ++u)
 #pragma unroll
@@ -590,7 +606,7 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(PrefillParams 
                     for (int u = 0; u < NQ; ++u)
 #pragma unroll
                         for (int r = 0; r < 4; ++r)
-                            if (first + 16 * u + r > pos[mb]) sc[u][r] = -INFINITY;
+                            if (16 * u + r > lim) sc[u][r] = -INFINITY;
                 }
                 float mt = -INFINITY;
 #pragma unroll
@@ -617,7 +633,7 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(PrefillParams 
                     for (int u = 0; u < NQ; ++u)
 #pragma unroll
                         for (int r = 0; r < 4; ++r)
-                            if (first + 16 * u + r > pos[mb]) arg[u][r] = -INFINITY;
+                            if (16 * u + r > lim) arg[u][r] = -INFINITY;
                 }
                 uint32_t w[NQ][2];
 #pragma unroll
