@@ -123,7 +123,7 @@ constexpr int kSchedLdsRead = 0x100;
 // unit read the same K/V tiles through L2, and the non-temporal hint
 // measured 5% slower.  M0 is a reserved register that the compiler does
 // not preserve around the statement; none of the code generated for these
-// kernels uses it otherwise.
+// kernels uses it otherwise (a host test compiles this file and checks).
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"
 __device__ inline void load_to_lds16(const char *g, uint32_t lds) {
@@ -178,8 +178,9 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(PrefillParams 
     constexpr int VROW = DMA ? D : VSTR;
 
     // The two tile buffers.  With the loads straight to LDS each buffer is a
-    // variable of its own (the compiler then knows that loads into one do
-    // not touch reads of the other); otherwise one array of two.
+    // variable of its own and the tile loop names it by a compile-time
+    // constant, so that every LDS address of a tile is a fixed offset from
+    // one register; otherwise one array of two.
     constexpr int NKB = DMA ? 1 : 2;
     __shared__ __attribute__((aligned(16))) uint16_t k_lds[NKB][DMA ? 8 : TT * KROW];
     __shared__ __attribute__((aligned(16))) uint16_t v_lds[NKB][DMA ? 8 : TT * VROW];
@@ -533,10 +534,8 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(PrefillParams 
         }
     }
     // One tile: its scores, softmax and value product, with the next tile's
-    // loads in flight.  The LDS buffer is bufc: a compile-time constant when
-    // the loads go straight to LDS, so that the compiler can tell the next
-    // tile's loads (the other buffer) from this tile's reads and does not
-    // wait for them.
+    // loads in flight.  The LDS buffer is bufc, a compile-time constant when
+    // the loads go straight to LDS (the loop runs two tiles at a time).
     auto tile_step = [&](int tile, auto bufc) {
         const int buf = bufc;
         const int t0 = tb + tile * TT;
