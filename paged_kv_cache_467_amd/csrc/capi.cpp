@@ -133,6 +133,10 @@ DecodeParams decode_params(const void *query, const void *key_cache, const void 
     p.new_value = nullptr;
     p.slot_mapping = nullptr;
     p.num_slots = (int64_t)num_blocks * block_size;
+    p.query_start = nullptr;
+    p.total_q = 0;
+    p.max_query_len = 0;
+    p.mq_group = 0;
     return p;
 }
 
@@ -383,6 +387,28 @@ int paged_attn_prefill(const void *query, const void *key_cache, const void *val
         !aligned16(out) || !aligned4(block_tables) || !aligned4(context_lens) ||
         !aligned4(query_start))
         return PAGED_KV_ERR_BAD_SHAPE;
+    // A few new tokens per sequence -- every (new token, query head) row of
+    // a kv head in one 16-row tile -- and no split: the decode kernel's
+    // structure (one wave per kv head, the context read once per kv head)
+    // computes them, with a causal limit per row.
+    if (dtype != PAGED_KV_F32 && (int64_t)max_query_len * group <= pkv::kMultiQueryRows) {
+        const pkv::DecodePlan pl =
+            pkv::plan_decode(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
+                             max_blocks_per_seq, max_ctx, 0, dtype);
+        if (pl.status == PAGED_KV_OK && pl.num_partitions == 1 && pl.num_chunks == 0) {
+            pkv::DecodeParams d = pkv::decode_params(
+                query, key_cache, value_cache, block_tables, context_lens, scale, out, num_seqs,
+                num_q_heads, num_kv_heads, head_dim, block_size, num_blocks, max_blocks_per_seq,
+                pl, nullptr, 0, dtype);
+            d.query_start = query_start;
+            d.total_q = total_q;
+            d.max_query_len = max_query_len;
+            d.mq_group = group;
+            const hipError_t err = pkv::launch_decode_multiquery(
+                d, dtype, head_dim, static_cast<hipStream_t>(stream));
+            return err == hipSuccess ? PAGED_KV_OK : PAGED_KV_ERR_HIP;
+        }
+    }
     pkv::PrefillParams p;
     p.query = query;
     p.key_cache = static_cast<const char *>(key_cache);

@@ -63,6 +63,14 @@ struct DecodeParams {
     const char *new_value;
     const int32_t *slot_mapping;
     int64_t num_slots;          // num_blocks * block_size
+    // Multi-token decode (launch_decode_multiquery only; null otherwise):
+    // sequence s's new tokens are query rows query_start[s] ..
+    // query_start[s + 1] - 1 (at most max_query_len of them), token i seeing
+    // positions 0 .. L - q_len + i; mq_group = num_q_heads / num_kv_heads.
+    const int32_t *query_start;
+    int total_q;                // query rows in all
+    int max_query_len;
+    int mq_group;
 };
 
 // dtype codes match paged_kv_dtype; kernel = 0 VALU, 1 MFMA.
@@ -76,6 +84,13 @@ struct DeviceOccupancy {
 };
 DeviceOccupancy decode_occupancy(int dtype, int head_dim, int group, int block_size,
                                  int heads_per_group);
+// The multi-token decode: paged_attn_prefill's computation for a batch with
+// max_query_len * group <= 16 and no split, on the decode MFMA kernel (one
+// wave per kv head, every (new token, query head) row of the kv head in one
+// 16-row tile).  16-bit types only.
+hipError_t launch_decode_multiquery(const DecodeParams &p, int dtype, int head_dim,
+                                    hipStream_t stream);
+constexpr int kMultiQueryRows = 16;
 // Which decode kernel launch_decode uses for this shape.
 int decode_kernel_choice(int dtype, int head_dim, int group);
 

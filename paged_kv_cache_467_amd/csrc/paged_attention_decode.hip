@@ -721,11 +721,16 @@ __device__ inline void write_result4(const DecodeParams &p, const WorkItem &w, i
     }
 }
 
-template <class T, int D, int G, bool BT, bool BAL, bool FW = false>
+// MQ: the multi-token decode (launch_decode_multiquery).  G is then the
+// 16 rows of the tile, row v = (new token v / mq_group, query head
+// v % mq_group of the kv head), each with its own last visible position;
+// no split, no fused write.
+template <class T, int D, int G, bool BT, bool BAL, bool FW = false, bool MQ = false>
 __global__ __launch_bounds__(kMaxDecodeThreads) void decode_mfma_kernel(DecodeParams p) {
     static_assert(T::kBytes == 2, "MFMA path is for 16-bit element types");
     static_assert(!(FW && BAL), "the fused write takes the plain split");
-    static_assert(G == 2 || G == 4 || G == 8, "group size");
+    static_assert(MQ ? G == kMultiQueryRows && !FW && !BAL : (G == 2 || G == 4 || G == 8),
+                  "group size");
     constexpr int KS = D / 32;        // MFMA k-steps per tile
     constexpr int CPR = D / 8;        // 16-byte chunks per row
     constexpr int TPI = kWave / CPR;  // tokens per V load instruction
@@ -747,6 +752,10 @@ __global__ __launch_bounds__(kMaxDecodeThreads) void decode_mfma_kernel(DecodePa
     // K tiles turned from row layout to the B layout, and V tiles: one slice
     // per wave, kv_lds_wave_bytes<D>() each (dynamic, sized by the launch)
     extern __shared__ __attribute__((aligned(16))) char k_lds[];
+
+    // MQ: the sequence's first query row, its new tokens computed (at most
+    // max_query_len) and the last position its first new token sees
+    int mq_q0 = 0, mq_nq = 0, mq_lim0 = 0;
 
     // one partition (or, with the balanced split, one segment) of a sequence
     auto segment = [&](const WorkItem &w) {
@@ -785,7 +794,17 @@ __global__ __launch_bounds__(kMaxDecodeThreads) void decode_mfma_kernel(DecodePa
 
     // A operand: query head (kt % G) of this kv head's group
     u32x4 qa[KS];
-    {
+    if constexpr (MQ) {
+        // row kt: new token kt / mq_group, query head kt % mq_group; rows
+        // past the sequence's new tokens are zero
+        const int i = kt / p.mq_group;
+        const char *qrow = static_cast<const char *>(p.query) +
+                           (((int64_t)(mq_q0 + i) * p.num_q_heads + w.kvh * p.mq_group +
+                             kt % p.mq_group) * D) * 2;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+            qa[ks] = i < mq_nq ? load16(qrow + 16 * (rg + 4 * ks)) : u32x4{0, 0, 0, 0};
+    } else {
         const char *qrow = static_cast<const char *>(p.query) +
                            (((int64_t)w.s * p.num_q_heads + w.kvh * G + kt % G) * D) * 2;
 #pragma unroll
@@ -797,6 +816,16 @@ __global__ __launch_bounds__(kMaxDecodeThreads) void decode_mfma_kernel(DecodePa
     for (int r = 0; r < 4; ++r) {
         m[r] = -INFINITY;
         l[r] = 0.0f;
+    }
+    // MQ: the last position result row 4 * rg + r sees (-1: a row past the
+    // new tokens, which sees nothing and is not written)
+    int lim[4] = {0, 0, 0, 0};
+    if constexpr (MQ) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int i = (4 * rg + r) / p.mq_group;
+            lim[r] = i < mq_nq ? mq_lim0 + i : -1;
+        }
     }
     float acc[PVM ? 1 : G][8];
     f32x4 accm[PVM ? DB : 1];
@@ -922,7 +951,10 @@ __global__ __launch_bounds__(kMaxDecodeThreads) void decode_mfma_kernel(DecodePa
         bool up = false;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-            sc[r] = valid ? s[r] * p.scale_log2 : -INFINITY;
+            if constexpr (MQ)  // causal: each row's own last position (always < tok_end)
+                sc[r] = w.tok_begin + tile * TILE + kt <= lim[r] ? s[r] * p.scale_log2 : -INFINITY;
+            else
+                sc[r] = valid ? s[r] * p.scale_log2 : -INFINITY;
             up |= sc[r] > m[r];
         }
         // Every head is held by some lane, so "no lane's score exceeds its
@@ -941,7 +973,8 @@ __global__ __launch_bounds__(kMaxDecodeThreads) void decode_mfma_kernel(DecodePa
         float pr[4];
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-            pr[r] = fast_exp2(sc[r] - m[r]);
+            // (MQ: a masked score is 0 also in a row that has seen nothing)
+            pr[r] = MQ && sc[r] == -INFINITY ? 0.0f : fast_exp2(sc[r] - m[r]);
             l[r] += pr[r];
         }
         if (owns_rows) {
@@ -1025,7 +1058,31 @@ __global__ __launch_bounds__(kMaxDecodeThreads) void decode_mfma_kernel(DecodePa
         }
     }
     __builtin_amdgcn_wave_barrier();
-    if constexpr (PVM) {
+    if constexpr (MQ) {
+        // lane (row ph, d group pkg) holds d = 16 b + 4 pkg .. + 3 of new
+        // token ph / mq_group, query head ph % mq_group; no split
+        const int i = ph / p.mq_group;
+        if (i < mq_nq) {
+            const float lh = lex[wave][ph];
+            const float inv = lh > 0.0f ? 1.0f / lh : 0.0f;
+            const int64_t o = ((int64_t)(mq_q0 + i) * p.num_q_heads + w.kvh * p.mq_group +
+                               ph % p.mq_group) * D;
+#pragma unroll
+            for (int b = 0; b < DB; ++b) {
+                uint64_t c;
+                if (bad) {
+                    c = ((uint64_t)T::kNanPair << 32) | T::kNanPair;
+                } else {
+                    const float v[8] = {accm[b][0] * inv, accm[b][1] * inv, accm[b][2] * inv,
+                                        accm[b][3] * inv, 0.0f, 0.0f, 0.0f, 0.0f};
+                    const u32x4 n = T::narrow_chunk(v);
+                    c = (uint64_t)n[0] | ((uint64_t)n[1] << 32);
+                }
+                *reinterpret_cast<uint64_t *>(static_cast<char *>(p.out) +
+                                              (o + 16 * b + 4 * pkg) * T::kBytes) = c;
+            }
+        }
+    } else if constexpr (PVM) {
         // lane (head ph, d group pkg) holds d = 16 b + 4 pkg .. + 3
         if (ph < G) {
             const float mh = aex[wave][ph], lh = lex[wave][ph];
@@ -1046,6 +1103,28 @@ __global__ __launch_bounds__(kMaxDecodeThreads) void decode_mfma_kernel(DecodePa
         __shared__ int32_t seq_start[kBalancedMaxSeqs + 1];
         __shared__ int32_t wave_tot[kMaxDecodeWaves];
         for_each_segment(p, seq_start, wave_tot, segment);
+    } else if constexpr (MQ) {
+        // the prefill's rules: rows of a sequence whose query range cannot be
+        // identified are not written; a length outside [q_len,
+        // max_context_len] gives NaN rows
+        const WorkItem w = work_item(p);
+        const int qs0 = p.query_start[w.s], qs1 = p.query_start[w.s + 1];
+        if (qs0 < 0 || qs1 > p.total_q || qs1 < qs0) return;
+        const int q_len = qs1 - qs0;
+        mq_q0 = qs0;
+        mq_nq = q_len < p.max_query_len ? q_len : p.max_query_len;
+        mq_lim0 = w.context_len - q_len;
+        if (mq_nq == 0) return;
+        if (w.bad_len || w.context_len < q_len) {
+            const int n = mq_nq * p.mq_group * D;  // this wave's kv head's rows
+            for (int e = threadIdx.x % kWave; e < n; e += kWave) {
+                const int i = e / (p.mq_group * D), rest = e % (p.mq_group * D);
+                T::store_nan(p.out, ((int64_t)(qs0 + i) * p.num_q_heads +
+                                     (int64_t)w.kvh * p.mq_group) * D + rest);
+            }
+            return;
+        }
+        segment(w);
     } else {
         const WorkItem w = work_item(p);
         if constexpr (FW) {
@@ -1421,6 +1500,44 @@ DeviceOccupancy decode_occupancy(int dtype, int head_dim, int group, int block_s
     r.compute_units = n_cu > 0 ? n_cu : 0;
     r.workgroups_per_cu = per_cu > 0 ? per_cu : 0;
     return r;
+}
+
+namespace {
+template <class T, int D>
+hipError_t launch_multiquery_d(const DecodeParams &p, hipStream_t stream) {
+    const unsigned grid = (unsigned)((int64_t)p.num_seqs * p.num_head_groups);
+    if (grid == 0) return hipSuccess;
+    const unsigned threads = (unsigned)(p.heads_per_group * kWave);
+    const size_t lds = p.heads_per_group * kv_lds_wave_bytes<D, kMultiQueryRows>();
+    if (p.block_size >= 16)
+        hipLaunchKernelGGL((decode_mfma_kernel<T, D, kMultiQueryRows, true, false, false, true>),
+                           dim3(grid), dim3(threads), lds, stream, p);
+    else
+        hipLaunchKernelGGL((decode_mfma_kernel<T, D, kMultiQueryRows, false, false, false, true>),
+                           dim3(grid), dim3(threads), lds, stream, p);
+    return hipGetLastError();
+}
+template <class T>
+hipError_t launch_multiquery_t(const DecodeParams &p, int head_dim, hipStream_t stream) {
+    switch (head_dim) {
+        case 64: return launch_multiquery_d<T, 64>(p, stream);
+        case 128: return launch_multiquery_d<T, 128>(p, stream);
+        case 256: return launch_multiquery_d<T, 256>(p, stream);
+        default: return hipErrorInvalidValue;
+    }
+}
+}  // namespace
+
+hipError_t launch_decode_multiquery(const DecodeParams &p, int dtype, int head_dim,
+                                    hipStream_t stream) {
+    if (p.heads_per_group < 1 || p.heads_per_group > kMaxDecodeWaves || p.num_partitions != 1 ||
+        p.num_chunks != 0 || p.mq_group < 1 || p.mq_group * p.max_query_len > kMultiQueryRows)
+        return hipErrorInvalidValue;
+    switch (dtype) {
+        case 1: return launch_multiquery_t<F16>(p, head_dim, stream);
+        case 2: return launch_multiquery_t<BF16>(p, head_dim, stream);
+        default: return hipErrorInvalidValue;
+    }
 }
 
 hipError_t launch_decode(const DecodeParams &p, int dtype, int head_dim, int group, int kernel,
