@@ -512,6 +512,89 @@ def bench_prefill(args) -> int:
     return 0
 
 
+def bench_multi_token(args) -> int:
+    """Multi-token decode: the Llama-3-8B-shaped decode batch (its pool,
+    tables and lengths) with the last --query-len positions of every
+    sequence as new queries, through paged_attn_prefill, which with at most
+    16 (new token, query head) rows per kv head and no split runs the decode
+    kernel's structure.  Bound by HBM like the decode: the algorithmic bytes
+    are every context's K/V read once per kv head, plus the queries, outputs,
+    tables and lengths."""
+    import numpy as np
+    import torch
+
+    import oracle
+    from paged_kv_cache_467_amd import binding, tensors, workloads as W
+
+    name = "llama3_8b_gqa_bf16"
+    dev = torch.device("cuda:0")
+    base = W.make_workload(name, values=False)
+    S, Hq, Hkv, D = base.num_seqs, base.num_q_heads, base.num_kv_heads, base.head_dim
+    ql = args.query_len
+    qs_host = np.arange(0, S * ql + 1, ql, dtype=np.int32)
+    dt = tensors.TORCH_DTYPE[base.dtype]
+    pool_shape = (base.num_blocks, base.block_size, Hkv, D)
+    copies = [(torch.randn(pool_shape, device=dev).to(dt), torch.randn(pool_shape, device=dev).to(dt))
+              for _ in range(max(1, args.copies))]
+    query = torch.randn((S * ql, Hq, D), device=dev).to(dt)
+    out = torch.empty_like(query)
+    bt = tensors.int32(base.block_tables, dev)
+    cl = tensors.int32(base.context_lens, dev)
+    qs = tensors.int32(qs_host, dev)
+
+    def step(i):
+        kc, vc = copies[i % len(copies)]
+        binding.paged_attn_prefill(query, kc, vc, bt, cl, qs, base.scale, out, max_query_len=ql,
+                                   max_context_len=base.max_context_len)
+
+    for i in range(SETTLE_LAUNCHES + args.warmup):
+        step(i)
+    elapsed, avg = time_back_to_back(step, args.warmup, max(args.steps, MIN_LAUNCH_PASS))
+    tokens = int(base.context_lens.sum())
+    nbytes = (tokens * Hkv * D * 2 * 2 + 2 * S * ql * Hq * D * 2
+              + int(np.ceil(base.context_lens / base.block_size).sum()) * 4 + S * 4 + (S + 1) * 4)
+    gbps = nbytes / (avg * 1e-3) / 1e9
+    result = {
+        "metric": "multi-token decode: achieved HBM GB/s (% of peak)",
+        "value": round(gbps, 2), "unit": "GB/s", "n_gpus": 1,
+        "steps": max(args.steps, MIN_LAUNCH_PASS), "warmup": args.warmup,
+        "ms_per_step": round(avg, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": base.dtype, "data": "synthetic",
+        "config": {"workload": f"{name} with {ql} new tokens per sequence", "num_seqs": S,
+                   "new_tokens": S * ql, "context_tokens": tokens, "num_q_heads": Hq,
+                   "num_kv_heads": Hkv, "head_dim": D, "block_size": base.block_size,
+                   "pool_copies": len(copies)},
+        "multi_token_ms": round(avg, 5),
+        "algorithmic_bytes_per_launch": nbytes,
+        "roofline": {"bound": "hbm", "achieved": round(gbps, 2), "peak": HBM_PEAK_GBPS,
+                     "unit": "GB/s", "frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic": None,
+                     "kernel": "paged_attn_prefill (multi-token decode)",
+                     "algorithmic_bytes_per_launch": nbytes},
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        host = W.make_workload(name)
+        rng = np.random.default_rng(0)
+        hq = rng.standard_normal((S * ql, Hq, D)).astype(np.float32)
+        hq = (hq.view(np.uint32) >> 16).astype(np.uint16)   # bf16 bits
+        orc = oracle.default()
+        orc.set_threads(len(os.sched_getaffinity(0)))
+        times = []
+        while len(times) < 3 or sum(times) < 5.0:
+            t1 = time.perf_counter()
+            orc.paged_attention_prefill(hq, host.key_cache, host.value_cache, host.block_tables,
+                                        host.context_lens, qs_host, host.scale, host.dtype)
+            times.append(time.perf_counter() - t1)
+        t = statistics.median(times)
+        result["cpu_baseline"] = {
+            "value": round(nbytes / t / 1e9, 3), "unit": "GB/s", "cores": orc.max_threads(),
+            "kind": "oracle",
+            "sample": f"the whole batch ({S * ql} new tokens), fp64, median of {len(times)} "
+                      f"runs of {t:.3f} s"}
+    print(json.dumps(result), flush=True)
+    return 0
+
+
 DEFAULT_WORKLOAD = "llama3_8b_gqa_bf16"
 # Untimed decode launches before anything is measured, whatever --warmup
 # says: a fresh GPU needs a few hundred launches (tens of ms of work) to
@@ -725,14 +808,18 @@ def main() -> int:
     ap.add_argument("--prefill-dtype", choices=("bf16", "f16", "f32"), default=None,
                     help="--op prefill: element type of the pool and queries (default: the "
                          "workload's, bf16)")
+    ap.add_argument("--query-len", type=int, default=4,
+                    help="--op multi_token: new tokens per sequence (default 4: with 4 query "
+                         "heads per kv head, 16 rows per kv head)")
     ap.add_argument("--op", choices=("decode", "copy_blocks", "prefill", "swap_out", "swap_in",
-                                     "prefix_cache"),
+                                     "prefix_cache", "multi_token"),
                     default="decode",
                     help="decode: the decode step (default); copy_blocks: the copy-on-write "
                          "block copy on the same pool; prefill: multi-token attention on the "
                          "chunked-prefill workload; swap_out / swap_in: block swap between the "
                          "pool and pinned host memory; prefix_cache: block hashing and "
-                         "cached-prefix lookup")
+                         "cached-prefix lookup; multi_token: a few new tokens per sequence "
+                         "on the decode batch")
     ap.add_argument("--pairs", type=int, default=2048, help="block pairs per copy_blocks step")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="also run one plain device copy of this many MiB (counter calibration)")
@@ -762,6 +849,8 @@ def main() -> int:
         return bench_copy_blocks(args)
     if args.op == "prefill":
         return bench_prefill(args)
+    if args.op == "multi_token":
+        return bench_multi_token(args)
     # Every workload's device inputs are allocated up front, before anything
     # is freed: pools allocated after others were freed measured 3-5% slower
     # for the same launches (the first workload allocated in a process was
