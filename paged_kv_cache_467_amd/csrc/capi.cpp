@@ -387,11 +387,12 @@ int paged_attn_prefill(const void *query, const void *key_cache, const void *val
         !aligned16(out) || !aligned4(block_tables) || !aligned4(context_lens) ||
         !aligned4(query_start))
         return PAGED_KV_ERR_BAD_SHAPE;
-    // A few new tokens per sequence -- every (new token, query head) row of
-    // a kv head in one 16-row tile -- and no split: the decode kernel's
+    // A few new tokens per sequence -- the (new token, query head) rows of a
+    // kv head in one or two 16-row tiles -- and no split: the decode kernel's
     // structure (one wave per kv head, the context read once per kv head)
     // computes them, with a causal limit per row.
-    if (dtype != PAGED_KV_F32 && (int64_t)max_query_len * group <= pkv::kMultiQueryRows) {
+    const int mq_max_rows = head_dim <= 128 ? 2 * pkv::kMultiQueryRows : pkv::kMultiQueryRows;
+    if (dtype != PAGED_KV_F32 && (int64_t)max_query_len * group <= mq_max_rows) {
         const pkv::DecodePlan pl =
             pkv::plan_decode(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
                              max_blocks_per_seq, max_ctx, 0, dtype);

@@ -85,9 +85,9 @@ struct DeviceOccupancy {
 DeviceOccupancy decode_occupancy(int dtype, int head_dim, int group, int block_size,
                                  int heads_per_group);
 // The multi-token decode: paged_attn_prefill's computation for a batch with
-// max_query_len * group <= 16 and no split, on the decode MFMA kernel (one
-// wave per kv head, every (new token, query head) row of the kv head in one
-// 16-row tile).  16-bit types only.
+// max_query_len * group <= 32 and no split, on the decode MFMA kernel (one
+// wave per kv head, the (new token, query head) rows of the kv head in one
+// or two 16-row tiles).  16-bit types only.
 hipError_t launch_decode_multiquery(const DecodeParams &p, int dtype, int head_dim,
                                     hipStream_t stream);
 constexpr int kMultiQueryRows = 16;

@@ -729,8 +729,12 @@ template <class T, int D, int G, bool BT, bool BAL, bool FW = false, bool MQ = f
 __global__ __launch_bounds__(kMaxDecodeThreads) void decode_mfma_kernel(DecodeParams p) {
     static_assert(T::kBytes == 2, "MFMA path is for 16-bit element types");
     static_assert(!(FW && BAL), "the fused write takes the plain split");
-    static_assert(MQ ? G == kMultiQueryRows && !FW && !BAL : (G == 2 || G == 4 || G == 8),
+    static_assert(MQ ? (G == kMultiQueryRows || G == 2 * kMultiQueryRows) && !FW && !BAL
+                     : (G == 2 || G == 4 || G == 8),
                   "group size");
+    // row tiles of 16 per wave: MQ with 32 rows holds two, each its own
+    // score and value products over the same K and V operands
+    constexpr int NT = MQ ? G / kMultiQueryRows : 1;
     constexpr int KS = D / 32;        // MFMA k-steps per tile
     constexpr int CPR = D / 8;        // 16-byte chunks per row
     constexpr int TPI = kWave / CPR;  // tokens per V load instruction
@@ -793,45 +797,55 @@ __global__ __launch_bounds__(kMaxDecodeThreads) void decode_mfma_kernel(DecodePa
     const bool owns_rows = 4 * rg < G;
 
     // A operand: query head (kt % G) of this kv head's group
-    u32x4 qa[KS];
+    u32x4 qa[NT][KS];
     if constexpr (MQ) {
-        // row kt: new token kt / mq_group, query head kt % mq_group; rows
-        // past the sequence's new tokens are zero
-        const int i = kt / p.mq_group;
-        const char *qrow = static_cast<const char *>(p.query) +
-                           (((int64_t)(mq_q0 + i) * p.num_q_heads + w.kvh * p.mq_group +
-                             kt % p.mq_group) * D) * 2;
+        // row 16 t + kt of tile t: new token (16 t + kt) / mq_group, query
+        // head (16 t + kt) % mq_group; rows past the sequence's new tokens
+        // are zero
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks)
-            qa[ks] = i < mq_nq ? load16(qrow + 16 * (rg + 4 * ks)) : u32x4{0, 0, 0, 0};
+        for (int t = 0; t < NT; ++t) {
+            const int v = kMultiQueryRows * t + kt, i = v / p.mq_group;
+            const char *qrow = static_cast<const char *>(p.query) +
+                               (((int64_t)(mq_q0 + i) * p.num_q_heads + w.kvh * p.mq_group +
+                                 v % p.mq_group) * D) * 2;
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks)
+                qa[t][ks] = i < mq_nq ? load16(qrow + 16 * (rg + 4 * ks)) : u32x4{0, 0, 0, 0};
+        }
     } else {
         const char *qrow = static_cast<const char *>(p.query) +
                            (((int64_t)w.s * p.num_q_heads + w.kvh * G + kt % G) * D) * 2;
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) qa[ks] = load16(qrow + 16 * (rg + 4 * ks));
+        for (int ks = 0; ks < KS; ++ks) qa[0][ks] = load16(qrow + 16 * (rg + 4 * ks));
     }
-    // result row 4 * rg + r holds query head (4 * rg + r) % G
-    float m[4], l[4];
+    // result row 4 * rg + r (of tile t) holds query head (4 * rg + r) % G
+    float m[NT][4], l[NT][4];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-        m[r] = -INFINITY;
-        l[r] = 0.0f;
-    }
-    // MQ: the last position result row 4 * rg + r sees (-1: a row past the
-    // new tokens, which sees nothing and is not written)
-    int lim[4] = {0, 0, 0, 0};
-    if constexpr (MQ) {
+    for (int t = 0; t < NT; ++t)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-            const int i = (4 * rg + r) / p.mq_group;
-            lim[r] = i < mq_nq ? mq_lim0 + i : -1;
+            m[t][r] = -INFINITY;
+            l[t][r] = 0.0f;
         }
+    // MQ: the last position result row 16 t + 4 * rg + r sees (-1: a row past
+    // the new tokens, which sees nothing and is not written)
+    int lim[NT][4] = {};
+    if constexpr (MQ) {
+#pragma unroll
+        for (int t = 0; t < NT; ++t)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int i = (kMultiQueryRows * t + 4 * rg + r) / p.mq_group;
+                lim[t][r] = i < mq_nq ? mq_lim0 + i : -1;
+            }
     }
     float acc[PVM ? 1 : G][8];
-    f32x4 accm[PVM ? DB : 1];
+    f32x4 accm[NT][PVM ? DB : 1];
     if constexpr (PVM) {
 #pragma unroll
-        for (int b = 0; b < DB; ++b) accm[b] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+        for (int t = 0; t < NT; ++t)
+#pragma unroll
+            for (int b = 0; b < DB; ++b) accm[t][b] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
     } else {
 #pragma unroll
         for (int g = 0; g < G; ++g)
@@ -942,51 +956,66 @@ __global__ __launch_bounds__(kMaxDecodeThreads) void decode_mfma_kernel(DecodePa
         u32x4 kb[KS];
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) kb[ks] = *reinterpret_cast<const u32x4 *>(k_rd + 64 * ks);
-        f32x4 s = {0.0f, 0.0f, 0.0f, 0.0f};
+        f32x4 s[NT];
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) s = mfma16x16x32<T>(qa[ks], kb[ks], s);
+        for (int t = 0; t < NT; ++t) {
+            s[t] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) s[t] = mfma16x16x32<T>(qa[t][ks], kb[ks], s[t]);
+        }
 
         const bool valid = full || w.tok_begin + tile * TILE + kt < w.tok_end;
-        float sc[4];
+        float sc[NT][4];
         bool up = false;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            if constexpr (MQ)  // causal: each row's own last position (always < tok_end)
-                sc[r] = w.tok_begin + tile * TILE + kt <= lim[r] ? s[r] * p.scale_log2 : -INFINITY;
-            else
-                sc[r] = valid ? s[r] * p.scale_log2 : -INFINITY;
-            up |= sc[r] > m[r];
-        }
+        for (int t = 0; t < NT; ++t)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                if constexpr (MQ)  // causal: each row's own last position (always < tok_end)
+                    sc[t][r] = w.tok_begin + tile * TILE + kt <= lim[t][r] ? s[t][r] * p.scale_log2
+                                                                         : -INFINITY;
+                else
+                    sc[t][r] = valid ? s[t][r] * p.scale_log2 : -INFINITY;
+                up |= sc[t][r] > m[t][r];
+            }
         // Every head is held by some lane, so "no lane's score exceeds its
         // row's max" means no head's max moves in this tile.
         const bool rescale = __builtin_amdgcn_ballot_w64(up) != 0;
         if (rescale) {
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const float mn = vmax(m[r], group_max<16>(sc[r]));  // 16 tokens of the tile
-                const float alpha = fast_exp2(m[r] - mn);          // 0 on the first tile
-                m[r] = mn;
-                l[r] *= alpha;
-                if (r < HW && owns_rows && kt == 0) aex[wave][4 * rg + r] = alpha;
-            }
-        }
-        float pr[4];
+            for (int t = 0; t < NT; ++t)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            // (MQ: a masked score is 0 also in a row that has seen nothing)
-            pr[r] = MQ && sc[r] == -INFINITY ? 0.0f : fast_exp2(sc[r] - m[r]);
-            l[r] += pr[r];
+                for (int r = 0; r < 4; ++r) {
+                    const float mn = vmax(m[t][r], group_max<16>(sc[t][r]));  // 16 tokens
+                    const float alpha = fast_exp2(m[t][r] - mn);  // 0 on the first tile
+                    m[t][r] = mn;
+                    l[t][r] *= alpha;
+                    if (r < HW && owns_rows && kt == 0)
+                        aex[wave][kMultiQueryRows * t + 4 * rg + r] = alpha;
+                }
         }
+        float pr[NT][4];
+#pragma unroll
+        for (int t = 0; t < NT; ++t)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                // (MQ: a masked score is 0 also in a row that has seen nothing)
+                pr[t][r] = MQ && sc[t][r] == -INFINITY ? 0.0f : fast_exp2(sc[t][r] - m[t][r]);
+                l[t][r] += pr[t][r];
+            }
         if (owns_rows) {
             if constexpr (PVM) {
 #pragma unroll
-                for (int r = 0; r < HW; ++r) pt[(4 * rg + r) * TILE + kt] = pr[r];
+                for (int t = 0; t < NT; ++t)
+#pragma unroll
+                    for (int r = 0; r < HW; ++r)
+                        pt[(kMultiQueryRows * t + 4 * rg + r) * TILE + kt] = pr[t][r];
             } else if constexpr (HW == 4) {
                 *reinterpret_cast<f32x4 *>(&pex[wave][kt][4 * rg]) =
-                    f32x4{pr[0], pr[1], pr[2], pr[3]};
+                    f32x4{pr[0][0], pr[0][1], pr[0][2], pr[0][3]};
             } else {
 #pragma unroll
-                for (int r = 0; r < HW; ++r) pex[wave][kt][4 * rg + r] = pr[r];
+                for (int r = 0; r < HW; ++r) pex[wave][kt][4 * rg + r] = pr[0][r];
             }
         }
         // The weights were written by this wave; LDS executes a wave's
@@ -996,16 +1025,29 @@ __global__ __launch_bounds__(kMaxDecodeThreads) void decode_mfma_kernel(DecodePa
             // lane (head ph, tokens 4 pkg .. 4 pkg + 3): B = P^T; heads past
             // G (columns no result reads) get zero weights
             if (rescale) {
-                const float a = ph < G ? aex[wave][ph] : 1.0f;
 #pragma unroll
-                for (int b = 0; b < DB; ++b) accm[b] *= a;
+                for (int t = 0; t < NT; ++t) {
+                    const int hr = kMultiQueryRows * t + ph;
+                    const float a = hr < G ? aex[wave][hr] : 1.0f;
+#pragma unroll
+                    for (int b = 0; b < DB; ++b) accm[t][b] *= a;
+                }
             }
-            const f32x4 wq = ph < G ? *reinterpret_cast<const f32x4 *>(&pt[ph * TILE + 4 * pkg])
-                                    : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-            const uint64_t bw = narrow4<T>(wq);
+            uint64_t bw[NT];
 #pragma unroll
-            for (int b = 0; b < DB; ++b)
-                accm[b] = mfma16x16x16<T>(lds_read_tr16(v_tr + 32 * b), bw, accm[b]);
+            for (int t = 0; t < NT; ++t) {
+                const int hr = kMultiQueryRows * t + ph;
+                const f32x4 wq = hr < G
+                                     ? *reinterpret_cast<const f32x4 *>(&pt[hr * TILE + 4 * pkg])
+                                     : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+                bw[t] = narrow4<T>(wq);
+            }
+#pragma unroll
+            for (int b = 0; b < DB; ++b) {
+                const uint64_t va = lds_read_tr16(v_tr + 32 * b);
+#pragma unroll
+                for (int t = 0; t < NT; ++t) accm[t][b] = mfma16x16x16<T>(va, bw[t], accm[t][b]);
+            }
         } else {
             if (rescale) {
                 float alpha[G];
@@ -1043,7 +1085,9 @@ __global__ __launch_bounds__(kMaxDecodeThreads) void decode_mfma_kernel(DecodePa
     // l: sum over the 16 tokens of each row; acc: over the value token
     // slots (the value MFMA sums over the tokens itself).
 #pragma unroll
-    for (int r = 0; r < 4; ++r) l[r] = group_sum<16>(l[r]);
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) l[t][r] = group_sum<16>(l[t][r]);
     if constexpr (!PVM) {
 #pragma unroll
         for (int g = 0; g < G; ++g)
@@ -1052,30 +1096,36 @@ __global__ __launch_bounds__(kMaxDecodeThreads) void decode_mfma_kernel(DecodePa
     }
     if (kt == 0 && owns_rows) {
 #pragma unroll
-        for (int r = 0; r < HW; ++r) {
-            aex[wave][4 * rg + r] = m[r];
-            lex[wave][4 * rg + r] = l[r];
-        }
+        for (int t = 0; t < NT; ++t)
+#pragma unroll
+            for (int r = 0; r < HW; ++r) {
+                aex[wave][kMultiQueryRows * t + 4 * rg + r] = m[t][r];
+                lex[wave][kMultiQueryRows * t + 4 * rg + r] = l[t][r];
+            }
     }
     __builtin_amdgcn_wave_barrier();
     if constexpr (MQ) {
-        // lane (row ph, d group pkg) holds d = 16 b + 4 pkg .. + 3 of new
-        // token ph / mq_group, query head ph % mq_group; no split
-        const int i = ph / p.mq_group;
-        if (i < mq_nq) {
-            const float lh = lex[wave][ph];
+        // lane (row 16 t + ph, d group pkg) holds d = 16 b + 4 pkg .. + 3 of
+        // new token (16 t + ph) / mq_group, query head (16 t + ph) %
+        // mq_group; no split
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+            const int v = kMultiQueryRows * t + ph, i = v / p.mq_group;
+            if (i >= mq_nq) continue;
+            const float lh = lex[wave][v];
             const float inv = lh > 0.0f ? 1.0f / lh : 0.0f;
             const int64_t o = ((int64_t)(mq_q0 + i) * p.num_q_heads + w.kvh * p.mq_group +
-                               ph % p.mq_group) * D;
+                               v % p.mq_group) * D;
 #pragma unroll
             for (int b = 0; b < DB; ++b) {
                 uint64_t c;
                 if (bad) {
                     c = ((uint64_t)T::kNanPair << 32) | T::kNanPair;
                 } else {
-                    const float v[8] = {accm[b][0] * inv, accm[b][1] * inv, accm[b][2] * inv,
-                                        accm[b][3] * inv, 0.0f, 0.0f, 0.0f, 0.0f};
-                    const u32x4 n = T::narrow_chunk(v);
+                    const float x[8] = {accm[t][b][0] * inv, accm[t][b][1] * inv,
+                                        accm[t][b][2] * inv, accm[t][b][3] * inv,
+                                        0.0f, 0.0f, 0.0f, 0.0f};
+                    const u32x4 n = T::narrow_chunk(x);
                     c = (uint64_t)n[0] | ((uint64_t)n[1] << 32);
                 }
                 *reinterpret_cast<uint64_t *>(static_cast<char *>(p.out) +
@@ -1088,7 +1138,7 @@ __global__ __launch_bounds__(kMaxDecodeThreads) void decode_mfma_kernel(DecodePa
             const float mh = aex[wave][ph], lh = lex[wave][ph];
 #pragma unroll
             for (int b = 0; b < DB; ++b)
-                write_result4<T, D>(p, w, w.kvh * G + ph, 16 * b + 4 * pkg, accm[b], mh, lh,
+                write_result4<T, D>(p, w, w.kvh * G + ph, 16 * b + 4 * pkg, accm[0][b], mh, lh,
                                     bad, b == 0 && pkg == 0);
         }
     } else if (vtg == 0) {
@@ -1503,19 +1553,29 @@ DeviceOccupancy decode_occupancy(int dtype, int head_dim, int group, int block_s
 }
 
 namespace {
-template <class T, int D>
-hipError_t launch_multiquery_d(const DecodeParams &p, hipStream_t stream) {
+template <class T, int D, int R>
+hipError_t launch_multiquery_r(const DecodeParams &p, hipStream_t stream) {
     const unsigned grid = (unsigned)((int64_t)p.num_seqs * p.num_head_groups);
     if (grid == 0) return hipSuccess;
     const unsigned threads = (unsigned)(p.heads_per_group * kWave);
-    const size_t lds = p.heads_per_group * kv_lds_wave_bytes<D, kMultiQueryRows>();
+    const size_t lds = p.heads_per_group * kv_lds_wave_bytes<D, R>();
     if (p.block_size >= 16)
-        hipLaunchKernelGGL((decode_mfma_kernel<T, D, kMultiQueryRows, true, false, false, true>),
-                           dim3(grid), dim3(threads), lds, stream, p);
+        hipLaunchKernelGGL((decode_mfma_kernel<T, D, R, true, false, false, true>), dim3(grid),
+                           dim3(threads), lds, stream, p);
     else
-        hipLaunchKernelGGL((decode_mfma_kernel<T, D, kMultiQueryRows, false, false, false, true>),
-                           dim3(grid), dim3(threads), lds, stream, p);
+        hipLaunchKernelGGL((decode_mfma_kernel<T, D, R, false, false, false, true>), dim3(grid),
+                           dim3(threads), lds, stream, p);
     return hipGetLastError();
+}
+// one 16-row tile per wave, or two (17..32 rows; head_dim up to 128: at 256
+// the two tiles' accumulators do not fit in registers)
+template <class T, int D>
+hipError_t launch_multiquery_d(const DecodeParams &p, hipStream_t stream) {
+    if (p.mq_group * p.max_query_len <= kMultiQueryRows)
+        return launch_multiquery_r<T, D, kMultiQueryRows>(p, stream);
+    if constexpr (D <= 128)
+        return launch_multiquery_r<T, D, 2 * kMultiQueryRows>(p, stream);
+    return hipErrorInvalidValue;
 }
 template <class T>
 hipError_t launch_multiquery_t(const DecodeParams &p, int head_dim, hipStream_t stream) {
@@ -1531,7 +1591,8 @@ hipError_t launch_multiquery_t(const DecodeParams &p, int head_dim, hipStream_t 
 hipError_t launch_decode_multiquery(const DecodeParams &p, int dtype, int head_dim,
                                     hipStream_t stream) {
     if (p.heads_per_group < 1 || p.heads_per_group > kMaxDecodeWaves || p.num_partitions != 1 ||
-        p.num_chunks != 0 || p.mq_group < 1 || p.mq_group * p.max_query_len > kMultiQueryRows)
+        p.num_chunks != 0 || p.mq_group < 1 ||
+        p.mq_group * p.max_query_len > 2 * kMultiQueryRows)
         return hipErrorInvalidValue;
     switch (dtype) {
         case 1: return launch_multiquery_t<F16>(p, head_dim, stream);

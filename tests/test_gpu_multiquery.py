@@ -1,7 +1,8 @@
 """GPU parity of the multi-token decode: paged_attn_prefill with few new
-tokens per sequence (max_query_len * group <= 16) and no split goes to the
-decode kernel's structure, one wave per kv head with all of the kv head's
-(new token, query head) rows in one 16-row tile and a causal limit per row.
+tokens per sequence (max_query_len * group <= 32, 16 at head_dim 256) and
+no split goes to the decode kernel's structure, one wave per kv head with
+all of the kv head's (new token, query head) rows in one or two 16-row
+tiles and a causal limit per row.
 Checked against the fp64 oracle of the multi-token attention, to the bar of
 tests/parity.py, on the same inputs and rules as the prefill tests (invalid
 lengths and block ids give NaN rows, rows past max_query_len and sequences
@@ -62,7 +63,7 @@ def takes_multiquery(B, b, max_query_len=None):
     ws = B.paged_attn_decode_workspace_bytes(b.num_seqs, b.num_q_heads, b.num_kv_heads,
                                              b.head_dim, b.block_size, b.max_blocks_per_seq,
                                              b.base.max_context_len, 0, code)
-    return mq * b.group <= 16 and ws == 0
+    return mq * b.group <= (32 if b.head_dim <= 128 else 16) and ws == 0
 
 
 def ref(b):
@@ -98,7 +99,29 @@ def test_multiquery_shapes(B, dtype, D, G, bs):
     check_close(got, ref(b), f"{dtype} D={D} G={G} bs={bs} q_len<={qmax}", dtype)
 
 
-@pytest.mark.parametrize("G,qlen", [(4, 1), (4, 2), (4, 3), (2, 5), (1, 11), (8, 1)])
+SHAPES2 = [(dt, D, G, bs) for dt in ("bf16", "f16") for D in (64, 128) for G in (1, 2, 4, 8)
+           for bs in (1, 16, 32)]
+
+
+@pytest.mark.parametrize("dtype,D,G,bs", SHAPES2)
+def test_multiquery_two_tiles(B, dtype, D, G, bs):
+    """17..32 rows per kv head: two 16-row tiles in each wave."""
+    qmax = 32 // G
+    b = batch(4050 + D + 10 * G + bs, dtype, D, G, bs, qmax)
+    assert takes_multiquery(B, b)
+    got = tensors.widen(run(B, b), dtype)
+    check_close(got, ref(b), f"{dtype} D={D} G={G} bs={bs} q_len<={qmax}", dtype)
+
+
+def test_multiquery_head_dim_256_takes_one_tile_only(B):
+    """At head_dim 256 more than 16 rows per kv head take the prefill kernel."""
+    b = batch(4090, "bf16", 256, 4, 16, 8)
+    assert not takes_multiquery(B, b)
+    check_close(tensors.widen(run(B, b), "bf16"), ref(b), "D=256, 32 rows", "bf16")
+
+
+@pytest.mark.parametrize("G,qlen", [(4, 1), (4, 2), (4, 3), (2, 5), (1, 11), (8, 1),
+                                    (4, 5), (4, 7), (2, 9), (1, 20), (8, 3)])
 def test_multiquery_below_the_tile(B, G, qlen):
     """Fewer rows than the tile holds: the rows past them are masked out and
     never written."""
@@ -153,7 +176,7 @@ def test_multiquery_invalid_device_values(B, dtype):
 def test_multiquery_unwritten_rows(B):
     """Rows past max_query_len, and every row of a sequence whose query range
     reaches past the query rows, keep what the output held."""
-    b = batch(4501, "bf16", 128, 2, 16, 8, S=6)
+    b = batch(4501, "bf16", 128, 2, 16, 12, S=6)
     want = ref(b)
     got = tensors.widen(run(B, b, max_query_len=5, out_fill=7.0), "bf16")
     q = b.query_start
@@ -195,7 +218,7 @@ def test_multiquery_many_long_contexts(B):
     """A batch large enough to need no split (256 sequences x 8 kv heads) with
     contexts of 300..900 tokens: many tiles and blocks per wave."""
     rng = np.random.default_rng(4751)
-    qlens = tuple(int(x) for x in rng.integers(0, 5, size=256))
+    qlens = tuple(int(x) for x in rng.integers(0, 9, size=256))
     lens = tuple(q + int(x) for q, x in zip(qlens, rng.integers(300, 900, size=256)))
     b = W.make_prefill(4751, dtype="bf16", num_q_heads=32, num_kv_heads=8, head_dim=128,
                        block_size=16, context_lens=lens, query_lens=qlens, poison=True)
