@@ -336,10 +336,11 @@ PAGED_KV_API int kv_cache_write(
  * structure, below); rows past max_query_len are not written, nor are the
  * rows of a sequence whose query_start range leaves [0, total_q] or
  * decreases.  Nothing out of range is read or written.
- * Few new tokens (max_query_len * num_q_heads / num_kv_heads <= 16, f16 or
- * bf16) in a batch the decode's plan does not split run the decode kernel's
- * structure, one wave per kv head (the multi-token decode): the same
- * results to rounding, with one new token the decode's bits.
+ * Few new tokens (max_query_len * num_q_heads / num_kv_heads <= 32, or 16
+ * at head_dim 256; f16 or bf16) in a batch the decode's plan does not split
+ * run the decode kernel's structure, one wave per kv head (the multi-token
+ * decode): the same results to rounding, with one new token the decode's
+ * bits.
  */
 PAGED_KV_API int paged_attn_prefill(
     const void *query, const void *key_cache, const void *value_cache,
