@@ -513,24 +513,39 @@ def bench_prefill(args) -> int:
 
 
 def bench_multi_token(args) -> int:
-    """Multi-token decode: the Llama-3-8B-shaped decode batch (its pool,
-    tables and lengths) with the last --query-len positions of every
-    sequence as new queries, through paged_attn_prefill, which with at most
-    16 (new token, query head) rows per kv head and no split runs the decode
-    kernel's structure.  Bound by HBM like the decode: the algorithmic bytes
-    are every context's K/V read once per kv head, plus the queries, outputs,
-    tables and lengths."""
+    """Multi-token decode: a decode workload's batch (its pool, tables and
+    lengths; --workload, the Llama-3-8B-shaped one by default) with the last
+    --query-len positions of every sequence as new queries, through
+    paged_attn_prefill.  With at most 32 (new token, query head) rows per kv
+    head (16 at head_dim 256) and a batch the decode plan does not split, the
+    call runs the decode kernel's multi-token instance; otherwise the prefill
+    kernel ("path" in the output says which).  Bound by HBM like the decode:
+    the algorithmic bytes are every context's K/V read once per kv head, plus
+    the queries, outputs, tables and lengths."""
     import numpy as np
     import torch
 
     import oracle
     from paged_kv_cache_467_amd import binding, tensors, workloads as W
 
-    name = "llama3_8b_gqa_bf16"
+    name = args.workload
     dev = torch.device("cuda:0")
     base = W.make_workload(name, values=False)
     S, Hq, Hkv, D = base.num_seqs, base.num_q_heads, base.num_kv_heads, base.head_dim
     ql = args.query_len
+    if ql < 1 or ql > int(base.context_lens.min()):
+        print(f"--query-len must lie in 1..{int(base.context_lens.min())} (the shortest context)",
+              file=sys.stderr)
+        return 2
+    esz = 4 if base.dtype == "f32" else 2
+    code = {"f16": binding.PAGED_KV_F16, "bf16": binding.PAGED_KV_BF16,
+            "f32": binding.PAGED_KV_F32}[base.dtype]
+    ws = binding.paged_attn_decode_workspace_bytes(S, Hq, Hkv, D, base.block_size,
+                                                   base.max_blocks_per_seq, base.max_context_len,
+                                                   0, code)
+    rows = ql * (Hq // Hkv)
+    on_decode = (base.dtype != "f32" and ws == 0 and rows <= (32 if D <= 128 else 16))
+    path = "decode kernel, multi-token instance" if on_decode else "prefill kernel"
     qs_host = np.arange(0, S * ql + 1, ql, dtype=np.int32)
     dt = tensors.TORCH_DTYPE[base.dtype]
     pool_shape = (base.num_blocks, base.block_size, Hkv, D)
@@ -551,7 +566,7 @@ def bench_multi_token(args) -> int:
         step(i)
     elapsed, avg = time_back_to_back(step, args.warmup, max(args.steps, MIN_LAUNCH_PASS))
     tokens = int(base.context_lens.sum())
-    nbytes = (tokens * Hkv * D * 2 * 2 + 2 * S * ql * Hq * D * 2
+    nbytes = (tokens * Hkv * D * 2 * esz + 2 * S * ql * Hq * D * esz
               + int(np.ceil(base.context_lens / base.block_size).sum()) * 4 + S * 4 + (S + 1) * 4)
     gbps = nbytes / (avg * 1e-3) / 1e9
     result = {
@@ -565,6 +580,7 @@ def bench_multi_token(args) -> int:
                    "num_kv_heads": Hkv, "head_dim": D, "block_size": base.block_size,
                    "pool_copies": len(copies)},
         "multi_token_ms": round(avg, 5),
+        "path": path,
         "algorithmic_bytes_per_launch": nbytes,
         "roofline": {"bound": "hbm", "achieved": round(gbps, 2), "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic": None,
@@ -576,7 +592,10 @@ def bench_multi_token(args) -> int:
         host = W.make_workload(name)
         rng = np.random.default_rng(0)
         hq = rng.standard_normal((S * ql, Hq, D)).astype(np.float32)
-        hq = (hq.view(np.uint32) >> 16).astype(np.uint16)   # bf16 bits
+        if base.dtype == "bf16":
+            hq = (hq.view(np.uint32) >> 16).astype(np.uint16)   # bf16 bits (truncated)
+        elif base.dtype == "f16":
+            hq = hq.astype(np.float16).view(np.uint16)
         orc = oracle.default()
         orc.set_threads(len(os.sched_getaffinity(0)))
         times = []
